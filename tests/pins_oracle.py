@@ -1,0 +1,349 @@
+"""Pins of the f64 oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+brute-force loop, a closed form, an invariant, a library routine or the
+hand-worked example in tests/golden.  ``test_oracle_pins.py`` runs them;
+``test_oracle_mutants.py`` plants plausible mistakes in the oracle and checks
+that at least one pin catches each.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+
+import oracle
+from oracle import brute, experts, int4, router
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def T(fmt, gs, O, C, packed, scales):
+    return SimpleNamespace(fmt=fmt, gs=gs, O=O, C=C, packed=np.asarray(packed, dtype=np.uint8).reshape(O, C // 2),
+                           scales=np.asarray(scales, dtype=np.float32))
+
+
+def rand_tensor(rng, fmt, gs, O, C):
+    ng = -(-C // gs) if (fmt == 4 and gs > 0) else 1
+    return T(fmt, gs, O, C, rng.integers(0, 256, (O, C // 2), dtype=np.uint8),
+             rng.lognormal(math.log(0.01), 0.5, O * ng).astype(np.float32))
+
+
+def pack_test(q):
+    """Test-local packer written from the layout rule: column c -> byte c//2, even c in the low nibble."""
+    q = np.asarray(q, dtype=np.uint8)
+    O, C = q.shape
+    out = np.zeros((O, C // 2), dtype=np.uint8)
+    for o in range(O):
+        for c in range(C):
+            shift = 0 if c % 2 == 0 else 4
+            out[o, c // 2] |= np.uint8(int(q[o, c]) << shift)
+    return out
+
+
+# ---------------------------------------------------------------- int4 decoding
+
+def pin_nibble_roundtrip():
+    rng = np.random.default_rng(11)
+    for (O, C) in [(1, 2), (3, 10), (7, 64), (2, 200)]:
+        q = rng.integers(0, 16, (O, C), dtype=np.uint8)
+        assert np.array_equal(int4.unpack_nibbles(pack_test(q), O, C), q)
+    allb = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = int4.unpack_nibbles(allb, 1, 512)
+    assert np.array_equal(pack_test(q), allb)
+    # byte 0x8F: column 0 holds 15 (weight +7), column 1 holds 8 (weight 0)
+    assert list(int4.unpack_nibbles(np.array([[0x8F]], np.uint8), 1, 2)[0]) == [15, 8]
+
+
+def pin_dequant_vs_brute():
+    rng = np.random.default_rng(12)
+    cases = [(2, 0, 3, 8), (4, 64, 3, 200), (4, 64, 2, 2000), (4, 6, 4, 22), (4, 2, 3, 10),
+             (4, 0, 3, 16), (4, 300, 2, 200), (4, 64, 5, 128)]
+    for fmt, gs, O, C in cases:
+        t = rand_tensor(rng, fmt, gs, O, C)
+        W = int4.dequantize(t.packed, t.scales, fmt, gs, O, C)
+        cols = range(C) if C <= 64 else sorted(set(rng.integers(0, C, 40).tolist()) | {0, C - 1, 63, 64, C - 16})
+        for o in range(O):
+            for c in cols:
+                assert W[o, c] == brute.weight(t.packed, t.scales, fmt, gs, O, C, o, c), (fmt, gs, o, c)
+
+
+def pin_group_degenerate_cases():
+    rng = np.random.default_rng(13)
+    O, C = 5, 96
+    p = rng.integers(0, 256, (O, C // 2), dtype=np.uint8)
+    s_row = rng.lognormal(-4.6, 0.5, O).astype(np.float32)
+    W_row = int4.dequantize(p, s_row, 2, 0, O, C)
+    # gs = 0 degrades to per-row
+    assert np.array_equal(int4.dequantize(p, s_row, 4, 0, O, C), W_row)
+    # gs >= C: a single group per row
+    assert np.array_equal(int4.dequantize(p, s_row, 4, 128, O, C), W_row)
+    # every group of a row sharing that row's scale is per-row
+    ng = -(-C // 64)
+    assert np.array_equal(int4.dequantize(p, np.repeat(s_row, ng), 4, 64, O, C), W_row)
+
+
+def pin_matvec_closed_forms():
+    rng = np.random.default_rng(14)
+    O, C = 4, 40
+    s = np.array([0.5, 1.0, 2.0, 0.25], np.float32)
+    x = rng.standard_normal(C)
+    zero = T(2, 0, O, C, np.full((O, C // 2), 0x88), s)
+    assert np.all(int4.matvec_rows(zero, x) == 0.0)
+    ones = T(2, 0, O, C, np.full((O, C // 2), 0x99), s)
+    assert np.allclose(int4.matvec_rows(ones, x), s.astype(np.float64) * math.fsum(x), rtol=1e-13, atol=1e-13)
+    # 0x0F: even columns +7, odd columns -8
+    alt = T(2, 0, O, C, np.full((O, C // 2), 0x0F), s)
+    e0 = np.zeros(C); e0[0] = 1.0
+    e1 = np.zeros(C); e1[1] = 1.0
+    assert np.array_equal(int4.matvec_rows(alt, e0), 7.0 * s.astype(np.float64))
+    assert np.array_equal(int4.matvec_rows(alt, e1), -8.0 * s.astype(np.float64))
+    assert np.array_equal(int4.matvec_rows(alt, np.ones(C)), -0.5 * C * s.astype(np.float64))
+    # one-hot input picks one column of a random group-wise tensor: tail group column
+    t = rand_tensor(rng, 4, 16, 3, 40)
+    ec = np.zeros(40); ec[37] = 1.0
+    col = [brute.weight(t.packed, t.scales, 4, 16, 3, 40, o, 37) for o in range(3)]
+    assert np.array_equal(int4.matvec_rows(t, ec), np.array(col))
+
+
+def pin_matvec_vs_fsum():
+    rng = np.random.default_rng(15)
+    for fmt, gs, O, C in [(2, 0, 6, 24), (4, 8, 5, 36), (4, 64, 3, 200), (2, 0, 12, 12), (4, 4, 10, 10)]:
+        t = rand_tensor(rng, fmt, gs, O, C)
+        v = rng.standard_normal(C)
+        ref = np.array(brute.matvec(t, v.tolist()))
+        got = int4.matvec_rows(t, v)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max()), (fmt, gs, O, C)
+
+
+# ---------------------------------------------------------------- activation / silu
+
+def pin_silu():
+    assert experts.silu(0.0) == 0.0
+    for z in [0.1, 0.5, 1.0, 2.0, 3.7, 10.0, 25.0]:
+        assert abs((experts.silu(z) - experts.silu(-z)) - z) <= 4e-16 * max(1.0, z)
+        assert abs(experts.silu(z) - z / (1.0 + math.exp(-z))) <= 1e-15 * z
+    assert abs(experts.silu(50.0) - 50.0) < 1e-18 * 1e6
+    assert abs(experts.silu(-50.0)) < 1e-19
+    assert experts.silu(-1000.0) == 0.0
+
+
+def pin_widen_bf16():
+    bits = np.array([0x3F80, 0xC000, 0x4049, 0x0001, 0x7F7F], np.uint16)
+    v = router.widen_activations(bits, "bf16")
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 3.140625
+    assert v[3] == 2.0 ** -133
+    assert v[4] == (2 - 2.0 ** -7) * 2.0 ** 127
+
+
+# ---------------------------------------------------------------- router
+
+def pin_logits():
+    rng = np.random.default_rng(16)
+    W = rng.normal(0, 0.02, (6, 64)).astype(np.float32)
+    x = rng.standard_normal((2, 64)).astype(np.float32).astype(np.float64)
+    L = router.router_logits(W, x)
+    for t in range(2):
+        assert L[t].tolist() == brute.logits(W, x[t].tolist())
+        assert np.allclose(L[t], W.astype(np.float64) @ x[t], rtol=1e-12, atol=1e-15)
+    onehot = np.zeros((1, 64)); onehot[0, 5] = 1.0
+    assert np.array_equal(router.router_logits(W, onehot)[0], W[:, 5].astype(np.float64))
+
+
+def pin_topk_vs_sort():
+    rng = np.random.default_rng(17)
+    for E in [1, 2, 5, 8, 64, 256]:
+        c = rng.standard_normal(E)
+        for K in sorted({1, min(2, E), min(8, E), E}):
+            assert router.select_topk(c, K) == brute.topk_by_sort(c.tolist(), K)
+            assert router.select_topk(c, K) == np.lexsort((np.arange(E), -c))[:K].tolist()
+    c = np.array([0.3, 0.7, 0.7, 0.1, 0.7, 0.3])
+    assert router.select_topk(c, 6) == [1, 2, 4, 0, 5, 3]
+    assert sorted(router.select_topk(rng.standard_normal(17), 17)) == list(range(17))
+
+
+def pin_topp_hand():
+    w = [0.5, 0.25, 0.125, 0.125]
+    assert router.finish_weights(w, 0.75, False, 1.0)[0] == 2
+    assert router.finish_weights(w, 0.7, False, 1.0)[0] == 2
+    assert router.finish_weights(w, 0.8, False, 1.0)[0] == 3
+    assert router.finish_weights(w, 0.5, False, 1.0)[0] == 1
+    assert router.finish_weights(w, 1.0, False, 1.0)[0] == 4
+    assert router.finish_weights(w, 0.0, False, 1.0)[0] == 4
+    assert router.finish_weights(w, 1e-30, False, 1.0)[0] == 1
+    n, ww = router.finish_weights(w, 0.8, True, 1.0)
+    assert n == 3 and ww == [0.5 / 0.875, 0.25 / 0.875, 0.125 / 0.875, 0.0]
+
+
+def pin_norm_and_scale():
+    rng = np.random.default_rng(18)
+    for scale in [1.0, 2.5, 0.3]:
+        w = rng.uniform(0.05, 1.0, 8).tolist()
+        n, ww = router.finish_weights(w, 0.0, True, scale)
+        assert n == 8 and abs(math.fsum(ww) - float(np.float32(scale))) <= 1e-14 * scale
+        n, ww = router.finish_weights(w, 0.0, False, scale)
+        assert ww == [v * float(np.float32(scale)) for v in w]
+
+
+def pin_bias_only_in_choice():
+    # l = [0, 0.1]; bias favours expert 0, whose weight must still be sigma(0) = 0.5
+    W = np.array([[0.0, 0.0], [0.1, 0.0]], np.float32)
+    x = np.array([[1.0, 0.0]])
+    b = np.array([0.1, 0.0], np.float32)
+    r = router.route(W, b, x, 1, 0.0, False, 1.0)[0]
+    assert r.idx == [0] and r.n == 1 and r.w64[0] == 0.5
+
+
+def pin_route_vs_brute():
+    rng = np.random.default_rng(19)
+    for trial in range(40):
+        E = int(rng.choice([4, 8, 16]))
+        D = 32
+        K = int(rng.integers(1, min(E, 8) + 1))
+        W = rng.normal(0, 0.3, (E, D)).astype(np.float32)
+        b = rng.normal(0, 0.1, E).astype(np.float32)
+        x = rng.standard_normal((2, D)).astype(np.float32).astype(np.float64)
+        topp = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
+        norm = bool(rng.integers(0, 2))
+        scale = float(rng.choice([1.0, 2.5, 0.75]))
+        rs = router.route(W, b, x, K, topp, norm, scale)
+        for t in range(2):
+            n, idx, w = brute.route(W, b, x[t].tolist(), K, topp, norm, scale)
+            assert rs[t].n == n and rs[t].idx == idx, trial
+            assert np.allclose(rs[t].w64[:n], w, rtol=1e-15, atol=0)
+            assert all(v == 0.0 for v in rs[t].w64[n:])
+
+
+# ---------------------------------------------------------------- groups and the whole layer
+
+def pin_group_build_hand():
+    mk = lambda idx: router.RouteResult(n=len(idx), idx=idx, w64=[0.0] * len(idx),
+                                        w32=np.zeros(len(idx), np.float32), logits=None, sigma=None, scores=None)
+    g = experts.build_group([mk([3, 1]), mk([1, 5]), mk([5, 3])])
+    assert g["entries"] == [3, 1, 5]
+    assert g["entry_rows"] == [[(0, 0), (2, 1)], [(0, 1), (1, 0)], [(1, 1), (2, 0)]]
+    assert g["rows"] == [(3, 0, 0), (3, 2, 1), (1, 0, 1), (1, 1, 0), (5, 1, 1), (5, 2, 0)]
+    assert g["token_rows"] == [[0, 2], [3, 4], [5, 1]]
+    r = mk([2, 7, 4])
+    r.n = 2
+    g = experts.build_group([r])
+    assert g["entries"] == [2, 7] and g["token_rows"] == [[0, 1]]
+
+
+def identity_expert(D, diag_nibble=9, scale=1.0):
+    q = np.full((D, D), 8, np.uint8)
+    np.fill_diagonal(q, diag_nibble)
+    t = T(2, 0, D, D, pack_test(q), np.full(D, scale, np.float32))
+    return SimpleNamespace(gate=t, up=t, down=t)
+
+
+def pin_layer_closed_form():
+    D = 6
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal((1, D)).astype(np.float32).astype(np.float64)
+    r = rng.standard_normal((1, D)).astype(np.float32)
+    W = rng.normal(0, 0.5, (1, D)).astype(np.float32)
+    b = np.zeros(1, np.float32)
+    ex = identity_expert(D)
+    # one expert, norm on: weight = routed_scale exactly; y = silu(x) * x elementwise
+    _, _, delta, out = experts.moe_layer(W, b, x, lambda e: ex, 1, 0.0, True, 2.5, residual=r)
+    y = np.array([v / (1.0 + math.exp(-v)) * v for v in x[0]])
+    assert np.allclose(delta[0], 2.5 * y, rtol=1e-14, atol=0)
+    assert np.allclose(out[0], r[0].astype(np.float64) + 2.5 * y, rtol=1e-14, atol=1e-15)
+    # norm off, scale 1: the weight is float32(sigma(l)) -- the route carries float32
+    _, _, delta, _ = experts.moe_layer(W, b, x, lambda e: ex, 1, 0.0, False, 1.0)
+    l = math.fsum((W[0].astype(np.float64) * x[0]).tolist())
+    w32 = float(np.float32(1.0 / (1.0 + math.exp(-l))))
+    assert np.allclose(delta[0], w32 * y, rtol=1e-14, atol=0)
+
+
+def pin_layer_linearity():
+    rng = np.random.default_rng(21)
+    D, I, E = 16, 8, 4
+    ex = {e: SimpleNamespace(gate=rand_tensor(rng, 2, 0, I, D), up=rand_tensor(rng, 4, 4, I, D),
+                             down=rand_tensor(rng, 4, 6, D, I)) for e in range(E)}
+    W = rng.normal(0, 0.3, (E, D)).astype(np.float32)
+    b = rng.normal(0, 0.1, E).astype(np.float32)
+    x = rng.standard_normal((2, D)).astype(np.float32).astype(np.float64)
+    _, _, d1, _ = experts.moe_layer(W, b, x, lambda e: ex[e], 2, 0.0, True, 1.0)
+    ex2 = {e: SimpleNamespace(gate=v.gate, up=v.up,
+                              down=T(4, 6, D, I, v.down.packed, v.down.scales * 2)) for e, v in ex.items()}
+    _, _, d2, _ = experts.moe_layer(W, b, x, lambda e: ex2[e], 2, 0.0, True, 1.0)
+    assert np.array_equal(d2, 2 * d1)
+    ex3 = {e: SimpleNamespace(gate=v.gate, up=T(4, 4, I, D, v.up.packed, v.up.scales * 4),
+                              down=v.down) for e, v in ex.items()}
+    _, _, d3, _ = experts.moe_layer(W, b, x, lambda e: ex3[e], 2, 0.0, True, 1.0)
+    assert np.array_equal(d3, 4 * d1)
+
+
+def pin_layer_vs_brute():
+    rng = np.random.default_rng(22)
+    D, I, E, K, S = 12, 6, 5, 2, 2
+    ex = {}
+    for e in range(E):
+        fmt, gs = [(2, 0), (4, 4), (4, 6)][e % 3]
+        ex[e] = SimpleNamespace(gate=rand_tensor(rng, fmt, gs, I, D), up=rand_tensor(rng, fmt, gs, I, D),
+                                down=rand_tensor(rng, fmt, gs, D, I))
+    W = rng.normal(0, 0.3, (E, D)).astype(np.float32)
+    b = rng.normal(0, 0.1, E).astype(np.float32)
+    x = rng.standard_normal((S, D)).astype(np.float32).astype(np.float64)
+    routes, _, delta, _ = experts.moe_layer(W, b, x, lambda e: ex[e], K, 0.9, True, 2.5)
+    for t in range(S):
+        n, idx, w = brute.route(W, b, x[t].tolist(), K, 0.9, True, 2.5)
+        ref = [0.0] * D
+        for k in range(n):
+            y = brute.expert(ex[idx[k]].gate, ex[idx[k]].up, ex[idx[k]].down, x[t].tolist())
+            ref = [a + float(np.float32(w[k])) * v for a, v in zip(ref, y)]
+        assert np.allclose(delta[t], ref, rtol=1e-11, atol=1e-14 * max(map(abs, ref)))
+
+
+def load_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    exs = []
+    for e in g["experts"]:
+        def t(name, O, C):
+            pk = np.array([[int(h, 16) for h in row] for row in e[name]["packed"]], np.uint8)
+            return T(e["fmt"], e["gs"], O, C, pk, e[name]["scales"])
+        exs.append(SimpleNamespace(gate=t("gate", g["I"], g["D"]), up=t("up", g["I"], g["D"]),
+                                   down=t("down", g["D"], g["I"])))
+    return g, exs
+
+
+def pin_worked_example():
+    g, exs = load_worked_example()
+    x = np.array([g["x"]])
+    W = np.array(g["router_W"], np.float32)
+    b = np.array(g["router_b"], np.float32)
+    r = np.array([g["residual"]], np.float32)
+    s = lambda z: z / (1.0 + math.exp(-z))
+    # Hand derivation.  All three logits are 0, so sigma = 1/2 and the scores are
+    # 1/2 + b = [0.5, 0.75, 0.25]: top-2 = [1, 0], weights 1/2 each, norm -> 1/2,
+    # times 2.5 -> 1.25.  Expert 1 (per-row): g = [x0, x2] = [1, 2],
+    # u = [-x1, 2*0.5*x3] = [1, 0.5], h = [s(1), 0.5 s(2)],
+    # y = 0.5*[2h0, 2h1, h0+h1, -h0].  Expert 0 (gs=2): g = [(x0+x1) + 0.5(x2+x3), 2 x2]
+    # = [1.25, 4], u = [2 x0, 0.25*4*x3] = [2, 0.5], h = [2 s(1.25), 0.5 s(4)],
+    # y = [h0, h1, h0-h1, 0].
+    h1 = [s(1.0), 0.5 * s(2.0)]
+    y1 = [h1[0], h1[1], 0.5 * (h1[0] + h1[1]), -0.5 * h1[0]]
+    h0 = [2.0 * s(1.25), 0.5 * s(4.0)]
+    y0 = [h0[0], h0[1], h0[0] - h0[1], 0.0]
+    routes, group, delta, out = experts.moe_layer(W, b, x, lambda e: exs[e], 2, 0.0, True, g["routed_scale"],
+                                                  residual=r)
+    assert routes[0].idx == [1, 0] and routes[0].n == 2
+    assert routes[0].w32.tolist() == [1.25, 1.25]
+    exp = [1.25 * a + 1.25 * c for a, c in zip(y1, y0)]
+    assert np.allclose(delta[0], exp, rtol=1e-15, atol=1e-16)
+    assert np.allclose(out[0], [rv + ev for rv, ev in zip(g["residual"], exp)], rtol=1e-15, atol=1e-15)
+    assert group["entries"] == [1, 0]
+    # top-p 0.4: prefix 0.5 >= 0.4 * 1.0 keeps one expert, renormalised to 1, times 2.5
+    routes, _, delta, _ = experts.moe_layer(W, b, x, lambda e: exs[e], 2, 0.4, True, g["routed_scale"])
+    assert routes[0].n == 1 and routes[0].w32.tolist() == [2.5, 0.0]
+    assert np.allclose(delta[0], [2.5 * v for v in y1], rtol=1e-15, atol=1e-16)
+
+
+PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}
