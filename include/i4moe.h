@@ -1,0 +1,229 @@
+/*
+ * i4moe -- decode-time int4 grouped MoE expert path for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer at decode is three calls on one HIP stream:
+ *
+ *   i4moe_route                  device router: E x D logits GEMV, sigmoid, bias-augmented
+ *                                top-K with strict tie-break, top-p, norm_topk, routed_scale,
+ *                                and the expert group (which experts run on which token rows)
+ *   i4moe_expert_group_issue     grouped W4A16 experts over that group: dual gate/up
+ *                                projection with the SiLU-gated product fused in, then the
+ *                                down projection into a per-issue slot
+ *   i4moe_expert_group_take      per token, the per-expert weighted sum in route order, the
+ *                                slots in issue order, added into the residual; no atomics
+ *
+ * Sources (web pages on the colibri int4 MoE engine):
+ *   [LOG-g4]  "Commit history of c/backend_cuda.cu", commit opening "The grouped MoE kernels
+ *             were per-row-only": fmt=4 group-wise int4, gs, O*ceil(C/gs) scales, gs even,
+ *             gs=0 per-row, fmt=2 and fmt=4 members in one launch, reject unknown formats,
+ *             upload_g carrying gs, handle 0 = not uploaded.
+ *   [LOG-tc]  same page, commit gating the TC_W4A16 branch: the grouped 3-launch decode path
+ *             (dual gate/up, silu, down).
+ *   [LOG-rt]  same page, commit "First increment of the #431 plan": the device router and its
+ *             packed route result (~68 B at K=8).
+ *   [LOG-fix] same page, "Three vendor-neutral fixes": cached tensors usable with stale host
+ *             pointers, sticky device errors consumed, a fail-after-N fault hook on compute
+ *             entry points only.
+ *   [PR342]   "cuda: COLI_GROUP_ASYNC=1 - overlap the CPU expert rows with the GPU groups at
+ *             decode", section "What": issue/take split, S<=4 small-batch groups.
+ *   [PR434]   "cuda: COLI_CUDA_RESID=1 - expert-group results stay on device", section "What":
+ *             per-expert weighting and fixed-order reduce, per-issue slots reserved at the
+ *             64-expert cap, take in issue order without atomics, failed take is fatal.
+ *
+ * Conventions for every call
+ *   - Return value: I4MOE_OK (0) or a negative I4MOE_E* code; i4moe_last_error() gives the
+ *     message of the most recent failure on that context.  A failed call enqueues nothing
+ *     unless stated otherwise, and no device error is left pending for a later call.
+ *   - Device pointers ("_dev") are plain HIP device addresses (e.g. torch tensor data_ptr()).
+ *     Host pointers are read during the call only; the caller may free or overwrite them as
+ *     soon as the call returns.
+ *   - A context is bound to one device and one stream and is not thread-safe.
+ *   - Compute calls (route, issue, take) only enqueue work; they never synchronise the host
+ *     unless a host output is requested.
+ */
+#ifndef I4MOE_H
+#define I4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Limits. */
+#define I4MOE_MAX_ROWS   64    /* expert-token rows in one issue: the 64-expert cap [PR434] */
+#define I4MOE_MAX_TOKENS 64    /* tokens S per call */
+#define I4MOE_MAX_K      64    /* top-K */
+#define I4MOE_MAX_E      1024  /* routed experts per layer */
+#define I4MOE_MAX_COLS   8192  /* columns C of an int4 tensor (D for gate/up, I for down) */
+#define I4MOE_MAX_SLOTS  16    /* issues pending before a take */
+
+/* Weight formats: the pages' own codes [LOG-g4]. */
+enum { I4MOE_FMT_ROW = 2, I4MOE_FMT_GROUP = 4 };
+
+/* Activation dtypes. */
+enum { I4MOE_DTYPE_F32 = 0, I4MOE_DTYPE_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  I4MOE_OK = 0,
+  I4MOE_EINVAL = -1,       /* bad argument, shape, handle or state                      */
+  I4MOE_ENOMEM = -2,       /* device or host allocation failed                            */
+  I4MOE_EDEVICE = -3,      /* a HIP call or kernel launch failed                          */
+  I4MOE_EUNSUPPORTED = -4, /* well-formed request outside what the kernels decode       */
+  I4MOE_EINJECTED = -5,    /* failure injected by the fail-after hook                     */
+  I4MOE_EPOISONED = -6     /* an earlier take failed; compute calls refuse until destroy */
+};
+
+typedef struct i4moe_ctx i4moe_ctx;
+typedef uint32_t i4moe_tensor;  /* 0 = invalid / not uploaded [LOG-g4] */
+
+/* Per-token route result, host side.  n = experts kept after top-p; idx[0..K) are the K
+ * selections in selection order; w[0..n) the final float32 weights, w[n..K) = 0.
+ * On the device the same record is the packed route [LOG-rt]. */
+typedef struct {
+  int32_t n;
+  int32_t idx[I4MOE_MAX_K];
+  float w[I4MOE_MAX_K];
+} i4moe_route_host;
+
+/* Explicit group for issue (host arrays of n_rows entries): each row runs expert[r] on token
+ * row token[r] of x and is weighted by weight[r].  Per token, rows are summed in the order
+ * listed.  Rows of one expert share one pass over its weights. */
+typedef struct {
+  int32_t n_rows;
+  const int32_t *expert;
+  const int32_t *token;
+  const float *weight;
+} i4moe_group;
+
+/* ---- context ---------------------------------------------------------------------------- */
+
+/* Create a context on HIP device `device`, bound to the null stream.  The fault hook starts
+ * from the environment variable I4MOE_FAIL_AFTER when it holds a non-negative integer.
+ * Errors: EINVAL (bad device, out == NULL), EDEVICE, ENOMEM. */
+int i4moe_ctx_create(int device, i4moe_ctx **out);
+
+/* Synchronise the stream and free everything the context owns.  NULL is a no-op. */
+int i4moe_ctx_destroy(i4moe_ctx *ctx);
+
+/* Bind the stream later compute calls enqueue on (a hipStream_t; NULL = null stream). */
+int i4moe_set_stream(i4moe_ctx *ctx, void *hip_stream);
+
+/* Message of the most recent failure on ctx (static text if ctx is NULL).  Never NULL. */
+const char *i4moe_last_error(const i4moe_ctx *ctx);
+
+/* ---- weights ---------------------------------------------------------------------------- */
+
+/* Upload one int4 tensor of O rows x C columns [LOG-g4].
+ *   fmt    I4MOE_FMT_ROW (gs must be 0) or I4MOE_FMT_GROUP (gs even, >= 0; gs = 0 is per-row)
+ *   packed O * C/2 bytes, row-major; byte c/2 of a row holds column c in its low nibble when
+ *          c is even, in its high nibble when c is odd; nibble q encodes the integer q - 8
+ *   scales float32: O of them (per-row) or O * ceil(C/gs) row-major [o][group] (group-wise);
+ *          the last group of a row may be narrower than gs and has its own scale
+ * C must be even and <= I4MOE_MAX_COLS; O >= 1.  Synchronous: the data is on the device when
+ * the call returns and the host buffers may then be freed or reused.
+ * Returns a handle > 0, or 0 on failure (EINVAL / EUNSUPPORTED / ENOMEM / EDEVICE in
+ * i4moe_last_error); a failed upload leaves nothing allocated. */
+i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *ctx, int fmt, int gs, int O, int C,
+                                        const uint8_t *packed, const float *scales);
+
+/* Release a tensor.  Synchronises the stream first.  Experts still bound to it become unset. */
+int i4moe_tensor_free(i4moe_ctx *ctx, i4moe_tensor t);
+
+/* Bind expert `expert` of layer `layer` to three uploaded tensors: gate and up are I x D,
+ * down is D x I, with D and I equal across the layer (and D equal to the router's D when one
+ * is uploaded).  Formats may differ between experts and between the three tensors. */
+int i4moe_set_expert(i4moe_ctx *ctx, int layer, int expert, i4moe_tensor gate, i4moe_tensor up,
+                     i4moe_tensor down);
+
+/* Upload the router of `layer`: W is E x D float32 row-major, bias E float32 (NULL = zeros)
+ * [LOG-rt].  Values must be finite.  E <= I4MOE_MAX_E.  Synchronous. */
+int i4moe_upload_router(i4moe_ctx *ctx, int layer, int E, int D, const float *W, const float *bias);
+
+/* ---- compute ---------------------------------------------------------------------------- */
+
+/* Route S tokens of x_dev ([S][D], dtype F32 or BF16, row-major, device) with the router of
+ * `layer` [LOG-rt]:
+ *   l = W x (f64 accumulation of exact products), sigma = 1/(1+exp(-l)), score = sigma + bias,
+ *   K rounds of "first strictly greater" over ascending expert index, weights sigma of the
+ *   chosen, top-p over the K in selection order (active when 0 < topp < 1), then division by
+ *   their sum when norm_topk != 0, then times routed_scale, rounded once to float32.
+ * The route and the expert group (distinct experts in first-appearance order, token-major)
+ * stay in the layer's device route buffer for i4moe_expert_group_issue.  If host_out != NULL
+ * it receives S records and the call synchronises the stream (one small copy back).
+ * Limits: 1 <= S <= I4MOE_MAX_TOKENS, 1 <= K <= min(E, I4MOE_MAX_K), S*K <= I4MOE_MAX_ROWS.
+ * Fault-hook gated.  Non-finite activations give an unspecified (but in-range) route. */
+int i4moe_route(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S, int K, float topp,
+                int norm_topk, float routed_scale, i4moe_route_host *host_out);
+
+/* Run the experts of one group over x_dev ([S][D], F32 or BF16) and keep the per-row outputs
+ * in the next free slot.  group == NULL consumes the device group of `layer` written by the
+ * latest i4moe_route of that layer (no host round trip); the route of that layer must not be
+ * recomputed before this issue has executed on the stream.  Otherwise the explicit group is
+ * used (rows <= I4MOE_MAX_ROWS, experts set, tokens < S).  Every expert the group may name
+ * must be set; with group == NULL that is every expert 0..E-1 of the layer.
+ * Returns the slot index (>= 0) or a negative code with nothing enqueued, so the caller can
+ * fall back to another path [PR342].  x_dev must stay valid until the issue has executed.
+ * Fault-hook gated. */
+int i4moe_expert_group_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S,
+                             const i4moe_group *group);
+
+/* For every token t < S and column i < D of the issued slots:
+ *   residual_dev[t][i] += sum over slots in issue order of
+ *                         (sum over the slot's rows of token t, in route order, of w * y)
+ * in float32 with a fixed order and no atomics [PR434], then frees all slots.  residual_dev is
+ * [S][D] float32 on the device, updated in place on the stream.  All pending slots must have
+ * been issued for the same D and with S equal to this S.  With no slot pending it is a no-op.
+ * On failure (including an injected one) the context is poisoned: routed experts would be
+ * dropped silently, so every later compute call returns I4MOE_EPOISONED [PR434]. */
+int i4moe_expert_group_take(i4moe_ctx *ctx, float *residual_dev, int S);
+
+/* ---- test hooks ----------------------------------------------------------------------------- */
+
+/* Fault hook [LOG-fix]: after n more successful compute calls (route, issue, take), every
+ * compute call fails with I4MOE_EINJECTED without enqueuing anything; n < 0 disables it.
+ * Uploads, binds and queries are never gated. */
+int i4moe_set_fail_after(i4moe_ctx *ctx, long long n);
+
+/* Debug taps for tests; each synchronises the stream and copies to host_dst (bytes must
+ * equal the size stated).
+ *   I4MOE_TAP_LOGITS  index ignored: f64 [S][E] logits of the latest route
+ *   I4MOE_TAP_ROUTE   index = layer: i4moe_route_host [S] of that layer's latest route
+ *   I4MOE_TAP_GROUP   index = layer: int32 [I4MOE_GROUP_WORDS] device group record of the layer
+ *                     (layout below)
+ *   I4MOE_TAP_H       index ignored: f32 [rows][I] SiLU-gated products of the latest issue
+ *   I4MOE_TAP_Y       index = slot: f32 [rows][D] down-projection rows of that pending slot */
+enum { I4MOE_TAP_LOGITS = 1, I4MOE_TAP_ROUTE = 2, I4MOE_TAP_GROUP = 3, I4MOE_TAP_H = 4, I4MOE_TAP_Y = 5 };
+int i4moe_debug_read(i4moe_ctx *ctx, int what, int index, void *host_dst, size_t bytes);
+
+/* Size in bytes a tap needs for the given layer/slot right now (0 if unavailable). */
+size_t i4moe_debug_size(i4moe_ctx *ctx, int what, int index);
+
+/* Group record layout (int32 words; row_weight holds float32 bit patterns):
+ *   [0] n_entries  [1] n_rows  [2] S  [3] reserved
+ *   entry_expert[64], entry_row0[65], row_token[64], row_expert[64], row_weight[64],
+ *   tok_row0[65], red_rows[64]
+ * Rows of entry j are entry_row0[j] .. entry_row0[j+1]-1 (an expert's rows are its tokens in
+ * ascending order); rows of token t in reduce order (route order) are
+ * red_rows[tok_row0[t] .. tok_row0[t+1]-1]. */
+#define I4MOE_GROUP_WORDS (4 + 64 + 65 + 64 + 64 + 64 + 65 + 64)
+
+/* ---- profiling ---------------------------------------------------------------------------- */
+
+/* Kernel families timed when profiling is on. */
+enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_COUNT = 4 };
+
+/* on != 0: bracket every later kernel launch with a pair of HIP events on the context's
+ * stream; on == 0 stops.  Switching resets the accumulated figures. */
+int i4moe_set_profiling(i4moe_ctx *ctx, int on);
+
+/* Synchronise, then report the total device milliseconds and launch count accumulated for one
+ * kernel family since profiling was switched on. */
+int i4moe_profile_query(i4moe_ctx *ctx, int kernel, double *total_ms, long long *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* I4MOE_H */

@@ -1,0 +1,887 @@
+// C ABI of the i4moe library: weight and router memory, route buffers, issue slots, launch
+// planning, error conventions and the test hooks.  Declarations and contracts: include/i4moe.h.
+//
+// Error conventions follow the vendor-neutral-fixes commit ("Commit history of
+// c/backend_cuda.cu"): every HIP error is consumed where it is seen so it cannot poison a
+// later healthy call, uploaded tensors never look at the caller's host buffers again, and the
+// fail-after hook gates compute entry points only.  The take is fatal on failure, as in the
+// COLI_CUDA_RESID page: a take that did not run would silently drop routed experts.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace i4moe;
+
+namespace {
+
+struct Tensor {
+  uint8_t *q = nullptr;
+  float *s = nullptr;
+  TensorDesc desc{};
+  int fmt = 0;
+};
+
+struct Layer {
+  int E = 0, D = 0, I = 0;             // router experts; model dim; expert intermediate
+  float *W = nullptr, *b = nullptr;    // router
+  std::vector<i4moe_tensor> gate, up, down;
+  TensorDesc *d_tab = nullptr;         // [3][kMaxE]: gate, up, down descriptors
+  std::vector<TensorDesc> h_tab;       // host copy of d_tab
+  RouteTok *d_route = nullptr;         // [kTokens]
+  GroupDev *d_group = nullptr;
+  bool routed = false;
+  int route_S = 0, route_K = 0;
+};
+
+struct SlotInfo {
+  int S = 0, D = 0, rows = 0;
+};
+
+struct ProfRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+
+struct Plan {
+  int V = 4, P = 1;
+  bool gen = false;
+  int tile_rows = 1, tiles = 1, blocks = 1;
+};
+
+}  // namespace
+
+struct i4moe_ctx {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  std::string err;
+  uint32_t next_handle = 1;
+  std::map<uint32_t, Tensor> tensors;
+  std::map<int, Layer> layers;
+
+  double *d_partial = nullptr;
+  size_t partial_cap = 0;  // doubles
+  double *d_logits = nullptr;
+  size_t logits_cap = 0;   // doubles
+  unsigned *d_counter = nullptr;
+
+  float *d_h = nullptr;    // [kRows][h_ld]
+  int h_ld = 0;
+  float *d_y = nullptr;    // [kSlots][kRows][y_ld]
+  int y_ld = 0;
+  GroupDev *d_slot_groups = nullptr;  // [kSlots]
+  SlotInfo slots[kSlots];
+  int nslots = 0;
+
+  int last_route_S = 0, last_route_E = 0;
+  int last_issue_rows = 0, last_issue_I = 0;
+
+  long long fail_after = -1, calls = 0;
+  bool poisoned = false;
+
+  bool profiling = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<ProfRec> recs;
+  double prof_ms[I4MOE_K_COUNT] = {0, 0, 0, 0};
+  long long prof_n[I4MOE_K_COUNT] = {0, 0, 0, 0};
+};
+
+namespace {
+
+int fail(i4moe_ctx *c, int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return code;
+}
+
+// Consume the pending device error so it cannot leak into the next call.
+int hip_fail(i4moe_ctx *c, hipError_t e, const char *what) {
+  (void)hipGetLastError();
+  return fail(c, e == hipErrorOutOfMemory ? I4MOE_ENOMEM : I4MOE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool ensure_device(i4moe_ctx *c) {
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess && cur == c->device) return true;
+  return hipSetDevice(c->device) == hipSuccess;
+}
+
+void dfree(void *p) {
+  if (p) (void)hipFree(p);
+}
+
+template <class T>
+hipError_t dalloc(T **p, size_t bytes) {
+  *p = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(p), bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+  }
+  return e;
+}
+
+int gate_compute(i4moe_ctx *c) {
+  if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
+  if (c->fail_after >= 0 && c->calls >= c->fail_after)
+    return fail(c, I4MOE_EINJECTED, "injected failure (fail-after %lld)", c->fail_after);
+  return I4MOE_OK;
+}
+
+hipEvent_t get_event(i4moe_ctx *c) {
+  if (!c->ev_pool.empty()) {
+    hipEvent_t e = c->ev_pool.back();
+    c->ev_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+// Launch wrapper: brackets the launch with events when profiling.
+template <class F>
+hipError_t timed(i4moe_ctx *c, int kernel, F &&f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (c->profiling) {
+    a = get_event(c);
+    b = get_event(c);
+    if (a && b) (void)hipEventRecord(a, c->stream);
+  }
+  hipError_t e = f();
+  if (c->profiling && a && b) {
+    (void)hipEventRecord(b, c->stream);
+    c->recs.push_back({kernel, a, b});
+  } else {
+    if (a) c->ev_pool.push_back(a);
+    if (b) c->ev_pool.push_back(b);
+  }
+  return e;
+}
+
+void drain_profile(i4moe_ctx *c) {
+  for (auto &r : c->recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      c->prof_ms[r.kernel] += ms;
+      c->prof_n[r.kernel] += 1;
+    } else {
+      (void)hipGetLastError();
+    }
+    c->ev_pool.push_back(r.a);
+    c->ev_pool.push_back(r.b);
+  }
+  c->recs.clear();
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Scratch for S*K <= kRows rows of the largest D and I seen.  Grows only with no issue pending.
+int ensure_rows_scratch(i4moe_ctx *c, int D, int I) {
+  const int need_h = round_up(I, 64), need_y = round_up(D, 64);
+  if (need_h <= c->h_ld && need_y <= c->y_ld) return I4MOE_OK;
+  if (c->nslots > 0) return fail(c, I4MOE_EINVAL, "cannot grow issue scratch while %d issue(s) are pending", c->nslots);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  const int h_ld = need_h > c->h_ld ? need_h : c->h_ld;
+  const int y_ld = need_y > c->y_ld ? need_y : c->y_ld;
+  float *h = nullptr, *y = nullptr;
+  if ((e = dalloc(&h, sizeof(float) * (size_t)kRows * h_ld)) != hipSuccess) return hip_fail(c, e, "hipMalloc(h)");
+  if ((e = dalloc(&y, sizeof(float) * (size_t)kSlots * kRows * y_ld)) != hipSuccess) {
+    dfree(h);
+    return hip_fail(c, e, "hipMalloc(y)");
+  }
+  dfree(c->d_h);
+  dfree(c->d_y);
+  c->d_h = h;
+  c->d_y = y;
+  c->h_ld = h_ld;
+  c->y_ld = y_ld;
+  return I4MOE_OK;
+}
+
+int ensure_route_scratch(i4moe_ctx *c, size_t partial, size_t logits) {
+  if (partial <= c->partial_cap && logits <= c->logits_cap) return I4MOE_OK;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  const size_t pc = partial > c->partial_cap ? partial : c->partial_cap;
+  const size_t lc = logits > c->logits_cap ? logits : c->logits_cap;
+  double *p = nullptr, *l = nullptr;
+  if ((e = dalloc(&p, sizeof(double) * pc)) != hipSuccess) return hip_fail(c, e, "hipMalloc(partials)");
+  if ((e = dalloc(&l, sizeof(double) * lc)) != hipSuccess) {
+    dfree(p);
+    return hip_fail(c, e, "hipMalloc(logits)");
+  }
+  dfree(c->d_partial);
+  dfree(c->d_logits);
+  c->d_partial = p;
+  c->d_logits = l;
+  c->partial_cap = pc;
+  c->logits_cap = lc;
+  return I4MOE_OK;
+}
+
+int ensure_layer_tables(i4moe_ctx *c, Layer &L) {
+  if (L.d_tab) return I4MOE_OK;
+  hipError_t e;
+  if ((e = dalloc(&L.d_tab, sizeof(TensorDesc) * 3 * kMaxE)) != hipSuccess) return hip_fail(c, e, "hipMalloc(table)");
+  L.h_tab.assign(3 * kMaxE, TensorDesc{});
+  e = hipMemcpyAsync(L.d_tab, L.h_tab.data(), sizeof(TensorDesc) * 3 * kMaxE, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "table init");
+  return I4MOE_OK;
+}
+
+int ensure_layer_route(i4moe_ctx *c, Layer &L) {
+  if (L.d_route) return I4MOE_OK;
+  hipError_t e;
+  if ((e = dalloc(&L.d_route, sizeof(RouteTok) * kTokens)) != hipSuccess) return hip_fail(c, e, "hipMalloc(route)");
+  if ((e = dalloc(&L.d_group, sizeof(GroupDev))) != hipSuccess) {
+    dfree(L.d_route);
+    L.d_route = nullptr;
+    return hip_fail(c, e, "hipMalloc(group)");
+  }
+  return I4MOE_OK;
+}
+
+int write_table_entry(i4moe_ctx *c, Layer &L, int which, int expert) {
+  const size_t i = (size_t)which * kMaxE + expert;
+  hipError_t e = hipMemcpyAsync(L.d_tab + i, &L.h_tab[i], sizeof(TensorDesc), hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "table update");
+  return I4MOE_OK;
+}
+
+// Pick the per-lane span V (dwords) and pass count P for rows of C columns, then tile the rows.
+Plan plan_proj(int C, int O, int max_rows, bool dual, const std::vector<int> &group_sizes) {
+  const int RD = (C + 7) / 8;
+  Plan best;
+  double best_key = -1.0;
+  for (int V = 4; V >= 1; --V) {
+    if (V == 3 && RD % 3 != 0) continue;
+    const int P = (RD + 64 * V - 1) / (64 * V);
+    if (P > 4) continue;
+    bool gen = false;
+    for (int gs : group_sizes)
+      if (gs % (8 * V) != 0) gen = true;
+    const double eff = (double)RD / (64.0 * V * P);
+    const double key = (gen ? 0.0 : 2.0) + eff;
+    if (key > best_key + 1e-12) {
+      best_key = key;
+      best.V = V;
+      best.P = P;
+      best.gen = gen;
+    }
+  }
+  const int RB = rows_per_step(best.V, best.P, dual ? 2 : 1);
+  const long long units = (long long)max_rows * O;
+  int tr = (int)((units + 4095) / 4096);
+  tr = round_up(tr < RB ? RB : tr, RB);
+  best.tile_rows = tr;
+  best.tiles = (O + tr - 1) / tr;
+  const long long waves = (long long)max_rows * best.tiles;
+  best.blocks = (int)((waves + 3) / 4);
+  return best;
+}
+
+Layer *find_layer(i4moe_ctx *c, int layer) {
+  auto it = c->layers.find(layer);
+  return it == c->layers.end() ? nullptr : &it->second;
+}
+
+bool all_finite(const float *p, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int i4moe_ctx_create(int device, i4moe_ctx **out) {
+  if (!out) return I4MOE_EINVAL;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) {
+    (void)hipGetLastError();
+    return I4MOE_EDEVICE;
+  }
+  if (device < 0 || device >= n) return I4MOE_EINVAL;
+  if (hipSetDevice(device) != hipSuccess) {
+    (void)hipGetLastError();
+    return I4MOE_EDEVICE;
+  }
+  i4moe_ctx *c = new (std::nothrow) i4moe_ctx();
+  if (!c) return I4MOE_ENOMEM;
+  c->device = device;
+  hipError_t e = dalloc(&c->d_counter, sizeof(unsigned) * 64);
+  if (e == hipSuccess) e = dalloc(&c->d_slot_groups, sizeof(GroupDev) * kSlots);
+  if (e == hipSuccess) e = hipMemset(c->d_counter, 0, sizeof(unsigned) * 64);
+  if (e == hipSuccess) e = hipMemset(c->d_slot_groups, 0, sizeof(GroupDev) * kSlots);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    dfree(c->d_counter);
+    dfree(c->d_slot_groups);
+    delete c;
+    return e == hipErrorOutOfMemory ? I4MOE_ENOMEM : I4MOE_EDEVICE;
+  }
+  if (const char *fa = std::getenv("I4MOE_FAIL_AFTER")) {
+    char *end = nullptr;
+    const long long v = std::strtoll(fa, &end, 10);
+    if (end && end != fa && *end == '\0' && v >= 0) c->fail_after = v;
+  }
+  *out = c;
+  return I4MOE_OK;
+}
+
+int i4moe_ctx_destroy(i4moe_ctx *c) {
+  if (!c) return I4MOE_OK;
+  ensure_device(c);
+  (void)hipStreamSynchronize(c->stream);
+  for (auto &kv : c->tensors) {
+    dfree(kv.second.q);
+    dfree(kv.second.s);
+  }
+  for (auto &kv : c->layers) {
+    Layer &L = kv.second;
+    dfree(L.W);
+    dfree(L.b);
+    dfree(L.d_tab);
+    dfree(L.d_route);
+    dfree(L.d_group);
+  }
+  dfree(c->d_partial);
+  dfree(c->d_logits);
+  dfree(c->d_counter);
+  dfree(c->d_h);
+  dfree(c->d_y);
+  dfree(c->d_slot_groups);
+  for (auto &r : c->recs) {
+    c->ev_pool.push_back(r.a);
+    c->ev_pool.push_back(r.b);
+  }
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+  (void)hipGetLastError();
+  delete c;
+  return I4MOE_OK;
+}
+
+int i4moe_set_stream(i4moe_ctx *c, void *stream) {
+  if (!c) return I4MOE_EINVAL;
+  c->stream = reinterpret_cast<hipStream_t>(stream);
+  return I4MOE_OK;
+}
+
+const char *i4moe_last_error(const i4moe_ctx *c) {
+  if (!c) return "no context";
+  return c->err.c_str();
+}
+
+i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, int C, const uint8_t *packed,
+                                        const float *scales) {
+  if (!c) return 0;
+  if (fmt != I4MOE_FMT_ROW && fmt != I4MOE_FMT_GROUP) {
+    fail(c, I4MOE_EUNSUPPORTED, "unsupported weight format %d (only 2 = per-row and 4 = group-wise int4)", fmt);
+    return 0;
+  }
+  if (fmt == I4MOE_FMT_ROW && gs != 0) {
+    fail(c, I4MOE_EINVAL, "per-row tensors take gs = 0 (got %d)", gs);
+    return 0;
+  }
+  if (fmt == I4MOE_FMT_GROUP && (gs < 0 || gs % 2 != 0)) {
+    fail(c, I4MOE_EINVAL, "group size must be even and >= 0 (got %d)", gs);
+    return 0;
+  }
+  if (O < 1 || C < 2 || C % 2 != 0) {
+    fail(c, I4MOE_EINVAL, "bad tensor shape %d x %d (C must be even)", O, C);
+    return 0;
+  }
+  if (C > kMaxCols) {
+    fail(c, I4MOE_EUNSUPPORTED, "C = %d exceeds %d columns", C, kMaxCols);
+    return 0;
+  }
+  if (!packed || !scales) {
+    fail(c, I4MOE_EINVAL, "packed and scales must be non-NULL");
+    return 0;
+  }
+  const int row_bytes = round_up(C / 2, 16);
+  const size_t qbytes = (size_t)O * row_bytes + 64;
+  if (qbytes > (size_t)0x7fffffff) {
+    fail(c, I4MOE_EUNSUPPORTED, "tensor too large (%zu bytes)", qbytes);
+    return 0;
+  }
+  const int ng = (fmt == I4MOE_FMT_GROUP && gs > 0) ? (C + gs - 1) / gs : 1;
+  if (!ensure_device(c)) {
+    hip_fail(c, hipErrorInvalidDevice, "hipSetDevice");
+    return 0;
+  }
+  Tensor t;
+  hipError_t e = dalloc(&t.q, qbytes);
+  if (e != hipSuccess) {
+    hip_fail(c, e, "hipMalloc(weights)");
+    return 0;
+  }
+  if ((e = dalloc(&t.s, sizeof(float) * (size_t)O * ng)) != hipSuccess) {
+    dfree(t.q);
+    hip_fail(c, e, "hipMalloc(scales)");
+    return 0;
+  }
+  e = hipMemsetAsync(t.q, 0x88, qbytes, c->stream);  // padding decodes to weight 0
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(t.q, row_bytes, packed, C / 2, C / 2, O, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(t.s, scales, sizeof(float) * (size_t)O * ng, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    dfree(t.q);
+    dfree(t.s);
+    hip_fail(c, e, "upload copy");
+    return 0;
+  }
+  t.fmt = fmt;
+  t.desc.q = t.q;
+  t.desc.s = t.s;
+  t.desc.O = O;
+  t.desc.C = C;
+  t.desc.row_bytes = row_bytes;
+  t.desc.gs = ng > 1 ? gs : 0;
+  t.desc.ng = ng;
+  t.desc.pad = 0;
+  const uint32_t h = c->next_handle++;
+  c->tensors[h] = t;
+  return h;
+}
+
+int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
+  if (!c) return I4MOE_EINVAL;
+  auto it = c->tensors.find(h);
+  if (it == c->tensors.end()) return fail(c, I4MOE_EINVAL, "unknown tensor handle %u", h);
+  ensure_device(c);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  for (auto &kv : c->layers) {
+    Layer &L = kv.second;
+    std::vector<i4moe_tensor> *v[3] = {&L.gate, &L.up, &L.down};
+    for (size_t x = 0; x < L.gate.size(); ++x) {
+      bool hit = false;
+      for (int w = 0; w < 3; ++w) hit = hit || (*v[w])[x] == h;
+      if (!hit) continue;
+      for (int w = 0; w < 3; ++w) {
+        (*v[w])[x] = 0;
+        L.h_tab[(size_t)w * kMaxE + x] = TensorDesc{};
+        int rc = write_table_entry(c, L, w, (int)x);
+        if (rc) return rc;
+      }
+    }
+  }
+  dfree(it->second.q);
+  dfree(it->second.s);
+  c->tensors.erase(it);
+  return I4MOE_OK;
+}
+
+int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
+  if (!c) return I4MOE_EINVAL;
+  if (layer < 0 || expert < 0 || expert >= kMaxE) return fail(c, I4MOE_EINVAL, "bad layer %d / expert %d", layer, expert);
+  auto tg = c->tensors.find(gate), tu = c->tensors.find(up), td = c->tensors.find(down);
+  if (tg == c->tensors.end() || tu == c->tensors.end() || td == c->tensors.end())
+    return fail(c, I4MOE_EINVAL, "unknown tensor handle");
+  const TensorDesc &G = tg->second.desc, &U = tu->second.desc, &Dn = td->second.desc;
+  const int I = G.O, D = G.C;
+  if (U.O != I || U.C != D || Dn.O != D || Dn.C != I)
+    return fail(c, I4MOE_EINVAL, "expert shapes: gate %dx%d, up %dx%d, down %dx%d (need I x D, I x D, D x I)", G.O, G.C,
+                U.O, U.C, Dn.O, Dn.C);
+  Layer &L = c->layers[layer];
+  if ((L.D && L.D != D) || (L.I && L.I != I))
+    return fail(c, I4MOE_EINVAL, "layer %d has D=%d I=%d, expert has D=%d I=%d", layer, L.D, L.I, D, I);
+  if (L.E && expert >= L.E) return fail(c, I4MOE_EINVAL, "expert %d >= router E=%d", expert, L.E);
+  ensure_device(c);
+  int rc = ensure_rows_scratch(c, D, I);
+  if (rc) return rc;
+  if ((rc = ensure_layer_tables(c, L))) return rc;
+  L.D = D;
+  L.I = I;
+  if ((int)L.gate.size() <= expert) {
+    L.gate.resize(expert + 1, 0);
+    L.up.resize(expert + 1, 0);
+    L.down.resize(expert + 1, 0);
+  }
+  L.gate[expert] = gate;
+  L.up[expert] = up;
+  L.down[expert] = down;
+  const TensorDesc *d[3] = {&G, &U, &Dn};
+  for (int w = 0; w < 3; ++w) {
+    L.h_tab[(size_t)w * kMaxE + expert] = *d[w];
+    if ((rc = write_table_entry(c, L, w, expert))) return rc;
+  }
+  return I4MOE_OK;
+}
+
+int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, const float *bias) {
+  if (!c) return I4MOE_EINVAL;
+  if (layer < 0 || E < 1 || E > kMaxE || D < 1 || !W) return fail(c, I4MOE_EINVAL, "bad router arguments");
+  if ((size_t)E * D > ((size_t)1 << 28)) return fail(c, I4MOE_EUNSUPPORTED, "router too large");
+  Layer &L = c->layers[layer];
+  bool any_expert = false;
+  for (i4moe_tensor g : L.gate) any_expert = any_expert || g != 0;
+  if (any_expert && L.D != D) return fail(c, I4MOE_EINVAL, "router D=%d but layer experts have D=%d", D, L.D);
+  if ((int)L.gate.size() > E) {
+    for (size_t x = E; x < L.gate.size(); ++x)
+      if (L.gate[x]) return fail(c, I4MOE_EINVAL, "expert %zu is set but router E=%d", x, E);
+  }
+  if (!all_finite(W, (size_t)E * D) || (bias && !all_finite(bias, E)))
+    return fail(c, I4MOE_EINVAL, "router weights and bias must be finite");
+  ensure_device(c);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  int rc = ensure_layer_route(c, L);
+  if (rc) return rc;
+  float *dW = nullptr, *db = nullptr;
+  if ((e = dalloc(&dW, sizeof(float) * (size_t)E * D)) != hipSuccess) return hip_fail(c, e, "hipMalloc(router)");
+  if ((e = dalloc(&db, sizeof(float) * E)) != hipSuccess) {
+    dfree(dW);
+    return hip_fail(c, e, "hipMalloc(bias)");
+  }
+  std::vector<float> zeros;
+  if (!bias) {
+    zeros.assign(E, 0.f);
+    bias = zeros.data();
+  }
+  e = hipMemcpyAsync(dW, W, sizeof(float) * (size_t)E * D, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(db, bias, sizeof(float) * E, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    dfree(dW);
+    dfree(db);
+    return hip_fail(c, e, "router copy");
+  }
+  dfree(L.W);
+  dfree(L.b);
+  L.W = dW;
+  L.b = db;
+  L.E = E;
+  L.D = D;
+  L.routed = false;
+  return I4MOE_OK;
+}
+
+int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
+                float routed_scale, i4moe_route_host *host_out) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->W) return fail(c, I4MOE_EINVAL, "layer %d has no router", layer);
+  if (!x_dev) return fail(c, I4MOE_EINVAL, "x_dev is NULL");
+  if (dtype != I4MOE_DTYPE_F32 && dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", dtype);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  if (K < 1 || K > L->E || K > kMaxK) return fail(c, I4MOE_EINVAL, "K=%d outside 1..min(E=%d, %d)", K, L->E, kMaxK);
+  if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
+  if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
+  ensure_device(c);
+  int splits = (1024 + L->E - 1) / L->E;
+  const int max_split = L->D / 256 > 1 ? L->D / 256 : 1;
+  if (splits > max_split) splits = max_split;
+  if (splits > 16) splits = 16;
+  if (splits < 1) splits = 1;
+  if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
+  RouteArgs a{};
+  a.W = L->W;
+  a.bias = L->b;
+  a.x = x_dev;
+  a.partial = c->d_partial;
+  a.logits = c->d_logits;
+  a.counter = c->d_counter;
+  a.route = L->d_route;
+  a.group = L->d_group;
+  a.E = L->E;
+  a.D = L->D;
+  a.S = S;
+  a.K = K;
+  a.x_bf16 = dtype == I4MOE_DTYPE_BF16;
+  a.splits = splits;
+  a.cols_per_split = (L->D + splits - 1) / splits;
+  a.norm_topk = norm_topk ? 1 : 0;
+  a.topp = topp;
+  a.routed_scale = routed_scale;
+  hipError_t e = timed(c, I4MOE_K_ROUTE, [&] { return launch_route(a, c->stream); });
+  if (e != hipSuccess) return hip_fail(c, e, "route launch");
+  L->routed = true;
+  L->route_S = S;
+  L->route_K = K;
+  c->last_route_S = S;
+  c->last_route_E = L->E;
+  c->calls++;
+  if (host_out) {
+    e = hipMemcpyAsync(host_out, L->d_route, sizeof(RouteTok) * S, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "route copy back");
+  }
+  return I4MOE_OK;
+}
+
+int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->D || !L->I || !L->d_tab) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
+  if (!x_dev) return fail(c, I4MOE_EINVAL, "x_dev is NULL");
+  if (dtype != I4MOE_DTYPE_F32 && dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", dtype);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  if (reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 8 : 4) != 0)
+    return fail(c, I4MOE_EINVAL, "x_dev must be %d-byte aligned", dtype == I4MOE_DTYPE_F32 ? 8 : 4);
+  if (c->nslots >= kSlots) return fail(c, I4MOE_EINVAL, "%d issues pending; take before issuing more", kSlots);
+  if (c->nslots > 0 && (c->slots[0].S != S || c->slots[0].D != L->D))
+    return fail(c, I4MOE_EINVAL, "pending issues have S=%d D=%d; this issue has S=%d D=%d", c->slots[0].S,
+                c->slots[0].D, S, L->D);
+  ensure_device(c);
+
+  // The experts this issue may touch decide the kernel variant.
+  std::vector<int> gs_in, gs_dn;
+  auto note = [&](int e) {
+    const TensorDesc &g = L->h_tab[e], &u = L->h_tab[kMaxE + e], &d = L->h_tab[2 * kMaxE + e];
+    if (g.ng > 1) gs_in.push_back(g.gs);
+    if (u.ng > 1) gs_in.push_back(u.gs);
+    if (d.ng > 1) gs_dn.push_back(d.gs);
+  };
+  const int s = c->nslots;
+  GroupDev *slot_group = c->d_slot_groups + s;
+  int max_rows = 0;
+  const GroupDev *src = nullptr;
+  GroupDev *copy = nullptr;
+  GroupDev hg;
+  if (!group) {
+    if (!L->routed) return fail(c, I4MOE_EINVAL, "layer %d has no device route; call i4moe_route first", layer);
+    if (L->route_S != S) return fail(c, I4MOE_EINVAL, "route has S=%d, issue has S=%d", L->route_S, S);
+    if ((int)L->gate.size() < L->E) return fail(c, I4MOE_EINVAL, "layer %d: experts 0..%d must all be set", layer, L->E - 1);
+    for (int e = 0; e < L->E; ++e) {
+      if (!L->gate[e]) return fail(c, I4MOE_EINVAL, "layer %d: expert %d is not set", layer, e);
+      note(e);
+    }
+    max_rows = S * L->route_K;
+    src = L->d_group;
+    copy = slot_group;
+  } else {
+    const int n = group->n_rows;
+    if (n < 1 || n > kRows || !group->expert || !group->token || !group->weight)
+      return fail(c, I4MOE_EINVAL, "explicit group needs 1..%d rows and non-NULL arrays", kRows);
+    std::memset(&hg, 0, sizeof hg);
+    int order[kRows];
+    int n_ent = 0, ent_of[kRows];
+    for (int r = 0; r < n; ++r) {
+      const int e = group->expert[r], t = group->token[r];
+      if (e < 0 || e >= (int)L->gate.size() || !L->gate[e])
+        return fail(c, I4MOE_EINVAL, "group row %d: expert %d is not set", r, e);
+      if (t < 0 || t >= S) return fail(c, I4MOE_EINVAL, "group row %d: token %d outside 0..%d", r, t, S - 1);
+      if (!std::isfinite(group->weight[r])) return fail(c, I4MOE_EINVAL, "group row %d: weight not finite", r);
+      int j = 0;
+      while (j < n_ent && hg.entry_expert[j] != e) ++j;
+      if (j == n_ent) hg.entry_expert[n_ent++] = e;
+      ent_of[r] = j;
+      note(e);
+    }
+    // rows entry-major, listed order inside an entry
+    int pos = 0;
+    for (int j = 0; j < n_ent; ++j) {
+      hg.entry_row0[j] = pos;
+      for (int r = 0; r < n; ++r)
+        if (ent_of[r] == j) order[r] = pos++;
+    }
+    hg.entry_row0[n_ent] = pos;
+    for (int r = 0; r < n; ++r) {
+      hg.row_token[order[r]] = group->token[r];
+      hg.row_expert[order[r]] = group->expert[r];
+      hg.row_weight[order[r]] = group->weight[r];
+    }
+    // reduce order per token: listed order
+    int q = 0;
+    for (int t = 0; t < S; ++t) {
+      hg.tok_row0[t] = q;
+      for (int r = 0; r < n; ++r)
+        if (group->token[r] == t) hg.red_rows[q++] = order[r];
+    }
+    hg.tok_row0[S] = q;
+    hg.n_entries = n_ent;
+    hg.n_rows = n;
+    hg.S = S;
+    max_rows = n;
+    src = slot_group;
+    copy = nullptr;
+  }
+
+  const Plan pd = plan_proj(L->D, L->I, max_rows, true, gs_in);
+  const Plan pn = plan_proj(L->I, L->D, max_rows, false, gs_dn);
+  ProjArgs ad{};
+  ad.group = src;
+  ad.group_copy = copy;
+  ad.tA = L->d_tab;
+  ad.tB = L->d_tab + kMaxE;
+  ad.act = x_dev;
+  ad.act_ld = L->D;
+  ad.act_bf16 = dtype == I4MOE_DTYPE_BF16;
+  ad.out = c->d_h;
+  ad.out_ld = c->h_ld;
+  ad.O = L->I;
+  ad.C = L->D;
+  ad.tiles = pd.tiles;
+  ad.tile_rows = pd.tile_rows;
+  ProjArgs an{};
+  an.group = slot_group;
+  an.group_copy = nullptr;
+  an.tA = L->d_tab + 2 * kMaxE;
+  an.tB = nullptr;
+  an.act = c->d_h;
+  an.act_ld = c->h_ld;
+  an.act_bf16 = 0;
+  an.out = c->d_y + (size_t)s * kRows * c->y_ld;
+  an.out_ld = c->y_ld;
+  an.O = L->D;
+  an.C = L->I;
+  an.tiles = pn.tiles;
+  an.tile_rows = pn.tile_rows;
+
+  hipError_t e = hipSuccess;
+  if (group) e = launch_group_store(hg, slot_group, c->stream);
+  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&] { return launch_dual(pd.V, pd.P, pd.gen, ad, pd.blocks, c->stream); });
+  if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&] { return launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream); });
+  if (e != hipSuccess) return hip_fail(c, e, "issue launch");
+  c->slots[s].S = S;
+  c->slots[s].D = L->D;
+  c->slots[s].rows = max_rows;
+  c->nslots = s + 1;
+  c->last_issue_rows = max_rows;
+  c->last_issue_I = L->I;
+  c->calls++;
+  return s;
+}
+
+int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
+  if (!c) return I4MOE_EINVAL;
+  if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
+  int rc = gate_compute(c);
+  if (rc) {
+    c->poisoned = true;
+    return rc;
+  }
+  if (c->nslots == 0) {
+    c->calls++;
+    return I4MOE_OK;
+  }
+  if (!residual_dev || S != c->slots[0].S) {
+    c->poisoned = true;
+    return fail(c, I4MOE_EINVAL, "take: residual NULL or S=%d differs from the issued S=%d", S, c->slots[0].S);
+  }
+  ensure_device(c);
+  TakeArgs a{};
+  for (int s = 0; s < c->nslots; ++s) {
+    a.groups[s] = c->d_slot_groups + s;
+    a.y[s] = c->d_y + (size_t)s * kRows * c->y_ld;
+  }
+  a.resid = residual_dev;
+  a.nslots = c->nslots;
+  a.y_ld = c->y_ld;
+  a.S = S;
+  a.D = c->slots[0].D;
+  hipError_t e = timed(c, I4MOE_K_TAKE, [&] { return launch_take(a, c->stream); });
+  if (e != hipSuccess) {
+    c->poisoned = true;
+    return hip_fail(c, e, "take launch");
+  }
+  c->nslots = 0;
+  c->calls++;
+  return I4MOE_OK;
+}
+
+int i4moe_set_fail_after(i4moe_ctx *c, long long n) {
+  if (!c) return I4MOE_EINVAL;
+  c->fail_after = n < 0 ? -1 : n;
+  c->calls = 0;
+  return I4MOE_OK;
+}
+
+size_t i4moe_debug_size(i4moe_ctx *c, int what, int index) {
+  if (!c) return 0;
+  switch (what) {
+    case I4MOE_TAP_LOGITS:
+      return sizeof(double) * (size_t)c->last_route_S * c->last_route_E;
+    case I4MOE_TAP_ROUTE: {
+      Layer *L = find_layer(c, index);
+      return (L && L->routed) ? sizeof(RouteTok) * L->route_S : 0;
+    }
+    case I4MOE_TAP_GROUP: {
+      Layer *L = find_layer(c, index);
+      return (L && L->routed) ? sizeof(GroupDev) : 0;
+    }
+    case I4MOE_TAP_H:
+      return sizeof(float) * (size_t)c->last_issue_rows * c->last_issue_I;
+    case I4MOE_TAP_Y:
+      return (index >= 0 && index < c->nslots) ? sizeof(float) * (size_t)c->slots[index].rows * c->slots[index].D : 0;
+    default:
+      return 0;
+  }
+}
+
+int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t bytes) {
+  if (!c || !host_dst) return I4MOE_EINVAL;
+  const size_t need = i4moe_debug_size(c, what, index);
+  if (need == 0 || bytes != need) return fail(c, I4MOE_EINVAL, "tap %d/%d: need %zu bytes, got %zu", what, index, need, bytes);
+  ensure_device(c);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  if (what == I4MOE_TAP_LOGITS) {
+    e = hipMemcpy(host_dst, c->d_logits, bytes, hipMemcpyDeviceToHost);
+  } else if (what == I4MOE_TAP_ROUTE) {
+    e = hipMemcpy(host_dst, find_layer(c, index)->d_route, bytes, hipMemcpyDeviceToHost);
+  } else if (what == I4MOE_TAP_GROUP) {
+    e = hipMemcpy(host_dst, find_layer(c, index)->d_group, bytes, hipMemcpyDeviceToHost);
+  } else if (what == I4MOE_TAP_H) {
+    e = hipMemcpy2D(host_dst, sizeof(float) * c->last_issue_I, c->d_h, sizeof(float) * c->h_ld,
+                    sizeof(float) * c->last_issue_I, c->last_issue_rows, hipMemcpyDeviceToHost);
+  } else {
+    const SlotInfo &si = c->slots[index];
+    e = hipMemcpy2D(host_dst, sizeof(float) * si.D, c->d_y + (size_t)index * kRows * c->y_ld, sizeof(float) * c->y_ld,
+                    sizeof(float) * si.D, si.rows, hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) return hip_fail(c, e, "tap copy");
+  return I4MOE_OK;
+}
+
+int i4moe_set_profiling(i4moe_ctx *c, int on) {
+  if (!c) return I4MOE_EINVAL;
+  ensure_device(c);
+  (void)hipStreamSynchronize(c->stream);
+  drain_profile(c);
+  for (int k = 0; k < I4MOE_K_COUNT; ++k) {
+    c->prof_ms[k] = 0;
+    c->prof_n[k] = 0;
+  }
+  c->profiling = on != 0;
+  return I4MOE_OK;
+}
+
+int i4moe_profile_query(i4moe_ctx *c, int kernel, double *total_ms, long long *launches) {
+  if (!c || kernel < 0 || kernel >= I4MOE_K_COUNT) return I4MOE_EINVAL;
+  ensure_device(c);
+  drain_profile(c);
+  if (total_ms) *total_ms = c->prof_ms[kernel];
+  if (launches) *launches = c->prof_n[kernel];
+  return I4MOE_OK;
+}
+
+}  // extern "C"

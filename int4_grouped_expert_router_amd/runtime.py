@@ -1,0 +1,155 @@
+"""Thin Python wrapper over the C ABI: owns a context, turns status codes into exceptions,
+passes numpy host arrays and torch device tensors through.  No computation happens here."""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import binding as B
+
+
+class I4moeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"i4moe error {code}: {msg}")
+        self.code = code
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return B.I4MOE_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return B.I4MOE_DTYPE_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+class Context:
+    def __init__(self, device: int = 0, stream=None):
+        B.load()
+        p = C.c_void_p()
+        rc = B.i4moe_ctx_create(device, C.byref(p))
+        if rc != 0:
+            raise I4moeError(rc, "i4moe_ctx_create failed")
+        self.p = p
+        self.device = device
+        if stream is not None:
+            self.set_stream(stream)
+
+    # -- plumbing
+    def check(self, rc: int) -> int:
+        if rc < 0:
+            raise I4moeError(rc, B.i4moe_last_error(self.p).decode())
+        return rc
+
+    def last_error(self) -> str:
+        return B.i4moe_last_error(self.p).decode()
+
+    def close(self):
+        if self.p:
+            B.i4moe_ctx_destroy(self.p)
+            self.p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_stream(self, stream):
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+        self.check(B.i4moe_set_stream(self.p, C.c_void_p(handle)))
+
+    # -- weights
+    def upload_tensor(self, fmt: int, gs: int, O: int, C_: int, packed: np.ndarray, scales: np.ndarray) -> int:
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        h = B.i4moe_upload_expert_tensor(self.p, fmt, gs, O, C_, _ptr(packed), _ptr(scales))
+        if h == 0:
+            raise I4moeError(-1, self.last_error())
+        return h
+
+    def upload_host_tensor(self, t) -> int:
+        return self.upload_tensor(t.fmt, t.gs, t.O, t.C, t.packed, t.scales)
+
+    def free_tensor(self, h: int):
+        self.check(B.i4moe_tensor_free(self.p, h))
+
+    def set_expert(self, layer: int, e: int, gate: int, up: int, down: int):
+        self.check(B.i4moe_set_expert(self.p, layer, e, gate, up, down))
+
+    def upload_router(self, layer: int, W: np.ndarray, bias=None):
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        E, D = W.shape
+        bp = None
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32)
+            bp = _ptr(bias)
+        self.check(B.i4moe_upload_router(self.p, layer, E, D, _ptr(W), bp))
+
+    # -- compute
+    def route(self, layer: int, x, K: int, topp: float = 0.0, norm_topk: bool = True, routed_scale: float = 1.0,
+              host_out: bool = False):
+        S = x.shape[0]
+        out = (B.i4moe_route_host * S)() if host_out else None
+        self.check(B.i4moe_route(self.p, layer, C.c_void_p(x.data_ptr()), _dtype_code(x), S, K, topp,
+                                 1 if norm_topk else 0, routed_scale,
+                                 C.cast(out, C.POINTER(B.i4moe_route_host)) if out is not None else None))
+        return out
+
+    def issue(self, layer: int, x, rows=None) -> int:
+        """rows: None (device route of the layer) or a list of (expert, token, weight)."""
+        S = x.shape[0]
+        g = None
+        if rows is not None:
+            n = len(rows)
+            ex = (C.c_int32 * max(n, 1))(*[int(r[0]) for r in rows])
+            tk = (C.c_int32 * max(n, 1))(*[int(r[1]) for r in rows])
+            wt = (C.c_float * max(n, 1))(*[float(r[2]) for r in rows])
+            g = B.i4moe_group(n, ex, tk, wt)
+            self._keep = (ex, tk, wt)
+        return self.check(B.i4moe_expert_group_issue(self.p, layer, C.c_void_p(x.data_ptr()), _dtype_code(x), S,
+                                                     C.byref(g) if g is not None else None))
+
+    def take(self, residual):
+        import torch
+        if residual.dtype != torch.float32 or not residual.is_contiguous():
+            raise TypeError("residual must be a contiguous float32 device tensor")
+        self.check(B.i4moe_expert_group_take(self.p, C.c_void_p(residual.data_ptr()), residual.shape[0]))
+
+    def set_fail_after(self, n: int):
+        self.check(B.i4moe_set_fail_after(self.p, n))
+
+    # -- taps and profiling
+    def tap(self, what: int, index: int = 0, dtype=np.float32) -> np.ndarray:
+        n = B.i4moe_debug_size(self.p, what, index)
+        if n == 0:
+            raise I4moeError(-1, f"tap {what}/{index} unavailable")
+        buf = np.empty(n // np.dtype(dtype).itemsize, dtype=dtype)
+        self.check(B.i4moe_debug_read(self.p, what, index, _ptr(buf), n))
+        return buf
+
+    def tap_group(self, layer: int) -> dict:
+        w = self.tap(B.I4MOE_TAP_GROUP, layer, np.int32)
+        o = 4
+        rec = {"n_entries": int(w[0]), "n_rows": int(w[1]), "S": int(w[2])}
+        for name, n in [("entry_expert", 64), ("entry_row0", 65), ("row_token", 64), ("row_expert", 64),
+                        ("row_weight", 64), ("tok_row0", 65), ("red_rows", 64)]:
+            rec[name] = w[o:o + n].copy()
+            o += n
+        rec["row_weight"] = rec["row_weight"].view(np.float32)
+        return rec
+
+    def set_profiling(self, on: bool):
+        self.check(B.i4moe_set_profiling(self.p, 1 if on else 0))
+
+    def profile(self, kernel: int):
+        ms = C.c_double()
+        n = C.c_longlong()
+        self.check(B.i4moe_profile_query(self.p, kernel, C.byref(ms), C.byref(n)))
+        return ms.value, n.value

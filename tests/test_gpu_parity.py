@@ -1,0 +1,313 @@
+"""HIP path vs the f64 oracle through the C ABI, on seeded synthetic layers (MI355X only)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from harness import (TOL, digest, make_layer, near_tie, normwise_err, oracle_routes, route_matches, upload_layer,
+                     x_to_device)
+from synth import get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def new_ctx():
+    import torch
+    from int4_grouped_expert_router_amd import Context
+    assert torch.cuda.is_available()
+    return Context(0, torch.cuda.current_stream())
+
+
+def issue_with_taps(ctx, cfg, L, layer, x, K, topp, norm, scale):
+    """route + issue, read the h and y taps before take; returns (route recs, h, y)."""
+    from int4_grouped_expert_router_amd import binding as B
+    rec = ctx.route(layer, x, K, topp, norm, scale, host_out=True)
+    slot = ctx.issue(layer, x)
+    h = ctx.tap(B.I4MOE_TAP_H)
+    y = ctx.tap(B.I4MOE_TAP_Y, slot)
+    return rec, h.reshape(-1, cfg.I), y.reshape(-1, cfg.D)
+
+
+def check_group(ctx, layer, routes):
+    g = ctx.tap_group(layer)
+    og = oracle.build_group(routes)
+    assert g["n_entries"] == len(og["entries"])
+    assert g["entry_expert"][:g["n_entries"]].tolist() == og["entries"]
+    assert g["n_rows"] == len(og["rows"])
+    for row, (e, t, k) in enumerate(og["rows"]):
+        assert g["row_expert"][row] == e and g["row_token"][row] == t
+        assert g["row_weight"][row].view(np.uint32) == routes[t].w32[k].view(np.uint32)
+    for t, rows in enumerate(og["token_rows"]):
+        lo, hi = g["tok_row0"][t], g["tok_row0"][t + 1]
+        assert g["red_rows"][lo:hi].tolist() == rows
+    return og
+
+
+def full_layer_check(cfg, layer=0, taps=True):
+    import torch
+    L = make_layer(cfg, layer)
+    ctx = new_ctx()
+    upload_layer(ctx, L, layer)
+    x = x_to_device(L.x, L.x_dtype)
+    routes, x64 = oracle_routes(cfg, L)
+    rec, h, y = issue_with_taps(ctx, cfg, L, layer, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    zero = torch.zeros((cfg.S, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(zero)
+    torch.cuda.synchronize()
+    delta_gpu = zero.cpu().numpy()
+    ties = [near_tie(routes[t], cfg.K, cfg.topp) for t in range(cfg.S)]
+    for t in range(cfg.S):
+        if not ties[t]:
+            assert route_matches(rec[t], routes[t], cfg.K), (t, list(rec[t].idx[:cfg.K]), routes[t].idx)
+    if any(ties):
+        pytest.skip("near-tie route; selection not comparable bit for bit")
+    og = check_group(ctx, layer, routes)
+    delta, inter = oracle.experts.layer_delta(routes, L.expert, x64)
+    for row, (e, t, k) in enumerate(og["rows"]):
+        assert normwise_err(h[row], inter[(t, k)][2]) < TOL, ("h", row)
+        assert normwise_err(y[row], inter[(t, k)][3]) < TOL, ("y", row)
+    err = normwise_err(delta_gpu, delta)
+    assert err < TOL, err
+    # residual join: out = residual + delta, bit for bit the f32 sum of the same delta
+    ctx.route(layer, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.issue(layer, x)
+    r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+    ctx.take(r)
+    torch.cuda.synchronize()
+    out = r.cpu().numpy()
+    assert np.array_equal(out, (L.residual + delta_gpu).astype(np.float32))
+    ctx.close()
+    return err
+
+
+@pytest.mark.parametrize("name", ["tiny", "medium", "mix"])
+def test_full_layer(name):
+    print(f"[parity] full layer {name}", flush=True)
+    full_layer_check(get_config(name))
+
+
+RAGGED = [
+    # D, I, E, K, S, formats, gs, x dtype
+    (1000, 200, 16, 4, 1, "mix_even_odd", 64, "f32"),
+    (2050, 650, 8, 2, 3, "mix_even_odd", 6, "bf16"),
+    (4096, 1536, 32, 8, 2, "row", 0, "bf16"),
+    (7168, 2048, 16, 8, 1, "mix_even_odd", 64, "f32"),
+    (512, 256, 4, 2, 1, "group", 128, "f32"),
+    (512, 96, 6, 3, 2, "group", 256, "bf16"),
+    (256, 128, 8, 8, 8, "mix_even_odd", 2, "f32"),
+    (130, 34, 5, 5, 1, "mix_even_odd", 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: f"D{s[0]}_I{s[1]}_E{s[2]}_K{s[3]}_S{s[4]}_{s[5]}_gs{s[6]}_{s[7]}")
+def test_ragged_shapes(shape):
+    D, I, E, K, S, formats, gs, xd = shape
+    print(f"[parity] ragged {shape}", flush=True)
+    cfg = get_config("tiny", D=D, I=I, E=E, K=K, S=S, formats=formats, gs=gs, x_dtype=xd, topp=0.9,
+                     routed_scale=2.5, seed=100 + D + I)
+    full_layer_check(cfg)
+
+
+def test_determinism_medium():
+    import torch
+    print("[parity] determinism medium x10", flush=True)
+    cfg = get_config("medium")
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    seen = set()
+    for _ in range(10):
+        r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+        rec = ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+        ctx.issue(0, x)
+        ctx.take(r)
+        torch.cuda.synchronize()
+        seen.add(digest(r.cpu().numpy(), np.frombuffer(bytes(rec), dtype=np.uint8)))
+    assert len(seen) == 1
+    ctx.close()
+
+
+def test_explicit_group_matches_device_route():
+    import torch
+    print("[parity] explicit group vs device route", flush=True)
+    cfg = get_config("mix", E=16, layers=1)
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    rec = ctx.route(0, x, cfg.K, 0.0, True, 1.0, host_out=True)
+    ctx.issue(0, x)
+    a = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(a)
+    rows = [(rec[0].idx[k], 0, rec[0].w[k]) for k in range(rec[0].n)]
+    ctx.issue(0, x, rows=rows)
+    b = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(b)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+    # two issues (slots) of the same experts split in halves: take sums slots in issue order
+    h1, h2 = rows[: len(rows) // 2], rows[len(rows) // 2:]
+    ctx.issue(0, x, rows=h1)
+    ctx.issue(0, x, rows=h2)
+    c = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(c)
+    ctx.issue(0, x, rows=h1)
+    p1 = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(p1)
+    ctx.issue(0, x, rows=h2)
+    p2 = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(p2)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy(), (p1.cpu().numpy() + p2.cpu().numpy()).astype(np.float32))
+    routes, x64 = oracle_routes(cfg, L, topp=0.0, scale=1.0)
+    delta, _ = oracle.experts.layer_delta(routes, L.expert, x64)
+    assert normwise_err(c.cpu().numpy(), delta) < TOL
+    ctx.close()
+
+
+def test_g4_page_design_50x3():
+    """50 trials x 3 experts in one launch: gs=64, a 200 % 64 tail group, and a per-row member."""
+    import torch
+    print("[parity] g4 50x3", flush=True)
+    rng = np.random.default_rng(4242)
+    D, I = 256, 200
+    ctx = new_ctx()
+    from harness import host_tensor
+    for trial in range(50):
+        ex = {}
+        for e, (fmt, gs) in enumerate([(4, 64), (4, 64), (2, 0)]):
+            def t(O, C_):
+                ng = -(-C_ // gs) if gs else 1
+                return host_tensor(fmt, gs, O, C_, rng.integers(0, 256, (O, C_ // 2), dtype=np.uint8),
+                                   rng.lognormal(np.log(0.01), 0.5, O * ng).astype(np.float32))
+            ex[e] = type("E", (), {})()
+            ex[e].gate, ex[e].up, ex[e].down = t(I, D), t(I, D), t(D, I)
+            hs = [ctx.upload_host_tensor(ex[e].gate), ctx.upload_host_tensor(ex[e].up), ctx.upload_host_tensor(ex[e].down)]
+            ctx.set_expert(trial, e, *hs)
+        S = int(rng.integers(1, 4))
+        xs = rng.standard_normal((S, D)).astype(np.float32)
+        rows = [(e, t_, float(rng.uniform(0.1, 1.0))) for t_ in range(S) for e in range(3)]
+        x = torch.from_numpy(xs).to("cuda:0")
+        ctx.issue(trial, x, rows=rows)
+        out = torch.zeros((S, D), dtype=torch.float32, device="cuda:0")
+        ctx.take(out)
+        torch.cuda.synchronize()
+        ref = np.zeros((S, D))
+        for (e, t_, w) in rows:
+            y = oracle.expert_forward(ex[e].gate, ex[e].up, ex[e].down, xs[t_].astype(np.float64))[3]
+            ref[t_] += float(np.float32(w)) * y
+        assert normwise_err(out.cpu().numpy(), ref) < TOL, trial
+    ctx.close()
+
+
+def test_router_page_design_200_trials():
+    """200 random router trials mixing top-p, norm_topk and routed_scale; selections and weights
+    must equal the oracle's bit for bit away from near-ties, and always equal the oracle's
+    selection taken on the GPU's own logits."""
+    import torch
+    from int4_grouped_expert_router_amd import binding as B
+    print("[parity] router 200 trials", flush=True)
+    rng = np.random.default_rng(2024)
+    ctx = new_ctx()
+    mism = ties = 0
+    for trial in range(200):
+        E = int(rng.choice([8, 64, 256]))
+        D = int(rng.choice([256, 512, 1536]))
+        S = int(rng.integers(1, 5))
+        K = int(rng.integers(1, min(E, 64 // S, 16) + 1))
+        W = rng.normal(0, float(rng.choice([0.02, 0.1])), (E, D)).astype(np.float32)
+        b = rng.normal(0, 0.1, E).astype(np.float32)
+        xs = rng.standard_normal((S, D)).astype(np.float32)
+        topp = float(rng.choice([0.0, 0.5, 0.8, 0.95, 1.0]))
+        norm = bool(rng.integers(0, 2))
+        scale = float(rng.choice([1.0, 2.5, 0.5]))
+        bf = bool(rng.integers(0, 2))
+        if bf:
+            from synth import round_f32_to_bf16_bits
+            xbits = round_f32_to_bf16_bits(xs)
+            x = x_to_device(xbits, "bf16")
+            x64 = oracle.widen_activations(xbits, "bf16")
+        else:
+            x = x_to_device(xs, "f32")
+            x64 = xs.astype(np.float64)
+        ctx.upload_router(0, W, b)
+        rec = ctx.route(0, x, K, topp, norm, scale, host_out=True)
+        logits = ctx.tap(B.I4MOE_TAP_LOGITS, 0, np.float64).reshape(S, E)
+        routes = oracle.route(W, b, x64, K, topp, norm, scale)
+        for t in range(S):
+            # R2: oracle selection on the GPU's logits
+            r2 = oracle.route_token(logits[t], b, K, topp, norm, scale)
+            assert route_matches(rec[t], r2, K) or near_tie(r2, K, topp), (trial, t)
+            if near_tie(routes[t], K, topp):
+                ties += 1
+                continue
+            if not route_matches(rec[t], routes[t], K):
+                mism += 1
+    print(f"[parity] router trials: {mism} mismatches, {ties} near-tie tokens", flush=True)
+    assert mism == 0
+    ctx.close()
+
+
+def test_router_exact_ties_take_lower_index():
+    import torch
+    ctx = new_ctx()
+    E, D = 16, 256
+    rng = np.random.default_rng(7)
+    W = rng.normal(0, 0.05, (E, D)).astype(np.float32)
+    W[9] = W[3]
+    W[12] = W[3]
+    b = np.zeros(E, np.float32)
+    W[5] = W[3] * 0  # logit 0 exactly; sigma 0.5
+    x = torch.from_numpy(rng.standard_normal((1, D)).astype(np.float32)).to("cuda:0")
+    ctx.upload_router(0, W, b)
+    rec = ctx.route(0, x, E, 0.0, False, 1.0, host_out=True)
+    idx = list(rec[0].idx[:E])
+    assert sorted(idx) == list(range(E))
+    pos = {e: idx.index(e) for e in (3, 9, 12)}
+    assert pos[3] < pos[9] < pos[12] and pos[12] - pos[3] == 2
+    ctx.close()
+
+
+@pytest.mark.parametrize("name", ["small_batch", "sustained"])
+def test_full_size_sampled(name):
+    """Full-size layers in the benchmark's launch configuration; the oracle checks sampled rows of
+    h (from x), sampled rows of y (from the GPU's h) and every output column (from the GPU's y)."""
+    import torch
+    print(f"[parity] full size sampled {name}", flush=True)
+    cfg = get_config(name)
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    routes, x64 = oracle_routes(cfg, L)
+    rec, h, y = issue_with_taps(ctx, cfg, L, 0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    out = torch.zeros((cfg.S, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    if any(near_tie(routes[t], cfg.K, cfg.topp) for t in range(cfg.S)):
+        pytest.skip("near-tie route")
+    for t in range(cfg.S):
+        assert route_matches(rec[t], routes[t], cfg.K)
+    og = check_group(ctx, 0, routes)
+    rng = np.random.default_rng(5)
+    o_rows = np.unique(np.concatenate([rng.integers(0, cfg.I, 24), [0, cfg.I - 1]]))
+    d_rows = np.unique(np.concatenate([rng.integers(0, cfg.D, 24), [0, cfg.D - 1]]))
+    for row, (e, t, k) in enumerate(og["rows"]):
+        ew = L.expert(e)
+        g = oracle.matvec_rows(ew.gate, x64[t], o_rows)
+        u = oracle.matvec_rows(ew.up, x64[t], o_rows)
+        href = oracle.silu(g) * u
+        assert normwise_err(h[row, o_rows], href) < TOL, ("h", row)
+        yref = oracle.matvec_rows(ew.down, h[row].astype(np.float64), d_rows)
+        assert normwise_err(y[row, d_rows], yref) < TOL, ("y", row)
+    # every output column from the GPU's own y rows, with the route's f32 weights
+    ref = np.zeros((cfg.S, cfg.D))
+    for t, rows in enumerate(og["token_rows"]):
+        for k, row in enumerate(rows):
+            ref[t] += float(routes[t].w32[k]) * y[row].astype(np.float64)
+    assert normwise_err(out, ref) < TOL
+    ctx.close()
