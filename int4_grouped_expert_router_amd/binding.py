@@ -69,6 +69,12 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise OSError(f"libi4moe.so not built at {path}; run __graft_entry__.build() first")
+    # PyTorch-ROCm carries its own HIP runtime; load it first so that the library binds to
+    # the same runtime instance as the tensors and streams it is handed.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

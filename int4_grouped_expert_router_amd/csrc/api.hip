@@ -34,15 +34,18 @@ struct Layer {
   std::vector<i4moe_tensor> gate, up, down;
   TensorDesc *d_tab = nullptr;         // [3][kMaxE]: gate, up, down descriptors
   std::vector<TensorDesc> h_tab;       // host copy of d_tab
-  RouteTok *d_route = nullptr;         // [kTokens]
-  GroupDev *d_group = nullptr;
+  int route_buf = -1;                  // ring entry holding this layer's latest route
   bool routed = false;
   int route_S = 0, route_K = 0;
 };
 
 struct SlotInfo {
   int S = 0, D = 0, rows = 0;
+  const GroupBuf *grp = nullptr;  // group record + row descriptors this issue ran
+  int ring = -1;                  // route ring entry it came from, -1 for an explicit group
 };
+
+constexpr int kRing = 32;  // route buffers: a layer may be re-routed up to 31 times before a take
 
 struct ProfRec {
   int kernel;
@@ -52,7 +55,7 @@ struct ProfRec {
 struct Plan {
   int V = 4, P = 1;
   bool gen = false;
-  int tile_rows = 1, tiles = 1, blocks = 1;
+  int tile_rows = 1, tile_groups = 1, blocks = 1;
 };
 
 }  // namespace
@@ -69,14 +72,17 @@ struct i4moe_ctx {
   size_t partial_cap = 0;  // doubles
   double *d_logits = nullptr;
   size_t logits_cap = 0;   // doubles
-  unsigned *d_counter = nullptr;
 
   float *d_h = nullptr;    // [kRows][h_ld]
   int h_ld = 0;
   float *d_y = nullptr;    // [kSlots][kRows][y_ld]
   int y_ld = 0;
-  GroupDev *d_slot_groups = nullptr;  // [kSlots]
+  GroupBuf *d_ring = nullptr;       // [kRing] route outputs
+  int ring_next = 0;
+  GroupBuf *d_slot_bufs = nullptr;  // [kSlots] explicit groups
   SlotInfo slots[kSlots];
+  int n_cu = 256;
+  double wave_factor = 1.0;
   int nslots = 0;
 
   int last_route_S = 0, last_route_E = 0;
@@ -245,18 +251,6 @@ int ensure_layer_tables(i4moe_ctx *c, Layer &L) {
   return I4MOE_OK;
 }
 
-int ensure_layer_route(i4moe_ctx *c, Layer &L) {
-  if (L.d_route) return I4MOE_OK;
-  hipError_t e;
-  if ((e = dalloc(&L.d_route, sizeof(RouteTok) * kTokens)) != hipSuccess) return hip_fail(c, e, "hipMalloc(route)");
-  if ((e = dalloc(&L.d_group, sizeof(GroupDev))) != hipSuccess) {
-    dfree(L.d_route);
-    L.d_route = nullptr;
-    return hip_fail(c, e, "hipMalloc(group)");
-  }
-  return I4MOE_OK;
-}
-
 int write_table_entry(i4moe_ctx *c, Layer &L, int which, int expert) {
   const size_t i = (size_t)which * kMaxE + expert;
   hipError_t e = hipMemcpyAsync(L.d_tab + i, &L.h_tab[i], sizeof(TensorDesc), hipMemcpyHostToDevice, c->stream);
@@ -266,7 +260,8 @@ int write_table_entry(i4moe_ctx *c, Layer &L, int which, int expert) {
 }
 
 // Pick the per-lane span V (dwords) and pass count P for rows of C columns, then tile the rows.
-Plan plan_proj(int C, int O, int max_rows, bool dual, const std::vector<int> &group_sizes) {
+Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector<int> &group_sizes, int n_cu,
+               double wave_factor) {
   const int RD = (C + 7) / 8;
   Plan best;
   double best_key = -1.0;
@@ -286,14 +281,20 @@ Plan plan_proj(int C, int O, int max_rows, bool dual, const std::vector<int> &gr
       best.gen = gen;
     }
   }
-  const int RB = rows_per_step(best.V, best.P, dual ? 2 : 1);
+  const bool use_xb = dual && xb && !best.gen;
+  const int RB = rows_per_step(best.V, best.P, dual ? 2 : 1, use_xb ? 32 : 16);
   const long long units = (long long)max_rows * O;
-  int tr = (int)((units + 4095) / 4096);
+  // one wave per resident slot: the tiles fill the chip once
+  const long long resident = (long long)proj_blocks_per_cu(best.V, best.P, dual ? 2 : 1, best.gen, use_xb) * 4 * n_cu;
+  long long target = (long long)(resident * wave_factor);
+  if (target < 64) target = 64;
+  int tr = (int)((units + target - 1) / target);
   tr = round_up(tr < RB ? RB : tr, RB);
+  if (tr > (kWave / RB) * RB) tr = (kWave / RB) * RB;  // one result per lane of the tile's wave
   best.tile_rows = tr;
-  best.tiles = (O + tr - 1) / tr;
-  const long long waves = (long long)max_rows * best.tiles;
-  best.blocks = (int)((waves + 3) / 4);
+  const int tiles = (O + tr - 1) / tr;
+  best.tile_groups = (tiles + 3) / 4;
+  best.blocks = max_rows * best.tile_groups;
   return best;
 }
 
@@ -328,17 +329,25 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
   i4moe_ctx *c = new (std::nothrow) i4moe_ctx();
   if (!c) return I4MOE_ENOMEM;
   c->device = device;
-  hipError_t e = dalloc(&c->d_counter, sizeof(unsigned) * 64);
-  if (e == hipSuccess) e = dalloc(&c->d_slot_groups, sizeof(GroupDev) * kSlots);
-  if (e == hipSuccess) e = hipMemset(c->d_counter, 0, sizeof(unsigned) * 64);
-  if (e == hipSuccess) e = hipMemset(c->d_slot_groups, 0, sizeof(GroupDev) * kSlots);
+  hipError_t e = dalloc(&c->d_ring, sizeof(GroupBuf) * kRing);
+  if (e == hipSuccess) e = dalloc(&c->d_slot_bufs, sizeof(GroupBuf) * kSlots);
+  if (e == hipSuccess) e = hipMemset(c->d_ring, 0, sizeof(GroupBuf) * kRing);
+  if (e == hipSuccess) e = hipMemset(c->d_slot_bufs, 0, sizeof(GroupBuf) * kSlots);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    dfree(c->d_counter);
-    dfree(c->d_slot_groups);
+    dfree(c->d_ring);
+    dfree(c->d_slot_bufs);
     delete c;
     return e == hipErrorOutOfMemory ? I4MOE_ENOMEM : I4MOE_EDEVICE;
+  }
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && ncu > 0)
+    c->n_cu = ncu;
+  (void)hipGetLastError();
+  if (const char *wf = std::getenv("I4MOE_WAVE_FACTOR")) {
+    const double v = std::atof(wf);
+    if (v >= 0.05 && v <= 64.0) c->wave_factor = v;
   }
   if (const char *fa = std::getenv("I4MOE_FAIL_AFTER")) {
     char *end = nullptr;
@@ -362,15 +371,13 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
     dfree(L.W);
     dfree(L.b);
     dfree(L.d_tab);
-    dfree(L.d_route);
-    dfree(L.d_group);
   }
   dfree(c->d_partial);
   dfree(c->d_logits);
-  dfree(c->d_counter);
+  dfree(c->d_ring);
+  dfree(c->d_slot_bufs);
   dfree(c->d_h);
   dfree(c->d_y);
-  dfree(c->d_slot_groups);
   for (auto &r : c->recs) {
     c->ev_pool.push_back(r.a);
     c->ev_pool.push_back(r.b);
@@ -549,8 +556,6 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
   ensure_device(c);
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
-  int rc = ensure_layer_route(c, L);
-  if (rc) return rc;
   float *dW = nullptr, *db = nullptr;
   if ((e = dalloc(&dW, sizeof(float) * (size_t)E * D)) != hipSuccess) return hip_fail(c, e, "hipMalloc(router)");
   if ((e = dalloc(&db, sizeof(float) * E)) != hipSuccess) {
@@ -594,33 +599,40 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
   if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
   ensure_device(c);
-  int splits = (1024 + L->E - 1) / L->E;
-  const int max_split = L->D / 256 > 1 ? L->D / 256 : 1;
-  if (splits > max_split) splits = max_split;
+  // about 256 GEMV waves, each over a multiple of 256 columns
+  int splits = (256 + L->E - 1) / L->E;
   if (splits > 16) splits = 16;
-  if (splits < 1) splits = 1;
+  int cps = round_up((L->D + splits - 1) / splits, 256);
+  splits = (L->D + cps - 1) / cps;
   if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
+  const int ring = c->ring_next;
+  for (int s = 0; s < c->nslots; ++s)
+    if (c->slots[s].ring == ring)
+      return fail(c, I4MOE_EINVAL, "%d routes since a pending issue; take before routing again", kRing);
   RouteArgs a{};
   a.W = L->W;
   a.bias = L->b;
   a.x = x_dev;
   a.partial = c->d_partial;
   a.logits = c->d_logits;
-  a.counter = c->d_counter;
-  a.route = L->d_route;
-  a.group = L->d_group;
+  a.out = c->d_ring + ring;
+  a.table = L->d_tab;
   a.E = L->E;
   a.D = L->D;
   a.S = S;
   a.K = K;
   a.x_bf16 = dtype == I4MOE_DTYPE_BF16;
   a.splits = splits;
-  a.cols_per_split = (L->D + splits - 1) / splits;
+  a.cols_per_split = cps;
+  a.vec = (L->D % 4 == 0) && reinterpret_cast<uintptr_t>(L->W) % 16 == 0 &&
+          reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 16 : 8) == 0;
   a.norm_topk = norm_topk ? 1 : 0;
   a.topp = topp;
   a.routed_scale = routed_scale;
   hipError_t e = timed(c, I4MOE_K_ROUTE, [&] { return launch_route(a, c->stream); });
   if (e != hipSuccess) return hip_fail(c, e, "route launch");
+  c->ring_next = (ring + 1) % kRing;
+  L->route_buf = ring;
   L->routed = true;
   L->route_S = S;
   L->route_K = K;
@@ -628,7 +640,7 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   c->last_route_E = L->E;
   c->calls++;
   if (host_out) {
-    e = hipMemcpyAsync(host_out, L->d_route, sizeof(RouteTok) * S, hipMemcpyDeviceToHost, c->stream);
+    e = hipMemcpyAsync(host_out, c->d_ring[ring].route, sizeof(RouteTok) * S, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "route copy back");
   }
@@ -661,10 +673,9 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
     if (d.ng > 1) gs_dn.push_back(d.gs);
   };
   const int s = c->nslots;
-  GroupDev *slot_group = c->d_slot_groups + s;
   int max_rows = 0;
-  const GroupDev *src = nullptr;
-  GroupDev *copy = nullptr;
+  const GroupBuf *grp = nullptr;
+  int ring = -1;
   GroupDev hg;
   if (!group) {
     if (!L->routed) return fail(c, I4MOE_EINVAL, "layer %d has no device route; call i4moe_route first", layer);
@@ -675,8 +686,8 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
       note(e);
     }
     max_rows = S * L->route_K;
-    src = L->d_group;
-    copy = slot_group;
+    ring = L->route_buf;
+    grp = c->d_ring + ring;
   } else {
     const int n = group->n_rows;
     if (n < 1 || n > kRows || !group->expert || !group->token || !group->weight)
@@ -721,17 +732,13 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
     hg.n_rows = n;
     hg.S = S;
     max_rows = n;
-    src = slot_group;
-    copy = nullptr;
+    grp = c->d_slot_bufs + s;
   }
 
-  const Plan pd = plan_proj(L->D, L->I, max_rows, true, gs_in);
-  const Plan pn = plan_proj(L->I, L->D, max_rows, false, gs_dn);
+  const Plan pd = plan_proj(L->D, L->I, max_rows, true, dtype == I4MOE_DTYPE_BF16, gs_in, c->n_cu, c->wave_factor);
+  const Plan pn = plan_proj(L->I, L->D, max_rows, false, false, gs_dn, c->n_cu, c->wave_factor);
   ProjArgs ad{};
-  ad.group = src;
-  ad.group_copy = copy;
-  ad.tA = L->d_tab;
-  ad.tB = L->d_tab + kMaxE;
+  ad.grp = grp;
   ad.act = x_dev;
   ad.act_ld = L->D;
   ad.act_bf16 = dtype == I4MOE_DTYPE_BF16;
@@ -739,13 +746,10 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   ad.out_ld = c->h_ld;
   ad.O = L->I;
   ad.C = L->D;
-  ad.tiles = pd.tiles;
+  ad.tile_groups = pd.tile_groups;
   ad.tile_rows = pd.tile_rows;
   ProjArgs an{};
-  an.group = slot_group;
-  an.group_copy = nullptr;
-  an.tA = L->d_tab + 2 * kMaxE;
-  an.tB = nullptr;
+  an.grp = grp;
   an.act = c->d_h;
   an.act_ld = c->h_ld;
   an.act_bf16 = 0;
@@ -753,17 +757,19 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   an.out_ld = c->y_ld;
   an.O = L->D;
   an.C = L->I;
-  an.tiles = pn.tiles;
+  an.tile_groups = pn.tile_groups;
   an.tile_rows = pn.tile_rows;
 
   hipError_t e = hipSuccess;
-  if (group) e = launch_group_store(hg, slot_group, c->stream);
-  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&] { return launch_dual(pd.V, pd.P, pd.gen, ad, pd.blocks, c->stream); });
+  if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
+  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&] { return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, ad, pd.blocks, c->stream); });
   if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&] { return launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream); });
   if (e != hipSuccess) return hip_fail(c, e, "issue launch");
   c->slots[s].S = S;
   c->slots[s].D = L->D;
   c->slots[s].rows = max_rows;
+  c->slots[s].grp = grp;
+  c->slots[s].ring = ring;
   c->nslots = s + 1;
   c->last_issue_rows = max_rows;
   c->last_issue_I = L->I;
@@ -790,7 +796,7 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
   ensure_device(c);
   TakeArgs a{};
   for (int s = 0; s < c->nslots; ++s) {
-    a.groups[s] = c->d_slot_groups + s;
+    a.groups[s] = c->slots[s].grp;
     a.y[s] = c->d_y + (size_t)s * kRows * c->y_ld;
   }
   a.resid = residual_dev;
@@ -847,9 +853,9 @@ int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t b
   if (what == I4MOE_TAP_LOGITS) {
     e = hipMemcpy(host_dst, c->d_logits, bytes, hipMemcpyDeviceToHost);
   } else if (what == I4MOE_TAP_ROUTE) {
-    e = hipMemcpy(host_dst, find_layer(c, index)->d_route, bytes, hipMemcpyDeviceToHost);
+    e = hipMemcpy(host_dst, c->d_ring[find_layer(c, index)->route_buf].route, bytes, hipMemcpyDeviceToHost);
   } else if (what == I4MOE_TAP_GROUP) {
-    e = hipMemcpy(host_dst, find_layer(c, index)->d_group, bytes, hipMemcpyDeviceToHost);
+    e = hipMemcpy(host_dst, &c->d_ring[find_layer(c, index)->route_buf].g, bytes, hipMemcpyDeviceToHost);
   } else if (what == I4MOE_TAP_H) {
     e = hipMemcpy2D(host_dst, sizeof(float) * c->last_issue_I, c->d_h, sizeof(float) * c->h_ld,
                     sizeof(float) * c->last_issue_I, c->last_issue_rows, hipMemcpyDeviceToHost);

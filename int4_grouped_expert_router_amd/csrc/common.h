@@ -28,6 +28,7 @@ struct TensorDesc {
   int32_t ng;          // scales per row (1 = per-row)
   int32_t pad;
 };
+static_assert(sizeof(TensorDesc) == 40, "tensor descriptor layout");
 
 // Group record (layout documented with I4MOE_GROUP_WORDS).
 struct GroupDev {
@@ -42,6 +43,15 @@ struct GroupDev {
 };
 static_assert(sizeof(GroupDev) == I4MOE_GROUP_WORDS * 4, "group record layout");
 
+// Everything a projection wave needs about its group row, in one 128-byte record: the
+// expert's gate / up / down tensors, the token row of x and the route weight.
+struct RowDesc {
+  TensorDesc t[3];
+  int32_t token;
+  float weight;
+};
+static_assert(sizeof(RowDesc) == 128, "row descriptor layout");
+
 // Packed per-token route record: same layout as i4moe_route_host.
 struct RouteTok {
   int32_t n;
@@ -50,37 +60,41 @@ struct RouteTok {
 };
 static_assert(sizeof(RouteTok) == sizeof(i4moe_route_host), "route record layout");
 
+// What one route (or one explicit group) hands to issue and take.
+struct GroupBuf {
+  RowDesc rows[kRows];
+  GroupDev g;
+  RouteTok route[kTokens];
+};
+
 struct RouteArgs {
-  const float *W;        // [E][D]
-  const float *bias;     // [E]
-  const void *x;         // [S][D] f32 or bf16
-  double *partial;       // [S][E][splits]
-  double *logits;        // [S][E]
-  unsigned *counter;     // finished-workgroup counter, left at 0 by the last workgroup
-  RouteTok *route;       // [S]
-  GroupDev *group;
+  const float *W;            // [E][D]
+  const float *bias;         // [E]
+  const void *x;             // [S][D] f32 or bf16
+  double *partial;           // [S][E][splits]
+  double *logits;            // [S][E]
+  GroupBuf *out;
+  const TensorDesc *table;   // layer expert table [3][kMaxE], or null (route only)
   int E, D, S, K;
   int x_bf16;
   int splits, cols_per_split;
+  int vec;                   // four-column loads in the GEMV
   int norm_topk;
   float topp, routed_scale;
 };
 
 struct ProjArgs {
-  const GroupDev *group;     // rows to run
-  GroupDev *group_copy;      // when non-null, workgroup 0 copies *group here
-  const TensorDesc *tA;      // per expert: gate (dual) or down
-  const TensorDesc *tB;      // per expert: up (dual only)
+  const GroupBuf *grp;       // rows to run
   const void *act;           // dual: x [S][act_ld]; down: h [rows][act_ld] f32
   float *out;                // dual: h [rows][out_ld]; down: y [rows][out_ld]
   int act_ld, out_ld;
   int act_bf16;
   int O, C;                  // rows and columns of every tensor in the launch
-  int tiles, tile_rows;      // tiles per group row, rows per tile
+  int tile_groups, tile_rows;  // workgroups per group row (4 tiles each), rows per tile
 };
 
 struct TakeArgs {
-  const GroupDev *groups[kSlots];
+  const GroupBuf *groups[kSlots];
   const float *y[kSlots];
   float *resid;              // [S][D]
   int nslots, y_ld, S, D;
@@ -88,14 +102,20 @@ struct TakeArgs {
 
 // Launchers (defined in the kernel translation units).  They return hipGetLastError().
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
-hipError_t launch_dual(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st);
+hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st);
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st);
 hipError_t launch_take(const TakeArgs &a, hipStream_t st);
-hipError_t launch_group_store(const GroupDev &g, GroupDev *dst, hipStream_t st);
+int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb);  // resident 256-thread workgroups per CU
+hipError_t launch_group_store(const GroupDev &g, const TensorDesc *table, GroupBuf *dst, hipStream_t st);
 
-// Rows per inner step for a launch shape: ~32 weight dwords in flight per lane.
-constexpr int rows_per_step(int V, int P, int tensors) {
-  return (32 / (tensors * V * P)) < 1 ? 1 : ((32 / (tensors * V * P)) > 8 ? 8 : 32 / (tensors * V * P));
+// Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.
+constexpr int rows_per_step(int V, int P, int tensors, int budget) {
+  return (budget / (tensors * V * P)) < 1 ? 1 : ((budget / (tensors * V * P)) > 8 ? 8 : budget / (tensors * V * P));
 }
+
+// Constant-address-space views: uniform records read with scalar loads.
+#define I4MOE_AS4 __attribute__((address_space(4)))
+typedef const GroupBuf I4MOE_AS4 *CGroupBuf;
+typedef const TensorDesc I4MOE_AS4 *CTensorDesc;
 
 }  // namespace i4moe

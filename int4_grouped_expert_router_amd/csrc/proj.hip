@@ -60,6 +60,36 @@ __device__ __forceinline__ float dot8(uint32_t w, const float (&xe)[4], const fl
   return acc;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+
+// Eight columns of one weight dword against packed bf16 activation pairs.  Nibble k (column
+// 8d+k) sits at bits 4k..4k+3.  t0 = w & 0x0F0F0F0F isolates nibbles 0,2,4,6 in the low bits
+// of its bytes, t1 = (w >> 4) & 0x0F0F0F0F nibbles 1,3,5,7; one v_perm_b32 then puts two of
+// them under the bf16 high byte 0x43, giving the exact bf16 values 128 + q.  v_dot2_f32_bf16
+// takes (128 + q_a) x_a + (128 + q_b) x_b into the f32 accumulator; the pairs are (0,4),
+// (2,6), (1,5), (3,7) and the activations are packed to match.  The 128 + 8 offset comes out
+// once per span through the initial value -136 * sum(x).  7 integer ops + 4 dot2 per 8 weights.
+__device__ __forceinline__ float dot8_bf16(uint32_t w, const uint32_t (&xp)[4], float acc) {
+  const uint32_t t0 = w & 0x0F0F0F0Fu;
+  const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t hi = 0x43434343u;
+  const uint32_t p04 = __builtin_amdgcn_perm(hi, t0, 0x04020400u);
+  const uint32_t p26 = __builtin_amdgcn_perm(hi, t0, 0x04030401u);
+  const uint32_t p15 = __builtin_amdgcn_perm(hi, t1, 0x04020400u);
+  const uint32_t p37 = __builtin_amdgcn_perm(hi, t1, 0x04030401u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p04), as_bf16x2(xp[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p26), as_bf16x2(xp[1]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p15), as_bf16x2(xp[2]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p37), as_bf16x2(xp[3]), acc, false);
+  return acc;
+}
+
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
@@ -110,21 +140,6 @@ __device__ __forceinline__ void load8(const void *act, int bf16, size_t row_off,
   }
 }
 
-template <int V>
-__device__ __forceinline__ void load_span(const uint8_t *p, uint32_t (&w)[V]) {
-  if constexpr (V == 4) {
-    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-  } else if constexpr (V == 2) {
-    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-    w[0] = u.x; w[1] = u.y;
-  } else {
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-#pragma unroll
-    for (int v = 0; v < V; ++v) w[v] = __builtin_nontemporal_load(q + v);
-  }
-}
-
 // Per-byte path for group sizes that split a lane's span (any even gs): each byte's two
 // columns share one group because gs is even.
 template <int V, int P>
@@ -154,160 +169,374 @@ __device__ float row_dot_generic(const TensorDesc &T, int o, const uint32_t (&w)
   return acc;
 }
 
-template <int V, int P, bool DUAL, bool GEN>
-__global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
-  constexpr int NT = DUAL ? 2 : 1;
-  constexpr int RB = rows_per_step(V, P, NT);
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
-  const GroupDev *__restrict__ g = a.group;
+// Field-wise copy out of the constant address space (scalar loads).
+__device__ __forceinline__ TensorDesc ld_desc(const TensorDesc I4MOE_AS4 &d) {
+  TensorDesc t;
+  t.q = d.q;
+  t.s = d.s;
+  t.O = d.O;
+  t.C = d.C;
+  t.row_bytes = d.row_bytes;
+  t.gs = d.gs;
+  t.ng = d.ng;
+  t.pad = 0;
+  return t;
+}
 
-  if (DUAL && a.group_copy != nullptr && blockIdx.x == 0) {
-    const int32_t *src = reinterpret_cast<const int32_t *>(g);
-    int32_t *dst = reinterpret_cast<int32_t *>(a.group_copy);
-    for (int i = threadIdx.x; i < I4MOE_GROUP_WORDS; i += kBlock) dst[i] = src[i];
-  }
+// Activation slice of one lane.  f32 path: x of the even columns and x/16 of the odd columns,
+// offset term -8 * sum(x) per span.  bf16 path: packed pairs (x_k, x_{k+4}) in the order the
+// weight pairs are built, offset term -136 * sum(x) per span.
+template <int V, int P, bool XB>
+struct Act {
+  float xe[P][V][4], xo[P][V][4];
+  float xm[P];
+};
+template <int V, int P>
+struct Act<V, P, true> {
+  uint32_t xp[P][V][4];
+  float xm[P];
+};
 
-  const int nrows = min(g->n_rows, kRows);
-  const int jr = wave / a.tiles;
-  if (jr >= nrows) return;
-  const int tile = wave - jr * a.tiles;
-  const int e = g->row_expert[jr];
-  const int arow = DUAL ? g->row_token[jr] : jr;
-  const TensorDesc TA = a.tA[e];
-  TensorDesc TB = TA;
-  if (DUAL) TB = a.tB[e];
+// Words of the staged activation row: the row padded with zeros to the columns all lanes of
+// all passes cover (8V columns per lane per pass); bf16 pairs for XB, f32 otherwise.
+template <int V, int P, bool XB>
+constexpr int act_words() {
+  return XB ? P * 64 * V * 4 : P * 64 * V * 8;
+}
 
-  const int C = a.C;
-  const int RD = (C + 7) >> 3;
+// The workgroup copies its activation row into LDS with coalesced 4-byte loads (every wave of
+// the workgroup works on the same group row).  A lane's slice is contiguous in the row but
+// 16V (bf16) or 32V (f32) bytes from its neighbour's, so reading it from global memory directly
+// would touch a separate cache line per lane and load; LDS takes that access pattern for free.
+// The copy is split in two so the kernel can issue these loads before its first weight loads:
+// the LDS writes then wait only for the (older) activation loads, not for weights in flight.
+template <int V, int P, bool XB>
+constexpr int stage_words() {
+  return act_words<V, P, XB>() / kBlock;
+}
 
-  // Activation slice of this lane, span sums and the group index of every span.
-  float xe[P][V][4], xo[P][V][4], xm8[P];
-  int giA[P], giB[P];
-  const size_t row_off = (size_t)arow * a.act_ld;
+template <bool XB, int N>
+__device__ __forceinline__ void stage_load(uint32_t (&xs)[N], const void *act, int bf16, size_t row_off, int C) {
+  if (XB) {
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(act) + row_off);
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const int ds = p * 64 * V + lane * V;
-    float span = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      float t[8];
-      load8(a.act, a.act_bf16, row_off, 8 * (ds + v), C, t);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xe[p][v][k] = t[2 * k];
-        xo[p][v][k] = t[2 * k + 1] * 0.0625f;
-        span += t[2 * k] + t[2 * k + 1];
-      }
+    for (int i = 0; i < N; ++i) {
+      const int w = threadIdx.x + i * kBlock;
+      xs[i] = row[2 * w < C ? w : 0];
     }
-    xm8[p] = -8.f * span;
-    giA[p] = (TA.ng == 1 || ds >= RD) ? 0 : (8 * ds) / TA.gs;
-    giB[p] = (TB.ng == 1 || ds >= RD) ? 0 : (8 * ds) / TB.gs;
-  }
-  // GEN launches carry the per-byte path; others only hold tensors whose groups align with spans.
-  const bool genA = GEN && TA.ng > 1 && (TA.gs % (8 * V)) != 0;
-  const bool genB = GEN && DUAL && TB.ng > 1 && (TB.gs % (8 * V)) != 0;
-
-  const int o_begin = tile * a.tile_rows;
-  const int o_end = min(o_begin + a.tile_rows, a.O);
-  float *outp = a.out + (size_t)jr * a.out_ld;
-
-  for (int o0 = o_begin; o0 < o_end; o0 += RB) {
-    uint32_t wa[RB][P][V], wb[RB][P][V];
-    float sa[RB][P], sb[RB][P];
+  } else if (bf16) {
+    const uint16_t *row = static_cast<const uint16_t *>(act) + row_off;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int o = o0 + r;
-      const bool rv = o < o_end;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int ds = p * 64 * V + lane * V;
-        const bool ok = rv && ds < RD;
-        if (ok) {
-          load_span<V>(TA.q + (size_t)o * TA.row_bytes + 4 * ds, wa[r][p]);
-          sa[r][p] = TA.s[(size_t)o * TA.ng + giA[p]];
-        } else {
-#pragma unroll
-          for (int v = 0; v < V; ++v) wa[r][p][v] = 0u;
-          sa[r][p] = 0.f;
-        }
-        if (DUAL) {
-          if (ok) {
-            load_span<V>(TB.q + (size_t)o * TB.row_bytes + 4 * ds, wb[r][p]);
-            sb[r][p] = TB.s[(size_t)o * TB.ng + giB[p]];
-          } else {
-#pragma unroll
-            for (int v = 0; v < V; ++v) wb[r][p][v] = 0u;
-            sb[r][p] = 0.f;
-          }
-        }
-      }
+    for (int i = 0; i < N; ++i) {
+      const int w = threadIdx.x + i * kBlock;
+      xs[i] = row[w < C ? w : 0];
     }
-
-    float outv = 0.f;
+  } else {
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const float *>(act) + row_off);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int o = o0 + r;
-      float accA = 0.f, accB = 0.f;
-      if (!genA) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          float ap = xm8[p];
-#pragma unroll
-          for (int v = 0; v < V; ++v) ap = dot8(wa[r][p][v], xe[p][v], xo[p][v], ap);
-          accA = fmaf(sa[r][p], ap, accA);
-        }
-      } else if constexpr (GEN) {
-        if (o < o_end) accA = row_dot_generic<V, P>(TA, o, wa[r], xe, xo, lane, RD);
-      }
-      const float sumA = wave_sum(accA);
-      float res = sumA;
-      if (DUAL) {
-        if (!genB) {
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            float bp = xm8[p];
-#pragma unroll
-            for (int v = 0; v < V; ++v) bp = dot8(wb[r][p][v], xe[p][v], xo[p][v], bp);
-            accB = fmaf(sb[r][p], bp, accB);
-          }
-        } else if constexpr (GEN) {
-          if (o < o_end) accB = row_dot_generic<V, P>(TB, o, wb[r], xe, xo, lane, RD);
-        }
-        const float sumB = wave_sum(accB);
-        res = sumA / (1.f + expf(-sumA)) * sumB;
-      }
-      if (lane == r) outv = res;
+    for (int i = 0; i < N; ++i) {
+      const int w = threadIdx.x + i * kBlock;
+      xs[i] = row[w < C ? w : 0];
     }
-    if (lane < RB && o0 + lane < o_end) outp[o0 + lane] = outv;
   }
 }
 
-template <bool DUAL>
-hipError_t launch(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st) {
-#define I4MOE_CASE(v, p)                                                                   \
-  if (V == v && P == p) {                                                                  \
-    if (gen)                                                                               \
-      hipLaunchKernelGGL((k_proj<v, p, DUAL, true>), dim3(blocks), dim3(kBlock), 0, st, a); \
-    else                                                                                   \
-      hipLaunchKernelGGL((k_proj<v, p, DUAL, false>), dim3(blocks), dim3(kBlock), 0, st, a); \
-    return hipGetLastError();                                                              \
+// Zeros past the row's C columns; bf16 values widened to f32 bits except for XB (pairs).
+template <bool XB, int N>
+__device__ __forceinline__ void stage_store(uint32_t *lds, const uint32_t (&xs)[N], int bf16, int C) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int w = threadIdx.x + i * kBlock;
+    uint32_t v;
+    if (XB)
+      v = 2 * w < C ? xs[i] : 0u;
+    else
+      v = w < C ? (bf16 ? xs[i] << 16 : xs[i]) : 0u;
+    lds[w] = v;
   }
-  I4MOE_CASE(1, 1) I4MOE_CASE(1, 2) I4MOE_CASE(1, 3) I4MOE_CASE(1, 4)
-  I4MOE_CASE(2, 1) I4MOE_CASE(2, 2) I4MOE_CASE(2, 3) I4MOE_CASE(2, 4)
-  I4MOE_CASE(3, 1) I4MOE_CASE(3, 2) I4MOE_CASE(3, 3) I4MOE_CASE(3, 4)
-  I4MOE_CASE(4, 1) I4MOE_CASE(4, 2) I4MOE_CASE(4, 3) I4MOE_CASE(4, 4)
-#undef I4MOE_CASE
-  return hipErrorInvalidValue;
+}
+
+template <int V, int P, bool XB>
+__device__ __forceinline__ void read_act(uint32_t (&raw)[P][V][XB ? 4 : 8], const uint32_t *lds, int lane) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int d = p * 64 * V + lane * V + v;
+      if constexpr (XB) {
+        const u4 q = *reinterpret_cast<const u4 *>(lds + 4 * d);
+        raw[p][v][0] = q.x; raw[p][v][1] = q.y; raw[p][v][2] = q.z; raw[p][v][3] = q.w;
+      } else {
+        const u4 q0 = *reinterpret_cast<const u4 *>(lds + 8 * d);
+        const u4 q1 = *reinterpret_cast<const u4 *>(lds + 8 * d + 4);
+        raw[p][v][0] = q0.x; raw[p][v][1] = q0.y; raw[p][v][2] = q0.z; raw[p][v][3] = q0.w;
+        raw[p][v][4] = q1.x; raw[p][v][5] = q1.y; raw[p][v][6] = q1.z; raw[p][v][7] = q1.w;
+      }
+    }
+  }
+}
+
+template <int V, int P, bool XB>
+__device__ __forceinline__ void finish_act(Act<V, P, XB> &A, const uint32_t (&raw)[P][V][XB ? 4 : 8]) {
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float span = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if constexpr (XB) {
+        const uint32_t *u = raw[p][v];  // u[k] holds columns 2k (low half) and 2k+1 (high half)
+        A.xp[p][v][0] = (u[0] & 0xffffu) | (u[2] << 16);          // columns 0, 4
+        A.xp[p][v][1] = (u[1] & 0xffffu) | (u[3] << 16);          // columns 2, 6
+        A.xp[p][v][2] = (u[0] >> 16) | (u[2] & 0xffff0000u);      // columns 1, 5
+        A.xp[p][v][3] = (u[1] >> 16) | (u[3] & 0xffff0000u);      // columns 3, 7
+#pragma unroll
+        for (int k = 0; k < 4; ++k) span += bf16_to_f32(u[k] & 0xffffu) + bf16_to_f32(u[k] >> 16);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float e = __uint_as_float(raw[p][v][2 * k]), o = __uint_as_float(raw[p][v][2 * k + 1]);
+          A.xe[p][v][k] = e;
+          A.xo[p][v][k] = o * 0.0625f;
+          span += e + o;
+        }
+      }
+    }
+    A.xm[p] = (XB ? -136.f : -8.f) * span;
+  }
+}
+
+// Weights (and their scales) of one pipeline step: RB consecutive rows of NT tensors.
+template <int V, int P, int NT, int RB>
+struct Step {
+  uint32_t w[NT][RB][P][V];
+  float s[NT][RB][P];
+};
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end return zero
+// without a memory access.  Word 3 selects 32-bit data for untyped buffer loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+constexpr int kNontemporal = 2;  // cache-policy bits of a streaming load
+
+template <int V>
+__device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[V]) {
+  if constexpr (V == 4) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNontemporal);
+    w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+  } else if constexpr (V == 2) {
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNontemporal);
+    w[0] = u.x; w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) w[v] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * v, 0, kNontemporal);
+  }
+}
+
+// Every load of a step is issued, whatever the tile: a row at or past o_end gets an empty
+// buffer range, so its loads return zeros and touch no memory.  Keeping the issue pattern
+// identical on every path keeps the wait counts exact (a load issued on one path only would
+// make the compiler wait for all loads in flight).  A span past the row's padded bytes reads
+// zeros the same way; its activations are zero, so it adds nothing.
+template <int V, int P, int NT, int RB>
+__device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
+                                          int o, int o_end, int lane) {
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const bool ok = o + r < o_end;
+    const int row = ok ? o + r : 0;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T[n].q + (size_t)row * T[n].row_bytes, ok ? T[n].row_bytes : 0);
+      const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T[n].s + (size_t)row * T[n].ng, ok ? 4 * T[n].ng : 0);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        load_span<V>(wr, 4 * (p * 64 * V + lane * V), st.w[n][r][p]);
+        st.s[n][r][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * gi[n][p], 0, 0));
+      }
+    }
+  }
+}
+
+// Dot products of one step's rows, reduced over the wave; lane (o - o_begin + r) keeps row
+// o + r's result, and the tile's results leave in one coalesced store at the end.
+template <int V, int P, int NT, int RB, bool GEN, bool XB>
+__device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT],
+                                             const bool (&gen)[NT], const Act<V, P, XB> &A, int o, int o_end,
+                                             int lane, int RD, int o_begin, float &outv) {
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    float sum[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float acc = 0.f;
+      if (!gen[n]) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          float ap = A.xm[p];
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            if constexpr (XB)
+              ap = dot8_bf16(st.w[n][r][p][v], A.xp[p][v], ap);
+            else
+              ap = dot8(st.w[n][r][p][v], A.xe[p][v], A.xo[p][v], ap);
+          }
+          acc = fmaf(st.s[n][r][p], ap, acc);
+        }
+      } else if constexpr (GEN && !XB) {
+        if (o + r < o_end) acc = row_dot_generic<V, P>(T[n], o + r, st.w[n][r], A.xe, A.xo, lane, RD);
+      }
+      sum[n] = wave_sum(acc);
+    }
+    float res = sum[0];
+    if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
+    if (lane == o - o_begin + r) outv = res;
+  }
+}
+
+// NT = 2: dual gate/up with the SiLU-gated product; NT = 1: down projection.  XB: bf16
+// activations through v_dot2_f32_bf16 (dual only).  A tile holds at most 64 rows (one result
+// per lane).
+template <int V, int P, int NT, bool GEN, bool XB>
+__global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
+  constexpr int RB = rows_per_step(V, P, NT, XB ? 32 : 16);
+  extern __shared__ uint32_t s_act[];
+  const int lane = threadIdx.x & 63;
+  // Every workgroup works on one group row; its four waves take consecutive tiles.  The wave
+  // index is uniform by construction and readfirstlane lets the compiler keep it (and the row,
+  // tile, descriptors and base addresses derived from it) in scalar registers.
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const CGroupBuf G = (CGroupBuf)a.grp;
+  const int jr = blockIdx.x / a.tile_groups;
+  if (jr >= min(G->g.n_rows, kRows)) return;
+  const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
+
+  // Everything about this row in one scalar record: tensors, token, weight.
+  TensorDesc T[NT];
+  if constexpr (NT == 2) {
+    T[0] = ld_desc(G->rows[jr].t[0]);
+    T[1] = ld_desc(G->rows[jr].t[1]);
+  } else {
+    T[0] = ld_desc(G->rows[jr].t[2]);
+  }
+  const int arow = NT == 2 ? G->rows[jr].token : jr;
+
+  const int C = a.C;
+  const int RD = (C + 7) >> 3;
+  int gi[NT][P];
+  bool gen[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) gi[n][p] = 0;
+    if (T[n].ng > 1) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int ds = p * 64 * V + lane * V;
+        gi[n][p] = ds < RD ? (8 * ds) / T[n].gs : 0;
+      }
+    }
+    // GEN launches carry the per-byte path; others hold only tensors whose groups align with spans.
+    gen[n] = GEN && T[n].ng > 1 && (T[n].gs % (8 * V)) != 0;
+  }
+
+  const int o_begin = tile * a.tile_rows;
+  const int o_end = min(o_begin + a.tile_rows, a.O);
+  const bool work = o_begin < o_end;
+
+  // Activation loads first, then the first two steps of weights (empty ranges for a wave
+  // without rows); the activation row goes to LDS as soon as its own loads have landed.
+  // Scheduling barriers keep the issue order: the wait counts below assume it.
+  uint32_t xs[stage_words<V, P, XB>()];
+  stage_load<XB>(xs, a.act, a.act_bf16, (size_t)arow * a.act_ld, C);
+  __builtin_amdgcn_sched_barrier(0);
+  Step<V, P, NT, RB> b0, b1;
+  load_step<V, P, NT, RB>(b0, T, gi, o_begin, o_end, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step<V, P, NT, RB>(b1, T, gi, o_begin + RB, o_end, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<XB>(s_act, xs, a.act_bf16, C);
+  __syncthreads();
+  if (!work) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  uint32_t raw[P][V][XB ? 4 : 8];
+  read_act<V, P, XB>(raw, s_act, lane);
+  Act<V, P, XB> A;
+  finish_act<V, P, XB>(A, raw);
+
+  // Two-stage pipeline: while one step computes, the other step's weights are in flight.  The
+  // loop has one exit, at the bottom; the last pass issues loads of empty ranges.
+  float outv = 0.f;
+  int o = o_begin;
+  do {
+    compute_step<V, P, NT, RB, GEN, XB>(b0, T, gen, A, o, o_end, lane, RD, o_begin, outv);
+    load_step<V, P, NT, RB>(b0, T, gi, o + 2 * RB, o_end, lane);
+    if (o + RB < o_end) compute_step<V, P, NT, RB, GEN, XB>(b1, T, gen, A, o + RB, o_end, lane, RD, o_begin, outv);
+    load_step<V, P, NT, RB>(b1, T, gi, o + 3 * RB, o_end, lane);
+    o += 2 * RB;
+  } while (o < o_end);
+  if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
+}
+
+template <int NT, bool GEN, bool XB>
+const void *kernel_ptr_t(int V, int P) {
+#define I4MOE_PTR(v, p) \
+  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, XB>);
+  I4MOE_PTR(1, 1) I4MOE_PTR(1, 2) I4MOE_PTR(1, 3) I4MOE_PTR(1, 4)
+  I4MOE_PTR(2, 1) I4MOE_PTR(2, 2) I4MOE_PTR(2, 3) I4MOE_PTR(2, 4)
+  I4MOE_PTR(3, 1) I4MOE_PTR(3, 2) I4MOE_PTR(3, 3) I4MOE_PTR(3, 4)
+  I4MOE_PTR(4, 1) I4MOE_PTR(4, 2) I4MOE_PTR(4, 3) I4MOE_PTR(4, 4)
+#undef I4MOE_PTR
+  return nullptr;
+}
+
+// The instantiation a launch uses: bf16 pairs only for dual launches over bf16 activations
+// without per-byte group tensors.
+const void *kernel_ptr(int V, int P, int NT, bool gen, bool xb) {
+  if (NT == 1) return gen ? kernel_ptr_t<1, true, false>(V, P) : kernel_ptr_t<1, false, false>(V, P);
+  if (gen) return kernel_ptr_t<2, true, false>(V, P);
+  return xb ? kernel_ptr_t<2, false, true>(V, P) : kernel_ptr_t<2, false, false>(V, P);
+}
+
+size_t lds_bytes(int V, int P, bool xb) { return 4u * (size_t)(xb ? P * 64 * V * 4 : P * 64 * V * 8); }
+
+hipError_t launch(int V, int P, int NT, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st) {
+  const void *k = kernel_ptr(V, P, NT, gen, xb);
+  if (!k) return hipErrorInvalidValue;
+  ProjArgs args = a;
+  void *params[] = {&args};
+  return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds_bytes(V, P, xb), st);
 }
 
 }  // namespace
 
-hipError_t launch_dual(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st) {
-  return launch<true>(V, P, gen, a, blocks, st);
+int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb) {
+  static int cache[5][5][3][2][2] = {};
+  if (V < 1 || V > 4 || P < 1 || P > 4 || NT < 1 || NT > 2) return 1;
+  int &c = cache[V][P][NT][gen ? 1 : 0][xb ? 1 : 0];
+  if (c == 0) {
+    const void *k = kernel_ptr(V, P, NT, gen, xb);
+    int n = 0;
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kBlock, lds_bytes(V, P, xb)) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    c = n;
+  }
+  return c;
+}
+
+hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st) {
+  hipError_t e = launch(V, P, 2, gen, xb && !gen, a, blocks, st);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st) {
-  return launch<false>(V, P, gen, a, blocks, st);
+  hipError_t e = launch(V, P, 1, gen, false, a, blocks, st);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace i4moe
