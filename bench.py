@@ -105,6 +105,31 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def calibrate_sleep(torch, stream, host_us_per_step: float = 150.0, burst: int = 40) -> int:
+    """GPU sleep cycles that outlast the host's enqueue of one burst of steps (with margin)."""
+    probe = 1_000_000
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record()
+        torch.cuda._sleep(probe)
+        b.record()
+    b.synchronize()
+    us = max(a.elapsed_time(b) * 1e3, 1.0)
+    return int(probe * host_us_per_step * burst / us)
+
+
+def copy_calibration(torch, nbytes: int = 256 << 20, reps: int = 5):
+    """Plain device-to-device copies of known size: what FETCH_SIZE and WRITE_SIZE report per
+    dispatch here, against nbytes, is the scale applied to the same counters on the kernels."""
+    torch.cuda.set_device(0)
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,18 +137,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="medium")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers to cycle (0 = workload default)")
-    ap.add_argument("--graph", action="store_true", help="replay the timed steps from a captured HIP graph")
+    ap.add_argument("--eager", action="store_true", help="launch the timed steps one call at a time (no graph)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain 256 MiB device copies (scale for the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this decode MoE expert path runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not run)"}))
+                                   "(expert-parallel sharding across GPUs is a design, not run here)"}))
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     from int4_grouped_expert_router_amd import Context
     from int4_grouped_expert_router_amd import binding as B
     from synth import get_config
@@ -160,8 +190,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # The timed steps replay from one captured graph (the host enqueues a whole sequence of
+    # layers at once, as a decode loop would); --eager launches them one call at a time.
     graph = None
-    if args.graph:
+    if not args.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(args.steps):
@@ -181,10 +213,16 @@ def main():
     elapsed = time.perf_counter() - t0
     us_per_layer = elapsed / args.steps * 1e6
 
-    # the same steps again with per-kernel HIP events on the launch stream
+    # The same steps again, eager, with HIP events around every launch on the library's stream.
+    # They go in bursts queued behind a GPU sleep, so the GPU runs each burst back to back and
+    # an event pair spans its kernel only, not host launch gaps.
     ctx.set_profiling(True)
-    for i in range(args.steps):
-        step(i)
+    sleep_cycles = calibrate_sleep(torch, stream)
+    burst = 40
+    for b0 in range(0, args.steps, burst):
+        torch.cuda._sleep(sleep_cycles)
+        for i in range(b0, min(args.steps, b0 + burst)):
+            step(i)
     torch.cuda.synchronize()
     kt = {name: ctx.profile(k) for name, k in
           [("route", B.I4MOE_K_ROUTE), ("dual", B.I4MOE_K_DUAL), ("down", B.I4MOE_K_DOWN), ("take", B.I4MOE_K_TAKE)]}

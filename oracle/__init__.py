@@ -27,8 +27,7 @@ Sources (the web pages the method is described on), cited in each module as:
             section "What": per-expert weighting, fixed-order reduce into a
             per-issue slot, take reduces slots in issue order into the residual.
 
-Readings of points the pages leave open are listed where they are used and
-collected in the design doc.  Every function here is pinned by ``tests/test_oracle_*``
+Readings of points the pages leave open are stated where they are used.  Every function here is pinned by ``tests/test_oracle_*``
 against brute force, closed forms, invariants or library routines; none is
 "parity unpinned".
 """
