@@ -32,8 +32,8 @@ struct Layer {
   int E = 0, D = 0, I = 0;             // router experts; model dim; expert intermediate
   float *W = nullptr, *b = nullptr;    // router
   std::vector<i4moe_tensor> gate, up, down;
-  TensorDesc *d_tab = nullptr;         // [3][kMaxE]: gate, up, down descriptors
-  std::vector<TensorDesc> h_tab;       // host copy of d_tab
+  ExpertRec *d_tab = nullptr;          // [kMaxE]: gate, up, down descriptors per expert
+  std::vector<ExpertRec> h_tab;        // host copy of d_tab
   int route_buf = -1;                  // ring entry holding this layer's latest route
   bool routed = false;
   int route_S = 0, route_K = 0;
@@ -158,22 +158,28 @@ hipEvent_t get_event(i4moe_ctx *c) {
   return e;
 }
 
-// Launch wrapper: brackets the launch with events when profiling.
+// Launch wrapper: when profiling, hands the launcher an event pair that records the kernel's
+// own start and end (the launch itself timestamps them), so host launch gaps are not counted.
 template <class F>
 hipError_t timed(i4moe_ctx *c, int kernel, F &&f) {
   hipEvent_t a = nullptr, b = nullptr;
   if (c->profiling) {
     a = get_event(c);
     b = get_event(c);
-    if (a && b) (void)hipEventRecord(a, c->stream);
+    if (!a || !b) {
+      if (a) c->ev_pool.push_back(a);
+      if (b) c->ev_pool.push_back(b);
+      a = b = nullptr;
+    }
   }
-  hipError_t e = f();
-  if (c->profiling && a && b) {
-    (void)hipEventRecord(b, c->stream);
-    c->recs.push_back({kernel, a, b});
-  } else {
-    if (a) c->ev_pool.push_back(a);
-    if (b) c->ev_pool.push_back(b);
+  hipError_t e = f(a, b);
+  if (a && b) {
+    if (e == hipSuccess) {
+      c->recs.push_back({kernel, a, b});
+    } else {
+      c->ev_pool.push_back(a);
+      c->ev_pool.push_back(b);
+    }
   }
   return e;
 }
@@ -243,52 +249,73 @@ int ensure_route_scratch(i4moe_ctx *c, size_t partial, size_t logits) {
 int ensure_layer_tables(i4moe_ctx *c, Layer &L) {
   if (L.d_tab) return I4MOE_OK;
   hipError_t e;
-  if ((e = dalloc(&L.d_tab, sizeof(TensorDesc) * 3 * kMaxE)) != hipSuccess) return hip_fail(c, e, "hipMalloc(table)");
-  L.h_tab.assign(3 * kMaxE, TensorDesc{});
-  e = hipMemcpyAsync(L.d_tab, L.h_tab.data(), sizeof(TensorDesc) * 3 * kMaxE, hipMemcpyHostToDevice, c->stream);
+  if ((e = dalloc(&L.d_tab, sizeof(ExpertRec) * kMaxE)) != hipSuccess) return hip_fail(c, e, "hipMalloc(table)");
+  L.h_tab.assign(kMaxE, ExpertRec{});
+  e = hipMemcpyAsync(L.d_tab, L.h_tab.data(), sizeof(ExpertRec) * kMaxE, hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "table init");
   return I4MOE_OK;
 }
 
-int write_table_entry(i4moe_ctx *c, Layer &L, int which, int expert) {
-  const size_t i = (size_t)which * kMaxE + expert;
-  hipError_t e = hipMemcpyAsync(L.d_tab + i, &L.h_tab[i], sizeof(TensorDesc), hipMemcpyHostToDevice, c->stream);
+int write_table_entry(i4moe_ctx *c, Layer &L, int expert) {
+  hipError_t e =
+      hipMemcpyAsync(L.d_tab + expert, &L.h_tab[expert], sizeof(ExpertRec), hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "table update");
   return I4MOE_OK;
 }
 
 // Pick the per-lane span V (dwords) and pass count P for rows of C columns, then tile the rows.
+//
+// Spans of 4 dwords (one aligned 16-byte load per lane) stream best, then 2, then 1; 3-dword
+// spans split across 16-byte boundaries and measured slower than any of them, so they are not
+// used.  A wider span wins while it wastes at most half of its lanes (lanes past the row load
+// nothing).  Tensors whose group size splits a span need the per-byte path, so a span that
+// avoids it is preferred.
+//
+// Tiles: enough of them to fill the chip once, but never less than kMinWaveBytes of weights
+// per wave (short tiles pay the startup latency of a wave for little data).
+constexpr int kMinWaveBytes = 12 * 1024;
+
 Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector<int> &group_sizes, int n_cu,
                double wave_factor) {
   const int RD = (C + 7) / 8;
   Plan best;
-  double best_key = -1.0;
-  for (int V = 4; V >= 1; --V) {
-    if (V == 3 && RD % 3 != 0) continue;
-    const int P = (RD + 64 * V - 1) / (64 * V);
-    if (P > 4) continue;
-    bool gen = false;
-    for (int gs : group_sizes)
-      if (gs % (8 * V) != 0) gen = true;
-    const double eff = (double)RD / (64.0 * V * P);
-    const double key = (gen ? 0.0 : 2.0) + eff;
-    if (key > best_key + 1e-12) {
-      best_key = key;
+  bool have = false;
+  for (int pass = 0; pass < 2 && !have; ++pass) {
+    for (int V : {4, 2, 1}) {
+      const int P = (RD + 64 * V - 1) / (64 * V);
+      if (P > 4) continue;
+      bool gen = false;
+      for (int gs : group_sizes)
+        if (gs % (8 * V) != 0) gen = true;
+      const double eff = (double)RD / (64.0 * V * P);
+      // pass 0: spans that need no per-byte path and use at least half their lanes
+      if (pass == 0 && (gen || (eff < 0.5 && V > 1))) continue;
       best.V = V;
       best.P = P;
       best.gen = gen;
+      have = true;
+      break;
     }
   }
+  if (!have) {  // only per-byte spans remain: the narrowest that fits
+    best.V = 1;
+    best.P = (RD + 63) / 64;
+    best.gen = true;
+  }
   const bool use_xb = dual && xb && !best.gen;
-  const int RB = rows_per_step(best.V, best.P, dual ? 2 : 1, use_xb ? 32 : 16);
+  const int NT = dual ? 2 : 1;
+  const int RB = rows_per_step(best.V, best.P, NT, use_xb ? 32 : 16);
   const long long units = (long long)max_rows * O;
   // one wave per resident slot: the tiles fill the chip once
-  const long long resident = (long long)proj_blocks_per_cu(best.V, best.P, dual ? 2 : 1, best.gen, use_xb) * 4 * n_cu;
+  const long long resident = (long long)proj_blocks_per_cu(best.V, best.P, NT, best.gen, use_xb) * 4 * n_cu;
   long long target = (long long)(resident * wave_factor);
   if (target < 64) target = 64;
   int tr = (int)((units + target - 1) / target);
+  const int row_bytes = 4 * RD;
+  const int tr_min = (kMinWaveBytes + NT * row_bytes - 1) / (NT * row_bytes);
+  if (tr < tr_min) tr = tr_min;
   tr = round_up(tr < RB ? RB : tr, RB);
   if (tr > (kWave / RB) * RB) tr = (kWave / RB) * RB;  // one result per lane of the tile's wave
   best.tile_rows = tr;
@@ -468,7 +495,7 @@ i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, in
   t.desc.row_bytes = row_bytes;
   t.desc.gs = ng > 1 ? gs : 0;
   t.desc.ng = ng;
-  t.desc.pad = 0;
+  t.desc.live = 0;
   const uint32_t h = c->next_handle++;
   c->tensors[h] = t;
   return h;
@@ -488,12 +515,10 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
       bool hit = false;
       for (int w = 0; w < 3; ++w) hit = hit || (*v[w])[x] == h;
       if (!hit) continue;
-      for (int w = 0; w < 3; ++w) {
-        (*v[w])[x] = 0;
-        L.h_tab[(size_t)w * kMaxE + x] = TensorDesc{};
-        int rc = write_table_entry(c, L, w, (int)x);
-        if (rc) return rc;
-      }
+      for (int w = 0; w < 3; ++w) (*v[w])[x] = 0;
+      L.h_tab[x] = ExpertRec{};
+      int rc = write_table_entry(c, L, (int)x);
+      if (rc) return rc;
     }
   }
   dfree(it->second.q);
@@ -531,12 +556,10 @@ int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4m
   L.gate[expert] = gate;
   L.up[expert] = up;
   L.down[expert] = down;
-  const TensorDesc *d[3] = {&G, &U, &Dn};
-  for (int w = 0; w < 3; ++w) {
-    L.h_tab[(size_t)w * kMaxE + expert] = *d[w];
-    if ((rc = write_table_entry(c, L, w, expert))) return rc;
-  }
-  return I4MOE_OK;
+  L.h_tab[expert].t[0] = G;
+  L.h_tab[expert].t[1] = U;
+  L.h_tab[expert].t[2] = Dn;
+  return write_table_entry(c, L, expert);
 }
 
 int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, const float *bias) {
@@ -604,6 +627,8 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   if (splits > 16) splits = 16;
   int cps = round_up((L->D + splits - 1) / splits, 256);
   splits = (L->D + cps - 1) / cps;
+  if (L->E * splits > kMaxE)  // partials of one token staged by the select kernel
+    return fail(c, I4MOE_EUNSUPPORTED, "router split plan out of range (E=%d, splits=%d)", L->E, splits);
   if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
   const int ring = c->ring_next;
   for (int s = 0; s < c->nslots; ++s)
@@ -629,7 +654,7 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   a.norm_topk = norm_topk ? 1 : 0;
   a.topp = topp;
   a.routed_scale = routed_scale;
-  hipError_t e = timed(c, I4MOE_K_ROUTE, [&] { return launch_route(a, c->stream); });
+  hipError_t e = timed(c, I4MOE_K_ROUTE, [&](hipEvent_t t0, hipEvent_t t1) { return launch_route(a, c->stream, t0, t1); });
   if (e != hipSuccess) return hip_fail(c, e, "route launch");
   c->ring_next = (ring + 1) % kRing;
   L->route_buf = ring;
@@ -667,7 +692,7 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   // The experts this issue may touch decide the kernel variant.
   std::vector<int> gs_in, gs_dn;
   auto note = [&](int e) {
-    const TensorDesc &g = L->h_tab[e], &u = L->h_tab[kMaxE + e], &d = L->h_tab[2 * kMaxE + e];
+    const TensorDesc &g = L->h_tab[e].t[0], &u = L->h_tab[e].t[1], &d = L->h_tab[e].t[2];
     if (g.ng > 1) gs_in.push_back(g.gs);
     if (u.ng > 1) gs_in.push_back(u.gs);
     if (d.ng > 1) gs_dn.push_back(d.gs);
@@ -762,8 +787,12 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
 
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
-  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&] { return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, ad, pd.blocks, c->stream); });
-  if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&] { return launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream); });
+  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, ad, pd.blocks, c->stream, t0, t1);
+    });
+  if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
+    });
   if (e != hipSuccess) return hip_fail(c, e, "issue launch");
   c->slots[s].S = S;
   c->slots[s].D = L->D;
@@ -804,7 +833,7 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
   a.y_ld = c->y_ld;
   a.S = S;
   a.D = c->slots[0].D;
-  hipError_t e = timed(c, I4MOE_K_TAKE, [&] { return launch_take(a, c->stream); });
+  hipError_t e = timed(c, I4MOE_K_TAKE, [&](hipEvent_t t0, hipEvent_t t1) { return launch_take(a, c->stream, t0, t1); });
   if (e != hipSuccess) {
     c->poisoned = true;
     return hip_fail(c, e, "take launch");

@@ -26,9 +26,17 @@ struct TensorDesc {
   int32_t row_bytes;
   int32_t gs;          // group size; 0 when ng == 1
   int32_t ng;          // scales per row (1 = per-row)
-  int32_t pad;
+  int32_t live;        // in a row descriptor's first record: 1 = the row is part of the group
 };
 static_assert(sizeof(TensorDesc) == 40, "tensor descriptor layout");
+
+// One expert of a layer's table: gate, up and down tensors in a 128-byte record, so a row
+// descriptor starts with a straight copy of it.
+struct ExpertRec {
+  TensorDesc t[3];
+  int32_t pad[2];
+};
+static_assert(sizeof(ExpertRec) == 128, "expert record layout");
 
 // Group record (layout documented with I4MOE_GROUP_WORDS).
 struct GroupDev {
@@ -43,7 +51,8 @@ struct GroupDev {
 };
 static_assert(sizeof(GroupDev) == I4MOE_GROUP_WORDS * 4, "group record layout");
 
-// Everything a projection wave needs about its group row, in one 128-byte record: the
+// Everything a projection wave needs about its group row, in one 128-byte record (t[0].live
+// marks the rows of the current group; every row of the buffer is rewritten per group): the
 // expert's gate / up / down tensors, the token row of x and the route weight.
 struct RowDesc {
   TensorDesc t[3];
@@ -74,7 +83,7 @@ struct RouteArgs {
   double *partial;           // [S][E][splits]
   double *logits;            // [S][E]
   GroupBuf *out;
-  const TensorDesc *table;   // layer expert table [3][kMaxE], or null (route only)
+  const ExpertRec *table;    // layer expert table [kMaxE], or null (route only)
   int E, D, S, K;
   int x_bf16;
   int splits, cols_per_split;
@@ -100,13 +109,17 @@ struct TakeArgs {
   int nslots, y_ld, S, D;
 };
 
-// Launchers (defined in the kernel translation units).  They return hipGetLastError().
-hipError_t launch_route(const RouteArgs &a, hipStream_t st);
-hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st);
-hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st);
-hipError_t launch_take(const TakeArgs &a, hipStream_t st);
+// Launchers (defined in the kernel translation units).  They return hipGetLastError().  With
+// t0/t1 non-null the launch records the kernel's own start and end into them
+// (hipExtLaunchKernel), so an event pair spans the kernel alone.
+hipError_t launch_route(const RouteArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st,
+                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
+                       hipEvent_t t1 = nullptr);
+hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb);  // resident 256-thread workgroups per CU
-hipError_t launch_group_store(const GroupDev &g, const TensorDesc *table, GroupBuf *dst, hipStream_t st);
+hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBuf *dst, hipStream_t st);
 
 // Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.
 constexpr int rows_per_step(int V, int P, int tensors, int budget) {

@@ -24,6 +24,8 @@
 // scale (the row scale, or the span's group scale when gs is a multiple of 8V), then the
 // lane partials are summed across the wave with DPP in a fixed pattern (deterministic).
 // Group sizes that split a span fall back to a per-byte path.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace i4moe {
@@ -179,7 +181,7 @@ __device__ __forceinline__ TensorDesc ld_desc(const TensorDesc I4MOE_AS4 &d) {
   t.row_bytes = d.row_bytes;
   t.gs = d.gs;
   t.ng = d.ng;
-  t.pad = 0;
+  t.live = d.live;
   return t;
 }
 
@@ -409,11 +411,11 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   // tile, descriptors and base addresses derived from it) in scalar registers.
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const CGroupBuf G = (CGroupBuf)a.grp;
-  const int jr = blockIdx.x / a.tile_groups;
-  if (jr >= min(G->g.n_rows, kRows)) return;
+  const int jr = blockIdx.x / a.tile_groups;  // < kRows: the grid never exceeds the row cap
   const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
 
-  // Everything about this row in one scalar record: tensors, token, weight.
+  // Everything about this row in one scalar record: tensors, token, weight, and whether the
+  // row belongs to the group (one memory round trip).
   TensorDesc T[NT];
   if constexpr (NT == 2) {
     T[0] = ld_desc(G->rows[jr].t[0]);
@@ -422,6 +424,15 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
     T[0] = ld_desc(G->rows[jr].t[2]);
   }
   const int arow = NT == 2 ? G->rows[jr].token : jr;
+  const int live = G->rows[jr].t[0].live;
+  // Pin the record's loads above the liveness branch (otherwise they are sunk below it and
+  // cost a second memory round trip).
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    asm volatile("" ::"s"(T[n].q), "s"(T[n].s), "s"(T[n].O), "s"(T[n].C), "s"(T[n].row_bytes), "s"(T[n].gs),
+                 "s"(T[n].ng));
+  asm volatile("" ::"s"(arow), "s"(live));
+  if (!live) return;
 
   const int C = a.C;
   const int RD = (C + 7) >> 3;
@@ -488,7 +499,6 @@ const void *kernel_ptr_t(int V, int P) {
   if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, XB>);
   I4MOE_PTR(1, 1) I4MOE_PTR(1, 2) I4MOE_PTR(1, 3) I4MOE_PTR(1, 4)
   I4MOE_PTR(2, 1) I4MOE_PTR(2, 2) I4MOE_PTR(2, 3) I4MOE_PTR(2, 4)
-  I4MOE_PTR(3, 1) I4MOE_PTR(3, 2) I4MOE_PTR(3, 3) I4MOE_PTR(3, 4)
   I4MOE_PTR(4, 1) I4MOE_PTR(4, 2) I4MOE_PTR(4, 3) I4MOE_PTR(4, 4)
 #undef I4MOE_PTR
   return nullptr;
@@ -504,11 +514,13 @@ const void *kernel_ptr(int V, int P, int NT, bool gen, bool xb) {
 
 size_t lds_bytes(int V, int P, bool xb) { return 4u * (size_t)(xb ? P * 64 * V * 4 : P * 64 * V * 8); }
 
-hipError_t launch(int V, int P, int NT, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st) {
+hipError_t launch(int V, int P, int NT, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
+                  hipEvent_t t1) {
   const void *k = kernel_ptr(V, P, NT, gen, xb);
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
+  if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds_bytes(V, P, xb), st, t0, t1, 0);
   return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds_bytes(V, P, xb), st);
 }
 
@@ -516,7 +528,7 @@ hipError_t launch(int V, int P, int NT, bool gen, bool xb, const ProjArgs &a, in
 
 int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb) {
   static int cache[5][5][3][2][2] = {};
-  if (V < 1 || V > 4 || P < 1 || P > 4 || NT < 1 || NT > 2) return 1;
+  if (V < 1 || V > 4 || V == 3 || P < 1 || P > 4 || NT < 1 || NT > 2) return 1;
   int &c = cache[V][P][NT][gen ? 1 : 0][xb ? 1 : 0];
   if (c == 0) {
     const void *k = kernel_ptr(V, P, NT, gen, xb);
@@ -530,12 +542,14 @@ int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb) {
   return c;
 }
 
-hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st) {
-  hipError_t e = launch(V, P, 2, gen, xb && !gen, a, blocks, st);
+hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
+                       hipEvent_t t1) {
+  hipError_t e = launch(V, P, 2, gen, xb && !gen, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
-hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st) {
-  hipError_t e = launch(V, P, 1, gen, false, a, blocks, st);
+hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
+                       hipEvent_t t1) {
+  hipError_t e = launch(V, P, 1, gen, false, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

@@ -10,27 +10,34 @@
 //
 // One thread owns one (t, i); the order of every sum is fixed, so results are bitwise
 // reproducible run to run.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace i4moe {
 namespace {
 
+static_assert(kRows == kWave, "take stages one slot per wave");
+
 __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
-  __shared__ int s_rows[kSlots][kRows];
-  __shared__ float s_w[kSlots][kRows];
-  __shared__ int s_cnt[kSlots];
+  __shared__ int s_rr[kSlots][kRows];    // reduce order of each slot (group rows, token-major)
+  __shared__ float s_rw[kSlots][kRows];  // route weight of each group row
+  __shared__ int s_r0[kSlots], s_cnt[kSlots];
   const int t = blockIdx.y;
-  // This token's rows of every slot, in reduce order, staged once per workgroup.
+  // Each slot's records for token t, staged once per workgroup: all reads of a slot are
+  // independent (whole arrays, not chased through the row indices), so they are in flight
+  // together.
   for (int q = threadIdx.x; q < a.nslots * kRows; q += kBlock) {
-    const int s = q / kRows, k = q - s * kRows;
+    // kRows == kWave: the slot is uniform across a wave, so its record pointer is a scalar load
+    const int s = __builtin_amdgcn_readfirstlane(q / kRows), k = q - s * kRows;
     const GroupDev &g = a.groups[s]->g;
+    const int rr = g.red_rows[k];
+    const float rw = g.row_weight[k];
     const int r0 = g.tok_row0[t], r1 = g.tok_row0[t + 1];
-    if (k == 0) s_cnt[s] = r1 - r0;
-    if (k < r1 - r0) {
-      const int row = g.red_rows[r0 + k];
-      s_rows[s][k] = row;
-      s_w[s][k] = g.row_weight[row];
-    }
+    s_rr[s][k] = rr;
+    s_rw[s][k] = rw;
+    s_r0[s] = r0;  // every lane stores the same value
+    s_cnt[s] = r1 - r0;
   }
   __syncthreads();
   const int i = blockIdx.x * kBlock + threadIdx.x;
@@ -38,8 +45,18 @@ __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
   float total = 0.f;
   for (int s = 0; s < a.nslots; ++s) {
     const float *__restrict__ y = a.y[s];
+    const int cnt = s_cnt[s];
     float acc = 0.f;
-    for (int k = 0; k < s_cnt[s]; ++k) acc = fmaf(s_w[s][k], y[(size_t)s_rows[s][k] * a.y_ld + i], acc);
+    // eight rows' loads in flight at a time (clamped row index, unconditional loads), then the
+    // FMAs in route order
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = y[(size_t)s_rr[s][s_r0[s] + min(k0 + j, cnt - 1)] * a.y_ld + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < cnt) acc = fmaf(s_rw[s][s_rr[s][s_r0[s] + k0 + j]], v[j], acc);
+    }
     total = (s == 0) ? acc : total + acc;
   }
   float *rp = a.resid + (size_t)t * a.D + i;
@@ -49,30 +66,38 @@ __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
 // Store an explicit (host-built) group record and fill its row descriptors from the layer's
 // expert table; the record travels as a kernel argument, so the store is ordered on the
 // stream like every other step.
-__global__ void k_group_store(GroupDev g, const TensorDesc *table, GroupBuf *dst) {
+__global__ void k_group_store(GroupDev g, const ExpertRec *table, GroupBuf *dst) {
   const int32_t *src = reinterpret_cast<const int32_t *>(&g);
   int32_t *d = reinterpret_cast<int32_t *>(&dst->g);
   for (int w = threadIdx.x; w < I4MOE_GROUP_WORDS; w += blockDim.x) d[w] = src[w];
-  for (int r = threadIdx.x; r < g.n_rows && r < kRows; r += blockDim.x) {
-    const int e = g.row_expert[r];
+  for (int r = threadIdx.x; r < kRows; r += blockDim.x) {
     RowDesc &rd = dst->rows[r];
-    rd.t[0] = table[e];
-    rd.t[1] = table[kMaxE + e];
-    rd.t[2] = table[2 * kMaxE + e];
-    rd.token = g.row_token[r];
-    rd.weight = g.row_weight[r];
+    if (r < g.n_rows) {
+      const int e = g.row_expert[r];
+      rd.t[0] = table[e].t[0];
+      rd.t[1] = table[e].t[1];
+      rd.t[2] = table[e].t[2];
+      rd.t[0].live = 1;
+      rd.token = g.row_token[r];
+      rd.weight = g.row_weight[r];
+    } else {
+      rd.t[0].live = 0;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_take(const TakeArgs &a, hipStream_t st) {
+hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   dim3 grid((a.D + kBlock - 1) / kBlock, a.S);
-  hipLaunchKernelGGL(k_take, grid, dim3(kBlock), 0, st, a);
+  if (t0 || t1)
+    hipExtLaunchKernelGGL(k_take, grid, dim3(kBlock), 0, st, t0, t1, 0, a);
+  else
+    hipLaunchKernelGGL(k_take, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_group_store(const GroupDev &g, const TensorDesc *table, GroupBuf *dst, hipStream_t st) {
+hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBuf *dst, hipStream_t st) {
   hipLaunchKernelGGL(k_group_store, dim3(1), dim3(kBlock), 0, st, g, table, dst);
   return hipGetLastError();
 }
