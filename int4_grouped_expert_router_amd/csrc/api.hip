@@ -55,6 +55,7 @@ struct ProfRec {
 struct Plan {
   int V = 4, P = 1;
   bool gen = false;
+  bool rows16 = false;  // down projection with 16 lanes per row
   int tile_rows = 1, tile_groups = 1, blocks = 1;
 };
 
@@ -306,10 +307,25 @@ Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector
   }
   const bool use_xb = dual && xb && !best.gen;
   const int NT = dual ? 2 : 1;
-  const int RB = rows_per_step(best.V, best.P, NT, use_xb ? 32 : 16);
+  // Short down rows run 16 lanes per row (four rows per wave instruction): a fully used wave
+  // and a 16-lane reduction instead of a 64-lane one.
+  if (!dual && RD <= 4 * 64) {
+    bool aligned = true;
+    for (int gs : group_sizes)
+      if (gs % 32 != 0) aligned = false;
+    if (aligned) {
+      best.rows16 = true;
+      best.V = 4;
+      best.P = (RD + 63) / 64;
+      best.gen = false;
+    }
+  }
+  const int RB = best.rows16 ? 4 : rows_per_step(best.V, best.P, NT, use_xb ? 32 : 16);
   const long long units = (long long)max_rows * O;
   // one wave per resident slot: the tiles fill the chip once
-  const long long resident = (long long)proj_blocks_per_cu(best.V, best.P, NT, best.gen, use_xb) * 4 * n_cu;
+  const long long resident =
+      (long long)(best.rows16 ? rows16_blocks_per_cu(best.P) : proj_blocks_per_cu(best.V, best.P, NT, best.gen, use_xb)) *
+      4 * n_cu;
   long long target = (long long)(resident * wave_factor);
   if (target < 64) target = 64;
   int tr = (int)((units + target - 1) / target);
@@ -455,7 +471,7 @@ i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, in
   }
   const int row_bytes = round_up(C / 2, 16);
   const size_t qbytes = (size_t)O * row_bytes + 64;
-  if (qbytes > (size_t)0x7fffffff) {
+  if (qbytes > (size_t)0x7fff0000) {  // buffer offsets (row * row_bytes, a few rows past the end) stay in int32
     fail(c, I4MOE_EUNSUPPORTED, "tensor too large (%zu bytes)", qbytes);
     return 0;
   }
@@ -772,6 +788,7 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   ad.O = L->I;
   ad.C = L->D;
   ad.tile_groups = pd.tile_groups;
+  ad.grid_rows = max_rows;
   ad.tile_rows = pd.tile_rows;
   ProjArgs an{};
   an.grp = grp;
@@ -783,6 +800,7 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   an.O = L->D;
   an.C = L->I;
   an.tile_groups = pn.tile_groups;
+  an.grid_rows = max_rows;
   an.tile_rows = pn.tile_rows;
 
   hipError_t e = hipSuccess;
@@ -791,7 +809,8 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
       return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, ad, pd.blocks, c->stream, t0, t1);
     });
   if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
-      return launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
+      return pn.rows16 ? launch_down16(pn.P, an, pn.blocks, c->stream, t0, t1)
+                       : launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
     });
   if (e != hipSuccess) return hip_fail(c, e, "issue launch");
   c->slots[s].S = S;

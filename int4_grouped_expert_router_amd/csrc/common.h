@@ -100,6 +100,7 @@ struct ProjArgs {
   int act_bf16;
   int O, C;                  // rows and columns of every tensor in the launch
   int tile_groups, tile_rows;  // workgroups per group row (4 tiles each), rows per tile
+  int grid_rows;             // group rows the grid covers (grid = grid_rows * tile_groups)
 };
 
 struct TakeArgs {
@@ -118,6 +119,11 @@ hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int b
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                        hipEvent_t t1 = nullptr);
 hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Down projection over rows of at most 256 weight dwords (C <= 2048): 16 lanes per row, P
+// passes of 4 dwords per lane; f32 activations, per-row or 32-column-aligned group scales.
+hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
+                         hipEvent_t t1 = nullptr);
+int rows16_blocks_per_cu(int P);
 int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb);  // resident 256-thread workgroups per CU
 hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBuf *dst, hipStream_t st);
 

@@ -258,14 +258,16 @@ __device__ __forceinline__ void stage_store(uint32_t *lds, const uint32_t (&xs)[
   }
 }
 
-template <int V, int P, bool XB>
+// The lane's slice of the staged row: dword spans p * LR * V + lane * V + [0, V) for LR lanes
+// per row.
+template <int V, int P, bool XB, int LR = kWave>
 __device__ __forceinline__ void read_act(uint32_t (&raw)[P][V][XB ? 4 : 8], const uint32_t *lds, int lane) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int p = 0; p < P; ++p) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int d = p * 64 * V + lane * V + v;
+      const int d = p * LR * V + lane * V + v;
       if constexpr (XB) {
         const u4 q = *reinterpret_cast<const u4 *>(lds + 4 * d);
         raw[p][v][0] = q.x; raw[p][v][1] = q.y; raw[p][v][2] = q.z; raw[p][v][3] = q.w;
@@ -410,6 +412,11 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   // index is uniform by construction and readfirstlane lets the compiler keep it (and the row,
   // tile, descriptors and base addresses derived from it) in scalar registers.
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Touch the first word of every row record of the grid, so the first workgroups to start
+  // bring all records into their XCD's L2 before the weight stream fills the memory queues
+  // (a later workgroup's record read then hits or joins a read already in flight).  The
+  // value is consumed at the very end, so nothing waits for it.
+  const uint32_t touch = reinterpret_cast<const uint32_t *>(a.grp->rows + min(lane, a.grid_rows - 1))[0];
   const CGroupBuf G = (CGroupBuf)a.grp;
   const int jr = blockIdx.x / a.tile_groups;  // < kRows: the grid never exceeds the row cap
   const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
@@ -491,7 +498,140 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
     o += 2 * RB;
   } while (o < o_end);
   if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
+  asm volatile("" ::"v"(touch));
 }
+
+// ---- Short rows (the down projection, C <= 2048 columns): 16 lanes per row, so one wave
+// instruction covers four rows.  A row's dot product is then summed over 16 lanes (four DPP
+// steps, all four rows at once) instead of 64, and no lane idles when a row is shorter than
+// 64 lanes x 16 bytes.  f32 activations, per-row or span-aligned group scales.
+constexpr int kLR = 16;                  // lanes per row
+constexpr int kGR = kWave / kLR;         // rows per wave instruction
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp<0x140, 0xF>(v);  // row_mirror: every lane of the 16 now holds the row's sum
+  return v;
+}
+
+template <int P>
+struct Step16 {
+  uint32_t w[P][4];
+  float s[P];
+};
+
+// One step: four consecutive rows o .. o+3, lane group g on row o + g.  The buffer ranges end
+// at row o_end, so rows past the tile read zeros without a memory access; spans past the row
+// get an offset past every range for the same effect.
+template <int P>
+__device__ __forceinline__ void load_step16(Step16<P> &st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                            const TensorDesc &T, const int (&woff)[P], const int (&gi)[P], int o,
+                                            int g) {
+  const int row = o + g;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    load_span<4>(wr, woff[p] < 0 ? 0x7ffffff0 : row * T.row_bytes + woff[p], st.w[p]);
+    st.s[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * (row * T.ng + gi[p]), 0, 0));
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void compute_step16(const Step16<P> &st, const Act<4, P, false> &A, int o, int o_begin,
+                                               int lane, float &outv) {
+  float acc = 0.f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float ap = A.xm[p];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) ap = dot8(st.w[p][v], A.xe[p][v], A.xo[p][v], ap);
+    acc = fmaf(st.s[p], ap, acc);
+  }
+  const float sum = row16_sum(acc);
+#pragma unroll
+  for (int g = 0; g < kGR; ++g) {
+    const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), g * kLR));
+    if (lane == o - o_begin + g) outv = r;
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
+  constexpr int V = 4;
+  extern __shared__ uint32_t s_act[];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (kLR - 1), g = lane / kLR;
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t touch = reinterpret_cast<const uint32_t *>(a.grp->rows + min(lane, a.grid_rows - 1))[0];
+  const CGroupBuf G = (CGroupBuf)a.grp;
+  const int jr = blockIdx.x / a.tile_groups;
+  const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
+  const TensorDesc T = ld_desc(G->rows[jr].t[2]);
+  const int live = G->rows[jr].t[0].live;
+  asm volatile("" ::"s"(T.q), "s"(T.s), "s"(T.O), "s"(T.C), "s"(T.row_bytes), "s"(T.gs), "s"(T.ng));
+  asm volatile("" ::"s"(live));
+  if (!live) return;
+
+  const int C = a.C;
+  const int RD = (C + 7) >> 3;
+  int gi[P], woff[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int ds = p * kLR * V + li * V;
+    gi[p] = (T.ng > 1 && ds < RD) ? (8 * ds) / T.gs : 0;
+    woff[p] = ds < RD ? 4 * ds : -1;
+  }
+  const int o_begin = tile * a.tile_rows;
+  const int o_end = min(o_begin + a.tile_rows, a.O);
+  const bool work = o_begin < o_end;
+  const int rows_in = work ? o_end : 0;  // buffer ranges: rows [0, o_end) of this tensor
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
+
+  uint32_t xs[stage_words<V, P, false>() * kLR / kWave];
+  stage_load<false>(xs, a.act, 0, (size_t)jr * a.act_ld, C);
+  __builtin_amdgcn_sched_barrier(0);
+  Step16<P> b0, b1;
+  load_step16<P>(b0, wr, sr, T, woff, gi, o_begin, g);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step16<P>(b1, wr, sr, T, woff, gi, o_begin + kGR, g);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<false>(s_act, xs, 0, C);
+  __syncthreads();
+  if (!work) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  uint32_t raw[P][V][8];
+  read_act<V, P, false, kLR>(raw, s_act, li);
+  Act<V, P, false> A;
+  finish_act<V, P, false>(A, raw);
+
+  float outv = 0.f;
+  int o = o_begin;
+  do {
+    compute_step16<P>(b0, A, o, o_begin, lane, outv);
+    load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
+    if (o + kGR < o_end) compute_step16<P>(b1, A, o + kGR, o_begin, lane, outv);
+    load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
+    o += 2 * kGR;
+  } while (o < o_end);
+  if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
+  asm volatile("" ::"v"(touch));
+}
+
+const void *rows16_ptr(int P) {
+  switch (P) {
+    case 1: return reinterpret_cast<const void *>(&k_rows16<1>);
+    case 2: return reinterpret_cast<const void *>(&k_rows16<2>);
+    case 3: return reinterpret_cast<const void *>(&k_rows16<3>);
+    case 4: return reinterpret_cast<const void *>(&k_rows16<4>);
+    default: return nullptr;
+  }
+}
+
+size_t rows16_lds_bytes(int P) { return 4u * (size_t)P * kLR * 4 * 8; }
 
 template <int NT, bool GEN, bool XB>
 const void *kernel_ptr_t(int V, int P) {
@@ -547,6 +687,31 @@ hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int b
   hipError_t e = launch(V, P, 2, gen, xb && !gen, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
+int rows16_blocks_per_cu(int P) {
+  static int cache[5] = {};
+  if (P < 1 || P > 4) return 1;
+  if (cache[P] == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, rows16_ptr(P), kBlock, rows16_lds_bytes(P)) != hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    cache[P] = n;
+  }
+  return cache[P];
+}
+
+hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  const void *k = rows16_ptr(P);
+  if (!k) return hipErrorInvalidValue;
+  ProjArgs args = a;
+  void *params[] = {&args};
+  hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st, t0, t1, 0)
+                            : hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
                        hipEvent_t t1) {
   hipError_t e = launch(V, P, 1, gen, false, a, blocks, st, t0, t1);
