@@ -274,8 +274,8 @@ int write_table_entry(i4moe_ctx *c, Layer &L, int expert) {
 // nothing).  Tensors whose group size splits a span need the per-byte path, so a span that
 // avoids it is preferred.
 //
-// Tiles: enough of them to fill the chip once, but never less than kMinWaveBytes of weights
-// per wave (short tiles pay the startup latency of a wave for little data).
+// Tiles: about two workgroups per CU, but never less than kMinWaveBytes of weights per wave
+// (short tiles pay the startup latency of a wave for little data).
 constexpr int kMinWaveBytes = 12 * 1024;
 
 Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector<int> &group_sizes, int n_cu,
@@ -320,13 +320,16 @@ Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector
       best.gen = false;
     }
   }
-  const int RB = best.rows16 ? 4 : rows_per_step(best.V, best.P, NT, use_xb ? 32 : 16);
+  const int RB = best.rows16 ? 4 : rows_per_step(best.V, best.P, NT, 16);
   const long long units = (long long)max_rows * O;
-  // one wave per resident slot: the tiles fill the chip once
+  // Two workgroups (eight waves) per CU, or fewer if fewer fit: every CU gets the same share
+  // and each wave streams several steps, which measured faster than filling every resident
+  // slot with shorter tiles.
   const long long resident =
       (long long)(best.rows16 ? rows16_blocks_per_cu(best.P) : proj_blocks_per_cu(best.V, best.P, NT, best.gen, use_xb)) *
       4 * n_cu;
-  long long target = (long long)(resident * wave_factor);
+  const long long per_cu = resident < 8LL * n_cu ? resident : 8LL * n_cu;
+  long long target = (long long)(per_cu * wave_factor);
   if (target < 64) target = 64;
   int tr = (int)((units + target - 1) / target);
   const int row_bytes = 4 * RD;

@@ -405,7 +405,7 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
 // per lane).
 template <int V, int P, int NT, bool GEN, bool XB>
 __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
-  constexpr int RB = rows_per_step(V, P, NT, XB ? 32 : 16);
+  constexpr int RB = rows_per_step(V, P, NT, 16);
   extern __shared__ uint32_t s_act[];
   const int lane = threadIdx.x & 63;
   // Every workgroup works on one group row; its four waves take consecutive tiles.  The wave
