@@ -537,15 +537,28 @@ __device__ __forceinline__ void load_step16(Step16<P> &st, __amdgpu_buffer_rsrc_
   }
 }
 
+// LDS word of column pair-half `half` of dword span (p, v) for lane li: the 16 lanes' 16-byte
+// chunks of one (p, v, half) are contiguous, so each read is conflict-free.
+__device__ __forceinline__ int act16_word(int p, int v, int half, int li) { return (((p * 4 + v) * 2 + half) * kLR + li) * 4; }
+
+// The activations are read from LDS per step (two ds_read_b128 per weight dword) rather than
+// held in registers: a 96-column slice would take 96 VGPRs, and with it the kernel fits
+// three waves per SIMD instead of six.  Odd columns are staged already divided by 16.
 template <int P>
-__device__ __forceinline__ void compute_step16(const Step16<P> &st, const Act<4, P, false> &A, int o, int o_begin,
-                                               int lane, float &outv) {
+__device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32_t *lds, int li, const float (&xm)[P],
+                                               int o, int o_begin, int lane, float &outv) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
   float acc = 0.f;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    float ap = A.xm[p];
+    float ap = xm[p];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) ap = dot8(st.w[p][v], A.xe[p][v], A.xo[p][v], ap);
+    for (int v = 0; v < 4; ++v) {
+      const f4 q0 = *reinterpret_cast<const f4 *>(lds + act16_word(p, v, 0, li));
+      const f4 q1 = *reinterpret_cast<const f4 *>(lds + act16_word(p, v, 1, li));
+      const float xe[4] = {q0.x, q0.z, q1.x, q1.z}, xo[4] = {q0.y, q0.w, q1.y, q1.w};
+      ap = dot8(st.w[p][v], xe, xo, ap);
+    }
     acc = fmaf(st.s[p], ap, acc);
   }
   const float sum = row16_sum(acc);
@@ -597,23 +610,42 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   load_step16<P>(b1, wr, sr, T, woff, gi, o_begin + kGR, g);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<false>(s_act, xs, 0, C);
+  // staged with odd columns divided by 16 (exact), as dot8 takes them
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(xs) / sizeof(xs[0])); ++i) {
+    const int w = threadIdx.x + i * kBlock;  // column
+    const float x = w < C ? __uint_as_float(xs[i]) : 0.f;
+    const int d = w >> 3, j = w & 7;         // dword span d = p * 64 + li * 4 + v, column j in it
+    s_act[act16_word(d >> 6, d & 3, j >> 2, (d >> 2) & (kLR - 1)) + (j & 3)] = __float_as_uint((w & 1) ? x * 0.0625f : x);
+  }
   __syncthreads();
   if (!work) {
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  uint32_t raw[P][V][8];
-  read_act<V, P, false, kLR>(raw, s_act, li);
-  Act<V, P, false> A;
-  finish_act<V, P, false>(A, raw);
+  // offset term of each span: -8 * (sum of its activations), summed in column-pair order
+  float xm[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float span = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = 2 * k;
+        span += __uint_as_float(s_act[act16_word(p, v, j >> 2, li) + (j & 3)]) +
+                16.f * __uint_as_float(s_act[act16_word(p, v, (j + 1) >> 2, li) + ((j + 1) & 3)]);
+      }
+    }
+    xm[p] = -8.f * span;
+  }
 
   float outv = 0.f;
   int o = o_begin;
   do {
-    compute_step16<P>(b0, A, o, o_begin, lane, outv);
+    compute_step16<P>(b0, s_act, li, xm, o, o_begin, lane, outv);
     load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
-    if (o + kGR < o_end) compute_step16<P>(b1, A, o + kGR, o_begin, lane, outv);
+    if (o + kGR < o_end) compute_step16<P>(b1, s_act, li, xm, o + kGR, o_begin, lane, outv);
     load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
     o += 2 * kGR;
   } while (o < o_end);
