@@ -846,9 +846,14 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
   }
   ensure_device(c);
   TakeArgs a{};
+  // Device routes at S = 1 hold distinct experts, one row each in route order, live rows first:
+  // the take can then read everything without first reading the reduce order.
+  a.in_order = S == 1 ? 1 : 0;
   for (int s = 0; s < c->nslots; ++s) {
     a.groups[s] = c->slots[s].grp;
     a.y[s] = c->d_y + (size_t)s * kRows * c->y_ld;
+    a.rows[s] = c->slots[s].rows;
+    if (c->slots[s].ring < 0) a.in_order = 0;  // explicit groups reduce in their listed order
   }
   a.resid = residual_dev;
   a.nslots = c->nslots;

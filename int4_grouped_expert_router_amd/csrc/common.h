@@ -108,6 +108,8 @@ struct TakeArgs {
   const float *y[kSlots];
   float *resid;              // [S][D]
   int nslots, y_ld, S, D;
+  int rows[kSlots];          // row capacity of each slot's group (its live rows are a prefix)
+  int in_order;              // 1: one token, and every slot reduces its live rows in row order
 };
 
 // Launchers (defined in the kernel translation units).  They return hipGetLastError().  With

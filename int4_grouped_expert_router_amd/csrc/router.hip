@@ -128,6 +128,7 @@ constexpr int kTabWords = 3 * sizeof(TensorDesc) / 4;          // tensor words o
 constexpr int kLiveWord = offsetof(TensorDesc, live) / 4;     // t[0].live inside a row descriptor
 constexpr int kDescWords = sizeof(RowDesc) / 4;               // 32
 constexpr int kDescPerThread = kRows * kDescWords / kBlock;   // 8
+constexpr int kTabPrefetchE = 64;                             // experts whose records are staged early
 
 // One workgroup; wave w ranks tokens w, w + 4, ...  The kernel runs once per layer on one CU, so
 // it is written for latency: every global read is issued in a batch (one memory round trip per
@@ -145,7 +146,7 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // (choice scores), E floats (bias), wpt * E ints (rank counts per wave of the token).
 __host__ __device__ inline int select_slots(int S) { return S < kWaves ? S : kWaves; }
 __host__ __device__ inline size_t select_slot_doubles(int E, int splits, int wpt) {
-  return (size_t)E * splits + 2 * (size_t)E + (E + 1) / 2 + ((size_t)wpt * E + 1) / 2;
+  return (size_t)E * splits + 3 * (size_t)E + (E + 1) / 2 + ((size_t)wpt * E + 1) / 2;
 }
 size_t select_lds_bytes(int E, int splits, int S) {
   const int slots = select_slots(S);
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   __shared__ int s_row_e[kRows], s_row_t[kRows];
   __shared__ float s_row_w[kRows];
   __shared__ int s_rows;
+  __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];  // expert records, when E is small
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,8 +180,19 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   double *s_v = s_dyn + slot * select_slot_doubles(E, splits, wpt);  // partials
   double *s_c = s_v + np;                   // logits
   double *s_x = s_c + E;                    // choice scores
-  float *s_b = reinterpret_cast<float *>(s_x + E);
+  double *s_sg = s_x + E;                   // sigma
+  float *s_b = reinterpret_cast<float *>(s_sg + E);
   int *s_r = reinterpret_cast<int *>(s_b + ((E + 1) & ~1));  // [wpt][E] rank counts
+
+  // With few experts, every expert's 128-byte record is loaded now, in the same batch as the
+  // partials, so the row descriptors need no further memory round trip at the end.
+  const bool tab_pre = a.table != nullptr && E <= kTabPrefetchE;
+  uint32_t tv[kTabPrefetchE * kDescWords / kBlock];
+  if (tab_pre) {
+    const uint32_t *tsrc = reinterpret_cast<const uint32_t *>(a.table);
+#pragma unroll
+    for (int j = 0; j < kTabPrefetchE * kDescWords / kBlock; ++j) tv[j] = tsrc[min(tid + j * kBlock, E * kDescWords - 1)];
+  }
 
   for (int t0 = 0; t0 < S; t0 += slots) {
     const int t = t0 + slot;
@@ -215,7 +228,9 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
         double l = 0.0;
         for (int sp = 0; sp < splits; ++sp) l += s_v[e * splits + sp];
         s_c[e] = l;
-        double c = 1.0 / (1.0 + exp(-l)) + (double)s_b[e];
+        const double sg = 1.0 / (1.0 + exp(-l));
+        s_sg[e] = sg;
+        double c = sg + (double)s_b[e];
         if (c != c) c = -__builtin_inf();
         s_x[e] = c;
       }
@@ -250,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
         for (int w = 0; w < wpt; ++w) rank += s_r[w * E + e];
         if (rank < K) {
           s_pidx[t * K + rank] = e;
-          s_sig[slot][rank] = 1.0 / (1.0 + exp(-s_c[e]));
+          s_sig[slot][rank] = s_sg[e];
         }
       }
     }
@@ -394,13 +409,20 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   // every row of the buffer rewritten, rows past the group cleared so a row's own record says
   // whether it is live.  All table reads are in flight together.
   const int rows = s_rows;
+  if (tab_pre) {
+#pragma unroll
+    for (int j = 0; j < kTabPrefetchE * kDescWords / kBlock; ++j) s_tab[tid + j * kBlock] = tv[j];
+    __syncthreads();
+  }
   uint32_t v[kDescPerThread];
 #pragma unroll
   for (int j = 0; j < kDescPerThread; ++j) {
     const int q = tid + j * kBlock;
     const int row = q / kDescWords, d = q % kDescWords;
     const int e = row < rows ? s_row_e[row] : 0;
-    v[j] = a.table ? reinterpret_cast<const uint32_t *>(a.table + e)[d < kTabWords ? d : 0] : 0u;
+    const int dd = d < kTabWords ? d : 0;
+    v[j] = tab_pre ? s_tab[e * kDescWords + dd]
+                   : (a.table ? reinterpret_cast<const uint32_t *>(a.table + e)[dd] : 0u);
   }
 #pragma unroll
   for (int j = 0; j < kDescPerThread; ++j) {

@@ -19,7 +19,46 @@ namespace {
 
 static_assert(kRows == kWave, "take stages one slot per wave");
 
+// One token whose rows reduce in row order (a device route at S = 1: its selections are
+// distinct experts, one row each, in route order): every read is independent of the group
+// record (live flags and weights come from the row descriptors, y rows are read
+// speculatively up to the slot's capacity), so the whole take is one memory round trip.
+// The arithmetic is the general path's: fmaf over the live rows in order, slots in order.
+__device__ __forceinline__ void take_in_order(const TakeArgs &a) {
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i >= a.D) return;
+  float *rp = a.resid + i;
+  const float r_in = *rp;  // in flight with the rows' loads
+  float total = 0.f;
+  for (int s = 0; s < a.nslots; ++s) {
+    const CGroupBuf G = (CGroupBuf)a.groups[s];
+    const float *__restrict__ y = a.y[s];
+    const int rows = a.rows[s];
+    float acc = 0.f;
+    for (int r0 = 0; r0 < rows; r0 += 8) {
+      float v[8], w[8];
+      int live[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = min(r0 + j, rows - 1);
+        v[j] = y[(size_t)r * a.y_ld + i];
+        w[j] = G->rows[r].weight;
+        live[j] = G->rows[r].t[0].live;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < rows && live[j]) acc = fmaf(w[j], v[j], acc);
+    }
+    total = (s == 0) ? acc : total + acc;
+  }
+  *rp = r_in + total;
+}
+
 __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
+  if (a.in_order) {
+    take_in_order(a);
+    return;
+  }
   __shared__ int s_rr[kSlots][kRows];    // reduce order of each slot (group rows, token-major)
   __shared__ float s_rw[kSlots][kRows];  // route weight of each group row
   __shared__ int s_r0[kSlots], s_cnt[kSlots];
