@@ -153,6 +153,11 @@ int i4moe_upload_router(i4moe_ctx *ctx, int layer, int E, int D, const float *W,
  * The route and the expert group (distinct experts in first-appearance order, token-major)
  * stay in the layer's device route buffer for i4moe_expert_group_issue.  If host_out != NULL
  * it receives S records and the call synchronises the stream (one small copy back).
+ * With S == 1, E <= 64 and host_out == NULL only the logits GEMV is enqueued here; the
+ * selection runs inside the dual projection of the issue that consumes this route, or as its
+ * own kernel on the context's stream when another call needs the route or the router scratch
+ * first (a route, a tap, a stream switch, a change of the layer's experts or router).  The
+ * results are bitwise the same either way.
  * Limits: 1 <= S <= I4MOE_MAX_TOKENS, 1 <= K <= min(E, I4MOE_MAX_K), S*K <= I4MOE_MAX_ROWS.
  * Fault-hook gated.  Non-finite activations give an unspecified (but in-range) route. */
 int i4moe_route(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S, int K, float topp,
@@ -212,7 +217,8 @@ size_t i4moe_debug_size(i4moe_ctx *ctx, int what, int index);
 
 /* ---- profiling ---------------------------------------------------------------------------- */
 
-/* Kernel families timed when profiling is on. */
+/* Kernel families timed when profiling is on.  A selection run inside the dual projection
+ * (see i4moe_route) is timed as part of I4MOE_K_DUAL. */
 enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_COUNT = 4 };
 
 /* on != 0: bracket every later kernel launch with a pair of HIP events on the context's

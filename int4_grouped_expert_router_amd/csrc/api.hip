@@ -87,6 +87,13 @@ struct i4moe_ctx {
   int nslots = 0;
 
   int last_route_S = 0, last_route_E = 0;
+
+  // A one-token device route of which only the GEMV is enqueued.  The next issue of that route
+  // runs the selection inside its dual projection (one launch less per layer); anything else
+  // that needs the route or the router scratch runs the selection kernel first (flush_sel).
+  bool sel_pending = false;
+  int sel_layer = -1;
+  RouteArgs sel_args{};
   int last_issue_rows = 0, last_issue_I = 0;
 
   long long fail_after = -1, calls = 0;
@@ -183,6 +190,17 @@ hipError_t timed(i4moe_ctx *c, int kernel, F &&f) {
     }
   }
   return e;
+}
+
+// Enqueue the selection of the pending route (see i4moe_ctx::sel_pending).
+int flush_sel(i4moe_ctx *c) {
+  if (!c->sel_pending) return I4MOE_OK;
+  hipError_t e = timed(c, I4MOE_K_ROUTE, [&](hipEvent_t t0, hipEvent_t t1) {
+    return launch_route(c->sel_args, kRouteSelect, c->stream, t0, t1);
+  });
+  if (e != hipSuccess) return hip_fail(c, e, "route selection launch");
+  c->sel_pending = false;
+  return I4MOE_OK;
 }
 
 void drain_profile(i4moe_ctx *c) {
@@ -436,6 +454,10 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
 
 int i4moe_set_stream(i4moe_ctx *c, void *stream) {
   if (!c) return I4MOE_EINVAL;
+  if (c->sel_pending) {
+    ensure_device(c);
+    if (int rc = flush_sel(c)) return rc;
+  }
   c->stream = reinterpret_cast<hipStream_t>(stream);
   return I4MOE_OK;
 }
@@ -525,6 +547,7 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
   auto it = c->tensors.find(h);
   if (it == c->tensors.end()) return fail(c, I4MOE_EINVAL, "unknown tensor handle %u", h);
   ensure_device(c);
+  if (int rc = flush_sel(c)) return rc;
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
   for (auto &kv : c->layers) {
@@ -548,6 +571,10 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
 
 int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
   if (!c) return I4MOE_EINVAL;
+  if (c->sel_pending) {
+    ensure_device(c);
+    if (int rc = flush_sel(c)) return rc;
+  }
   if (layer < 0 || expert < 0 || expert >= kMaxE) return fail(c, I4MOE_EINVAL, "bad layer %d / expert %d", layer, expert);
   auto tg = c->tensors.find(gate), tu = c->tensors.find(up), td = c->tensors.find(down);
   if (tg == c->tensors.end() || tu == c->tensors.end() || td == c->tensors.end())
@@ -585,6 +612,10 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
   if (!c) return I4MOE_EINVAL;
   if (layer < 0 || E < 1 || E > kMaxE || D < 1 || !W) return fail(c, I4MOE_EINVAL, "bad router arguments");
   if ((size_t)E * D > ((size_t)1 << 28)) return fail(c, I4MOE_EUNSUPPORTED, "router too large");
+  if (c->sel_pending) {
+    ensure_device(c);
+    if (int rc = flush_sel(c)) return rc;
+  }
   Layer &L = c->layers[layer];
   bool any_expert = false;
   for (i4moe_tensor g : L.gate) any_expert = any_expert || g != 0;
@@ -648,11 +679,13 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   splits = (L->D + cps - 1) / cps;
   if (L->E * splits > kMaxE)  // partials of one token staged by the select kernel
     return fail(c, I4MOE_EUNSUPPORTED, "router split plan out of range (E=%d, splits=%d)", L->E, splits);
-  if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
   const int ring = c->ring_next;
   for (int s = 0; s < c->nslots; ++s)
     if (c->slots[s].ring == ring)
       return fail(c, I4MOE_EINVAL, "%d routes since a pending issue; take before routing again", kRing);
+  // the previous route's selection reads the partials this route overwrites
+  if ((rc = flush_sel(c))) return rc;
+  if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
   RouteArgs a{};
   a.W = L->W;
   a.bias = L->b;
@@ -673,8 +706,18 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   a.norm_topk = norm_topk ? 1 : 0;
   a.topp = topp;
   a.routed_scale = routed_scale;
-  hipError_t e = timed(c, I4MOE_K_ROUTE, [&](hipEvent_t t0, hipEvent_t t1) { return launch_route(a, c->stream, t0, t1); });
+  // Without a host copy a one-token route defers its selection to the issue that consumes it.
+  const bool defer = !host_out && dual_sel_ok(a, false);
+  const int parts = defer ? kRouteGemv : kRouteGemv | kRouteSelect;
+  hipError_t e = timed(c, I4MOE_K_ROUTE, [&](hipEvent_t t0, hipEvent_t t1) {
+    return launch_route(a, parts, c->stream, t0, t1);
+  });
   if (e != hipSuccess) return hip_fail(c, e, "route launch");
+  if (defer) {
+    c->sel_pending = true;
+    c->sel_layer = layer;
+    c->sel_args = a;
+  }
   c->ring_next = (ring + 1) % kRing;
   L->route_buf = ring;
   L->routed = true;
@@ -806,11 +849,23 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   an.grid_rows = max_rows;
   an.tile_rows = pn.tile_rows;
 
+  // This layer's latest route still owes its selection: run it inside the dual projection
+  // when that variant can, else as its own kernel first.
+  bool sel = false;
+  if (!group && c->sel_pending && c->sel_layer == layer && c->sel_args.out == grp) {
+    if (dual_sel_ok(c->sel_args, pd.gen)) {
+      sel = true;
+      ad.ra = c->sel_args;
+    } else if ((rc = flush_sel(c))) {
+      return rc;
+    }
+  }
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
   if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
-      return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, ad, pd.blocks, c->stream, t0, t1);
+      return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, sel, ad, pd.blocks, c->stream, t0, t1);
     });
+  if (e == hipSuccess && sel) c->sel_pending = false;
   if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
       return pn.rows16 ? launch_down16(pn.P, an, pn.blocks, c->stream, t0, t1)
                        : launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
@@ -904,6 +959,7 @@ int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t b
   const size_t need = i4moe_debug_size(c, what, index);
   if (need == 0 || bytes != need) return fail(c, I4MOE_EINVAL, "tap %d/%d: need %zu bytes, got %zu", what, index, need, bytes);
   ensure_device(c);
+  if (int rc = flush_sel(c)) return rc;
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
   if (what == I4MOE_TAP_LOGITS) {

@@ -101,6 +101,7 @@ struct ProjArgs {
   int O, C;                  // rows and columns of every tensor in the launch
   int tile_groups, tile_rows;  // workgroups per group row (4 tiles each), rows per tile
   int grid_rows;             // group rows the grid covers (grid = grid_rows * tile_groups)
+  RouteArgs ra;              // dual with the fused selection: the route whose partials it ranks
 };
 
 struct TakeArgs {
@@ -115,8 +116,14 @@ struct TakeArgs {
 // Launchers (defined in the kernel translation units).  They return hipGetLastError().  With
 // t0/t1 non-null the launch records the kernel's own start and end into them
 // (hipExtLaunchKernel), so an event pair spans the kernel alone.
-hipError_t launch_route(const RouteArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
-hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st,
+// parts: kRouteGemv, kRouteSelect or both.  The selection reads the GEMV's partials.
+constexpr int kRouteGemv = 1, kRouteSelect = 2;
+hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
+// sel: the dual projection first runs the selection of a.ra itself (one token, E <= 64,
+// non-generic spans) and publishes its route, group and row descriptors.
+bool dual_sel_ok(const RouteArgs &ra, bool gen);
+hipError_t launch_dual(int V, int P, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                        hipEvent_t t1 = nullptr);

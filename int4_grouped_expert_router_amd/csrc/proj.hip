@@ -26,7 +26,7 @@
 // Group sizes that split a span fall back to a per-byte path.
 #include <hip/hip_ext.h>
 
-#include "common.h"
+#include "select.h"
 
 namespace i4moe {
 namespace {
@@ -401,9 +401,12 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
 }
 
 // NT = 2: dual gate/up with the SiLU-gated product; NT = 1: down projection.  XB: bf16
-// activations through v_dot2_f32_bf16 (dual only).  A tile holds at most 64 rows (one result
-// per lane).
-template <int V, int P, int NT, bool GEN, bool XB>
+// activations through v_dot2_f32_bf16 (dual only).  SEL (dual, one token): every workgroup
+// first runs the expert selection itself from the router's split partials, so no separate
+// selection launch sits between the router GEMV and the experts; workgroup 0 also publishes
+// the route, group record and row descriptors for the down projection, the take and the
+// taps.  A tile holds at most 64 rows (one result per lane).
+template <int V, int P, int NT, bool GEN, bool XB, bool SEL = false>
 __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   constexpr int RB = rows_per_step(V, P, NT, 16);
   extern __shared__ uint32_t s_act[];
@@ -412,34 +415,78 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   // index is uniform by construction and readfirstlane lets the compiler keep it (and the row,
   // tile, descriptors and base addresses derived from it) in scalar registers.
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Touch the first word of every row record of the grid, so the first workgroups to start
-  // bring all records into their XCD's L2 before the weight stream fills the memory queues
-  // (a later workgroup's record read then hits or joins a read already in flight).  The
-  // value is consumed at the very end, so nothing waits for it.
-  const uint32_t touch = reinterpret_cast<const uint32_t *>(a.grp->rows + min(lane, a.grid_rows - 1))[0];
-  const CGroupBuf G = (CGroupBuf)a.grp;
   const int jr = blockIdx.x / a.tile_groups;  // < kRows: the grid never exceeds the row cap
   const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
 
-  // Everything about this row in one scalar record: tensors, token, weight, and whether the
-  // row belongs to the group (one memory round trip).
   TensorDesc T[NT];
-  if constexpr (NT == 2) {
-    T[0] = ld_desc(G->rows[jr].t[0]);
-    T[1] = ld_desc(G->rows[jr].t[1]);
-  } else {
-    T[0] = ld_desc(G->rows[jr].t[2]);
-  }
-  const int arow = NT == 2 ? G->rows[jr].token : jr;
-  const int live = G->rows[jr].t[0].live;
-  // Pin the record's loads above the liveness branch (otherwise they are sunk below it and
-  // cost a second memory round trip).
+  int arow, live;
+  uint32_t touch = 0;
+  if constexpr (SEL) {
+    static_assert(NT == 2, "selection runs in the dual projection");
+    __shared__ double s_sig[kWavesPerBlock][kMaxK];
+    __shared__ int s_pidx[kRows];
+    __shared__ float s_pw[kRows];
+    __shared__ int s_n[kTokens];
+    __shared__ int s_row_e[kRows], s_row_t[kRows];
+    __shared__ float s_row_w[kRows];
+    __shared__ int s_rows;
+    __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];
+    uint32_t tv[kTabPerThread];
+    table_prefetch(tv, a.ra.table, a.ra.E);
+    // (the table is never null here; the test keeps the record from being folded into a
+    // constant initializer, which LDS addresses cannot be)
+    SelShared sh{s_sig, s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, a.ra.table ? s_tab : nullptr};
+    double *s_sel = reinterpret_cast<double *>(s_act + act_words<V, P, XB>());
+    select_pass(a.ra, s_sel, 0, sh, blockIdx.x == 0);
+    table_stage(s_tab, tv);
+    __syncthreads();
+    if (blockIdx.x == 0) publish_group(a.ra, sh);
+    // this row: rank jr of the one token (its selections are distinct experts, in route order)
+    live = __builtin_amdgcn_readfirstlane(jr < s_n[0] ? 1 : 0);
+    const int e = __builtin_amdgcn_readfirstlane(live ? s_pidx[jr] : 0);
+    arow = 0;
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-    asm volatile("" ::"s"(T[n].q), "s"(T[n].s), "s"(T[n].O), "s"(T[n].C), "s"(T[n].row_bytes), "s"(T[n].gs),
-                 "s"(T[n].ng));
-  asm volatile("" ::"s"(arow), "s"(live));
-  if (!live) return;
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t *w = s_tab + e * kDescWords + n * (kTabWords / 3);
+      uint32_t v[kTabWords / 3];
+#pragma unroll
+      for (int d = 0; d < kTabWords / 3; ++d) v[d] = __builtin_amdgcn_readfirstlane(w[d]);
+      T[n].q = reinterpret_cast<const uint8_t *>(((uint64_t)v[1] << 32) | v[0]);
+      T[n].s = reinterpret_cast<const float *>(((uint64_t)v[3] << 32) | v[2]);
+      T[n].O = (int)v[4];
+      T[n].C = (int)v[5];
+      T[n].row_bytes = (int)v[6];
+      T[n].gs = (int)v[7];
+      T[n].ng = (int)v[8];
+      T[n].live = live;
+    }
+    if (!live) return;
+  } else {
+    // Touch the first word of every row record of the grid, so the first workgroups to start
+    // bring all records into their XCD's L2 before the weight stream fills the memory queues
+    // (a later workgroup's record read then hits or joins a read already in flight).  The
+    // value is consumed at the very end, so nothing waits for it.
+    touch = reinterpret_cast<const uint32_t *>(a.grp->rows + min(lane, a.grid_rows - 1))[0];
+    const CGroupBuf G = (CGroupBuf)a.grp;
+    // Everything about this row in one scalar record: tensors, token, weight, and whether the
+    // row belongs to the group (one memory round trip).
+    if constexpr (NT == 2) {
+      T[0] = ld_desc(G->rows[jr].t[0]);
+      T[1] = ld_desc(G->rows[jr].t[1]);
+    } else {
+      T[0] = ld_desc(G->rows[jr].t[2]);
+    }
+    arow = NT == 2 ? G->rows[jr].token : jr;
+    live = G->rows[jr].t[0].live;
+    // Pin the record's loads above the liveness branch (otherwise they are sunk below it and
+    // cost a second memory round trip).
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      asm volatile("" ::"s"(T[n].q), "s"(T[n].s), "s"(T[n].O), "s"(T[n].C), "s"(T[n].row_bytes), "s"(T[n].gs),
+                   "s"(T[n].ng));
+    asm volatile("" ::"s"(arow), "s"(live));
+    if (!live) return;
+  }
 
   const int C = a.C;
   const int RD = (C + 7) >> 3;
@@ -665,10 +712,10 @@ const void *rows16_ptr(int P) {
 
 size_t rows16_lds_bytes(int P) { return 4u * (size_t)P * kLR * 4 * 8; }
 
-template <int NT, bool GEN, bool XB>
+template <int NT, bool GEN, bool XB, bool SEL = false>
 const void *kernel_ptr_t(int V, int P) {
 #define I4MOE_PTR(v, p) \
-  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, XB>);
+  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, XB, SEL>);
   I4MOE_PTR(1, 1) I4MOE_PTR(1, 2) I4MOE_PTR(1, 3) I4MOE_PTR(1, 4)
   I4MOE_PTR(2, 1) I4MOE_PTR(2, 2) I4MOE_PTR(2, 3) I4MOE_PTR(2, 4)
   I4MOE_PTR(4, 1) I4MOE_PTR(4, 2) I4MOE_PTR(4, 3) I4MOE_PTR(4, 4)
@@ -678,22 +725,24 @@ const void *kernel_ptr_t(int V, int P) {
 
 // The instantiation a launch uses: bf16 pairs only for dual launches over bf16 activations
 // without per-byte group tensors.
-const void *kernel_ptr(int V, int P, int NT, bool gen, bool xb) {
+const void *kernel_ptr(int V, int P, int NT, bool gen, bool xb, bool sel = false) {
   if (NT == 1) return gen ? kernel_ptr_t<1, true, false>(V, P) : kernel_ptr_t<1, false, false>(V, P);
-  if (gen) return kernel_ptr_t<2, true, false>(V, P);
+  if (gen) return sel ? nullptr : kernel_ptr_t<2, true, false>(V, P);
+  if (sel) return xb ? kernel_ptr_t<2, false, true, true>(V, P) : kernel_ptr_t<2, false, false, true>(V, P);
   return xb ? kernel_ptr_t<2, false, true>(V, P) : kernel_ptr_t<2, false, false>(V, P);
 }
 
 size_t lds_bytes(int V, int P, bool xb) { return 4u * (size_t)(xb ? P * 64 * V * 4 : P * 64 * V * 8); }
 
-hipError_t launch(int V, int P, int NT, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
-                  hipEvent_t t1) {
-  const void *k = kernel_ptr(V, P, NT, gen, xb);
+hipError_t launch(int V, int P, int NT, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
+                  hipEvent_t t0, hipEvent_t t1) {
+  const void *k = kernel_ptr(V, P, NT, gen, xb, sel);
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
-  if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds_bytes(V, P, xb), st, t0, t1, 0);
-  return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds_bytes(V, P, xb), st);
+  const size_t lds = lds_bytes(V, P, xb) + (sel ? select_lds_bytes(a.ra.E, a.ra.splits, 1) : 0);
+  if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st, t0, t1, 0);
+  return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st);
 }
 
 }  // namespace
@@ -714,9 +763,14 @@ int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb) {
   return c;
 }
 
-hipError_t launch_dual(int V, int P, bool gen, bool xb, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
-                       hipEvent_t t1) {
-  hipError_t e = launch(V, P, 2, gen, xb && !gen, a, blocks, st, t0, t1);
+bool dual_sel_ok(const RouteArgs &ra, bool gen) {
+  return !gen && ra.S == 1 && ra.E <= kTabPrefetchE && ra.table != nullptr && ra.K <= kRows;
+}
+
+hipError_t launch_dual(int V, int P, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
+                       hipEvent_t t0, hipEvent_t t1) {
+  if (sel && !dual_sel_ok(a.ra, gen)) return hipErrorInvalidValue;
+  hipError_t e = launch(V, P, 2, gen, xb && !gen, sel, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
 int rows16_blocks_per_cu(int P) {
@@ -746,7 +800,7 @@ hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, h
 
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
                        hipEvent_t t1) {
-  hipError_t e = launch(V, P, 1, gen, false, a, blocks, st, t0, t1);
+  hipError_t e = launch(V, P, 1, gen, false, false, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

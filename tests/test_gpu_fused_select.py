@@ -1,0 +1,209 @@
+"""One-token device routes without a host copy: the route call enqueues only the logits GEMV and
+the issue that consumes the route runs the selection inside its dual projection.  These tests
+hold that path to the oracle and, bit for bit, to the separate selection kernel (which runs when
+a host copy is requested), and walk the host-side cases in which the deferred selection must
+run on its own first (MI355X only)."""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from harness import TOL, digest, make_layer, near_tie, normwise_err, oracle_routes, route_matches, upload_layer, x_to_device
+from synth import get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def new_ctx():
+    import torch
+    from int4_grouped_expert_router_amd import Context
+    assert torch.cuda.is_available()
+    return Context(0, torch.cuda.current_stream())
+
+
+def layer_pass(ctx, cfg, L, x, host_out, layer=0):
+    """route + issue with every tap, then take into the layer's residual."""
+    import torch
+    from int4_grouped_expert_router_amd import binding as B
+    ctx.route(layer, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=host_out)
+    slot = ctx.issue(layer, x)
+    got = {
+        "h": ctx.tap(B.I4MOE_TAP_H),
+        "y": ctx.tap(B.I4MOE_TAP_Y, slot),
+        "route": ctx.tap(B.I4MOE_TAP_ROUTE, layer, np.uint8),
+        "group": ctx.tap(B.I4MOE_TAP_GROUP, layer, np.int32),
+        "logits": ctx.tap(B.I4MOE_TAP_LOGITS, 0, np.float64),
+    }
+    r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+    ctx.take(r)
+    torch.cuda.synchronize()
+    got["out"] = r.cpu().numpy()
+    return got
+
+
+def route_records(raw: np.ndarray, S: int):
+    from int4_grouped_expert_router_amd import binding as B
+    return (B.i4moe_route_host * S).from_buffer_copy(raw.tobytes())
+
+
+CASES = {
+    "tiny": {},
+    "tiny_k_eq_e": {"K": 8},
+    "tiny_topp_cut": {"topp": 0.3, "routed_scale": 2.5},
+    "tiny_no_norm": {"norm_topk": False, "topp": 0.0},
+    "ragged_16e": {"D": 1000, "I": 200, "E": 16, "K": 4, "formats": "mix_even_odd", "gs": 64, "topp": 0.9},
+    "ragged_wide": {"D": 7168, "I": 2048, "E": 16, "K": 8, "formats": "mix_even_odd", "gs": 64},
+    "generic_spans": {"D": 130, "I": 34, "E": 5, "K": 5, "formats": "mix_even_odd", "gs": 32, "x_dtype": "bf16"},
+}
+
+
+@pytest.mark.parametrize("name", ["medium", "mix", *CASES])
+def test_fused_matches_separate_and_oracle(name):
+    print(f"[fused] {name}", flush=True)
+    cfg = get_config(name) if name in ("medium", "mix") else get_config("tiny", seed=7, **CASES[name])
+    assert cfg.S == 1
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    sep = layer_pass(ctx, cfg, L, x, host_out=True)
+    fus = layer_pass(ctx, cfg, L, x, host_out=False)
+    for k in sep:
+        assert sep[k].tobytes() == fus[k].tobytes(), k
+    routes, x64 = oracle_routes(cfg, L)
+    if near_tie(routes[0], cfg.K, cfg.topp):
+        pytest.skip("near-tie route; selection not comparable bit for bit")
+    rec = route_records(fus["route"], 1)
+    assert route_matches(rec[0], routes[0], cfg.K)
+    import oracle
+    delta, _ = oracle.experts.layer_delta(routes, L.expert, x64)
+    assert normwise_err(fus["out"] - L.residual, delta) < TOL
+    ctx.close()
+
+
+def test_fused_determinism_medium():
+    import torch
+    print("[fused] determinism medium x10", flush=True)
+    cfg = get_config("medium")
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    seen = set()
+    for _ in range(10):
+        r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+        ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+        ctx.issue(0, x)
+        ctx.take(r)
+        torch.cuda.synchronize()
+        seen.add(digest(r.cpu().numpy()))
+    assert len(seen) == 1
+    ctx.close()
+
+
+def two_layers():
+    cfg = get_config("tiny", D=512, I=256, E=16, K=4, topp=0.9, routed_scale=2.5, seed=11)
+    L0, L1 = make_layer(cfg, 0), make_layer(cfg, 1)
+    ctx = new_ctx()
+    upload_layer(ctx, L0, 0)
+    upload_layer(ctx, L1, 1)
+    return cfg, L0, L1, ctx
+
+
+def reference_two(ctx, cfg, L0, L1, x0, x1):
+    """Both layers routed with host copies (separate selection kernels), one take."""
+    import torch
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    ctx.route(1, x1, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    ctx.issue(0, x0)
+    ctx.issue(1, x1)
+    r = torch.from_numpy(L0.residual.copy()).to("cuda:0")
+    ctx.take(r)
+    torch.cuda.synchronize()
+    return r.cpu().numpy()
+
+
+def test_pending_selection_runs_before_next_route():
+    """A second route overwrites the router scratch: the first route's selection runs before it,
+    and the first layer's issue then reads that materialised group."""
+    import torch
+    print("[fused] route, route, issue, issue", flush=True)
+    cfg, L0, L1, ctx = two_layers()
+    x0, x1 = x_to_device(L0.x, L0.x_dtype), x_to_device(L1.x, L1.x_dtype)
+    ref = reference_two(ctx, cfg, L0, L1, x0, x1)
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.route(1, x1, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.issue(0, x0)   # layer 0's selection already ran as its own kernel
+    ctx.issue(1, x1)   # layer 1's selection runs inside this dual projection
+    r = torch.from_numpy(L0.residual.copy()).to("cuda:0")
+    ctx.take(r)
+    torch.cuda.synchronize()
+    assert r.cpu().numpy().tobytes() == ref.tobytes()
+    ctx.close()
+
+
+def test_pending_selection_with_tap_stream_switch_and_explicit_group():
+    import torch
+    from int4_grouped_expert_router_amd import binding as B
+    print("[fused] tap / explicit group / stream switch / injected failure", flush=True)
+    cfg, L0, L1, ctx = two_layers()
+    x0, x1 = x_to_device(L0.x, L0.x_dtype), x_to_device(L1.x, L1.x_dtype)
+    ref = reference_two(ctx, cfg, L0, L1, x0, x1)
+    rec1 = ctx.route(1, x1, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    rows1 = [(int(rec1[0].idx[k]), 0, float(rec1[0].w[k])) for k in range(rec1[0].n)]
+
+    def finish():
+        r = torch.from_numpy(L0.residual.copy()).to("cuda:0")
+        ctx.take(r)
+        torch.cuda.synchronize()
+        return r.cpu().numpy()
+
+    # a tap of the pending route runs its selection first; the issue then reads that group
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    tapped = route_records(ctx.tap(B.I4MOE_TAP_ROUTE, 0, np.uint8), 1)
+    ctx.issue(0, x0)
+    ctx.issue(1, x1, rows=rows1)
+    assert finish().tobytes() == ref.tobytes()
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    assert bytes(tapped) == bytes(route_records(ctx.tap(B.I4MOE_TAP_ROUTE, 0, np.uint8), 1))
+
+    # an explicit-group issue of another layer leaves the pending selection to the next issue
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.issue(1, x1, rows=rows1)
+    ctx.issue(0, x0)
+    out = finish()
+    # same sums, slots taken in issue order: layer 1 first this time
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    ctx.issue(1, x1, rows=rows1)
+    ctx.issue(0, x0)
+    assert out.tobytes() == finish().tobytes()
+
+    # a stream switch runs the pending selection on the old stream
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.set_stream(s1)
+    s1.wait_stream(s0)
+    with torch.cuda.stream(s1):
+        ctx.issue(0, x0)
+        ctx.issue(1, x1, rows=rows1)
+        r = torch.from_numpy(L0.residual.copy()).to("cuda:0")
+        ctx.take(r)
+    s1.synchronize()
+    ctx.set_stream(s0)
+    assert r.cpu().numpy().tobytes() == ref.tobytes()
+
+    # an injected issue failure enqueues nothing; the selection still runs with the next issue
+    ctx.route(0, x0, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.set_fail_after(0)
+    from int4_grouped_expert_router_amd import I4moeError
+    with pytest.raises(I4moeError):
+        ctx.issue(0, x0)
+    ctx.set_fail_after(-1)
+    ctx.issue(0, x0)
+    ctx.issue(1, x1, rows=rows1)
+    assert finish().tobytes() == ref.tobytes()
+    ctx.close()
