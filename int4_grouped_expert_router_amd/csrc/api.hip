@@ -69,10 +69,8 @@ struct i4moe_ctx {
   std::map<uint32_t, Tensor> tensors;
   std::map<int, Layer> layers;
 
-  double *d_partial = nullptr;
-  size_t partial_cap = 0;  // doubles
-  double *d_logits = nullptr;
-  size_t logits_cap = 0;   // doubles
+  double2 *d_score = nullptr;  // [kTokens][kMaxE] router scores (choice score, sigma)
+  double *d_logits = nullptr;  // [kTokens][kMaxE]
 
   float *d_h = nullptr;    // [kRows][h_ld]
   int h_ld = 0;
@@ -244,24 +242,19 @@ int ensure_rows_scratch(i4moe_ctx *c, int D, int I) {
   return I4MOE_OK;
 }
 
-int ensure_route_scratch(i4moe_ctx *c, size_t partial, size_t logits) {
-  if (partial <= c->partial_cap && logits <= c->logits_cap) return I4MOE_OK;
-  hipError_t e = hipStreamSynchronize(c->stream);
-  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
-  const size_t pc = partial > c->partial_cap ? partial : c->partial_cap;
-  const size_t lc = logits > c->logits_cap ? logits : c->logits_cap;
-  double *p = nullptr, *l = nullptr;
-  if ((e = dalloc(&p, sizeof(double) * pc)) != hipSuccess) return hip_fail(c, e, "hipMalloc(partials)");
-  if ((e = dalloc(&l, sizeof(double) * lc)) != hipSuccess) {
+// Router scratch at its cap (1.5 MB), allocated by the first route.
+int ensure_route_scratch(i4moe_ctx *c) {
+  if (c->d_score) return I4MOE_OK;
+  hipError_t e;
+  double2 *p = nullptr;
+  double *l = nullptr;
+  if ((e = dalloc(&p, sizeof(double2) * kTokens * kMaxE)) != hipSuccess) return hip_fail(c, e, "hipMalloc(scores)");
+  if ((e = dalloc(&l, sizeof(double) * kTokens * kMaxE)) != hipSuccess) {
     dfree(p);
     return hip_fail(c, e, "hipMalloc(logits)");
   }
-  dfree(c->d_partial);
-  dfree(c->d_logits);
-  c->d_partial = p;
+  c->d_score = p;
   c->d_logits = l;
-  c->partial_cap = pc;
-  c->logits_cap = lc;
   return I4MOE_OK;
 }
 
@@ -436,7 +429,7 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
     dfree(L.b);
     dfree(L.d_tab);
   }
-  dfree(c->d_partial);
+  dfree(c->d_score);
   dfree(c->d_logits);
   dfree(c->d_ring);
   dfree(c->d_slot_bufs);
@@ -672,25 +665,25 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
   if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
   ensure_device(c);
-  // about 256 GEMV waves, each over a multiple of 256 columns
+  // about 256 GEMV waves, each over a multiple of 256 columns; an expert's splits (and up to
+  // four experts of one split each) share a workgroup of at most 16 waves
   int splits = (256 + L->E - 1) / L->E;
   if (splits > 16) splits = 16;
   int cps = round_up((L->D + splits - 1) / splits, 256);
   splits = (L->D + cps - 1) / cps;
-  if (L->E * splits > kMaxE)  // partials of one token staged by the select kernel
-    return fail(c, I4MOE_EUNSUPPORTED, "router split plan out of range (E=%d, splits=%d)", L->E, splits);
+  const int epb = splits >= 4 ? 1 : 4 / splits;
   const int ring = c->ring_next;
   for (int s = 0; s < c->nslots; ++s)
     if (c->slots[s].ring == ring)
       return fail(c, I4MOE_EINVAL, "%d routes since a pending issue; take before routing again", kRing);
-  // the previous route's selection reads the partials this route overwrites
+  // the previous route's selection reads the scores this route overwrites
   if ((rc = flush_sel(c))) return rc;
-  if ((rc = ensure_route_scratch(c, (size_t)S * L->E * splits, (size_t)kTokens * kMaxE))) return rc;
+  if ((rc = ensure_route_scratch(c))) return rc;
   RouteArgs a{};
   a.W = L->W;
   a.bias = L->b;
   a.x = x_dev;
-  a.partial = c->d_partial;
+  a.score = c->d_score;
   a.logits = c->d_logits;
   a.out = c->d_ring + ring;
   a.table = L->d_tab;
@@ -701,6 +694,7 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   a.x_bf16 = dtype == I4MOE_DTYPE_BF16;
   a.splits = splits;
   a.cols_per_split = cps;
+  a.epb = epb;
   a.vec = (L->D % 4 == 0) && reinterpret_cast<uintptr_t>(L->W) % 16 == 0 &&
           reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 16 : 8) == 0;
   a.norm_topk = norm_topk ? 1 : 0;

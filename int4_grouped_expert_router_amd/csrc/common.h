@@ -80,13 +80,14 @@ struct RouteArgs {
   const float *W;            // [E][D]
   const float *bias;         // [E]
   const void *x;             // [S][D] f32 or bf16
-  double *partial;           // [S][E][splits]
+  double2 *score;            // [S][E]: choice score c = sigma + bias (NaN as -inf), sigma
   double *logits;            // [S][E]
   GroupBuf *out;
   const ExpertRec *table;    // layer expert table [kMaxE], or null (route only)
   int E, D, S, K;
   int x_bf16;
-  int splits, cols_per_split;
+  int splits, cols_per_split;  // GEMV: column splits of an expert row, one wave each
+  int epb;                   // GEMV: experts per workgroup (splits * epb <= 16 waves)
   int vec;                   // four-column loads in the GEMV
   int norm_topk;
   float topp, routed_scale;
@@ -101,7 +102,7 @@ struct ProjArgs {
   int O, C;                  // rows and columns of every tensor in the launch
   int tile_groups, tile_rows;  // workgroups per group row (4 tiles each), rows per tile
   int grid_rows;             // group rows the grid covers (grid = grid_rows * tile_groups)
-  RouteArgs ra;              // dual with the fused selection: the route whose partials it ranks
+  RouteArgs ra;              // dual with the fused selection: the route whose scores it ranks
 };
 
 struct TakeArgs {
@@ -116,7 +117,7 @@ struct TakeArgs {
 // Launchers (defined in the kernel translation units).  They return hipGetLastError().  With
 // t0/t1 non-null the launch records the kernel's own start and end into them
 // (hipExtLaunchKernel), so an event pair spans the kernel alone.
-// parts: kRouteGemv, kRouteSelect or both.  The selection reads the GEMV's partials.
+// parts: kRouteGemv, kRouteSelect or both.  The selection reads the GEMV's scores.
 constexpr int kRouteGemv = 1, kRouteSelect = 2;
 hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);

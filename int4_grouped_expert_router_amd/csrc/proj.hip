@@ -401,11 +401,12 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
 }
 
 // NT = 2: dual gate/up with the SiLU-gated product; NT = 1: down projection.  XB: bf16
-// activations through v_dot2_f32_bf16 (dual only).  SEL (dual, one token): every workgroup
-// first runs the expert selection itself from the router's split partials, so no separate
-// selection launch sits between the router GEMV and the experts; workgroup 0 also publishes
-// the route, group record and row descriptors for the down projection, the take and the
-// taps.  A tile holds at most 64 rows (one result per lane).
+// activations through v_dot2_f32_bf16 (dual only).  SEL (dual, one token, E <= 64): every
+// workgroup first runs the expert selection itself from the router's finished scores, so no
+// selection launch sits between the router GEMV and the experts; workgroup 0 publishes the
+// route and group records, the first workgroup of each row that row's descriptor (for the
+// down projection, the take and the taps).  A tile holds at most 64 rows (one result per
+// lane).
 template <int V, int P, int NT, bool GEN, bool XB, bool SEL = false>
 __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   constexpr int RB = rows_per_step(V, P, NT, 16);
@@ -423,34 +424,68 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   uint32_t touch = 0;
   if constexpr (SEL) {
     static_assert(NT == 2, "selection runs in the dual projection");
-    __shared__ double s_sig[kWavesPerBlock][kMaxK];
-    __shared__ int s_pidx[kRows];
-    __shared__ float s_pw[kRows];
-    __shared__ int s_n[kTokens];
-    __shared__ int s_row_e[kRows], s_row_t[kRows];
-    __shared__ float s_row_w[kRows];
-    __shared__ int s_rows;
+    const RouteArgs &ra = a.ra;
+    __shared__ double s_cw[kWavesPerBlock][kWave];
+    __shared__ int s_cnt[kWavesPerBlock][kWave];
     __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];
+    // one batch of loads: this lane's expert score, the expert records (E <= 64)
+    const double2 cs = ra.score[min(lane, ra.E - 1)];
     uint32_t tv[kTabPerThread];
-    table_prefetch(tv, a.ra.table, a.ra.E);
-    // (the table is never null here; the test keeps the record from being folded into a
-    // constant initializer, which LDS addresses cannot be)
-    SelShared sh{s_sig, s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, a.ra.table ? s_tab : nullptr};
-    double *s_sel = reinterpret_cast<double *>(s_act + act_words<V, P, XB>());
-    select_pass(a.ra, s_sel, 0, sh, blockIdx.x == 0);
-    table_stage(s_tab, tv);
-    __syncthreads();
-    if (blockIdx.x == 0) publish_group(a.ra, sh);
-    // this row: rank jr of the one token (its selections are distinct experts, in route order)
-    live = __builtin_amdgcn_readfirstlane(jr < s_n[0] ? 1 : 0);
-    const int e = __builtin_amdgcn_readfirstlane(live ? s_pidx[jr] : 0);
+    table_prefetch(tv, ra.table, ra.E);
+    const SelOne r = select_one(ra, cs, s_cw, s_cnt, [&] { table_stage(s_tab, tv); });
+    // this row is selection jr of the one token
+    live = jr < r.n ? 1 : 0;
+    const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(r.e_k, jr));
+    const float w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(r.w_k), jr));
     arow = 0;
+    GroupBuf *out = ra.out;
+    if (blockIdx.x == 0 && wib == 0) {
+      // route record and group record of the token: its selections, one row each, in order
+      RouteTok *rt = out->route;
+      const int n = r.n;
+      if (lane == 0) rt->n = n;
+      rt->idx[lane] = lane < ra.K ? r.e_k : -1;
+      rt->w[lane] = r.w_k;
+      GroupDev *G = &out->g;
+      if (lane < n) {
+        G->entry_expert[lane] = r.e_k;
+        G->entry_row0[lane] = lane;
+        G->row_token[lane] = 0;
+        G->row_expert[lane] = r.e_k;
+        G->row_weight[lane] = r.w_k;
+        G->red_rows[lane] = lane;
+      }
+      if (lane == 0) {
+        G->entry_row0[n] = n;
+        G->tok_row0[0] = 0;
+        G->tok_row0[1] = n;
+        G->n_entries = n;
+        G->n_rows = n;
+        G->S = 1;
+        G->reserved = 0;
+      }
+    }
+    if (blockIdx.x == jr * a.tile_groups && wib == 0 && lane < kDescWords) {
+      // this row's descriptor for the down projection and the take (zeros for a dead row)
+      uint32_t val = 0u;
+      if (live) {
+        if (lane == kLiveWord)
+          val = 1u;
+        else if (lane < kTabWords)
+          val = s_tab[e * kDescWords + lane];
+        else if (lane == kTabWords)
+          val = 0u;  // token
+        else
+          val = __float_as_uint(w);
+      }
+      reinterpret_cast<uint32_t *>(out->rows + jr)[lane] = val;
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const uint32_t *w = s_tab + e * kDescWords + n * (kTabWords / 3);
+      const uint32_t *wd = s_tab + e * kDescWords + n * (kTabWords / 3);
       uint32_t v[kTabWords / 3];
 #pragma unroll
-      for (int d = 0; d < kTabWords / 3; ++d) v[d] = __builtin_amdgcn_readfirstlane(w[d]);
+      for (int d = 0; d < kTabWords / 3; ++d) v[d] = __builtin_amdgcn_readfirstlane(wd[d]);
       T[n].q = reinterpret_cast<const uint8_t *>(((uint64_t)v[1] << 32) | v[0]);
       T[n].s = reinterpret_cast<const float *>(((uint64_t)v[3] << 32) | v[2]);
       T[n].O = (int)v[4];
@@ -740,7 +775,7 @@ hipError_t launch(int V, int P, int NT, bool gen, bool xb, bool sel, const ProjA
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
-  const size_t lds = lds_bytes(V, P, xb) + (sel ? select_lds_bytes(a.ra.E, a.ra.splits, 1) : 0);
+  const size_t lds = lds_bytes(V, P, xb);
   if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st, t0, t1, 0);
   return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st);
 }

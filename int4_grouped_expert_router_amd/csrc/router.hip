@@ -99,28 +99,49 @@ __device__ __forceinline__ double gemv_vec(const float *wrow, const void *x, siz
   return acc;
 }
 
-// partial[t][e][split] = sum over the split's columns of W[e][c] * x[t][c], one wave per
-// (expert row, column split).  With a.vec (D % 4 == 0, 16-byte aligned W and x) every lane
+// One workgroup per `epb` experts, one wave per (expert, column split).  Each wave sums its
+// split of W[e] . x[t] (f64, DPP wave sum); then one thread per (token, expert) adds the
+// splits in split order into the logit and forms sigma and the choice score, so the selection
+// starts from finished scores.  With a.vec (D % 4 == 0, 16-byte aligned W and x) every lane
 // reads four consecutive columns per load.
-__global__ __launch_bounds__(kBlock) void k_route_gemv(RouteArgs a) {
+constexpr int kGemvWaves = 16;
+__global__ __launch_bounds__(kGemvWaves * kWave) void k_route_gemv(RouteArgs a) {
+  __shared__ double s_part[kTokens][kGemvWaves];
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (unit >= a.E * a.splits) return;
-  const int e = unit / a.splits;
-  const int sp = unit - e * a.splits;
-  const int c0 = sp * a.cols_per_split;
-  const int c1 = min(a.D, c0 + a.cols_per_split);
-  const float *wrow = a.W + (size_t)e * a.D;
-  for (int t = 0; t < a.S; ++t) {
-    const size_t xoff = (size_t)t * a.D;
-    double acc = 0.0;
-    if (a.vec) {
-      acc = a.x_bf16 ? gemv_vec<true>(wrow, a.x, xoff, c0, c1, lane) : gemv_vec<false>(wrow, a.x, xoff, c0, c1, lane);
-    } else {
-      for (int c = c0 + lane; c < c1; c += kWave) acc = fma((double)wrow[c], (double)x_at(a.x, a.x_bf16, xoff + c), acc);
+  const int wib = threadIdx.x >> 6;
+  const int el = wib / a.splits;
+  const int sp = wib - el * a.splits;
+  const int e = blockIdx.x * a.epb + el;
+  // the finishing thread's expert and its bias, loaded before the long stream
+  const int ft = threadIdx.x / a.epb, fe = blockIdx.x * a.epb + (threadIdx.x - ft * a.epb);
+  const bool fin = ft < a.S && fe < a.E;
+  const float fb = a.bias[min(fe, a.E - 1)];
+  if (e < a.E) {
+    const int c0 = sp * a.cols_per_split;
+    const int c1 = min(a.D, c0 + a.cols_per_split);
+    const float *wrow = a.W + (size_t)e * a.D;
+    for (int t = 0; t < a.S; ++t) {
+      const size_t xoff = (size_t)t * a.D;
+      double acc = 0.0;
+      if (a.vec) {
+        acc = a.x_bf16 ? gemv_vec<true>(wrow, a.x, xoff, c0, c1, lane) : gemv_vec<false>(wrow, a.x, xoff, c0, c1, lane);
+      } else {
+        for (int c = c0 + lane; c < c1; c += kWave) acc = fma((double)wrow[c], (double)x_at(a.x, a.x_bf16, xoff + c), acc);
+      }
+      acc = wave_sum_f64(acc);
+      if (lane == 0) s_part[t][wib] = acc;
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) a.partial[((size_t)t * a.E + e) * a.splits + sp] = acc;
+  }
+  __syncthreads();
+  if (fin) {
+    const int fl = threadIdx.x - ft * a.epb;
+    double l = 0.0;
+    for (int j = 0; j < a.splits; ++j) l += s_part[ft][fl * a.splits + j];
+    const double sg = 1.0 / (1.0 + exp(-l));
+    double c = sg + (double)fb;
+    if (c != c) c = -__builtin_inf();
+    a.logits[(size_t)ft * a.E + fe] = l;
+    a.score[(size_t)ft * a.E + fe] = make_double2(c, sg);
   }
 }
 
@@ -139,12 +160,12 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];  // expert records, when E is small
 
   // With few experts, every expert's 128-byte record is loaded now, in the same batch as the
-  // partials, so the row descriptors need no further memory round trip at the end.
+  // scores, so the row descriptors need no further memory round trip at the end.
   const bool tab_pre = a.table != nullptr && a.E <= kTabPrefetchE;
   uint32_t tv[kTabPerThread];
   if (tab_pre) table_prefetch(tv, a.table, a.E);
   SelShared sh{s_sig, s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, tab_pre ? s_tab : nullptr};
-  for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S)) select_pass(a, s_dyn, t0, sh, true);
+  for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S)) select_pass(a, s_dyn, t0, sh);
   if (tab_pre) table_stage(s_tab, tv);
   publish_group(a, sh);
 }
@@ -152,8 +173,8 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
-  const int units = a.E * a.splits;
-  const size_t lds = select_lds_bytes(a.E, a.splits, a.S);
+  if (a.splits * a.epb > kGemvWaves || a.S * a.epb > a.splits * a.epb * kWave) return hipErrorInvalidValue;
+  const size_t lds = select_lds_bytes(a.E, a.S);
   static bool lds_raised = false;
   if ((parts & kRouteSelect) && lds > 64 * 1024 && !lds_raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_route_select),
@@ -165,10 +186,11 @@ hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_
   hipEvent_t g1 = (parts & kRouteSelect) ? nullptr : t1;
   hipEvent_t s0 = (parts & kRouteGemv) ? nullptr : t0;
   if (parts & kRouteGemv) {
+    const dim3 grid((a.E + a.epb - 1) / a.epb), block(a.splits * a.epb * kWave);
     if (t0 || g1)
-      hipExtLaunchKernelGGL(k_route_gemv, dim3((units + kWaves - 1) / kWaves), dim3(kBlock), 0, st, t0, g1, 0, a);
+      hipExtLaunchKernelGGL(k_route_gemv, grid, block, 0, st, t0, g1, 0, a);
     else
-      hipLaunchKernelGGL(k_route_gemv, dim3((units + kWaves - 1) / kWaves), dim3(kBlock), 0, st, a);
+      hipLaunchKernelGGL(k_route_gemv, grid, block, 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,5 +1,5 @@
-// Expert selection of the device router, shared by the select kernel and the fused
-// select-in-dual path of the projection kernel (one token).  See router.hip for the method.
+// Expert selection of the device router, shared by the select kernel (any S) and the dual
+// projection, which runs the selection of one token itself.  See router.hip for the method.
 #pragma once
 
 #include <cstddef>
@@ -24,15 +24,13 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 }
 
 // Tokens are ranked in passes of up to four; a token gets 4 / (tokens in the pass) waves.
-// Dynamic LDS per token slot: np doubles (split partials), E doubles (logits), E doubles
-// (choice scores), E doubles (sigma), E floats (bias), wpt * E ints (rank counts per wave).
+// Dynamic LDS per token slot: E doubles (choice scores), E doubles (sigma), wpt * E ints (rank
+// counts per wave).
 __host__ __device__ inline int select_slots(int S) { return S < kWavesPerBlock ? S : kWavesPerBlock; }
-__host__ __device__ inline size_t select_slot_doubles(int E, int splits, int wpt) {
-  return (size_t)E * splits + 3 * (size_t)E + (E + 1) / 2 + ((size_t)wpt * E + 1) / 2;
-}
-__host__ __device__ inline size_t select_lds_bytes(int E, int splits, int S) {
+__host__ __device__ inline size_t select_slot_doubles(int E, int wpt) { return 2 * (size_t)E + ((size_t)wpt * E + 1) / 2; }
+__host__ __device__ inline size_t select_lds_bytes(int E, int S) {
   const int slots = select_slots(S);
-  return 8 * (size_t)slots * select_slot_doubles(E, splits, kWavesPerBlock / slots);
+  return 8 * (size_t)slots * select_slot_doubles(E, kWavesPerBlock / slots);
 }
 
 // Workgroup-shared results and scratch of a selection (static __shared__ arrays of the kernel).
@@ -47,7 +45,7 @@ struct SelShared {
   const uint32_t *tab;   // staged expert records [E][32] (E <= kTabPrefetchE), or null
 };
 
-// Expert records loaded early, in the same batch as the first partials (E <= kTabPrefetchE).
+// Expert records loaded early, in the same batch as the scores (E <= kTabPrefetchE).
 __device__ __forceinline__ void table_prefetch(uint32_t (&tv)[kTabPerThread], const ExpertRec *table, int E) {
   const uint32_t *tsrc = reinterpret_cast<const uint32_t *>(table);
 #pragma unroll
@@ -58,24 +56,45 @@ __device__ __forceinline__ void table_stage(uint32_t *s_tab, const uint32_t (&tv
   for (int j = 0; j < kTabPerThread; ++j) s_tab[threadIdx.x + j * kBlock] = tv[j];
 }
 
-// One pass: tokens t0 .. t0 + slots - 1.  All threads of the workgroup call it (it holds
-// workgroup barriers).  With `out`, the pass also writes the route records and the logits tap.
-static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh, bool out) {
+// Top-p, norm and scale of one token's selection.  Lane k < K holds sigma of selection k;
+// control is wave-uniform.  The running sums run over k in order, one chain of f64 adds whose
+// prefix k lane k keeps: the top-p total is the whole chain, the cut is the first prefix that
+// reaches p * total, and the norm divisor is the kept prefix.  Returns the lane's f32 weight
+// (0 from n on) and the kept count n.
+__device__ __forceinline__ float finish_weights(const RouteArgs &a, double my_sig, int &n_out) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K;
+  double run = 0.0, pre = 0.0;
+  for (int k = 0; k < K; ++k) {
+    run += readlane_f64(my_sig, k);
+    if (lane == k) pre = run;
+  }
+  int n = K;
+  const double p = (double)a.topp;
+  if (p > 0.0 && p < 1.0) {
+    const double thr = p * run;
+    const unsigned long long m = __ballot(lane < K && pre >= thr);
+    if (m) n = __ffsll((long long)m);
+  }
+  const double den = a.norm_topk ? readlane_f64(pre, n - 1) : 1.0;
+  const double wv = (a.norm_topk ? my_sig / den : my_sig) * (double)a.routed_scale;
+  n_out = n;
+  return lane < n ? (float)wv : 0.f;
+}
+
+// One pass of the select kernel: tokens t0 .. t0 + slots - 1.  All threads of the workgroup
+// call it (it holds workgroup barriers); it writes the route records.
+static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int E = a.E, K = a.K, S = a.S, splits = a.splits;
-  const int np = E * splits;  // <= kMaxE partials per token (checked on the host)
-  const int nq = np + E;
+  const int E = a.E, K = a.K, S = a.S;
   const int slots = select_slots(S), wpt = kWavesPerBlock / slots;
   const int slot = wid / wpt, u = wid - slot * wpt;  // token slot of this wave, index inside it
   const int gt = u * kWave + lane, gn = wpt * kWave;  // thread index / count within the slot
-  double *s_v = s_dyn + slot * select_slot_doubles(E, splits, wpt);  // partials
-  double *s_c = s_v + np;                   // logits
-  double *s_x = s_c + E;                    // choice scores
-  double *s_sg = s_x + E;                   // sigma
-  float *s_b = reinterpret_cast<float *>(s_sg + E);
-  int *s_r = reinterpret_cast<int *>(s_b + ((E + 1) & ~1));  // [wpt][E] rank counts
+  double *s_x = s_dyn + slot * select_slot_doubles(E, wpt);  // choice scores
+  double *s_sg = s_x + E;                                     // sigma
+  int *s_r = reinterpret_cast<int *>(s_sg + E);               // [wpt][E] rank counts
   int *s_pidx = sh.pidx;
   float *s_pw = sh.pw;
   int *s_n = sh.n;
@@ -83,42 +102,21 @@ static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s
 
   const int t = t0 + slot;
   const bool act = slot < slots && t < S;
-  // the token's partials ([e][split], contiguous) and the bias: clamped, unconditional
-  // loads, eight in flight per thread, no branch between them
+  // the token's scores: clamped, unconditional loads, four in flight per thread
   if (act) {
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(a.partial + (size_t)t * np);
-    const uint32_t *bsrc = reinterpret_cast<const uint32_t *>(a.bias);
-    for (int q0 = 0; q0 < nq; q0 += 8 * gn) {
-      uint64_t pv[8];
-      uint32_t bv[8];
+    const double2 *src = a.score + (size_t)t * E;
+    for (int e0 = 0; e0 < E; e0 += 4 * gn) {
+      double2 v[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = q0 + j * gn + gt;
-        pv[j] = src[min(q, np - 1)];
-        bv[j] = bsrc[min(max(q - np, 0), E - 1)];
-      }
+      for (int j = 0; j < 4; ++j) v[j] = src[min(e0 + j * gn + gt, E - 1)];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = q0 + j * gn + gt;
-        if (q < np)
-          s_v[q] = __longlong_as_double((long long)pv[j]);
-        else if (q < nq)
-          s_b[q - np] = __uint_as_float(bv[j]);
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + j * gn + gt;
+        if (e < E) {
+          s_x[e] = v[j].x;
+          s_sg[e] = v[j].y;
+        }
       }
-    }
-  }
-  __syncthreads();
-  // logit = the splits summed in split order; choice score c = sigma + bias, NaN ranked last
-  if (act) {
-    for (int e = gt; e < E; e += gn) {
-      double l = 0.0;
-      for (int sp = 0; sp < splits; ++sp) l += s_v[e * splits + sp];
-      s_c[e] = l;
-      const double sg = 1.0 / (1.0 + exp(-l));
-      s_sg[e] = sg;
-      double c = sg + (double)s_b[e];
-      if (c != c) c = -__builtin_inf();
-      s_x[e] = c;
     }
   }
   __syncthreads();
@@ -144,7 +142,7 @@ static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s
     }
   }
   __syncthreads();
-  // the experts of rank < K are the selection, in order; sigma from the raw logit
+  // the experts of rank < K are the selection, in order
   if (act && u == 0) {
     for (int e = lane; e < E; e += kWave) {
       int rank = 0;
@@ -157,41 +155,62 @@ static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s
   }
   __syncthreads();
   if (act && u == 0) {
-    // top-p, norm, scale: lane k holds sigma_k; the sums run over k in order (uniform values)
-    const double my_sig = lane < K ? s_sig[slot][lane] : 0.0;
-    int n = K;
-    const double p = (double)a.topp;
-    if (p > 0.0 && p < 1.0) {
-      double total = 0.0;
-      for (int k = 0; k < K; ++k) total += readlane_f64(my_sig, k);
-      const double thr = p * total;
-      double run = 0.0;
-      for (int m = 1; m <= K; ++m) {
-        run += readlane_f64(my_sig, m - 1);
-        if (run >= thr) {
-          n = m;
-          break;
-        }
-      }
-    }
-    double den = 0.0;
-    if (a.norm_topk)
-      for (int k = 0; k < n; ++k) den += readlane_f64(my_sig, k);
-    const double wv = (a.norm_topk ? my_sig / den : my_sig) * (double)a.routed_scale;
+    int n;
+    const float wk = finish_weights(a, lane < K ? s_sig[slot][lane] : 0.0, n);
     if (lane == 0) s_n[t] = n;
-    const float wk = lane < n ? (float)wv : 0.f;
-    if (out) {
-      RouteTok *rt = a.out->route + t;
-      if (lane == 0) rt->n = n;
-      rt->idx[lane] = lane < K ? s_pidx[t * K + lane] : -1;
-      rt->w[lane] = wk;
-    }
+    RouteTok *rt = a.out->route + t;
+    if (lane == 0) rt->n = n;
+    rt->idx[lane] = lane < K ? s_pidx[t * K + lane] : -1;
+    rt->w[lane] = wk;
     if (lane < K) s_pw[t * K + lane] = wk;
   }
-  if (act && out)
-    for (int e = gt; e < E; e += gn) a.logits[(size_t)t * E + e] = s_c[e];  // logits tap
   __syncthreads();
+}
 
+// The selection of one token (S == 1, E <= 64) inside a workgroup of four waves, with one
+// workgroup barrier.  Lane e holds expert e's score; each wave counts, for every expert, the
+// experts of its quarter that beat it; the counts meet in LDS; the ranks then send each
+// expert's index and sigma to the lane of its rank (ds_permute), and every wave finishes
+// the weights itself.  `cs` is the lane's (choice score, sigma); `s_cw` [4][64] doubles and
+// `s_cnt` [4][64] ints are scratch.  `before_barrier` runs just ahead of the barrier (it
+// stages the expert table).  Lane k < K returns selection k's expert in `e_k` and its weight.
+struct SelOne {
+  int e_k;      // expert of selection `lane` (lanes past E: unspecified)
+  float w_k;    // f32 weight of selection `lane` (0 from n on)
+  int n;        // kept count
+};
+template <class F>
+__device__ __forceinline__ SelOne select_one(const RouteArgs &a, double2 cs, double (*s_cw)[kWave], int (*s_cnt)[kWave],
+                                             F &&before_barrier) {
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int E = a.E;
+  const double c = cs.x;
+  s_cw[wid][lane] = c;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kQ = kWave / kWavesPerBlock;  // 16 experts per wave
+  const int f0 = wid * kQ;
+  double cf[kQ];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) cf[j] = s_cw[wid][f0 + j];  // broadcast reads
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) cnt += (f0 + j < E && (cf[j] > c || (cf[j] == c && f0 + j < lane))) ? 1 : 0;
+  s_cnt[wid][lane] = cnt;
+  before_barrier();
+  __syncthreads();
+  int rank = lane;
+  if (lane < E) rank = s_cnt[0][lane] + s_cnt[1][lane] + s_cnt[2][lane] + s_cnt[3][lane];
+  const uint64_t sb = __double_as_longlong(cs.y);
+  SelOne r;
+  r.e_k = __builtin_amdgcn_ds_permute(rank * 4, lane);
+  const uint32_t lo = __builtin_amdgcn_ds_permute(rank * 4, (int)(uint32_t)sb);
+  const uint32_t hi = __builtin_amdgcn_ds_permute(rank * 4, (int)(uint32_t)(sb >> 32));
+  const double sig_k = __longlong_as_double(((uint64_t)hi << 32) | lo);
+  r.w_k = finish_weights(a, lane < a.K ? sig_k : 0.0, r.n);
+  return r;
 }
 
 // Group record and row descriptors of the finished selection (all threads of the workgroup;
