@@ -171,6 +171,10 @@ int i4moe_route(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S, 
  * must be set; with group == NULL that is every expert 0..E-1 of the layer.
  * Returns the slot index (>= 0) or a negative code with nothing enqueued, so the caller can
  * fall back to another path [PR342].  x_dev must stay valid until the issue has executed.
+ * A lone one-token issue of a device route (no other slot pending, at most 8 rows, I <= 2048)
+ * enqueues only the dual projection: the take then runs the down projection and the
+ * reduction in one kernel.  A y tap, another issue, a stream switch or a change of the
+ * layer's experts runs the down projection on its own first; the results are bitwise the same.
  * Fault-hook gated. */
 int i4moe_expert_group_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S,
                              const i4moe_group *group);
@@ -218,7 +222,8 @@ size_t i4moe_debug_size(i4moe_ctx *ctx, int what, int index);
 /* ---- profiling ---------------------------------------------------------------------------- */
 
 /* Kernel families timed when profiling is on.  A selection run inside the dual projection
- * (see i4moe_route) is timed as part of I4MOE_K_DUAL. */
+ * (see i4moe_route) is timed as part of I4MOE_K_DUAL, a down projection run inside the take
+ * (see i4moe_expert_group_issue) as part of I4MOE_K_TAKE. */
 enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_COUNT = 4 };
 
 /* on != 0: bracket every later kernel launch with a pair of HIP events on the context's

@@ -43,6 +43,11 @@ struct SlotInfo {
   int S = 0, D = 0, rows = 0;
   const GroupBuf *grp = nullptr;  // group record + row descriptors this issue ran
   int ring = -1;                  // route ring entry it came from, -1 for an explicit group
+  // The down projection of a lone one-token issue waits for the take, which runs it fused
+  // with the reduction (k_down_take); anything else that needs y or h first runs it alone.
+  bool down_pending = false;
+  int down_P = 0, down_blocks = 0;
+  ProjArgs down{};
 };
 
 constexpr int kRing = 32;  // route buffers: a layer may be re-routed up to 31 times before a take
@@ -199,6 +204,26 @@ int flush_sel(i4moe_ctx *c) {
   if (e != hipSuccess) return hip_fail(c, e, "route selection launch");
   c->sel_pending = false;
   return I4MOE_OK;
+}
+
+// Enqueue the down projections still waiting for a take (see SlotInfo::down_pending).
+int flush_down(i4moe_ctx *c) {
+  for (int s = 0; s < c->nslots; ++s) {
+    SlotInfo &si = c->slots[s];
+    if (!si.down_pending) continue;
+    hipError_t e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_down16(si.down_P, si.down, si.down_blocks, c->stream, t0, t1);
+    });
+    if (e != hipSuccess) return hip_fail(c, e, "down launch");
+    si.down_pending = false;
+  }
+  return I4MOE_OK;
+}
+
+// Everything deferred, before a call that needs the route, h, y or the tensors as they are now.
+int flush_all(i4moe_ctx *c) {
+  int rc = flush_sel(c);
+  return rc ? rc : flush_down(c);
 }
 
 void drain_profile(i4moe_ctx *c) {
@@ -447,10 +472,8 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
 
 int i4moe_set_stream(i4moe_ctx *c, void *stream) {
   if (!c) return I4MOE_EINVAL;
-  if (c->sel_pending) {
-    ensure_device(c);
-    if (int rc = flush_sel(c)) return rc;
-  }
+  ensure_device(c);
+  if (int rc = flush_all(c)) return rc;
   c->stream = reinterpret_cast<hipStream_t>(stream);
   return I4MOE_OK;
 }
@@ -540,7 +563,7 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
   auto it = c->tensors.find(h);
   if (it == c->tensors.end()) return fail(c, I4MOE_EINVAL, "unknown tensor handle %u", h);
   ensure_device(c);
-  if (int rc = flush_sel(c)) return rc;
+  if (int rc = flush_all(c)) return rc;
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
   for (auto &kv : c->layers) {
@@ -564,10 +587,8 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
 
 int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
   if (!c) return I4MOE_EINVAL;
-  if (c->sel_pending) {
-    ensure_device(c);
-    if (int rc = flush_sel(c)) return rc;
-  }
+  ensure_device(c);
+  if (int rc = flush_all(c)) return rc;
   if (layer < 0 || expert < 0 || expert >= kMaxE) return fail(c, I4MOE_EINVAL, "bad layer %d / expert %d", layer, expert);
   auto tg = c->tensors.find(gate), tu = c->tensors.find(up), td = c->tensors.find(down);
   if (tg == c->tensors.end() || tu == c->tensors.end() || td == c->tensors.end())
@@ -605,10 +626,8 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
   if (!c) return I4MOE_EINVAL;
   if (layer < 0 || E < 1 || E > kMaxE || D < 1 || !W) return fail(c, I4MOE_EINVAL, "bad router arguments");
   if ((size_t)E * D > ((size_t)1 << 28)) return fail(c, I4MOE_EUNSUPPORTED, "router too large");
-  if (c->sel_pending) {
-    ensure_device(c);
-    if (int rc = flush_sel(c)) return rc;
-  }
+  ensure_device(c);
+  if (int rc = flush_all(c)) return rc;
   Layer &L = c->layers[layer];
   bool any_expert = false;
   for (i4moe_tensor g : L.gate) any_expert = any_expert || g != 0;
@@ -854,17 +873,27 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
       return rc;
     }
   }
+  // a waiting down projection reads h, which this issue's dual projection overwrites
+  if ((rc = flush_down(c))) return rc;
+  // A lone one-token issue of a device route leaves its down projection to the take.
+  const bool defer_down = S == 1 && !group && s == 0 && pn.rows16 && max_rows <= kDTRows;
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
   if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, sel, ad, pd.blocks, c->stream, t0, t1);
     });
   if (e == hipSuccess && sel) c->sel_pending = false;
-  if (e == hipSuccess) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
+  if (e == hipSuccess && !defer_down) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
       return pn.rows16 ? launch_down16(pn.P, an, pn.blocks, c->stream, t0, t1)
                        : launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
     });
   if (e != hipSuccess) return hip_fail(c, e, "issue launch");
+  c->slots[s].down_pending = defer_down;
+  if (defer_down) {
+    c->slots[s].down_P = pn.P;
+    c->slots[s].down_blocks = pn.blocks;
+    c->slots[s].down = an;
+  }
   c->slots[s].S = S;
   c->slots[s].D = L->D;
   c->slots[s].rows = max_rows;
@@ -894,6 +923,27 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
     return fail(c, I4MOE_EINVAL, "take: residual NULL or S=%d differs from the issued S=%d", S, c->slots[0].S);
   }
   ensure_device(c);
+  if (c->nslots == 1 && c->slots[0].down_pending && c->slots[0].ring >= 0 && S == 1) {
+    // the lone slot's down projection and the take in one launch
+    SlotInfo &si = c->slots[0];
+    ProjArgs dt = si.down;
+    dt.out = residual_dev;
+    hipError_t e = timed(c, I4MOE_K_TAKE, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_down_take(si.down_P, dt, c->stream, t0, t1);
+    });
+    if (e != hipSuccess) {
+      c->poisoned = true;
+      return hip_fail(c, e, "take launch");
+    }
+    si.down_pending = false;
+    c->nslots = 0;
+    c->calls++;
+    return I4MOE_OK;
+  }
+  if ((rc = flush_down(c))) {
+    c->poisoned = true;
+    return rc;
+  }
   TakeArgs a{};
   // Device routes at S = 1 hold distinct experts, one row each in route order, live rows first:
   // the take can then read everything without first reading the reduce order.
@@ -953,7 +1003,7 @@ int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t b
   const size_t need = i4moe_debug_size(c, what, index);
   if (need == 0 || bytes != need) return fail(c, I4MOE_EINVAL, "tap %d/%d: need %zu bytes, got %zu", what, index, need, bytes);
   ensure_device(c);
-  if (int rc = flush_sel(c)) return rc;
+  if (int rc = flush_all(c)) return rc;
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
   if (what == I4MOE_TAP_LOGITS) {

@@ -129,6 +129,12 @@ hipError_t launch_dual(int V, int P, bool gen, bool xb, bool sel, const ProjArgs
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                        hipEvent_t t1 = nullptr);
 hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Down projection and take in one launch, for one token and one issue of at most kDTRows
+// rows whose down rows fit k_rows16 (P passes), kDTTile outputs per workgroup: a.act = h,
+// a.grp = the group, a.grid_rows = its rows, a.O = D, a.C = I, a.out = the residual row,
+// updated in place.
+constexpr int kDTRows = 8, kDTTile = 16;
+hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Down projection over rows of at most 256 weight dwords (C <= 2048): 16 lanes per row, P
 // passes of 4 dwords per lane; f32 activations, per-row or 32-column-aligned group scales.
 hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,

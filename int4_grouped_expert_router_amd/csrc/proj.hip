@@ -651,6 +651,42 @@ __device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32
   }
 }
 
+// Stage column w (value x; 0 past the row) of a short row: odd columns divided by 16 (exact),
+// as dot8 takes them.
+__device__ __forceinline__ void stage16(uint32_t *lds, int w, float x) {
+  const int d = w >> 3, j = w & 7;  // dword span d = p * 64 + li * 4 + v, column j in it
+  lds[act16_word(d >> 6, d & 3, j >> 2, (d >> 2) & (kLR - 1)) + (j & 3)] = __float_as_uint((w & 1) ? x * 0.0625f : x);
+}
+
+// The same for columns c4 .. c4 + 3 (c4 a multiple of 4): one 16-byte LDS write.
+__device__ __forceinline__ void stage16x4(uint32_t *lds, int c4, float4 x) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int d = c4 >> 3;
+  f4 v = {x.x, x.y * 0.0625f, x.z, x.w * 0.0625f};
+  *reinterpret_cast<f4 *>(lds + act16_word(d >> 6, d & 3, (c4 & 7) >> 2, (d >> 2) & (kLR - 1))) = v;
+}
+
+// Offset term of each of the lane's spans: -8 * (sum of its activations), summed in
+// column-pair order.
+template <int P>
+__device__ __forceinline__ void span_offsets16(float (&xm)[P], const uint32_t *lds, int li) {
+  constexpr int V = 4;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float span = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = 2 * k;
+        span += __uint_as_float(lds[act16_word(p, v, j >> 2, li) + (j & 3)]) +
+                16.f * __uint_as_float(lds[act16_word(p, v, (j + 1) >> 2, li) + ((j + 1) & 3)]);
+      }
+    }
+    xm[p] = -8.f * span;
+  }
+}
+
 template <int P>
 __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   constexpr int V = 4;
@@ -692,35 +728,18 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   load_step16<P>(b1, wr, sr, T, woff, gi, o_begin + kGR, g);
   __builtin_amdgcn_sched_barrier(0);
-  // staged with odd columns divided by 16 (exact), as dot8 takes them
 #pragma unroll
   for (int i = 0; i < (int)(sizeof(xs) / sizeof(xs[0])); ++i) {
     const int w = threadIdx.x + i * kBlock;  // column
-    const float x = w < C ? __uint_as_float(xs[i]) : 0.f;
-    const int d = w >> 3, j = w & 7;         // dword span d = p * 64 + li * 4 + v, column j in it
-    s_act[act16_word(d >> 6, d & 3, j >> 2, (d >> 2) & (kLR - 1)) + (j & 3)] = __float_as_uint((w & 1) ? x * 0.0625f : x);
+    stage16(s_act, w, w < C ? __uint_as_float(xs[i]) : 0.f);
   }
   __syncthreads();
   if (!work) {
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  // offset term of each span: -8 * (sum of its activations), summed in column-pair order
   float xm[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    float span = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = 2 * k;
-        span += __uint_as_float(s_act[act16_word(p, v, j >> 2, li) + (j & 3)]) +
-                16.f * __uint_as_float(s_act[act16_word(p, v, (j + 1) >> 2, li) + ((j + 1) & 3)]);
-      }
-    }
-    xm[p] = -8.f * span;
-  }
+  span_offsets16<P>(xm, s_act, li);
 
   float outv = 0.f;
   int o = o_begin;
@@ -747,6 +766,115 @@ const void *rows16_ptr(int P) {
 
 size_t rows16_lds_bytes(int P) { return 4u * (size_t)P * kLR * 4 * 8; }
 
+// ---- Down projection and take in one launch (one token, one issue, at most kDTRows rows,
+// short down rows).  A workgroup owns TL = 16 output columns of the residual and has one wave
+// per group row: the wave stages its row's h in its own LDS region and computes its expert's
+// TL outputs exactly as k_rows16 does; the rows then meet in LDS and are summed in row
+// (route) order with the take's arithmetic, fmaf over the live rows, added to the residual.
+// No y rows go through memory and no take launch follows.  (Measured on the medium decode
+// layer: 8-column tiles double the h staging traffic and 32-column tiles leave half the CUs
+// idle; both are slower.)
+template <int P>
+__global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
+  constexpr int V = 4;
+  constexpr int TL = kDTTile;
+  static_assert(TL % (2 * kGR) == 0 && TL <= kWave, "whole pipeline passes, one output per lane");
+  extern __shared__ uint32_t s_act[];  // [kDTRows][P * 512] staged h rows
+  __shared__ float s_y[kDTRows][TL];
+  __shared__ float s_w[kDTRows];
+  __shared__ int s_live[kDTRows];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (kLR - 1), g = lane / kLR;
+  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // group row of this wave
+  const int i0 = blockIdx.x * TL;
+  const int i_end = min(i0 + TL, a.O);
+  const CGroupBuf G = (CGroupBuf)a.grp;
+  const int rr = min(r, a.grid_rows - 1);
+  const TensorDesc T = ld_desc(G->rows[rr].t[2]);
+  const int live = r < a.grid_rows ? G->rows[rr].t[0].live : 0;
+  const float wr_row = G->rows[rr].weight;
+  asm volatile("" ::"s"(T.q), "s"(T.s), "s"(T.O), "s"(T.C), "s"(T.row_bytes), "s"(T.gs), "s"(T.ng));
+  asm volatile("" ::"s"(live));
+  // the residual of the tile, in flight from the start
+  const float r_in = a.out[min(i0 + (lane % TL), a.O - 1)];
+
+  const int C = a.C;
+  const int RD = (C + 7) >> 3;
+  int gi[P], woff[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int ds = p * kLR * V + li * V;
+    gi[p] = (T.ng > 1 && ds < RD) ? (8 * ds) / T.gs : 0;
+    woff[p] = ds < RD ? 4 * ds : -1;
+  }
+  const int rows_in = live ? i_end : 0;  // a dead row's loads read nothing
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
+
+  // this row's h, loaded by its own wave, four columns per lane and load (clamped,
+  // unconditional; rows are 16-byte aligned and padded to a multiple of 64 columns)
+  constexpr int NX = P * 512 / (4 * kWave);
+  const float *hrow = static_cast<const float *>(a.act) + (size_t)rr * a.act_ld;
+  float4 xs[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int c4 = 4 * (lane + i * kWave);
+    xs[i] = *reinterpret_cast<const float4 *>(hrow + (c4 < C ? c4 : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Step16<P> b0, b1;
+  load_step16<P>(b0, wr, sr, T, woff, gi, i0, g);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step16<P>(b1, wr, sr, T, woff, gi, i0 + kGR, g);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t *lds = s_act + r * (P * 512);
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int c4 = 4 * (lane + i * kWave);
+    float4 x = xs[i];
+    // C is even: a group of four is whole, half or empty
+    if (c4 + 2 > C) x.x = x.y = 0.f;
+    if (c4 + 4 > C) x.z = x.w = 0.f;
+    stage16x4(lds, c4, x);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float xm[P];
+  span_offsets16<P>(xm, lds, li);
+
+  float outv = 0.f;
+  int o = i0;
+  do {
+    compute_step16<P>(b0, lds, li, xm, o, i0, lane, outv);
+    load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
+    if (o + kGR < i_end) compute_step16<P>(b1, lds, li, xm, o + kGR, i0, lane, outv);
+    load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
+    o += 2 * kGR;
+  } while (o < i_end);
+  if (lane < TL) s_y[r][lane] = outv;
+  if (lane == 0) {
+    s_w[r] = wr_row;
+    s_live[r] = live;
+  }
+  __syncthreads();
+  if (r == 0 && lane < TL && i0 + lane < a.O) {
+    float acc = 0.f;
+    for (int q = 0; q < a.grid_rows; ++q)
+      if (s_live[q]) acc = fmaf(s_w[q], s_y[q][lane], acc);
+    a.out[i0 + lane] = r_in + acc;
+  }
+}
+
+const void *down_take_ptr(int P) {
+  switch (P) {
+    case 1: return reinterpret_cast<const void *>(&k_down_take<1>);
+    case 2: return reinterpret_cast<const void *>(&k_down_take<2>);
+    case 3: return reinterpret_cast<const void *>(&k_down_take<3>);
+    case 4: return reinterpret_cast<const void *>(&k_down_take<4>);
+    default: return nullptr;
+  }
+}
 template <int NT, bool GEN, bool XB, bool SEL = false>
 const void *kernel_ptr_t(int V, int P) {
 #define I4MOE_PTR(v, p) \
@@ -830,6 +958,25 @@ hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, h
   void *params[] = {&args};
   hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st, t0, t1, 0)
                             : hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  const void *k = down_take_ptr(P);
+  if (!k || a.grid_rows < 1 || a.grid_rows > kDTRows || a.act_ld % 4 != 0 || reinterpret_cast<uintptr_t>(a.act) % 16 != 0)
+    return hipErrorInvalidValue;
+  const size_t lds = (size_t)kDTRows * rows16_lds_bytes(P);
+  static bool raised[5] = {};
+  if (lds > 48 * 1024 && !raised[P]) {
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised[P] = true;
+  }
+  ProjArgs args = a;
+  void *params[] = {&args};
+  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kWave);
+  hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, grid, block, params, lds, st, t0, t1, 0)
+                            : hipLaunchKernel(k, grid, block, params, lds, st);
   return e != hipSuccess ? e : hipGetLastError();
 }
 
