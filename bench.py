@@ -131,6 +131,63 @@ def copy_calibration(torch, nbytes: int = 256 << 20, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def sustained_stream(torch, B, layers: int = 2, steps: int = 60, reps: int = 3):
+    """The steady-state expert stream: the sustained workload (D=7168, I=2048, all 64 experts
+    of a layer taken, S=1, half g64 / half per-row), `layers` distinct layers (1.5 GB of int4
+    each, far more than the 256 MB Infinity Cache) cycled from one captured graph."""
+    from int4_grouped_expert_router_amd import Context
+    from synth import get_config
+    cfg = get_config("sustained")
+    stream = torch.cuda.current_stream()
+    ctx = Context(0, stream)
+    Ls = setup(cfg, layers, ctx, torch)
+    per_layer = [sum(L.bytes_gate_up[e] + L.bytes_down[e] for e in range(cfg.E)) for L in Ls]
+
+    def step(i):
+        L = Ls[i % layers]
+        ctx.route(i % layers, L.x_dev, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+        ctx.issue(i % layers, L.x_dev)
+        ctx.take(L.r_dev)
+
+    for i in range(2 * layers):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    elapsed = float(np.median(times))
+    ctx.set_profiling(True)
+    sleep_cycles = calibrate_sleep(torch, stream, burst=8)
+    for b0 in range(0, steps, 8):
+        torch.cuda._sleep(sleep_cycles)
+        for i in range(b0, min(steps, b0 + 8)):
+            step(i)
+    torch.cuda.synchronize()
+    kt = {name: ctx.profile(k) for name, k in
+          [("route", B.I4MOE_K_ROUTE), ("dual", B.I4MOE_K_DUAL), ("down", B.I4MOE_K_DOWN), ("take", B.I4MOE_K_TAKE)]}
+    ctx.close()
+    nbytes = sum(per_layer[i % layers] for i in range(steps))
+    gbps = nbytes / elapsed / 1e9
+    dual_gu = sum(sum(Ls[i % layers].bytes_gate_up[e] for e in range(cfg.E)) for i in range(steps))
+    dual_gbps = dual_gu / (kt["dual"][0] * 1e-3) / 1e9
+    return {"workload": f"sustained stream: D={cfg.D} I={cfg.I}, all {cfg.K} of E={cfg.E} experts per layer, S=1, "
+                        f"{cfg.formats} int4 (gs={cfg.gs}), {cfg.x_dtype} activations; {layers} distinct layers "
+                        f"({per_layer[0] / 1e9:.2f} GB each) cycled from one graph",
+            "steps": steps, "replays": f"median of {reps}", "us_per_layer": round(elapsed / steps * 1e6, 2),
+            "expert_weight_GBps_layer": round(gbps, 1), "pct_hbm_peak_layer": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "dual_GBps": round(dual_gbps, 1), "dual_pct_hbm_peak": round(100 * dual_gbps / HBM_PEAK_GBPS, 2),
+            "kernel_us": {k: round(v[0] * 1e3 / max(v[1], 1), 3) for k, v in kt.items()}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +198,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch the timed steps one call at a time (no graph)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sustained", action="store_true", help="skip the sustained-stream measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -270,10 +328,13 @@ def main():
                      "kernel": "k_proj dual gate/up+SiLU with the one-token expert selection", "bytes_per_launch": round(dual_alg / args.steps),
                      "avg_launch_us": round(dual_ms * 1e3 / max(dual_n, 1), 3)},
     }
+    ctx.close()
+    if not args.no_sustained and args.workload == "medium":
+        log("sustained stream")
+        line["sustained_stream"] = sustained_stream(torch, B)
     if not args.no_cpu:
         log("timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
-    ctx.close()
     print(json.dumps(line), flush=True)
 
 
