@@ -684,9 +684,11 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
   if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
   ensure_device(c);
-  // about 256 GEMV waves, each over a multiple of 256 columns; an expert's splits (and up to
-  // four experts of one split each) share a workgroup of at most 16 waves
+  // at least 256 GEMV waves and at most 1024 columns per wave (one batch of loads per lane and
+  // token group), each split a multiple of 256 columns; an expert's splits (and up to four
+  // experts of one split each) share a workgroup of at most 16 waves
   int splits = (256 + L->E - 1) / L->E;
+  if (splits < (L->D + 1023) / 1024) splits = (L->D + 1023) / 1024;
   if (splits > 16) splits = 16;
   int cps = round_up((L->D + splits - 1) / splits, 256);
   splits = (L->D + cps - 1) / cps;

@@ -22,7 +22,6 @@
 namespace i4moe {
 namespace {
 
-constexpr int kWaves = kWavesPerBlock;
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ double dpp_f64(double v) {
@@ -58,45 +57,55 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave's dot product of a W row segment [c0, c1) with x row t, in f64 (every f32 x f32
-// or f32 x bf16 product is exact in f64).  Vector path: four float4 chunks per lane in flight
-// per batch (addresses clamped into the segment, so the loads are unconditional), FMAs in
-// column order.
-template <bool XBF>
-__device__ __forceinline__ double gemv_vec(const float *wrow, const void *x, size_t xoff, int c0, int c1, int lane) {
-  double acc = 0.0;
+// One wave's dot products of a W row segment [c0, c1) with up to kGT consecutive x rows
+// t0 .. t0 + nt - 1, in f64 (every f32 x f32 or f32 x bf16 product is exact in f64).  Each
+// W chunk is loaded once for all of the group's tokens.  Vector path: four float4 chunks per
+// lane in flight per batch, with every x chunk they meet (addresses clamped into the segment
+// and the token range, so the loads are unconditional); per token, FMAs in column order.
+constexpr int kGT = 4;
+template <bool XBF, int NG>
+__device__ __forceinline__ void gemv_vec(double (&acc)[kGT], const float *wrow, const void *x, int D, int t0, int nt,
+                                         int c0, int c1, int lane) {
+#pragma unroll
+  for (int t = 0; t < kGT; ++t) acc[t] = 0.0;
   for (int c = c0 + 4 * lane; c < c1; c += 16 * kWave) {
     float4 w[4];
-    float xv[4][4];
+    float xv[NG][4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cj = c + 4 * kWave * j < c1 ? c + 4 * kWave * j : c;
       w[j] = *reinterpret_cast<const float4 *>(wrow + cj);
-      if constexpr (XBF) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + xoff + cj);
-        xv[j][0] = __uint_as_float(u.x << 16);
-        xv[j][1] = __uint_as_float(u.x & 0xffff0000u);
-        xv[j][2] = __uint_as_float(u.y << 16);
-        xv[j][3] = __uint_as_float(u.y & 0xffff0000u);
-      } else {
-        const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + xoff + cj);
-        xv[j][0] = q.x;
-        xv[j][1] = q.y;
-        xv[j][2] = q.z;
-        xv[j][3] = q.w;
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const size_t xoff = (size_t)(t0 + (t < nt ? t : nt - 1)) * D + cj;
+        if constexpr (XBF) {
+          const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + xoff);
+          xv[t][j][0] = __uint_as_float(u.x << 16);
+          xv[t][j][1] = __uint_as_float(u.x & 0xffff0000u);
+          xv[t][j][2] = __uint_as_float(u.y << 16);
+          xv[t][j][3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + xoff);
+          xv[t][j][0] = q.x;
+          xv[t][j][1] = q.y;
+          xv[t][j][2] = q.z;
+          xv[t][j][3] = q.w;
+        }
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (c + 4 * kWave * j < c1) {
-        acc = fma((double)w[j].x, (double)xv[j][0], acc);
-        acc = fma((double)w[j].y, (double)xv[j][1], acc);
-        acc = fma((double)w[j].z, (double)xv[j][2], acc);
-        acc = fma((double)w[j].w, (double)xv[j][3], acc);
+#pragma unroll
+        for (int t = 0; t < NG; ++t) {
+          acc[t] = fma((double)w[j].x, (double)xv[t][j][0], acc[t]);
+          acc[t] = fma((double)w[j].y, (double)xv[t][j][1], acc[t]);
+          acc[t] = fma((double)w[j].z, (double)xv[t][j][2], acc[t]);
+          acc[t] = fma((double)w[j].w, (double)xv[t][j][3], acc[t]);
+        }
       }
     }
   }
-  return acc;
 }
 
 // One workgroup per `epb` experts, one wave per (expert, column split).  Each wave sums its
@@ -120,16 +129,35 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void k_route_gemv(RouteArgs a) 
     const int c0 = sp * a.cols_per_split;
     const int c1 = min(a.D, c0 + a.cols_per_split);
     const float *wrow = a.W + (size_t)e * a.D;
-    for (int t = 0; t < a.S; ++t) {
-      const size_t xoff = (size_t)t * a.D;
-      double acc = 0.0;
+    for (int t0 = 0; t0 < a.S; t0 += kGT) {
+      const int nt = min(kGT, a.S - t0);
+      double acc[kGT];
       if (a.vec) {
-        acc = a.x_bf16 ? gemv_vec<true>(wrow, a.x, xoff, c0, c1, lane) : gemv_vec<false>(wrow, a.x, xoff, c0, c1, lane);
+        // one token: a group of one, no repeated x loads or FMAs
+        if (a.x_bf16)
+          nt == 1 ? gemv_vec<true, 1>(acc, wrow, a.x, a.D, t0, nt, c0, c1, lane)
+                  : gemv_vec<true, kGT>(acc, wrow, a.x, a.D, t0, nt, c0, c1, lane);
+        else
+          nt == 1 ? gemv_vec<false, 1>(acc, wrow, a.x, a.D, t0, nt, c0, c1, lane)
+                  : gemv_vec<false, kGT>(acc, wrow, a.x, a.D, t0, nt, c0, c1, lane);
       } else {
-        for (int c = c0 + lane; c < c1; c += kWave) acc = fma((double)wrow[c], (double)x_at(a.x, a.x_bf16, xoff + c), acc);
+#pragma unroll
+        for (int t = 0; t < kGT; ++t) {
+          acc[t] = 0.0;
+          if (t < nt) {
+            const size_t xoff = (size_t)(t0 + t) * a.D;
+            for (int c = c0 + lane; c < c1; c += kWave)
+              acc[t] = fma((double)wrow[c], (double)x_at(a.x, a.x_bf16, xoff + c), acc[t]);
+          }
+        }
       }
-      acc = wave_sum_f64(acc);
-      if (lane == 0) s_part[t][wib] = acc;
+#pragma unroll
+      for (int t = 0; t < kGT; ++t) {
+        if (t < nt) {  // uniform
+          const double v = wave_sum_f64(acc[t]);
+          if (lane == 0) s_part[t0 + t][wib] = v;
+        }
+      }
     }
   }
   __syncthreads();
@@ -145,12 +173,11 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void k_route_gemv(RouteArgs a) 
   }
 }
 
-// One workgroup, run once per layer on one CU, so written for latency: every global read of
-// a phase is issued in one batch, the waves of a token split its experts and its comparisons,
-// and the code is kept small.
+// One workgroup, run once per layer on one CU, so written for latency: each wave selects for
+// one token (four tokens per pass), every global read of a phase is issued in one batch, and
+// the code is kept small.
 __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   extern __shared__ double s_dyn[];
-  __shared__ double s_sig[kWaves][kMaxK];
   __shared__ int s_pidx[kRows];
   __shared__ float s_pw[kRows];
   __shared__ int s_n[kTokens];
@@ -164,7 +191,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   const bool tab_pre = a.table != nullptr && a.E <= kTabPrefetchE;
   uint32_t tv[kTabPerThread];
   if (tab_pre) table_prefetch(tv, a.table, a.E);
-  SelShared sh{s_sig, s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, tab_pre ? s_tab : nullptr};
+  SelShared sh{s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, tab_pre ? s_tab : nullptr};
   for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S)) select_pass(a, s_dyn, t0, sh);
   if (tab_pre) table_stage(s_tab, tv);
   publish_group(a, sh);

@@ -23,19 +23,13 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __longlong_as_double(((uint64_t)hi << 32) | lo);
 }
 
-// Tokens are ranked in passes of up to four; a token gets 4 / (tokens in the pass) waves.
-// Dynamic LDS per token slot: E doubles (choice scores), E doubles (sigma), wpt * E ints (rank
-// counts per wave).
+// Tokens are selected in passes of up to four, one wave per token.  Dynamic LDS per token
+// slot: E doubles (choice scores) and E doubles (sigma).
 __host__ __device__ inline int select_slots(int S) { return S < kWavesPerBlock ? S : kWavesPerBlock; }
-__host__ __device__ inline size_t select_slot_doubles(int E, int wpt) { return 2 * (size_t)E + ((size_t)wpt * E + 1) / 2; }
-__host__ __device__ inline size_t select_lds_bytes(int E, int S) {
-  const int slots = select_slots(S);
-  return 8 * (size_t)slots * select_slot_doubles(E, kWavesPerBlock / slots);
-}
+__host__ __device__ inline size_t select_lds_bytes(int E, int S) { return 16 * (size_t)select_slots(S) * E; }
 
 // Workgroup-shared results and scratch of a selection (static __shared__ arrays of the kernel).
 struct SelShared {
-  double (*sig)[kMaxK];  // [slot][k]: sigma of the selections
   int *pidx;             // [t * K + k]: selections of every token
   float *pw;             // [t * K + k]: final f32 weights
   int *n;                // [t]: kept count after top-p
@@ -82,87 +76,137 @@ __device__ __forceinline__ float finish_weights(const RouteArgs &a, double my_si
   return lane < n ? (float)wv : 0.f;
 }
 
-// One pass of the select kernel: tokens t0 .. t0 + slots - 1.  All threads of the workgroup
-// call it (it holds workgroup barriers); it writes the route records.
-static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int E = a.E, K = a.K, S = a.S;
-  const int slots = select_slots(S), wpt = kWavesPerBlock / slots;
-  const int slot = wid / wpt, u = wid - slot * wpt;  // token slot of this wave, index inside it
-  const int gt = u * kWave + lane, gn = wpt * kWave;  // thread index / count within the slot
-  double *s_x = s_dyn + slot * select_slot_doubles(E, wpt);  // choice scores
-  double *s_sg = s_x + E;                                     // sigma
-  int *s_r = reinterpret_cast<int *>(s_sg + E);               // [wpt][E] rank counts
-  int *s_pidx = sh.pidx;
-  float *s_pw = sh.pw;
-  int *s_n = sh.n;
-  double (*s_sig)[kMaxK] = sh.sig;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64s(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROW_MASK>((int)(uint32_t)u);
+  const int hi = dpp_i32<CTRL, ROW_MASK>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
 
+// (c, e) beats (c2, e2) in the selection order: larger score, then lower index; e = kNoExpert
+// marks "no candidate" and beats nothing.
+constexpr int kNoExpert = 0x7fffffff;
+__device__ __forceinline__ bool beats(double c, int e, double c2, int e2) {
+  return e != kNoExpert && (e2 == kNoExpert || c > c2 || (c == c2 && e < e2));
+}
+template <int CTRL>
+__device__ __forceinline__ void best_step(double &c, int &e) {
+  const double c2 = dpp_f64s<CTRL, 0xF>(c);
+  const int e2 = dpp_i32<CTRL, 0xF>(e);
+  if (beats(c2, e2, c, e)) {
+    c = c2;
+    e = e2;
+  }
+}
+
+// One pass of the select kernel: tokens t0 .. t0 + slots - 1, wave w on token t0 + w.  All
+// threads of the workgroup call it (it holds workgroup barriers); it writes the route records.
+//   E <= 64: lane e counts the experts that beat expert e (its rank); ranks below K are the
+//            selection positions.
+//   E > 64:  K rounds; each takes the best expert not yet taken (lanes hold experts e = lane +
+//            64 i; a lane's best, then the wave's over DPP steps and the four rows), which is
+//            the strict ascending scan itself.
+// Both give the experts of rank 0 .. K-1 in the order (score desc, index asc).
+static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh) {
+  const int lane = threadIdx.x & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int E = a.E, K = a.K, S = a.S;
+  double *s_x = s_dyn + (size_t)slot * 2 * E;  // choice scores
+  double *s_sg = s_x + E;                       // sigma
   const int t = t0 + slot;
-  const bool act = slot < slots && t < S;
-  // the token's scores: clamped, unconditional loads, four in flight per thread
+  const bool act = slot < select_slots(S) && t < S;
   if (act) {
+    // the token's scores: clamped, unconditional loads, four in flight per lane
     const double2 *src = a.score + (size_t)t * E;
-    for (int e0 = 0; e0 < E; e0 += 4 * gn) {
+    for (int e0 = 0; e0 < E; e0 += 4 * kWave) {
       double2 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = src[min(e0 + j * gn + gt, E - 1)];
+      for (int j = 0; j < 4; ++j) v[j] = src[min(e0 + j * kWave + lane, E - 1)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = e0 + j * gn + gt;
+        const int e = e0 + j * kWave + lane;
         if (e < E) {
           s_x[e] = v[j].x;
           s_sg[e] = v[j].y;
         }
       }
     }
-  }
-  __syncthreads();
-  // rank in (score desc, index asc), the comparisons split over the token's waves: wave u
-  // counts the experts f = u, u + wpt, ... that beat e
-  if (act) {
-    for (int e = lane; e < E; e += kWave) {
-      const double c = s_x[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int sel_e = 0;         // lane k < K: expert of selection k
+    double my_sig = 0.0;   // lane k < K: its sigma
+    if (E <= kWave) {
+      const double c = lane < E ? s_x[lane] : 0.0;
       int rank = 0;
-      int f = u;
-      for (; f + 7 * wpt < E; f += 8 * wpt) {  // eight broadcast reads in flight
+      int f = 0;
+      for (; f + 8 <= E; f += 8) {  // eight broadcast reads in flight
         double cf[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cf[j] = s_x[f + j * wpt];
+        for (int j = 0; j < 8; ++j) cf[j] = s_x[f + j];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) rank += (cf[j] > c || (cf[j] == c && f + j * wpt < e)) ? 1 : 0;
+        for (int j = 0; j < 8; ++j) rank += (cf[j] > c || (cf[j] == c && f + j < lane)) ? 1 : 0;
       }
-      for (; f < E; f += wpt) {
+      for (; f < E; ++f) {
         const double cf = s_x[f];
-        rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+        rank += (cf > c || (cf == c && f < lane)) ? 1 : 0;
       }
-      s_r[u * E + e] = rank;
-    }
-  }
-  __syncthreads();
-  // the experts of rank < K are the selection, in order
-  if (act && u == 0) {
-    for (int e = lane; e < E; e += kWave) {
-      int rank = 0;
-      for (int w = 0; w < wpt; ++w) rank += s_r[w * E + e];
-      if (rank < K) {
-        s_pidx[t * K + rank] = e;
-        s_sig[slot][rank] = s_sg[e];
+      if (lane >= E) rank = lane;
+      // each expert's index goes to the lane of its rank
+      sel_e = __builtin_amdgcn_ds_permute(rank * 4, lane);
+      my_sig = lane < K ? s_sg[sel_e] : 0.0;
+    } else {
+      const int per = (E + kWave - 1) / kWave;  // experts per lane (<= 16)
+      uint32_t taken = 0;
+      for (int k = 0; k < K; ++k) {
+        double bc = 0.0;
+        int be = kNoExpert;
+        for (int i = 0; i < per; ++i) {
+          const int e = lane + kWave * i;
+          if (e < E && !((taken >> i) & 1u)) {
+            const double c = s_x[e];
+            if (be == kNoExpert || c > bc) {  // ascending e: the first maximum stays
+              bc = c;
+              be = e;
+            }
+          }
+        }
+        best_step<0xB1>(bc, be);   // quad_perm [1,0,3,2]
+        best_step<0x4E>(bc, be);   // quad_perm [2,3,0,1]
+        best_step<0x141>(bc, be);  // row_half_mirror
+        best_step<0x140>(bc, be);  // row_mirror: every lane holds its row's best
+        double wc = readlane_f64(bc, 0);
+        int we = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+          const double rc = readlane_f64(bc, 16 * r);
+          const int re = __builtin_amdgcn_readlane(be, 16 * r);
+          if (beats(rc, re, wc, we)) {
+            wc = rc;
+            we = re;
+          }
+        }
+        if (lane == (we & (kWave - 1))) taken |= 1u << (we / kWave);
+        if (lane == k) sel_e = we;
       }
+      my_sig = lane < K ? s_sg[sel_e] : 0.0;
     }
-  }
-  __syncthreads();
-  if (act && u == 0) {
     int n;
-    const float wk = finish_weights(a, lane < K ? s_sig[slot][lane] : 0.0, n);
-    if (lane == 0) s_n[t] = n;
+    const float wk = finish_weights(a, my_sig, n);
+    if (lane == 0) sh.n[t] = n;
     RouteTok *rt = a.out->route + t;
     if (lane == 0) rt->n = n;
-    rt->idx[lane] = lane < K ? s_pidx[t * K + lane] : -1;
+    rt->idx[lane] = lane < K ? sel_e : -1;
     rt->w[lane] = wk;
-    if (lane < K) s_pw[t * K + lane] = wk;
+    if (lane < K) {
+      sh.pidx[t * K + lane] = sel_e;
+      sh.pw[t * K + lane] = wk;
+    }
   }
   __syncthreads();
 }
@@ -260,6 +304,7 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_rows = n;
       }
     } else {
+      // lane p < npairs holds pair p = (token t, selection k < n_t), token-major
       int my_t = -1, my_k = 0, base = 0;
       for (int t = 0; t < S; ++t) {
         const int nt = s_n[t];
@@ -272,37 +317,44 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
       const int npairs = base;  // <= S * K <= 64
       const int my_e = my_t >= 0 ? s_pidx[my_t * K + my_k] : -1;
       const float my_w = my_t >= 0 ? s_pw[my_t * K + my_k] : 0.f;
-
-      int ent_e = -1, n_ent = 0, my_entry = -1;
-      for (int p = 0; p < npairs; ++p) {
-        const int ep = __shfl(my_e, p, kWave);
-        const unsigned long long hit = __ballot(lane < n_ent && ent_e == ep);
-        int j;
-        if (hit) {
-          j = __ffsll((long long)hit) - 1;
-        } else {
-          j = n_ent;
-          if (lane == n_ent) ent_e = ep;
-          ++n_ent;
-        }
-        if (lane == p) my_entry = j;
+      // first appearance of each pair's expert (a token's selections are distinct, so the
+      // pairs of one expert are its tokens in ascending order)
+      int first = lane;
+      for (int q = 0; q < npairs; ++q) {
+        const int eq = __builtin_amdgcn_readlane(my_e, q);
+        if (q < first && eq == my_e) first = q;
       }
-      // rows per entry and the rank of each pair inside its entry
+      // entries: the first appearances in pair order
+      const unsigned long long fm = __ballot(lane < npairs && first == lane);
+      const int n_ent = __popcll(fm);
+      const int my_entry = __popcll(fm & ((1ull << first) - 1ull));
+      // rows per entry (lane j counts entry j) and each pair's rank inside its entry
       int cnt = 0, rank = 0;
-      for (int p = 0; p < npairs; ++p) {
-        const int jp = __shfl(my_entry, p, kWave);
-        cnt += (jp == lane) ? 1 : 0;
-        rank += (p < lane && jp == my_entry) ? 1 : 0;
+      for (int q = 0; q < npairs; ++q) {
+        const int jq = __builtin_amdgcn_readlane(my_entry, q);
+        cnt += (jq == lane) ? 1 : 0;
+        rank += (q < lane && jq == my_entry) ? 1 : 0;
       }
       int row0 = 0;
       for (int j = 0; j < n_ent; ++j) {
-        const int cj = __shfl(cnt, j, kWave);
+        const int cj = __builtin_amdgcn_readlane(cnt, j);
         row0 += (j < lane) ? cj : 0;
       }
-      const int my_row = __shfl(row0, my_entry < 0 ? 0 : my_entry, kWave) + rank;
+      const int my_row = __shfl(row0, lane < npairs ? my_entry : 0, kWave) + rank;
+      // expert of entry j: the pair at the j-th set bit of fm
+      int ent_src = 0;
+      {
+        unsigned long long m = fm;
+        for (int j = 0; j < n_ent; ++j) {
+          const int q = __ffsll((long long)m) - 1;
+          if (lane == j) ent_src = q;
+          m &= m - 1ull;
+        }
+      }
+      const int entry_expert = __shfl(my_e, ent_src, kWave);
 
       if (lane < n_ent) {
-        G->entry_expert[lane] = ent_e;
+        G->entry_expert[lane] = entry_expert;
         G->entry_row0[lane] = row0;
       }
       if (lane == n_ent) G->entry_row0[lane] = npairs;

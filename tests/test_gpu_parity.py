@@ -271,6 +271,35 @@ def test_router_exact_ties_take_lower_index():
     ctx.close()
 
 
+@pytest.mark.parametrize("S", [1, 3])
+def test_router_exact_ties_many_experts(S):
+    """E > 64 takes the K-rounds selection: exact ties between experts held by one lane
+    (3, 67, 131) and by different lanes (9, 200) still go to the lower index, for every token."""
+    import torch
+    print(f"[parity] exact ties E=230 S={S}", flush=True)
+    ctx = new_ctx()
+    E, D = 230, 256
+    rng = np.random.default_rng(11)
+    W = rng.normal(0, 0.05, (E, D)).astype(np.float32)
+    for e in (67, 131):
+        W[e] = W[3]
+    W[200] = W[9]
+    b = np.zeros(E, np.float32)
+    xs = rng.standard_normal((S, D)).astype(np.float32)
+    x = torch.from_numpy(xs).to("cuda:0")
+    ctx.upload_router(0, W, b)
+    K = 64 // S
+    rec = ctx.route(0, x, K, 0.0, False, 1.0, host_out=True)
+    routes = oracle.route(W, b, xs.astype(np.float64), K, 0.0, False, 1.0)
+    for t in range(S):
+        idx = list(rec[t].idx[:K])
+        assert idx == list(routes[t].idx), (t, idx, list(routes[t].idx))
+        for group in ((3, 67, 131), (9, 200)):
+            at = [idx.index(e) for e in group if e in idx]
+            assert at == sorted(at)
+    ctx.close()
+
+
 @pytest.mark.parametrize("name", ["small_batch", "sustained"])
 def test_full_size_sampled(name):
     """Full-size layers in the benchmark's launch configuration; the oracle checks sampled rows of
