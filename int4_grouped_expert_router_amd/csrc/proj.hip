@@ -773,21 +773,24 @@ size_t rows16_lds_bytes(int P) { return 4u * (size_t)P * kLR * 4 * 8; }
 // (route) order with the take's arithmetic, fmaf over the live rows, added to the residual.
 // No y rows go through memory and no take launch follows.  (Measured on the medium decode
 // layer: 8-column tiles double the h staging traffic and 32-column tiles leave half the CUs
-// idle; both are slower.)
-template <int P>
-__global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
+// idle; both are slower.)  W > 1 splits a row's outputs over W waves that share its staged h.
+template <int P, int W>
+__global__ __launch_bounds__(kDTRows * W * kWave) void k_down_take(ProjArgs a) {
   constexpr int V = 4;
   constexpr int TL = kDTTile;
-  static_assert(TL % (2 * kGR) == 0 && TL <= kWave, "whole pipeline passes, one output per lane");
+  constexpr int RW = TL / W;  // outputs per wave
+  static_assert(RW % (2 * kGR) == 0 && RW <= kWave, "whole pipeline passes, one output per lane");
   extern __shared__ uint32_t s_act[];  // [kDTRows][P * 512] staged h rows
   __shared__ float s_y[kDTRows][TL];
   __shared__ float s_w[kDTRows];
   __shared__ int s_live[kDTRows];
   const int lane = threadIdx.x & 63;
   const int li = lane & (kLR - 1), g = lane / kLR;
-  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // group row of this wave
-  const int i0 = blockIdx.x * TL;
-  const int i_end = min(i0 + TL, a.O);
+  const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = wi / W;          // group row of this wave
+  const int part = wi - r * W;   // its share of the tile's outputs and of the row's staging
+  const int i0 = blockIdx.x * TL + part * RW;
+  const int i_end = min(i0 + RW, a.O);
   const CGroupBuf G = (CGroupBuf)a.grp;
   const int rr = min(r, a.grid_rows - 1);
   const TensorDesc T = ld_desc(G->rows[rr].t[2]);
@@ -796,7 +799,7 @@ __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
   asm volatile("" ::"s"(T.q), "s"(T.s), "s"(T.O), "s"(T.C), "s"(T.row_bytes), "s"(T.gs), "s"(T.ng));
   asm volatile("" ::"s"(live));
   // the residual of the tile, in flight from the start
-  const float r_in = a.out[min(i0 + (lane % TL), a.O - 1)];
+  const float r_in = a.out[min(i0 + (lane % RW), a.O - 1)];
 
   const int C = a.C;
   const int RD = (C + 7) >> 3;
@@ -807,18 +810,18 @@ __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
     gi[p] = (T.ng > 1 && ds < RD) ? (8 * ds) / T.gs : 0;
     woff[p] = ds < RD ? 4 * ds : -1;
   }
-  const int rows_in = live ? i_end : 0;  // a dead row's loads read nothing
+  const int rows_in = live && i0 < a.O ? i_end : 0;  // a dead row's loads read nothing
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
   const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
 
-  // this row's h, loaded by its own wave, four columns per lane and load (clamped,
-  // unconditional; rows are 16-byte aligned and padded to a multiple of 64 columns)
-  constexpr int NX = P * 512 / (4 * kWave);
+  // the wave's share of its row's h, four columns per lane and load (clamped, unconditional;
+  // rows are 16-byte aligned and padded to a multiple of 64 columns)
+  constexpr int NX = P * 512 / (4 * kWave * W);
   const float *hrow = static_cast<const float *>(a.act) + (size_t)rr * a.act_ld;
   float4 xs[NX];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
-    const int c4 = 4 * (lane + i * kWave);
+    const int c4 = 4 * (lane + (i * W + part) * kWave);
     xs[i] = *reinterpret_cast<const float4 *>(hrow + (c4 < C ? c4 : 0));
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -830,16 +833,20 @@ __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
   uint32_t *lds = s_act + r * (P * 512);
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
-    const int c4 = 4 * (lane + i * kWave);
+    const int c4 = 4 * (lane + (i * W + part) * kWave);
     float4 x = xs[i];
     // C is even: a group of four is whole, half or empty
     if (c4 + 2 > C) x.x = x.y = 0.f;
     if (c4 + 4 > C) x.z = x.w = 0.f;
     stage16x4(lds, c4, x);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (W == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
   float xm[P];
   span_offsets16<P>(xm, lds, li);
 
@@ -852,26 +859,29 @@ __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
     load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
     o += 2 * kGR;
   } while (o < i_end);
-  if (lane < TL) s_y[r][lane] = outv;
-  if (lane == 0) {
+  if (lane < RW) s_y[r][part * RW + lane] = outv;
+  if (lane == 0 && part == 0) {
     s_w[r] = wr_row;
     s_live[r] = live;
   }
   __syncthreads();
-  if (r == 0 && lane < TL && i0 + lane < a.O) {
+  if (r == 0 && lane < RW && i0 + lane < a.O) {
     float acc = 0.f;
     for (int q = 0; q < a.grid_rows; ++q)
-      if (s_live[q]) acc = fmaf(s_w[q], s_y[q][lane], acc);
+      if (s_live[q]) acc = fmaf(s_w[q], s_y[q][part * RW + lane], acc);
     a.out[i0 + lane] = r_in + acc;
   }
 }
 
+// Waves per group row.  Measured on the medium decode layer: one wave of 16 outputs per row
+// 9.7 us, two waves of 8 outputs per row (16 waves per workgroup) 11.4 us.
+constexpr int kDTWaves = 1;
 const void *down_take_ptr(int P) {
   switch (P) {
-    case 1: return reinterpret_cast<const void *>(&k_down_take<1>);
-    case 2: return reinterpret_cast<const void *>(&k_down_take<2>);
-    case 3: return reinterpret_cast<const void *>(&k_down_take<3>);
-    case 4: return reinterpret_cast<const void *>(&k_down_take<4>);
+    case 1: return reinterpret_cast<const void *>(&k_down_take<1, kDTWaves>);
+    case 2: return reinterpret_cast<const void *>(&k_down_take<2, kDTWaves>);
+    case 3: return reinterpret_cast<const void *>(&k_down_take<3, kDTWaves>);
+    case 4: return reinterpret_cast<const void *>(&k_down_take<4, kDTWaves>);
     default: return nullptr;
   }
 }
@@ -974,7 +984,7 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
   }
   ProjArgs args = a;
   void *params[] = {&args};
-  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kWave);
+  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kDTWaves * kWave);
   hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, grid, block, params, lds, st, t0, t1, 0)
                             : hipLaunchKernel(k, grid, block, params, lds, st);
   return e != hipSuccess ? e : hipGetLastError();

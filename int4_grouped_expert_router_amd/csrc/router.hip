@@ -184,15 +184,18 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   __shared__ int s_row_e[kRows], s_row_t[kRows];
   __shared__ float s_row_w[kRows];
   __shared__ int s_rows;
-  __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];  // expert records, when E is small
+  __shared__ uint32_t s_tab[kSelTabE * kDescWords];  // expert records, when E <= 256
 
-  // With few experts, every expert's 128-byte record is loaded now, in the same batch as the
-  // scores, so the row descriptors need no further memory round trip at the end.
-  const bool tab_pre = a.table != nullptr && a.E <= kTabPrefetchE;
-  uint32_t tv[kTabPerThread];
-  if (tab_pre) table_prefetch(tv, a.table, a.E);
+  // With up to 256 experts, every expert's 128-byte record is loaded now, in the same batch as
+  // the scores, so the row descriptors need no further memory round trip at the end.
+  const bool tab_pre = a.table != nullptr && a.E <= kSelTabE;
+  uint32_t tv[kSelTabPerThread];
   SelShared sh{s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, tab_pre ? s_tab : nullptr};
-  for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S)) select_pass(a, s_dyn, t0, sh);
+  // behind each pass's first scores (the same records every pass, so the loads and the wait
+  // counts do not depend on the pass)
+  const int tab_bytes = tab_pre ? a.E * (int)sizeof(ExpertRec) : 0;
+  for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S))
+    select_pass(a, s_dyn, t0, sh, [&] { table_prefetch_rsrc(tv, a.table, tab_bytes); });
   if (tab_pre) table_stage(s_tab, tv);
   publish_group(a, sh);
 }
@@ -201,11 +204,12 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
 
 hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if (a.splits * a.epb > kGemvWaves || a.S * a.epb > a.splits * a.epb * kWave) return hipErrorInvalidValue;
+  // dynamic LDS up to 64 KB (E = 1024, four tokens per pass) beside 34 KB of static arrays
   const size_t lds = select_lds_bytes(a.E, a.S);
   static bool lds_raised = false;
-  if ((parts & kRouteSelect) && lds > 64 * 1024 && !lds_raised) {
+  if ((parts & kRouteSelect) && !lds_raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_route_select),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)select_lds_bytes(kMaxE, kTokens));
     if (e != hipSuccess) return e;
     lds_raised = true;
   }

@@ -13,8 +13,10 @@ constexpr int kTabWords = 3 * sizeof(TensorDesc) / 4;          // tensor words o
 constexpr int kLiveWord = offsetof(TensorDesc, live) / 4;     // t[0].live inside a row descriptor
 constexpr int kDescWords = sizeof(RowDesc) / 4;               // 32
 constexpr int kDescPerThread = kRows * kDescWords / kBlock;   // 8
-constexpr int kTabPrefetchE = 64;                             // experts whose records are staged early
+constexpr int kTabPrefetchE = 64;                             // fused selection: records staged early
 constexpr int kTabPerThread = kTabPrefetchE * kDescWords / kBlock;
+constexpr int kSelTabE = 256;                                 // select kernel: records staged early
+constexpr int kSelTabPerThread = kSelTabE * kDescWords / kBlock;
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint64_t u = __double_as_longlong(v);
@@ -36,18 +38,29 @@ struct SelShared {
   int *row_e, *row_t;    // per group row: expert, token
   float *row_w;          // per group row: weight
   int *rows;             // group rows
-  const uint32_t *tab;   // staged expert records [E][32] (E <= kTabPrefetchE), or null
+  const uint32_t *tab;   // staged expert records [E][32], or null
 };
 
-// Expert records loaded early, in the same batch as the scores (E <= kTabPrefetchE).
-__device__ __forceinline__ void table_prefetch(uint32_t (&tv)[kTabPerThread], const ExpertRec *table, int E) {
+// Expert records loaded early, in the same batch as the scores (E <= N * kBlock / 32).
+template <int N>
+__device__ __forceinline__ void table_prefetch(uint32_t (&tv)[N], const ExpertRec *table, int E) {
   const uint32_t *tsrc = reinterpret_cast<const uint32_t *>(table);
 #pragma unroll
-  for (int j = 0; j < kTabPerThread; ++j) tv[j] = tsrc[min((int)threadIdx.x + j * kBlock, E * kDescWords - 1)];
+  for (int j = 0; j < N; ++j) tv[j] = tsrc[min((int)threadIdx.x + j * kBlock, E * kDescWords - 1)];
 }
-__device__ __forceinline__ void table_stage(uint32_t *s_tab, const uint32_t (&tv)[kTabPerThread]) {
+// The same through a buffer range of `bytes` (0: the loads read nothing and return zeros), so
+// the load pattern does not depend on whether the table is wanted.
+template <int N>
+__device__ __forceinline__ void table_prefetch_rsrc(uint32_t (&tv)[N], const ExpertRec *table, int bytes) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<ExpertRec *>(table), (short)0, bytes,
+                                                                     0x00020000);
 #pragma unroll
-  for (int j = 0; j < kTabPerThread; ++j) s_tab[threadIdx.x + j * kBlock] = tv[j];
+  for (int j = 0; j < N; ++j) tv[j] = __builtin_amdgcn_raw_buffer_load_b32(r, 4 * ((int)threadIdx.x + j * kBlock), 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void table_stage(uint32_t *s_tab, const uint32_t (&tv)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) s_tab[threadIdx.x + j * kBlock] = tv[j];
 }
 
 // Top-p, norm and scale of one token's selection.  Lane k < K holds sigma of selection k;
@@ -112,7 +125,9 @@ __device__ __forceinline__ void best_step(double &c, int &e) {
 //            64 i; a lane's best, then the wave's over DPP steps and the four rows), which is
 //            the strict ascending scan itself.
 // Both give the experts of rank 0 .. K-1 in the order (score desc, index asc).
-static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh) {
+template <class F>
+__device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh,
+                                            F &&after_loads) {
   const int lane = threadIdx.x & 63;
   const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int E = a.E, K = a.K, S = a.S;
@@ -120,13 +135,19 @@ static __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s
   double *s_sg = s_x + E;                       // sigma
   const int t = t0 + slot;
   const bool act = slot < select_slots(S) && t < S;
-  if (act) {
-    // the token's scores: clamped, unconditional loads, four in flight per lane
-    const double2 *src = a.score + (size_t)t * E;
-    for (int e0 = 0; e0 < E; e0 += 4 * kWave) {
-      double2 v[4];
+  // the token's scores: clamped, unconditional loads, four in flight per lane; the first
+  // batch is issued before `after_loads` (which may issue loads of its own for later use)
+  const double2 *src = a.score + (size_t)min(t, S - 1) * E;
+  double2 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = src[min(e0 + j * kWave + lane, E - 1)];
+  for (int j = 0; j < 4; ++j) v[j] = src[min(j * kWave + lane, E - 1)];
+  after_loads();
+  if (act) {
+    for (int e0 = 0; e0 < E; e0 += 4 * kWave) {
+      if (e0 > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = src[min(e0 + j * kWave + lane, E - 1)];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + j * kWave + lane;

@@ -300,6 +300,31 @@ def test_router_exact_ties_many_experts(S):
     ctx.close()
 
 
+@pytest.mark.parametrize("S,K", [(1, 8), (4, 16), (16, 4), (64, 1)])
+def test_router_max_experts(S, K):
+    """The 1024-expert cap: 16 experts per lane in the K-rounds selection and the largest
+    score staging (four tokens of 1024 experts per pass)."""
+    print(f"[parity] router E=1024 S={S} K={K}", flush=True)
+    ctx = new_ctx()
+    E, D = 1024, 512
+    rng = np.random.default_rng(31 + S)
+    W = rng.normal(0, 0.05, (E, D)).astype(np.float32)
+    b = rng.normal(0, 0.1, E).astype(np.float32)
+    xs = rng.standard_normal((S, D)).astype(np.float32)
+    x = x_to_device(xs, "f32")
+    ctx.upload_router(0, W, b)
+    rec = ctx.route(0, x, K, 0.9, True, 2.5, host_out=True)
+    routes = oracle.route(W, b, xs.astype(np.float64), K, 0.9, True, 2.5)
+    checked = 0
+    for t in range(S):
+        if near_tie(routes[t], K, 0.9):
+            continue
+        assert route_matches(rec[t], routes[t], K), t
+        checked += 1
+    assert checked >= S // 2
+    ctx.close()
+
+
 @pytest.mark.parametrize("name", ["small_batch", "sustained"])
 def test_full_size_sampled(name):
     """Full-size layers in the benchmark's launch configuration; the oracle checks sampled rows of
