@@ -378,7 +378,7 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         G->entry_expert[lane] = entry_expert;
         G->entry_row0[lane] = row0;
       }
-      if (lane == n_ent) G->entry_row0[lane] = npairs;
+      if (lane == 0) G->entry_row0[n_ent] = npairs;  // n_ent may be 64
       if (lane < npairs) {
         G->row_token[my_row] = my_t;
         G->row_expert[my_row] = my_e;
@@ -390,8 +390,9 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
       }
       int tb = 0;
       for (int t = 0; t < S; ++t) tb += (t < lane) ? s_n[t] : 0;
-      if (lane <= S) G->tok_row0[lane] = tb;
+      if (lane < S) G->tok_row0[lane] = tb;
       if (lane == 0) {
+        G->tok_row0[S] = npairs;  // S may be 64
         G->n_entries = n_ent;
         G->n_rows = npairs;
         G->S = S;

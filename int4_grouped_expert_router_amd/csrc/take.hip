@@ -72,8 +72,10 @@ __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
     const GroupDev &g = a.groups[s]->g;
     const int rr = g.red_rows[k];
     const float rw = g.row_weight[k];
-    const int r0 = g.tok_row0[t], r1 = g.tok_row0[t + 1];
-    s_rr[s][k] = rr;
+    // clamped into the record's arrays: every index below stays inside them whatever the
+    // record holds
+    const int r0 = min(max(g.tok_row0[t], 0), kRows), r1 = min(max(g.tok_row0[t + 1], r0), kRows);
+    s_rr[s][k] = min(max(rr, 0), kRows - 1);
     s_rw[s][k] = rw;
     s_r0[s] = r0;  // every lane stores the same value
     s_cnt[s] = r1 - r0;

@@ -42,6 +42,9 @@ def check_group(ctx, layer, routes):
     for t, rows in enumerate(og["token_rows"]):
         lo, hi = g["tok_row0"][t], g["tok_row0"][t + 1]
         assert g["red_rows"][lo:hi].tolist() == rows
+    # the ends of both offset arrays, also when they sit at index 64
+    assert g["entry_row0"][g["n_entries"]] == g["n_rows"]
+    assert g["tok_row0"][len(og["token_rows"])] == g["n_rows"]
     return og
 
 
@@ -98,6 +101,8 @@ RAGGED = [
     (512, 96, 6, 3, 2, "group", 256, "bf16"),
     (256, 128, 8, 8, 8, "mix_even_odd", 2, "f32"),
     (130, 34, 5, 5, 1, "mix_even_odd", 32, "bf16"),
+    (256, 128, 64, 1, 64, "row", 0, "f32"),         # 64 tokens: the group's offsets end at 64
+    (512, 256, 128, 2, 32, "group", 64, "bf16"),    # up to 64 distinct experts in one group
 ]
 
 
