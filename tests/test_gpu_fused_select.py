@@ -248,3 +248,28 @@ def test_down_take_fused_matches_separate(name):
     delta, _ = oracle.experts.layer_delta(routes, L.expert, x64)
     assert normwise_err(outs[1] - L.residual, delta) < TOL
     ctx.close()
+
+
+def test_same_route_issued_twice():
+    """Two issues of one deferred route: the first runs the selection inside its dual
+    projection and leaves its down projection waiting; the second issue runs that down
+    projection first and then reads the group the first one published. The take then adds
+    two identical slots: exactly twice one slot's sum."""
+    import torch
+    print("[fused] one route, two issues", flush=True)
+    cfg = get_config("medium")
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    outs = []
+    for issues in (1, 2):
+        ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+        for _ in range(issues):
+            ctx.issue(0, x)
+        r = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+        ctx.take(r)
+        torch.cuda.synchronize()
+        outs.append(r.cpu().numpy())
+    assert outs[1].tobytes() == (2 * outs[0]).astype(np.float32).tobytes()
+    ctx.close()
