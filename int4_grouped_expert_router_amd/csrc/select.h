@@ -280,7 +280,8 @@ __device__ __forceinline__ SelOne select_one(const RouteArgs &a, double2 cs, dou
 
 // Group record and row descriptors of the finished selection (all threads of the workgroup;
 // holds workgroup barriers).
-static __device__ __forceinline__ void publish_group(const RouteArgs &a, const SelShared &sh) {
+// `scratch` holds at least E ints (the selection's score staging, free by now).
+static __device__ __forceinline__ void publish_group(const RouteArgs &a, const SelShared &sh, int *scratch) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -338,41 +339,47 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
       const int npairs = base;  // <= S * K <= 64
       const int my_e = my_t >= 0 ? s_pidx[my_t * K + my_k] : -1;
       const float my_w = my_t >= 0 ? s_pw[my_t * K + my_k] : 0.f;
-      // first appearance of each pair's expert (a token's selections are distinct, so the
-      // pairs of one expert are its tokens in ascending order)
-      int first = lane;
-      for (int q = 0; q < npairs; ++q) {
-        const int eq = __builtin_amdgcn_readlane(my_e, q);
-        if (q < first && eq == my_e) first = q;
-      }
+      // first appearance of each pair's expert: the lowest pair index of that expert, by an
+      // LDS minimum per expert (a token's selections are distinct, so the pairs of one expert
+      // are its tokens in ascending order)
+      const bool pl = lane < npairs;
+      if (pl) scratch[my_e] = kRows;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (pl) atomicMin(&scratch[my_e], lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int first = pl ? scratch[my_e] : lane;
       // entries: the first appearances in pair order
-      const unsigned long long fm = __ballot(lane < npairs && first == lane);
+      const unsigned long long fm = __ballot(pl && first == lane);
       const int n_ent = __popcll(fm);
       const int my_entry = __popcll(fm & ((1ull << first) - 1ull));
-      // rows per entry (lane j counts entry j) and each pair's rank inside its entry
-      int cnt = 0, rank = 0;
-      for (int q = 0; q < npairs; ++q) {
-        const int jq = __builtin_amdgcn_readlane(my_entry, q);
-        cnt += (jq == lane) ? 1 : 0;
-        rank += (q < lane && jq == my_entry) ? 1 : 0;
-      }
-      int row0 = 0;
+      // per entry j: its pairs (a ballot), their count, the entry's first row, and each pair's
+      // rank inside it
+      int cnt = 0, row0 = 0, rank = 0, run = 0;
       for (int j = 0; j < n_ent; ++j) {
-        const int cj = __builtin_amdgcn_readlane(cnt, j);
-        row0 += (j < lane) ? cj : 0;
-      }
-      const int my_row = __shfl(row0, lane < npairs ? my_entry : 0, kWave) + rank;
-      // expert of entry j: the pair at the j-th set bit of fm
-      int ent_src = 0;
-      {
-        unsigned long long m = fm;
-        for (int j = 0; j < n_ent; ++j) {
-          const int q = __ffsll((long long)m) - 1;
-          if (lane == j) ent_src = q;
-          m &= m - 1ull;
+        const unsigned long long mj = __ballot(pl && my_entry == j);
+        const int cj = __popcll(mj);
+        if (pl && my_entry == j) rank = __popcll(mj & ((1ull << lane) - 1ull));
+        if (lane == j) {
+          cnt = cj;
+          row0 = run;
         }
+        run += cj;
       }
-      const int entry_expert = __shfl(my_e, ent_src, kWave);
+      (void)cnt;
+      const int my_row = __shfl(row0, pl ? my_entry : 0, kWave) + rank;
+      // expert of entry j: its first pair's expert, through LDS
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (pl && first == lane) scratch[my_entry] = my_e;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int entry_expert = lane < n_ent ? scratch[lane] : 0;
 
       if (lane < n_ent) {
         G->entry_expert[lane] = entry_expert;
