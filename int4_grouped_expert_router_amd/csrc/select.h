@@ -356,20 +356,15 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
       const unsigned long long fm = __ballot(pl && first == lane);
       const int n_ent = __popcll(fm);
       const int my_entry = __popcll(fm & ((1ull << first) - 1ull));
-      // per entry j: its pairs (a ballot), their count, the entry's first row, and each pair's
-      // rank inside it
-      int cnt = 0, row0 = 0, rank = 0, run = 0;
+      // per entry j: its pairs (a ballot), the entry's first row (the pairs of the entries
+      // before it), and each pair's rank inside it
+      int row0 = 0, rank = 0, run = 0;
       for (int j = 0; j < n_ent; ++j) {
         const unsigned long long mj = __ballot(pl && my_entry == j);
-        const int cj = __popcll(mj);
         if (pl && my_entry == j) rank = __popcll(mj & ((1ull << lane) - 1ull));
-        if (lane == j) {
-          cnt = cj;
-          row0 = run;
-        }
-        run += cj;
+        if (lane == j) row0 = run;
+        run += __popcll(mj);
       }
-      (void)cnt;
       const int my_row = __shfl(row0, pl ? my_entry : 0, kWave) + rank;
       // expert of entry j: its first pair's expert, through LDS
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
