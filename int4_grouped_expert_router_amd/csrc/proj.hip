@@ -24,6 +24,14 @@
 // scale (the row scale, or the span's group scale when gs is a multiple of 8V), then the
 // lane partials are summed across the wave with DPP in a fixed pattern (deterministic).
 // Group sizes that split a span fall back to a per-byte path.
+//
+// Kernels here:
+//   k_proj<V, P, NT, GEN, XB, SEL>  the dual (NT = 2) and long-row down (NT = 1) projections;
+//                                   SEL runs a one-token expert selection first (select.h)
+//   k_rows16<P>                     down projection of short rows, 16 lanes per row
+//   k_down_take<P, W>               down projection of short rows fused with the take (one
+//                                   token, one issue): the weighted, fixed-order sum of the
+//                                   rows is added to the residual in the same launch
 #include <hip/hip_ext.h>
 
 #include "select.h"
