@@ -436,10 +436,13 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
     __shared__ double s_cw[kWavesPerBlock][kWave];
     __shared__ int s_cnt[kWavesPerBlock][kWave];
     __shared__ uint32_t s_tab[kTabPrefetchE * kDescWords];
-    // one batch of loads: this lane's expert score, the expert records (E <= 64)
+    // one batch of loads: this lane's expert score, and in the first workgroup of each row
+    // (which writes the row's descriptor) the expert records (E <= 64); the other workgroups
+    // issue the same loads over an empty range, so nothing is read
+    const bool writer = blockIdx.x == jr * a.tile_groups;
     const double2 cs = ra.score[min(lane, ra.E - 1)];
     uint32_t tv[kTabPerThread];
-    table_prefetch(tv, ra.table, ra.E);
+    table_prefetch_rsrc(tv, ra.table, writer ? ra.E * (int)sizeof(ExpertRec) : 0);
     const SelOne r = select_one(ra, cs, s_cw, s_cnt, [&] { table_stage(s_tab, tv); });
     // this row is selection jr of the one token
     live = jr < r.n ? 1 : 0;
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
         G->reserved = 0;
       }
     }
-    if (blockIdx.x == jr * a.tile_groups && wib == 0 && lane < kDescWords) {
+    if (writer && wib == 0 && lane < kDescWords) {
       // this row's descriptor for the down projection and the take (zeros for a dead row)
       uint32_t val = 0u;
       if (live) {
@@ -488,19 +491,12 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
       }
       reinterpret_cast<uint32_t *>(out->rows + jr)[lane] = val;
     }
+    // the row's gate and up records: scalar loads of the (L2-resident) layer table
+    typedef const ExpertRec I4MOE_AS4 *CExpertRec;
+    const CExpertRec rec = (CExpertRec)ra.table + e;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const uint32_t *wd = s_tab + e * kDescWords + n * (kTabWords / 3);
-      uint32_t v[kTabWords / 3];
-#pragma unroll
-      for (int d = 0; d < kTabWords / 3; ++d) v[d] = __builtin_amdgcn_readfirstlane(wd[d]);
-      T[n].q = reinterpret_cast<const uint8_t *>(((uint64_t)v[1] << 32) | v[0]);
-      T[n].s = reinterpret_cast<const float *>(((uint64_t)v[3] << 32) | v[2]);
-      T[n].O = (int)v[4];
-      T[n].C = (int)v[5];
-      T[n].row_bytes = (int)v[6];
-      T[n].gs = (int)v[7];
-      T[n].ng = (int)v[8];
+      T[n] = ld_desc(rec->t[n]);
       T[n].live = live;
     }
     if (!live) return;
