@@ -273,3 +273,28 @@ def test_same_route_issued_twice():
         outs.append(r.cpu().numpy())
     assert outs[1].tobytes() == (2 * outs[0]).astype(np.float32).tobytes()
     ctx.close()
+
+
+def test_tensor_free_runs_the_waiting_down_projection_first():
+    """Freeing a tensor while a down projection waits for the take: the library runs that
+    down projection (and waits for it) before it frees anything, so the take still adds the
+    same bits."""
+    import torch
+    print("[fused] free while the down projection waits", flush=True)
+    cfg = get_config("tiny", K=2, seed=3)
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    handles = upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    rec = ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    ctx.issue(0, x)
+    ref = torch.from_numpy(L.residual.copy()).to("cuda:0")
+    ctx.take(ref)
+    ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.issue(0, x)
+    ctx.free_tensor(handles[int(rec[0].idx[0])][2])  # the first selected expert's down tensor
+    r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+    ctx.take(r)
+    torch.cuda.synchronize()
+    assert r.cpu().numpy().tobytes() == ref.cpu().numpy().tobytes()
+    ctx.close()
