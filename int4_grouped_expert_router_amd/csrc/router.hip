@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   for (int t0 = 0; t0 < a.S; t0 += select_slots(a.S))
     select_pass(a, s_dyn, t0, sh, [&] { table_prefetch_rsrc(tv, a.table, tab_bytes); });
   if (tab_pre) table_stage(s_tab, tv);
-  publish_group(a, sh, reinterpret_cast<int *>(s_dyn));
+  publish_group(a, sh);
 }
 
 }  // namespace

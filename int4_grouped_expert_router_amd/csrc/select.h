@@ -101,29 +101,73 @@ __device__ __forceinline__ double dpp_f64s(double v) {
   return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-// (c, e) beats (c2, e2) in the selection order: larger score, then lower index; e = kNoExpert
-// marks "no candidate" and beats nothing.
-constexpr int kNoExpert = 0x7fffffff;
-__device__ __forceinline__ bool beats(double c, int e, double c2, int e2) {
-  return e != kNoExpert && (e2 == kNoExpert || c > c2 || (c == c2 && e < e2));
-}
-template <int CTRL>
-__device__ __forceinline__ void best_step(double &c, int &e) {
-  const double c2 = dpp_f64s<CTRL, 0xF>(c);
-  const int e2 = dpp_i32<CTRL, 0xF>(e);
-  if (beats(c2, e2, c, e)) {
-    c = c2;
-    e = e2;
+// The larger of two scores (scores are never NaN: the GEMV maps a NaN score to -inf).
+__device__ __forceinline__ double max_score(double x, double y) { return y > x ? y : x; }
+
+// K rounds of the selection for E > 64 (lane e & 63 holds expert e in column e / 64, PER
+// columns).  A round takes the largest score among the experts not yet taken (the lane's
+// maximum, DPP steps inside rows of 16 lanes, then the four rows) and then the lowest index
+// holding it (one ballot per column, lowest column first): the first maximum of an ascending
+// scan.  A taken expert's score becomes -inf, and its bit in `taken` keeps it out of the
+// ballots should the remaining scores be -inf too.  Lane k < K returns selection k.
+template <int PER>
+__device__ __forceinline__ int select_rounds(const double *s_x, int E, int K, int lane) {
+  double cv[PER];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    const double x = s_x[min(e, E - 1)];
+    cv[i] = e < E ? x : -__builtin_inf();
+    if (e >= E) taken |= 1u << i;
   }
+  int sel_e = 0;
+  for (int k = 0; k < K; ++k) {
+    double m = cv[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) m = max_score(m, cv[i]);
+    m = max_score(m, dpp_f64s<0xB1, 0xF>(m));   // quad_perm [1,0,3,2]
+    m = max_score(m, dpp_f64s<0x4E, 0xF>(m));   // quad_perm [2,3,0,1]
+    m = max_score(m, dpp_f64s<0x141, 0xF>(m));  // row_half_mirror
+    m = max_score(m, dpp_f64s<0x140, 0xF>(m));  // row_mirror: every lane holds its row's maximum
+    const double M = max_score(max_score(readlane_f64(m, 0), readlane_f64(m, 16)),
+                               max_score(readlane_f64(m, 32), readlane_f64(m, 48)));
+    // M is one of the untaken scores, so some column holds it
+    int we = 0;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      const unsigned long long hit = __ballot(!((taken >> i) & 1u) && cv[i] == M);
+      if (hit) we = kWave * i + __ffsll((long long)hit) - 1;
+    }
+    const int wc = we / kWave;
+    const bool mine = lane == (we & (kWave - 1));
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i == wc && mine) cv[i] = -__builtin_inf();
+    if (mine) taken |= 1u << wc;
+    if (lane == k) sel_e = we;
+  }
+  return sel_e;
+}
+
+// Inclusive prefix sum over the 64 lanes (Kogge-Stone steps inside rows of 16 lanes, then
+// the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += dpp_i32<0x111, 0xF>(v);  // row_shr:1 (lanes without a source add 0)
+  v += dpp_i32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_i32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_i32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_i32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 // One pass of the select kernel: tokens t0 .. t0 + slots - 1, wave w on token t0 + w.  All
 // threads of the workgroup call it (it holds workgroup barriers); it writes the route records.
 //   E <= 64: lane e counts the experts that beat expert e (its rank); ranks below K are the
 //            selection positions.
-//   E > 64:  K rounds; each takes the best expert not yet taken (lanes hold experts e = lane +
-//            64 i; a lane's best, then the wave's over DPP steps and the four rows), which is
-//            the strict ascending scan itself.
+//   E > 64:  K rounds; each takes the largest score not yet taken and, among experts holding
+//            it, the lowest index, which is the strict ascending scan itself.
 // Both give the experts of rank 0 .. K-1 in the order (score desc, index asc).
 template <class F>
 __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, int t0, const SelShared &sh,
@@ -182,39 +226,11 @@ __device__ __forceinline__ void select_pass(const RouteArgs &a, double *s_dyn, i
       sel_e = __builtin_amdgcn_ds_permute(rank * 4, lane);
       my_sig = lane < K ? s_sg[sel_e] : 0.0;
     } else {
-      const int per = (E + kWave - 1) / kWave;  // experts per lane (<= 16)
-      uint32_t taken = 0;
-      for (int k = 0; k < K; ++k) {
-        double bc = 0.0;
-        int be = kNoExpert;
-        for (int i = 0; i < per; ++i) {
-          const int e = lane + kWave * i;
-          if (e < E && !((taken >> i) & 1u)) {
-            const double c = s_x[e];
-            if (be == kNoExpert || c > bc) {  // ascending e: the first maximum stays
-              bc = c;
-              be = e;
-            }
-          }
-        }
-        best_step<0xB1>(bc, be);   // quad_perm [1,0,3,2]
-        best_step<0x4E>(bc, be);   // quad_perm [2,3,0,1]
-        best_step<0x141>(bc, be);  // row_half_mirror
-        best_step<0x140>(bc, be);  // row_mirror: every lane holds its row's best
-        double wc = readlane_f64(bc, 0);
-        int we = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-        for (int r = 1; r < 4; ++r) {
-          const double rc = readlane_f64(bc, 16 * r);
-          const int re = __builtin_amdgcn_readlane(be, 16 * r);
-          if (beats(rc, re, wc, we)) {
-            wc = rc;
-            we = re;
-          }
-        }
-        if (lane == (we & (kWave - 1))) taken |= 1u << (we / kWave);
-        if (lane == k) sel_e = we;
-      }
+      const int per = (E + kWave - 1) / kWave;
+      sel_e = per <= 2 ? select_rounds<2>(s_x, E, K, lane)
+            : per <= 4 ? select_rounds<4>(s_x, E, K, lane)
+            : per <= 8 ? select_rounds<8>(s_x, E, K, lane)
+                       : select_rounds<16>(s_x, E, K, lane);
       my_sig = lane < K ? s_sg[sel_e] : 0.0;
     }
     int n;
@@ -280,8 +296,7 @@ __device__ __forceinline__ SelOne select_one(const RouteArgs &a, double2 cs, dou
 
 // Group record and row descriptors of the finished selection (all threads of the workgroup;
 // holds workgroup barriers).
-// `scratch` holds at least E ints (the selection's score staging, free by now).
-static __device__ __forceinline__ void publish_group(const RouteArgs &a, const SelShared &sh, int *scratch) {
+static __device__ __forceinline__ void publish_group(const RouteArgs &a, const SelShared &sh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -339,49 +354,35 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
       const int npairs = base;  // <= S * K <= 64
       const int my_e = my_t >= 0 ? s_pidx[my_t * K + my_k] : -1;
       const float my_w = my_t >= 0 ? s_pw[my_t * K + my_k] : 0.f;
-      // first appearance of each pair's expert: the lowest pair index of that expert, by an
-      // LDS minimum per expert (a token's selections are distinct, so the pairs of one expert
-      // are its tokens in ascending order)
       const bool pl = lane < npairs;
-      if (pl) scratch[my_e] = kRows;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (pl) atomicMin(&scratch[my_e], lane);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int first = pl ? scratch[my_e] : lane;
-      // entries: the first appearances in pair order
-      const unsigned long long fm = __ballot(pl && first == lane);
+      // the pairs of my expert, one ballot per index bit (a token's selections are distinct,
+      // so the pairs of one expert are its tokens in ascending order)
+      const int ebits = 32 - __clz(a.E > 1 ? a.E - 1 : 1);
+      unsigned long long same = __ballot(pl);
+      for (int b = 0; b < ebits; ++b) {
+        const bool bit = (my_e >> b) & 1;
+        const unsigned long long m = __ballot(pl && bit);
+        same &= bit ? m : ~m;
+      }
+      // entries are the experts in first-appearance order: the head pair of an entry is its
+      // expert's lowest pair, and the entry's rows are its pairs in pair order
+      const int first = pl ? __ffsll((long long)same) - 1 : 0;
+      const bool head = pl && first == lane;
+      const int cnt = head ? __popcll(same) : 0;
+      const unsigned long long fm = __ballot(head);
       const int n_ent = __popcll(fm);
       const int my_entry = __popcll(fm & ((1ull << first) - 1ull));
-      // per entry j: its pairs (a ballot), the entry's first row (the pairs of the entries
-      // before it), and each pair's rank inside it
-      int row0 = 0, rank = 0, run = 0;
-      for (int j = 0; j < n_ent; ++j) {
-        const unsigned long long mj = __ballot(pl && my_entry == j);
-        if (pl && my_entry == j) rank = __popcll(mj & ((1ull << lane) - 1ull));
-        if (lane == j) row0 = run;
-        run += __popcll(mj);
-      }
-      const int my_row = __shfl(row0, pl ? my_entry : 0, kWave) + rank;
-      // expert of entry j: its first pair's expert, through LDS
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (pl && first == lane) scratch[my_entry] = my_e;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int entry_expert = lane < n_ent ? scratch[lane] : 0;
+      // an entry's first row: the pairs of the entries whose heads come before it
+      const int row0 = wave_scan_incl(cnt) - cnt;
+      const int rank = __popcll(same & ((1ull << lane) - 1ull));
+      const int my_row = __shfl(row0, first, kWave) + rank;
 
-      if (lane < n_ent) {
-        G->entry_expert[lane] = entry_expert;
-        G->entry_row0[lane] = row0;
+      if (head) {
+        G->entry_expert[my_entry] = my_e;
+        G->entry_row0[my_entry] = row0;
       }
       if (lane == 0) G->entry_row0[n_ent] = npairs;  // n_ent may be 64
-      if (lane < npairs) {
+      if (pl && my_row < kRows) {  // always: the rows are a permutation of the pairs
         G->row_token[my_row] = my_t;
         G->row_expert[my_row] = my_e;
         G->row_weight[my_row] = my_w;
