@@ -276,20 +276,24 @@ def test_router_exact_ties_take_lower_index():
     ctx.close()
 
 
-@pytest.mark.parametrize("S", [1, 3])
-def test_router_exact_ties_many_experts(S):
-    """E > 64 takes the K-rounds selection: exact ties between experts held by one lane
-    (3, 67, 131) and by different lanes (9, 200) still go to the lower index, for every token."""
+@pytest.mark.parametrize("E,S", [(230, 1), (230, 3), (130, 2), (300, 2), (512, 4), (1000, 1)])
+def test_router_exact_ties_many_experts(E, S):
+    """E > 64 takes the K-rounds selection (2, 4, 8 or 16 experts per lane): exact ties between
+    experts held by one lane in different columns (3, 67, 131, 259, 451, 963) and by different
+    lanes (9, 200, 457, 999) still go to the lower index, for every token.  A bias lifts both
+    groups to the top of the order so the ties are decided inside the selection."""
     import torch
-    print(f"[parity] exact ties E=230 S={S}", flush=True)
+    print(f"[parity] exact ties E={E} S={S}", flush=True)
     ctx = new_ctx()
-    E, D = 230, 256
-    rng = np.random.default_rng(11)
+    D = 256
+    rng = np.random.default_rng(11 + E)
     W = rng.normal(0, 0.05, (E, D)).astype(np.float32)
-    for e in (67, 131):
-        W[e] = W[3]
-    W[200] = W[9]
     b = np.zeros(E, np.float32)
+    groups = [[e for e in (3, 67, 131, 259, 451, 963) if e < E], [e for e in (9, 200, 457, 999) if e < E]]
+    for lift, group in zip((1.0, 0.5), groups):
+        for e in group:
+            W[e] = W[group[0]]
+            b[e] = lift
     xs = rng.standard_normal((S, D)).astype(np.float32)
     x = torch.from_numpy(xs).to("cuda:0")
     ctx.upload_router(0, W, b)
@@ -299,9 +303,9 @@ def test_router_exact_ties_many_experts(S):
     for t in range(S):
         idx = list(rec[t].idx[:K])
         assert idx == list(routes[t].idx), (t, idx, list(routes[t].idx))
-        for group in ((3, 67, 131), (9, 200)):
+        for group in groups:
             at = [idx.index(e) for e in group if e in idx]
-            assert at == sorted(at)
+            assert len(at) == min(len(group), K) and at == sorted(at)
     ctx.close()
 
 
