@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   __shared__ int s_row_e[kRows], s_row_t[kRows];
   __shared__ float s_row_w[kRows];
   __shared__ int s_rows;
-  __shared__ uint32_t s_tab[kSelTabE * kDescWords];  // expert records, when E <= 256
+  __shared__ __attribute__((aligned(16))) uint32_t s_tab[kSelTabE * kDescWords];  // expert records, E <= 256
 
   // With up to 256 experts, every expert's 128-byte record is loaded now, in the same batch as
   // the scores, so the row descriptors need no further memory round trip at the end.

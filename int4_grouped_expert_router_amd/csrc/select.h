@@ -12,7 +12,6 @@ constexpr int kWavesPerBlock = kBlock / kWave;                 // 4
 constexpr int kTabWords = 3 * sizeof(TensorDesc) / 4;          // tensor words of a row descriptor
 constexpr int kLiveWord = offsetof(TensorDesc, live) / 4;     // t[0].live inside a row descriptor
 constexpr int kDescWords = sizeof(RowDesc) / 4;               // 32
-constexpr int kDescPerThread = kRows * kDescWords / kBlock;   // 8
 constexpr int kTabPrefetchE = 64;                             // fused selection: records staged early
 constexpr int kTabPerThread = kTabPrefetchE * kDescWords / kBlock;
 constexpr int kSelTabE = 256;                                 // select kernel: records staged early
@@ -341,17 +340,23 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_rows = n;
       }
     } else {
-      // lane p < npairs holds pair p = (token t, selection k < n_t), token-major
-      int my_t = -1, my_k = 0, base = 0;
+      // lane p < npairs holds pair p = (token t, selection k < n_t), token-major.  Token t's
+      // first pair is the prefix sum of the kept counts before it (every count is at least 1,
+      // so the first pairs rise strictly and a pair's token is the last one starting at or
+      // before it).
+      const int nl = lane < S ? s_n[lane] : 0;
+      const int tok_end = wave_scan_incl(nl);
+      const int tok0 = tok_end - nl;
+      const int npairs = __builtin_amdgcn_readlane(tok_end, S - 1);  // <= S * K <= 64
+      int my_t = -1, my_k = 0;
       for (int t = 0; t < S; ++t) {
-        const int nt = s_n[t];
-        if (lane >= base && lane < base + nt) {
+        const int b = __builtin_amdgcn_readlane(tok0, t);
+        if (lane >= b) {
           my_t = t;
-          my_k = lane - base;
+          my_k = lane - b;
         }
-        base += nt;
       }
-      const int npairs = base;  // <= S * K <= 64
+      if (lane >= npairs) my_t = -1;
       const int my_e = my_t >= 0 ? s_pidx[my_t * K + my_k] : -1;
       const float my_w = my_t >= 0 ? s_pw[my_t * K + my_k] : 0.f;
       const bool pl = lane < npairs;
@@ -391,9 +396,7 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_row_t[my_row] = my_t;
         s_row_w[my_row] = my_w;
       }
-      int tb = 0;
-      for (int t = 0; t < S; ++t) tb += (t < lane) ? s_n[t] : 0;
-      if (lane < S) G->tok_row0[lane] = tb;
+      if (lane < S) G->tok_row0[lane] = tok0;
       if (lane == 0) {
         G->tok_row0[S] = npairs;  // S may be 64
         G->n_entries = n_ent;
@@ -406,36 +409,39 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
   }
   __syncthreads();
 
-  // ---- row descriptors: 32 words per row (the expert's three tensor records, token, weight),
-  // every row of the buffer rewritten, rows past the group cleared so a row's own record says
-  // whether it is live.  All table reads are in flight together.
-  const int rows = *sh.rows;
-  uint32_t v[kDescPerThread];
+  // ---- row descriptors: 32 words per row (the expert's three tensor records, token, weight)
+  // in 16-byte chunks; every row of the buffer rewritten, rows past the group cleared so a
+  // row's own record says whether it is live.  All table reads are in flight together.
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  static_assert(kTabWords == kDescWords - 2, "a row descriptor ends with token and weight");
+  constexpr int kChunks = kDescWords / 4;
+  constexpr int kChunksPerThread = kRows * kChunks / kBlock;
+  const int rows = a.table ? *sh.rows : 0;
+  u4 v[kChunksPerThread];
 #pragma unroll
-  for (int j = 0; j < kDescPerThread; ++j) {
+  for (int j = 0; j < kChunksPerThread; ++j) {
     const int q = tid + j * kBlock;
-    const int row = q / kDescWords, d = q % kDescWords;
+    const int row = q / kChunks, c = q % kChunks;
     const int e = row < rows ? s_row_e[row] : 0;
-    const int dd = d < kTabWords ? d : 0;
-    v[j] = tab_pre ? s_tab[e * kDescWords + dd]
-                   : (a.table ? reinterpret_cast<const uint32_t *>(a.table + e)[dd] : 0u);
+    if (tab_pre)
+      v[j] = *reinterpret_cast<const u4 *>(s_tab + e * kDescWords + 4 * c);
+    else
+      v[j] = a.table ? reinterpret_cast<const u4 *>(a.table + e)[c] : u4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int j = 0; j < kDescPerThread; ++j) {
+  for (int j = 0; j < kChunksPerThread; ++j) {
     const int q = tid + j * kBlock;
-    const int row = q / kDescWords, d = q % kDescWords;
-    uint32_t val = 0u;
-    if (row < rows && a.table) {
-      if (d == kLiveWord)
-        val = 1u;
-      else if (d < kTabWords)
-        val = v[j];
-      else if (d == kTabWords)
-        val = (uint32_t)s_row_t[row];
-      else
-        val = __float_as_uint(s_row_w[row]);
+    const int row = q / kChunks, c = q % kChunks;
+    u4 val = {0u, 0u, 0u, 0u};
+    if (row < rows) {
+      val = v[j];
+      if (c == kLiveWord / 4) val[kLiveWord % 4] = 1u;
+      if (c == kChunks - 1) {
+        val.z = (uint32_t)s_row_t[row];
+        val.w = __float_as_uint(s_row_w[row]);
+      }
     }
-    reinterpret_cast<uint32_t *>(a.out->rows)[q] = val;
+    reinterpret_cast<u4 *>(a.out->rows)[q] = val;
   }
 }
 
