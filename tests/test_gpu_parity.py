@@ -103,6 +103,8 @@ RAGGED = [
     (130, 34, 5, 5, 1, "mix_even_odd", 32, "bf16"),
     (256, 128, 64, 1, 64, "row", 0, "f32"),         # 64 tokens: the group's offsets end at 64
     (512, 256, 128, 2, 32, "group", 64, "bf16"),    # up to 64 distinct experts in one group
+    (1024, 512, 256, 8, 1, "group", 64, "bf16"),    # one token, 256 experts: the select kernel at S=1
+    (256, 128, 130, 4, 2, "row", 0, "f32"),         # 130 experts: a lane's third column holds two
 ]
 
 
@@ -306,6 +308,35 @@ def test_router_exact_ties_many_experts(E, S):
         for group in groups:
             at = [idx.index(e) for e in group if e in idx]
             assert len(at) == min(len(group), K) and at == sorted(at)
+    ctx.close()
+
+
+@pytest.mark.parametrize("E", [65, 127, 128, 129, 257, 640])
+def test_router_column_edges(E):
+    """Expert counts at the edges of the K-rounds variants (2, 4 and 8 experts per lane, with a
+    lane's last column holding one real expert or none): every token's selection and weights
+    equal the oracle's away from near-ties, and lanes past E are never chosen."""
+    print(f"[parity] router column edges E={E}", flush=True)
+    ctx = new_ctx()
+    D, S, K = 256, 3, 8
+    rng = np.random.default_rng(500 + E)
+    W = rng.normal(0, 0.05, (E, D)).astype(np.float32)
+    b = rng.normal(0, 0.1, E).astype(np.float32)
+    b[E - 1] = 2.0  # the last expert (alone in its column for E = 65, 129, 257) leads every token
+    xs = rng.standard_normal((S, D)).astype(np.float32)
+    x = x_to_device(xs, "f32")
+    ctx.upload_router(0, W, b)
+    rec = ctx.route(0, x, K, 0.9, True, 2.5, host_out=True)
+    routes = oracle.route(W, b, xs.astype(np.float64), K, 0.9, True, 2.5)
+    checked = 0
+    for t in range(S):
+        idx = list(rec[t].idx[:K])
+        assert all(0 <= e < E for e in idx) and idx[0] == E - 1, (t, idx)
+        if near_tie(routes[t], K, 0.9):
+            continue
+        assert route_matches(rec[t], routes[t], K), (t, idx, routes[t].idx)
+        checked += 1
+    assert checked >= 2
     ctx.close()
 
 
