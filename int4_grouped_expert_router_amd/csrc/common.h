@@ -148,6 +148,20 @@ constexpr int rows_per_step(int V, int P, int tensors, int budget) {
   return (budget / (tensors * V * P)) < 1 ? 1 : ((budget / (tensors * V * P)) > 8 ? 8 : budget / (tensors * V * P));
 }
 
+// Raise a kernel's dynamic LDS limit once per device (the attribute belongs to the kernel as
+// loaded on the current device); devices past the table raise it on every call.
+constexpr int kMaxDevices = 64;
+inline hipError_t raise_lds_once(const void *kernel, int bytes, bool (&done)[kMaxDevices]) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kMaxDevices;
+  if (tracked && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && tracked) done[dev] = true;
+  return e;
+}
+
 // Constant-address-space views: uniform records read with scalar loads.
 #define I4MOE_AS4 __attribute__((address_space(4)))
 typedef const GroupBuf I4MOE_AS4 *CGroupBuf;

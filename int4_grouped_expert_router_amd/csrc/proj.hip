@@ -982,11 +982,10 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
   if (!k || a.grid_rows < 1 || a.grid_rows > kDTRows || a.act_ld % 4 != 0 || reinterpret_cast<uintptr_t>(a.act) % 16 != 0)
     return hipErrorInvalidValue;
   const size_t lds = (size_t)kDTRows * rows16_lds_bytes(P);
-  static bool raised[5] = {};
-  if (lds > 48 * 1024 && !raised[P]) {
-    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static bool raised[5][kMaxDevices] = {};
+  if (lds > 48 * 1024) {
+    const hipError_t e = raise_lds_once(k, (int)lds, raised[P]);
     if (e != hipSuccess) return e;
-    raised[P] = true;
   }
   ProjArgs args = a;
   void *params[] = {&args};

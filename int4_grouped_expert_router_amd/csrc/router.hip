@@ -206,12 +206,11 @@ hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_
   if (a.splits * a.epb > kGemvWaves || a.S * a.epb > a.splits * a.epb * kWave) return hipErrorInvalidValue;
   // dynamic LDS up to 64 KB (E = 1024, four tokens per pass) beside 34 KB of static arrays
   const size_t lds = select_lds_bytes(a.E, a.S);
-  static bool lds_raised = false;
-  if ((parts & kRouteSelect) && !lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_route_select),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)select_lds_bytes(kMaxE, kTokens));
+  static bool raised[kMaxDevices] = {};
+  if (parts & kRouteSelect) {
+    const hipError_t e = raise_lds_once(reinterpret_cast<const void *>(&k_route_select),
+                                        (int)select_lds_bytes(kMaxE, kTokens), raised);
     if (e != hipSuccess) return e;
-    lds_raised = true;
   }
   // the event pair spans every launched part
   hipEvent_t g1 = (parts & kRouteSelect) ? nullptr : t1;
