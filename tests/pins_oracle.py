@@ -234,6 +234,37 @@ def pin_group_build_hand():
     assert g["entries"] == [2, 7] and g["token_rows"] == [[0, 1]]
 
 
+def pin_group_build_invariants():
+    """Random routes with repeated experts and top-p cuts: the rows are exactly the kept
+    (token, k) pairs, each under its own expert; entries follow first appearance in token-major
+    order; an entry's rows are contiguous with ascending tokens; a token's reduce list names
+    its own rows in route order."""
+    rng = np.random.default_rng(77)
+    for trial in range(300):
+        S, K, E = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(8, 20))
+        routes = []
+        for _ in range(S):
+            idx = [int(e) for e in rng.choice(E, size=K, replace=False)]
+            n = int(rng.integers(1, K + 1))
+            routes.append(router.RouteResult(n=n, idx=idx, w64=[0.0] * K, w32=np.zeros(K, np.float32),
+                                             logits=None, sigma=None, scores=None))
+        g = experts.build_group(routes)
+        kept = {(t, k) for t, r in enumerate(routes) for k in range(r.n)}
+        assert sorted((t, k) for _, t, k in g["rows"]) == sorted(kept), trial
+        assert all(e == routes[t].idx[k] for e, t, k in g["rows"]), trial
+        first = {}
+        for t, k in sorted(kept):
+            first.setdefault(routes[t].idx[k], (t, k))
+        assert g["entries"] == sorted(first, key=lambda e: first[e]), trial
+        row_entries = [e for e, _, _ in g["rows"]]
+        assert [e for j, e in enumerate(row_entries) if j == 0 or row_entries[j - 1] != e] == g["entries"], trial
+        for e in g["entries"]:
+            toks = [t for x, t, _ in g["rows"] if x == e]
+            assert toks == sorted(set(toks)), trial
+        for t, r in enumerate(routes):
+            assert [g["rows"][i][1:] for i in g["token_rows"][t]] == [(t, k) for k in range(r.n)], trial
+
+
 def identity_expert(D, diag_nibble=9, scale=1.0):
     q = np.full((D, D), 8, np.uint8)
     np.fill_diagonal(q, diag_nibble)
