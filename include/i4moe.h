@@ -37,6 +37,8 @@
  *   - Device pointers ("_dev") are plain HIP device addresses (e.g. torch tensor data_ptr()).
  *     Host pointers are read during the call only; the caller may free or overwrite them as
  *     soon as the call returns.
+ *   - A NULL context is refused before any HIP call: I4MOE_EINVAL, or 0 from the calls that
+ *     return a handle or a size (i4moe_ctx_destroy(NULL) is a no-op).
  *   - A context is bound to one device and one stream and is not thread-safe.
  *   - Compute calls (route, issue, take) only enqueue work; they never synchronise the host
  *     unless a host output is requested.

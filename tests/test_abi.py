@@ -76,3 +76,31 @@ def test_constants_match_header():
     assert consts, "no constants parsed"
     for name, val in consts.items():
         assert getattr(binding, name) == val, name
+
+
+def test_null_context_rejected_before_any_device_call(lib_path):
+    """Every entry point refuses a NULL context (or output pointer) with its documented error
+    value before it touches the HIP runtime, so these calls are safe without a GPU."""
+    import ctypes as C
+
+    from int4_grouped_expert_router_amd import binding as B
+    B.load(lib_path)
+    EINVAL, OK = B.I4MOE_EINVAL, B.I4MOE_OK
+    assert B.i4moe_ctx_create(0, None) == EINVAL
+    assert B.i4moe_ctx_destroy(None) == OK
+    assert B.i4moe_set_stream(None, None) == EINVAL
+    assert B.i4moe_last_error(None)  # static text, never NULL
+    assert B.i4moe_upload_expert_tensor(None, 2, 0, 16, 16, None, None) == 0  # handle 0: not uploaded
+    assert B.i4moe_tensor_free(None, 1) == EINVAL
+    assert B.i4moe_set_expert(None, 0, 0, 1, 2, 3) == EINVAL
+    assert B.i4moe_upload_router(None, 0, 8, 16, None, None) == EINVAL
+    assert B.i4moe_route(None, 0, None, 0, 1, 1, 0.0, 1, 1.0, None) == EINVAL
+    assert B.i4moe_expert_group_issue(None, 0, None, 0, 1, None) == EINVAL
+    assert B.i4moe_expert_group_take(None, None, 1) == EINVAL
+    assert B.i4moe_set_fail_after(None, 0) == EINVAL
+    buf = (C.c_char * 8)()
+    assert B.i4moe_debug_read(None, 0, 0, C.cast(buf, C.c_void_p), 8) == EINVAL
+    assert B.i4moe_debug_size(None, 0, 0) == 0
+    assert B.i4moe_set_profiling(None, 1) == EINVAL
+    ms, n = C.c_double(), C.c_longlong()
+    assert B.i4moe_profile_query(None, 0, C.byref(ms), C.byref(n)) == EINVAL
