@@ -104,6 +104,9 @@ typedef struct {
 
 /* Create a context on HIP device `device`, bound to the null stream.  The fault hook starts
  * from the environment variable I4MOE_FAIL_AFTER when it holds a non-negative integer.
+ * I4MOE_WAVE_FACTOR (0.05 .. 64, default 1) scales the number of waves the projections aim
+ * for per CU; it changes how output rows are tiled over waves, never the results (each row
+ * is still reduced by one wave in a fixed order).
  * Errors: EINVAL (bad device, out == NULL), EDEVICE, ENOMEM. */
 int i4moe_ctx_create(int device, i4moe_ctx **out);
 
