@@ -192,6 +192,31 @@ def m_sorted_entries(routes):
     return {"entries": entries, "entry_rows": entry_rows, "rows": rows, "token_rows": token_rows}
 
 
+def _group_from_entries(routes, entries, entry_rows):
+    rows, row_of = [], {}
+    for j, e in enumerate(entries):
+        for (t, k) in entry_rows[j]:
+            row_of[(t, k)] = len(rows)
+            rows.append((e, t, k))
+    token_rows = [[row_of[(t, k)] for k in range(r.n)] for t, r in enumerate(routes)]
+    return {"entries": entries, "entry_rows": entry_rows, "rows": rows, "token_rows": token_rows}
+
+
+def m_group_ignores_topp(routes):
+    # every one of the K selections becomes a row, also those the top-p cut dropped
+    full = [router.RouteResult(n=len(r.idx), idx=r.idx, w64=r.w64, w32=r.w32, logits=r.logits, sigma=r.sigma,
+                               scores=r.scores) for r in routes]
+    g = _orig_build(full)
+    return _group_from_entries(routes, g["entries"], g["entry_rows"])
+
+
+def m_entry_rows_by_rank(routes):
+    # an entry's rows ordered by selection rank (then token) instead of by token
+    g = _orig_build(routes)
+    entry_rows = [sorted(er, key=lambda tk: (tk[1], tk[0])) for er in g["entry_rows"]]
+    return _group_from_entries(routes, g["entries"], entry_rows)
+
+
 def m_drop_residual(W, bias, x64, expert_of, K, topp, norm_topk, routed_scale, residual=None):
     routes, group, delta, out = _orig_moe(W, bias, x64, expert_of, K, topp, norm_topk, routed_scale, residual)
     return routes, group, delta, (delta.copy() if out is not None else None)
@@ -224,6 +249,8 @@ MUTANTS = {
     "silu_sigma_only": (experts, "silu", m_silu_sigma_only),
     "gate_up_swapped": (experts, "expert_forward", m_swap_gate_up),
     "entries_sorted": (experts, "build_group", m_sorted_entries),
+    "group_ignores_topp": (experts, "build_group", m_group_ignores_topp),
+    "entry_rows_by_rank": (experts, "build_group", m_entry_rows_by_rank),
     "residual_dropped": (experts, "moe_layer", m_drop_residual),
     "f64_route_weights": (experts, "layer_delta", m_f64_weights),
 }
