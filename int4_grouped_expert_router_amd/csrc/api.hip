@@ -575,6 +575,9 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
       if (!hit) continue;
       for (int w = 0; w < 3; ++w) (*v[w])[x] = 0;
       L.h_tab[x] = ExpertRec{};
+      // the layer's route copied the old records into its row descriptors: it must be
+      // recomputed before an issue may consume it
+      L.routed = false;
       int rc = write_table_entry(c, L, (int)x);
       if (rc) return rc;
     }
@@ -619,6 +622,10 @@ int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4m
   L.h_tab[expert].t[0] = G;
   L.h_tab[expert].t[1] = U;
   L.h_tab[expert].t[2] = Dn;
+  // A device route copies the expert records into its row descriptors when it runs, so a
+  // route taken before this change would still name the old tensors (and the issue would
+  // plan its launch from the new ones): the layer has to be routed again.
+  L.routed = false;
   return write_table_entry(c, L, expert);
 }
 

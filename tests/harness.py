@@ -3,8 +3,10 @@ route/issue/take, and compare with the f64 oracle."""
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import hashlib
 import math
+import os
 from types import SimpleNamespace
 
 import numpy as np
@@ -12,6 +14,7 @@ import numpy as np
 import oracle
 from oracle import router as orouter
 from synth import gen_layer
+from synth.gen import gen_expert
 
 TOL = 1e-4          # normwise relative error bar for expert outputs (f32 accumulation vs f64)
 NEAR_TIE = 1e-9     # score / top-p distance below which a selection counts as a near-tie
@@ -31,17 +34,52 @@ def x_to_device(x: np.ndarray, dtype: str):
     return t.to(dev)
 
 
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def upload_layer(ctx, L, layer: int, experts=None):
+    """Upload the router and experts of L to `layer`.  Experts are drawn in a thread pool and
+    not kept on the host (the oracle draws the ones it needs again, with the same bytes)."""
     cfg = L.cfg
     ctx.upload_router(layer, L.router_W, L.router_b)
-    experts = range(cfg.E) if experts is None else experts
+    experts = list(range(cfg.E) if experts is None else experts)
     handles = {}
-    for e in experts:
-        ew = L.expert(e)
-        h = (ctx.upload_host_tensor(ew.gate), ctx.upload_host_tensor(ew.up), ctx.upload_host_tensor(ew.down))
-        ctx.set_expert(layer, e, *h)
-        handles[e] = h
+    draw = lambda e: L._experts.get(e) or gen_expert(cfg, L.layer, e)
+    with cf.ThreadPoolExecutor(WORKERS) as ex:
+        for e, ew in zip(experts, ex.map(draw, experts)):
+            h = (ctx.upload_host_tensor(ew.gate), ctx.upload_host_tensor(ew.up), ctx.upload_host_tensor(ew.down))
+            ctx.set_expert(layer, e, *h)
+            handles[e] = h
     return handles
+
+
+def layer_delta_threads(routes, expert_of, x64):
+    """oracle.experts.layer_delta with each (token, k) row's expert forward evaluated in a thread
+    pool (numpy releases the interpreter lock inside them); the weighted sums are then taken in
+    the oracle's own (token, k) order, so delta and the intermediates are the oracle's bit for
+    bit."""
+    x64 = np.atleast_2d(x64)
+    pairs = [(t, k) for t, r in enumerate(routes) for k in range(r.n)]
+    distinct = sorted({int(routes[t].idx[k]) for t, k in pairs})
+    with cf.ThreadPoolExecutor(WORKERS) as ex:
+        ws = dict(zip(distinct, ex.map(expert_of, distinct)))
+        outs = list(ex.map(lambda tk: oracle.expert_forward(ws[int(routes[tk[0]].idx[tk[1]])].gate,
+                                                            ws[int(routes[tk[0]].idx[tk[1]])].up,
+                                                            ws[int(routes[tk[0]].idx[tk[1]])].down, x64[tk[0]]),
+                           pairs))
+    delta = np.zeros(x64.shape, dtype=np.float64)
+    inter = {}
+    for (t, k), o in zip(pairs, outs):
+        inter[(t, k)] = o
+        delta[t] += float(routes[t].w32[k]) * o[3]
+    return delta, inter
+
+
+def gpu_routes(rec, S: int, K: int):
+    """The GPU's route records in the form the oracle's expert functions take (n, idx, w32): used to
+    check the experts on the GPU's own route when a selection is a near-tie."""
+    return [SimpleNamespace(n=int(rec[t].n), idx=[int(v) for v in rec[t].idx[:K]],
+                            w32=np.array(rec[t].w[:K], dtype=np.float32)) for t in range(S)]
 
 
 def near_tie(r: orouter.RouteResult, K: int, topp: float, tau: float = NEAR_TIE) -> bool:

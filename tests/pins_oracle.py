@@ -47,6 +47,33 @@ def pack_test(q):
 
 # ---------------------------------------------------------------- int4 decoding
 
+def pin_check_format():
+    """The format rules of the g4 commit ("Commit history of c/backend_cuda.cu"): only fmt 2
+    (per-row) and fmt 4 (group-wise) decode, a group size is even so that no packed byte holds two
+    groups, gs = 0 is per-row, and anything else is refused rather than decoded.  Odd C (half a
+    byte) and empty shapes are refused by the reading of a byte-packed row."""
+    for fmt, gs, O, C in [(2, 0, 4, 8), (4, 0, 4, 8), (4, 2, 4, 8), (4, 64, 3, 200), (4, 256, 1, 64)]:
+        int4.check_format(fmt, gs, O, C)
+    bad = [(3, 0, 4, 8), (1, 0, 4, 8), (0, 0, 4, 8), (5, 64, 4, 8),   # no other format codes
+           (4, 3, 4, 8), (4, 63, 4, 200), (4, -2, 4, 8),              # odd or negative group size
+           (2, 64, 4, 8), (2, 2, 4, 8),                                # a per-row tensor has no groups
+           (2, 0, 4, 7), (4, 2, 4, 9), (2, 0, 0, 8), (4, 2, 4, 0)]     # half bytes, empty shapes
+    for args in bad:
+        try:
+            int4.check_format(*args)
+        except ValueError:
+            continue
+        raise AssertionError(f"check_format accepted {args}")
+    # the decoder applies the rules: an unknown format or an odd group size never decodes
+    p = np.full((4, 4), 0x88, np.uint8)
+    for fmt, gs, s in [(3, 0, np.ones(4, np.float32)), (4, 3, np.ones(12, np.float32))]:
+        try:
+            int4.dequantize(p, s, fmt, gs, 4, 8)
+        except ValueError:
+            continue
+        raise AssertionError(f"dequantize decoded fmt={fmt} gs={gs}")
+
+
 def pin_nibble_roundtrip():
     rng = np.random.default_rng(11)
     for (O, C) in [(1, 2), (3, 10), (7, 64), (2, 200)]:

@@ -7,6 +7,7 @@ forced from the host; no kernel is ever launched on bad input."""
 from __future__ import annotations
 
 import ctypes as C
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
@@ -254,3 +255,112 @@ def test_sixteen_slots_reduce_in_issue_order():
             ref += w * oracle.expert_forward(ew.gate, ew.up, ew.down, x64[0])[3]
     assert normwise_err(total, ref[None, :]) < TOL
     ctx.close()
+
+
+def test_rebinding_an_expert_requires_a_new_route():
+    """A device route copies the expert records when it runs, so after set_expert or tensor_free
+    the layer's route is stale: the issue is refused (nothing enqueued) until the layer is routed
+    again, and the new route runs the new tensors."""
+    import torch
+    from int4_grouped_expert_router_amd import binding as B
+    from int4_grouped_expert_router_amd.runtime import I4moeError
+    print("[boundary] stale route after a re-bind", flush=True)
+    cfg = get_config("tiny")
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    handles = upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    rec = ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+    e0 = int(rec[0].idx[0])
+    # bind expert e0 to a copy of itself with every down scale doubled: its y doubles
+    ew = L.expert(e0)
+    down2 = SimpleNamespace(fmt=ew.down.fmt, gs=ew.down.gs, O=ew.down.O, C=ew.down.C, packed=ew.down.packed,
+                            scales=(2 * ew.down.scales).astype(np.float32))
+    new = (ctx.upload_host_tensor(ew.gate), ctx.upload_host_tensor(ew.up), ctx.upload_host_tensor(down2))
+    ctx.set_expert(0, e0, *new)
+    with pytest.raises(I4moeError) as ei:
+        ctx.issue(0, x)
+    assert ei.value.code == B.I4MOE_EINVAL and "route" in str(ei.value)
+    got = tiny_delta(ctx, cfg, L, x)   # routes again first
+    routes, x64 = oracle_routes(cfg, L)
+    ref = np.zeros((1, cfg.D))
+    for k in range(routes[0].n):
+        e = routes[0].idx[k]
+        ex = L.expert(e)
+        y = oracle.expert_forward(ex.gate, ex.up, down2 if e == e0 else ex.down, x64[0])[3]
+        ref[0] += float(routes[0].w32[k]) * y
+    assert normwise_err(got, ref) < TOL
+    # freeing a bound tensor also leaves the route stale (and the expert unbound)
+    ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.free_tensor(handles[e0][0])      # the old gate: no longer bound, route stays valid
+    ctx.issue(0, x)
+    z = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    ctx.take(z)
+    ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.free_tensor(new[2])              # bound to e0: the expert is unset, the route is stale
+    with pytest.raises(I4moeError) as ei:
+        ctx.issue(0, x)
+    assert ei.value.code == B.I4MOE_EINVAL
+    torch.cuda.synchronize()
+    assert np.array_equal(z.cpu().numpy(), got)
+    ctx.close()
+
+
+def test_fail_after_from_environment(monkeypatch):
+    """I4MOE_FAIL_AFTER=N set when the context is created: N compute calls pass, the next is
+    refused with I4MOE_EINJECTED; a value that is not a non-negative integer is ignored."""
+    import torch
+    from int4_grouped_expert_router_amd import binding as B
+    from int4_grouped_expert_router_amd.runtime import I4moeError
+    print("[boundary] fail-after from the environment", flush=True)
+    cfg = get_config("tiny")
+    L = make_layer(cfg, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    monkeypatch.setenv("I4MOE_FAIL_AFTER", "2")
+    ctx = new_ctx()
+    monkeypatch.delenv("I4MOE_FAIL_AFTER")
+    upload_layer(ctx, L, 0)             # uploads are never gated
+    ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+    ctx.issue(0, x)
+    z = torch.zeros((1, cfg.D), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(I4moeError) as ei:
+        ctx.take(z)
+    assert ei.value.code == B.I4MOE_EINJECTED
+    ctx.close()
+    for bad in ("-1", "two", "3x", ""):
+        monkeypatch.setenv("I4MOE_FAIL_AFTER", bad)
+        c2 = new_ctx()
+        monkeypatch.delenv("I4MOE_FAIL_AFTER")
+        upload_layer(c2, L, 0)
+        for _ in range(3):
+            assert normwise_err(tiny_delta(c2, cfg, L, x), oracle_delta(cfg, L)) < TOL
+        c2.close()
+
+
+@pytest.mark.parametrize("name", ["medium", "mix"])
+def test_wave_factor_changes_tiling_not_bits(name, monkeypatch):
+    """I4MOE_WAVE_FACTOR retiles the projections (rows per wave) but every row is still reduced by
+    one wave in a fixed order: contexts created with different factors give the same bits."""
+    import torch
+    print(f"[boundary] wave factor {name}", flush=True)
+    cfg = get_config(name)
+    L = make_layer(cfg, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    outs = []
+    for f in ("0.1", "1", "8"):
+        monkeypatch.setenv("I4MOE_WAVE_FACTOR", f)
+        ctx = new_ctx()
+        monkeypatch.delenv("I4MOE_WAVE_FACTOR")
+        upload_layer(ctx, L, 0)
+        pair = []
+        for host in (True, False):      # the separate kernels, and the fused ones the bench times
+            ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=host)
+            ctx.issue(0, x)
+            r = torch.from_numpy(L.residual.copy()).to("cuda:0")
+            ctx.take(r)
+            torch.cuda.synchronize()
+            pair.append(r.cpu().numpy().tobytes())
+        assert pair[0] == pair[1]
+        outs.append(pair[0])
+        ctx.close()
+    assert outs[0] == outs[1] == outs[2]

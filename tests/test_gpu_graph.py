@@ -1,13 +1,15 @@
 """One captured HIP graph per MoE layer (route -> issue -> take, no host work between the
 kernels): every replay, with eager work of the program between replays, gives the eager
-result bit for bit (MI355X only)."""
+result bit for bit, and a replay into a zero residual gives the oracle's two-layer delta
+(MI355X only)."""
 
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
-from harness import make_layer, upload_layer, x_to_device
+from harness import (TOL, gpu_routes, layer_delta_threads, make_layer, near_tie, normwise_err, oracle_routes,
+                     route_matches, upload_layer, x_to_device)
 from synth import get_config
 
 pytestmark = pytest.mark.gpu
@@ -42,6 +44,8 @@ def test_graph_replays_match_eager(name):
         two_layers()
     s.synchronize()
     eager = resid.cpu().numpy()
+    # the routes each layer takes (deterministic, so the graph's routes are these too)
+    recs = [ctx.route(l, xs[l], cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True) for l in range(2)]
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
@@ -62,4 +66,24 @@ def test_graph_replays_match_eager(name):
             ctx.take(other)
             other.mul_(0.5).add_(1.0)
         s.synchronize()
+    # one more replay into a zero residual: the sum of both layers' deltas, against the oracle
+    with torch.cuda.stream(s):
+        resid.zero_()
+    g.replay()
+    s.synchronize()
+    got = resid.cpu().numpy()
+    ref = np.zeros((cfg.S, cfg.D))
+    for l, L in enumerate(layers):
+        routes, x64 = oracle_routes(cfg, L)
+        use = []
+        for t in range(cfg.S):
+            if near_tie(routes[t], cfg.K, cfg.topp):
+                use.append(gpu_routes(recs[l], cfg.S, cfg.K)[t])
+            else:
+                assert route_matches(recs[l][t], routes[t], cfg.K), (l, t)
+                use.append(routes[t])
+        ref += layer_delta_threads(use, L.expert, x64)[0]
+    err = normwise_err(got, ref)
+    print(f"[graph] {name}: replay vs oracle normwise error {err:.2e}", flush=True)
+    assert err < TOL, err
     ctx.close()

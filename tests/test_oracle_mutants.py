@@ -228,7 +228,26 @@ def m_f64_weights(routes, expert_of, x64):
     return _orig_layer_delta(routes, expert_of, x64)
 
 
+_orig_check = int4.check_format
+
+
+def m_check_accepts_odd_gs(fmt, gs, O, C):
+    # only the format code is checked
+    if fmt not in (int4.FMT_ROW, int4.FMT_GROUP):
+        raise ValueError(f"unsupported fmt {fmt}")
+
+
+def m_dequant_unchecked(packed, scales, fmt, gs, O, C, rows):
+    # decodes whatever it is handed
+    rows = np.asarray(rows)
+    p = np.asarray(packed, dtype=np.uint8).reshape(O, C // 2)[rows]
+    q = _orig_unpack(p, len(rows), C).astype(np.float64) - 8.0
+    return q * _orig_scale(scales, fmt, gs, O, C, rows)
+
+
 MUTANTS = {
+    "check_accepts_odd_gs": (int4, "check_format", m_check_accepts_odd_gs),
+    "dequant_unchecked": (int4, "dequantize_rows", m_dequant_unchecked),
     "swap_nibbles": (int4, "unpack_nibbles", m_swap_nibbles),
     "no_offset": (int4, "dequantize_rows", m_no_offset),
     "offset7": (int4, "dequantize_rows", m_offset7),
