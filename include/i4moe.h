@@ -168,6 +168,24 @@ int i4moe_upload_router(i4moe_ctx *ctx, int layer, int E, int D, const float *W,
 int i4moe_route(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S, int K, float topp,
                 int norm_topk, float routed_scale, i4moe_route_host *host_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the route of i4moe_route, by the same kernels with the
+ * same bits, with every byte of its working memory (scores, logits, the selection's group
+ * buffer) in a static device array of I4MOE_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends.  Its address is looked up once per device when a context is created there; this call
+ * allocates nothing, also on its first use.
+ *   route_dev  device memory for S records (i4moe_route_host layout), written on the stream;
+ *              the layer's own device route (the one i4moe_expert_group_issue consumes) is left
+ *              as it was, and the host is not synchronised.
+ * Limits are those of the scratch: S <= I4MOE_MAX_TOKENS, E <= I4MOE_MAX_E, S*K <= I4MOE_MAX_ROWS
+ * (I4MOE_EUNSUPPORTED beyond them, with nothing enqueued); other errors as i4moe_route.
+ * Every context on a GPU shares that GPU's scratch: calls whose kernels overlap on one GPU (on
+ * two streams) race and must be ordered by the caller; calls on one stream are ordered already.
+ * Fault-hook gated; no profiling events are recorded for it. */
+#define I4MOE_NOALLOC_SCRATCH_BYTES (1048576 + 524288 + 43264)
+int i4moe_route_noalloc(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S, int K, float topp,
+                        int norm_topk, float routed_scale, i4moe_route_host *route_dev);
+
 /* Run the experts of one group over x_dev ([S][D], F32 or BF16) and keep the per-row outputs
  * in the next free slot.  group == NULL consumes the device group of `layer` written by the
  * latest i4moe_route of that layer (no host round trip); the route of that layer must not be

@@ -18,6 +18,7 @@ I4MOE_MAX_E = 1024
 I4MOE_MAX_COLS = 8192
 I4MOE_MAX_SLOTS = 16
 I4MOE_GROUP_WORDS = 4 + 64 + 65 + 64 + 64 + 64 + 65 + 64
+I4MOE_NOALLOC_SCRATCH_BYTES = 1048576 + 524288 + 43264
 
 I4MOE_FMT_ROW, I4MOE_FMT_GROUP = 2, 4
 I4MOE_DTYPE_F32, I4MOE_DTYPE_BF16 = 0, 1
@@ -50,6 +51,8 @@ SIGNATURES = {
     "i4moe_upload_router": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
     "i4moe_route": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int,
                               C.c_float, C.POINTER(i4moe_route_host)]),
+    "i4moe_route_noalloc": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int,
+                                      C.c_float, C.c_void_p]),
     "i4moe_expert_group_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.POINTER(i4moe_group)]),
     "i4moe_expert_group_take": (C.c_int, [_ctx_p, C.c_void_p, C.c_int]),
     "i4moe_set_fail_after": (C.c_int, [_ctx_p, C.c_longlong]),
@@ -100,6 +103,7 @@ i4moe_tensor_free = _fn("i4moe_tensor_free")
 i4moe_set_expert = _fn("i4moe_set_expert")
 i4moe_upload_router = _fn("i4moe_upload_router")
 i4moe_route = _fn("i4moe_route")
+i4moe_route_noalloc = _fn("i4moe_route_noalloc")
 i4moe_expert_group_issue = _fn("i4moe_expert_group_issue")
 i4moe_expert_group_take = _fn("i4moe_expert_group_take")
 i4moe_set_fail_after = _fn("i4moe_set_fail_after")

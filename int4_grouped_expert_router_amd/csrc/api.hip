@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -101,6 +102,8 @@ struct i4moe_ctx {
 
   long long fail_after = -1, calls = 0;
   bool poisoned = false;
+
+  void *scratch = nullptr;  // this device's copy of the static route scratch (i4moe_route_noalloc)
 
   bool profiling = false;
   std::vector<hipEvent_t> ev_pool;
@@ -391,6 +394,55 @@ bool all_finite(const float *p, size_t n) {
   return true;
 }
 
+// ---- Static route scratch for i4moe_route_noalloc: the router's score and logit scratch and the
+// group buffer its selection writes, at the route's own limits (I4MOE_MAX_TOKENS tokens of
+// I4MOE_MAX_E experts).  Every GPU the library runs on holds one copy until the process ends.
+constexpr size_t kScoreBytes = sizeof(double2) * kTokens * kMaxE;       // 1 MiB
+constexpr size_t kLogitBytes = sizeof(double) * kTokens * kMaxE;        // 512 KiB
+constexpr size_t kGroupBufBytes = (sizeof(GroupBuf) + 255) / 256 * 256;
+constexpr size_t kNoAllocScratchBytes = kScoreBytes + kLogitBytes + kGroupBufBytes;
+static_assert(kNoAllocScratchBytes == I4MOE_NOALLOC_SCRATCH_BYTES, "documented scratch size");
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// The device address of `scratch` on each device, looked up once per device with that device
+// current (the array's name is only a host-side handle).
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void **out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (device >= 0 && device < kMaxDevices && g_scratch_ptr[device]) {
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+  }
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+  if (device >= 0 && device < kMaxDevices) g_scratch_ptr[device] = p;
+  *out = p;
+  return hipSuccess;
+}
+
+// Launch geometry of the router GEMV for a layer: at least 256 waves and at most 1024 columns
+// per wave (one batch of loads per lane and token group), each split a multiple of 256
+// columns; an expert's splits (and up to four experts of one split each) share a workgroup of
+// at most 16 waves.
+void gemv_geometry(const Layer &L, RouteArgs &a) {
+  int splits = (256 + L.E - 1) / L.E;
+  if (splits < (L.D + 1023) / 1024) splits = (L.D + 1023) / 1024;
+  if (splits > 16) splits = 16;
+  const int cps = round_up((L.D + splits - 1) / splits, 256);
+  splits = (L.D + cps - 1) / cps;
+  a.splits = splits;
+  a.cols_per_split = cps;
+  a.epb = splits >= 4 ? 1 : 4 / splits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,6 +479,13 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && ncu > 0)
     c->n_cu = ncu;
   (void)hipGetLastError();
+  if (scratch_address(device, &c->scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    dfree(c->d_ring);
+    dfree(c->d_slot_bufs);
+    delete c;
+    return I4MOE_EDEVICE;
+  }
   if (const char *wf = std::getenv("I4MOE_WAVE_FACTOR")) {
     const double v = std::atof(wf);
     if (v >= 0.05 && v <= 64.0) c->wave_factor = v;
@@ -691,15 +750,6 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
   if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
   ensure_device(c);
-  // at least 256 GEMV waves and at most 1024 columns per wave (one batch of loads per lane and
-  // token group), each split a multiple of 256 columns; an expert's splits (and up to four
-  // experts of one split each) share a workgroup of at most 16 waves
-  int splits = (256 + L->E - 1) / L->E;
-  if (splits < (L->D + 1023) / 1024) splits = (L->D + 1023) / 1024;
-  if (splits > 16) splits = 16;
-  int cps = round_up((L->D + splits - 1) / splits, 256);
-  splits = (L->D + cps - 1) / cps;
-  const int epb = splits >= 4 ? 1 : 4 / splits;
   const int ring = c->ring_next;
   for (int s = 0; s < c->nslots; ++s)
     if (c->slots[s].ring == ring)
@@ -720,9 +770,7 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   a.S = S;
   a.K = K;
   a.x_bf16 = dtype == I4MOE_DTYPE_BF16;
-  a.splits = splits;
-  a.cols_per_split = cps;
-  a.epb = epb;
+  gemv_geometry(*L, a);
   a.vec = (L->D % 4 == 0) && reinterpret_cast<uintptr_t>(L->W) % 16 == 0 &&
           reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 16 : 8) == 0;
   a.norm_topk = norm_topk ? 1 : 0;
@@ -753,6 +801,58 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "route copy back");
   }
+  return I4MOE_OK;
+}
+
+int i4moe_route_noalloc(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
+                        float routed_scale, i4moe_route_host *route_dev) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->W) return fail(c, I4MOE_EINVAL, "layer %d has no router", layer);
+  if (!x_dev || !route_dev) return fail(c, I4MOE_EINVAL, "x_dev and route_dev must be device pointers");
+  if (reinterpret_cast<uintptr_t>(route_dev) % 4 != 0) return fail(c, I4MOE_EINVAL, "route_dev must be 4-byte aligned");
+  if (dtype != I4MOE_DTYPE_F32 && dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", dtype);
+  // the static scratch holds the scores of at most kTokens tokens of kMaxE experts and one group
+  if (S < 1 || S > kTokens)
+    return fail(c, I4MOE_EUNSUPPORTED, "S=%d outside 1..%d (the static route scratch holds %d tokens)", S, kTokens, kTokens);
+  if (L->E > kMaxE) return fail(c, I4MOE_EUNSUPPORTED, "E=%d exceeds the static route scratch (%d experts)", L->E, kMaxE);
+  if (K < 1 || K > L->E || K > kMaxK) return fail(c, I4MOE_EINVAL, "K=%d outside 1..min(E=%d, %d)", K, L->E, kMaxK);
+  if (S * K > kRows)
+    return fail(c, I4MOE_EUNSUPPORTED, "S*K=%d exceeds the %d rows of the static route scratch", S * K, kRows);
+  if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
+  if (!c->scratch) return fail(c, I4MOE_EDEVICE, "static route scratch has no device address");
+  ensure_device(c);
+  // Every part of the route's working memory comes from this device's static scratch, addressed
+  // through the pointer looked up at context creation: scores, logits, then the group buffer the
+  // selection writes.  Each is fully written by this call's kernels before it is read, so
+  // nothing needs clearing.
+  uint8_t *base = static_cast<uint8_t *>(c->scratch);
+  RouteArgs a{};
+  a.W = L->W;
+  a.bias = L->b;
+  a.x = x_dev;
+  a.score = reinterpret_cast<double2 *>(base);
+  a.logits = reinterpret_cast<double *>(base + kScoreBytes);
+  a.out = reinterpret_cast<GroupBuf *>(base + kScoreBytes + kLogitBytes);
+  a.table = nullptr;  // routes only: no row descriptors
+  a.E = L->E;
+  a.D = L->D;
+  a.S = S;
+  a.K = K;
+  a.x_bf16 = dtype == I4MOE_DTYPE_BF16;
+  gemv_geometry(*L, a);
+  a.vec = (L->D % 4 == 0) && reinterpret_cast<uintptr_t>(L->W) % 16 == 0 &&
+          reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 16 : 8) == 0;
+  a.norm_topk = norm_topk ? 1 : 0;
+  a.topp = topp;
+  a.routed_scale = routed_scale;
+  hipError_t e = launch_route(a, kRouteGemv | kRouteSelect, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(route_dev, a.out->route, sizeof(RouteTok) * S, hipMemcpyDeviceToDevice, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "route launch");
+  c->calls++;
   return I4MOE_OK;
 }
 

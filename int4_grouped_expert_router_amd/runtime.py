@@ -102,6 +102,15 @@ class Context:
                                  C.cast(out, C.POINTER(B.i4moe_route_host)) if out is not None else None))
         return out
 
+    def route_noalloc(self, layer: int, x, K: int, topp: float, norm_topk: bool, routed_scale: float, out):
+        """The route into `out`, a device tensor of S * sizeof(i4moe_route_host) bytes, with the
+        library's static scratch (no allocation)."""
+        S = x.shape[0]
+        if out.numel() * out.element_size() < S * C.sizeof(B.i4moe_route_host):
+            raise ValueError("out too small for S route records")
+        self.check(B.i4moe_route_noalloc(self.p, layer, C.c_void_p(x.data_ptr()), _dtype_code(x), S, K, topp,
+                                         1 if norm_topk else 0, routed_scale, C.c_void_p(out.data_ptr())))
+
     def issue(self, layer: int, x, rows=None) -> int:
         """rows: None (device route of the layer) or a list of (expert, token, weight)."""
         S = x.shape[0]

@@ -95,6 +95,7 @@ def test_null_context_rejected_before_any_device_call(lib_path):
     assert B.i4moe_set_expert(None, 0, 0, 1, 2, 3) == EINVAL
     assert B.i4moe_upload_router(None, 0, 8, 16, None, None) == EINVAL
     assert B.i4moe_route(None, 0, None, 0, 1, 1, 0.0, 1, 1.0, None) == EINVAL
+    assert B.i4moe_route_noalloc(None, 0, None, 0, 1, 1, 0.0, 1, 1.0, None) == EINVAL
     assert B.i4moe_expert_group_issue(None, 0, None, 0, 1, None) == EINVAL
     assert B.i4moe_expert_group_take(None, None, 1) == EINVAL
     assert B.i4moe_set_fail_after(None, 0) == EINVAL
