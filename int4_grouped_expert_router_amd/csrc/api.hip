@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -317,7 +318,7 @@ int write_table_entry(i4moe_ctx *c, Layer &L, int expert) {
 // (short tiles pay the startup latency of a wave for little data).
 constexpr int kMinWaveBytes = 12 * 1024;
 
-Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector<int> &group_sizes, int n_cu,
+Plan plan_proj(int C, int O, int max_rows, bool dual, const std::vector<int> &group_sizes, int n_cu,
                double wave_factor) {
   const int RD = (C + 7) / 8;
   Plan best;
@@ -344,7 +345,6 @@ Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector
     best.P = (RD + 63) / 64;
     best.gen = true;
   }
-  const bool use_xb = dual && xb && !best.gen;
   const int NT = dual ? 2 : 1;
   // Short down rows run 16 lanes per row (four rows per wave instruction): a fully used wave
   // and a 16-lane reduction instead of a 64-lane one.
@@ -365,7 +365,7 @@ Plan plan_proj(int C, int O, int max_rows, bool dual, bool xb, const std::vector
   // and each wave streams several steps, which measured faster than filling every resident
   // slot with shorter tiles.
   const long long resident =
-      (long long)(best.rows16 ? rows16_blocks_per_cu(best.P) : proj_blocks_per_cu(best.V, best.P, NT, best.gen, use_xb)) *
+      (long long)(best.rows16 ? rows16_blocks_per_cu(best.P) : proj_blocks_per_cu(best.V, best.P, NT, best.gen)) *
       4 * n_cu;
   const long long per_cu = resident < 8LL * n_cu ? resident : 8LL * n_cu;
   long long target = (long long)(per_cu * wave_factor);
@@ -591,9 +591,24 @@ i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, in
     hip_fail(c, e, "hipMalloc(scales)");
     return 0;
   }
-  e = hipMemsetAsync(t.q, 0x88, qbytes, c->stream);  // padding decodes to weight 0
-  if (e == hipSuccess)
-    e = hipMemcpy2DAsync(t.q, row_bytes, packed, C / 2, C / 2, O, hipMemcpyHostToDevice, c->stream);
+  // Nibbles are converted offset->signed here, as the g4 commit's upload does: xor 0x88 turns
+  // each nibble q into the 4-bit two's complement of q - 8, which the kernels' integer dot
+  // products take as it is.  Rows are padded to 16 bytes (and the tail slack filled) with
+  // zeros, i.e. weight 0.
+  std::unique_ptr<uint8_t[]> dev(new (std::nothrow) uint8_t[qbytes]);
+  if (!dev) {
+    dfree(t.q);
+    dfree(t.s);
+    fail(c, I4MOE_ENOMEM, "host staging for a %zu-byte tensor", qbytes);
+    return 0;
+  }
+  std::memset(dev.get(), 0, qbytes);
+  for (int o = 0; o < O; ++o) {
+    const uint8_t *src = packed + (size_t)o * (C / 2);
+    uint8_t *dst = dev.get() + (size_t)o * row_bytes;
+    for (int b = 0; b < C / 2; ++b) dst[b] = src[b] ^ 0x88u;
+  }
+  e = hipMemcpyAsync(t.q, dev.get(), qbytes, hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(t.s, scales, sizeof(float) * (size_t)O * ng, hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
@@ -944,8 +959,8 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
     grp = c->d_slot_bufs + s;
   }
 
-  const Plan pd = plan_proj(L->D, L->I, max_rows, true, dtype == I4MOE_DTYPE_BF16, gs_in, c->n_cu, c->wave_factor);
-  const Plan pn = plan_proj(L->I, L->D, max_rows, false, false, gs_dn, c->n_cu, c->wave_factor);
+  const Plan pd = plan_proj(L->D, L->I, max_rows, true, gs_in, c->n_cu, c->wave_factor);
+  const Plan pn = plan_proj(L->I, L->D, max_rows, false, gs_dn, c->n_cu, c->wave_factor);
   ProjArgs ad{};
   ad.grp = grp;
   ad.act = x_dev;
@@ -989,7 +1004,7 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
   if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
-      return launch_dual(pd.V, pd.P, pd.gen, dtype == I4MOE_DTYPE_BF16, sel, ad, pd.blocks, c->stream, t0, t1);
+      return launch_dual(pd.V, pd.P, pd.gen, sel, ad, pd.blocks, c->stream, t0, t1);
     });
   if (e == hipSuccess && sel) c->sel_pending = false;
   if (e == hipSuccess && !defer_down) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {

@@ -18,7 +18,8 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;                // 4 waves per workgroup
 
 // One uploaded int4 tensor as the kernels see it.  Rows are `row_bytes` apart (C/2 rounded
-// up to 16 B, pad bytes 0x88 i.e. weight 0); nibbles stay offset-binary (q encodes q - 8).
+// up to 16 B, pad bytes 0, i.e. weight 0); every nibble holds q - 8 in 4-bit two's complement
+// (the host's offset-binary q converted at upload).
 struct TensorDesc {
   const uint8_t *q;
   const float *s;      // [O][ng] scales
@@ -114,6 +115,17 @@ struct TakeArgs {
   int in_order;              // 1: one token, and every slot reduces its live rows in row order
 };
 
+// rmsnorm of S rows of D float32 values (row stride ld_x) times gamma, into S rows of the
+// experts' input dtype (row stride ld_out).
+struct NormArgs {
+  const float *x;
+  const float *gamma;        // [D]
+  void *out;                 // float32 or bf16 [S][ld_out]
+  int ld_x, ld_out, S, D;
+  int out_bf16;
+  float eps;
+};
+
 // Launchers (defined in the kernel translation units).  They return hipGetLastError().  With
 // t0/t1 non-null the launch records the kernel's own start and end into them
 // (hipExtLaunchKernel), so an event pair spans the kernel alone.
@@ -124,7 +136,7 @@ hipError_t launch_route(const RouteArgs &a, int parts, hipStream_t st, hipEvent_
 // sel: the dual projection first runs the selection of a.ra itself (one token, E <= 64,
 // non-generic spans) and publishes its route, group and row descriptors.
 bool dual_sel_ok(const RouteArgs &ra, bool gen);
-hipError_t launch_dual(int V, int P, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
+hipError_t launch_dual(int V, int P, bool gen, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                        hipEvent_t t1 = nullptr);
@@ -140,8 +152,9 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
 hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                          hipEvent_t t1 = nullptr);
 int rows16_blocks_per_cu(int P);
-int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb);  // resident 256-thread workgroups per CU
+int proj_blocks_per_cu(int V, int P, int NT, bool gen);  // resident 256-thread workgroups per CU
 hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBuf *dst, hipStream_t st);
+hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.
 constexpr int rows_per_step(int V, int P, int tensors, int budget) {

@@ -1,37 +1,42 @@
 // Grouped W4A16 projections for decode (gfx950, wave64, no MFMA: at S<=4 every int4 weight
-// feeds one to four FMAs, so the launch is bound by the HBM weight stream).
+// feeds one to four products, so the launch is bound by the HBM weight stream).
 //
 //   dual : h[row][o] = silu(G_e[o,:] . x_t) * (U_e[o,:] . x_t)     (gate/up fused, SiLU fused)
 //   down : y[row][o] = Dn_e[o,:] . h[row]
 //
 // for every group row (expert e, token t) and output row o.  Sources: the grouped
 // dual/silu/down decode path of the TC_W4A16 gating commit and the group-wise kernels of the
-// g4 commit ("Commit history of c/backend_cuda.cu"): the per-group scale is applied inside the
-// accumulation, gs = 0 is per-row, and per-row and group-wise tensors run in one launch.
+// g4 commit ("Commit history of c/backend_cuda.cu"): nibbles are converted offset->signed at
+// upload, the per-group scale is applied inside the accumulation, gs = 0 is per-row, and
+// per-row and group-wise tensors run in one launch.
 //
-// Work decomposition.  One wavefront owns a tile of consecutive output rows of one group row,
-// so the activation slice it needs is fixed: it is loaded once into registers and reused for
-// every row of the tile.  A row is covered by P passes of the whole wave; in pass p lane l
-// owns V consecutive weight dwords (8V columns) starting at dword p*64*V + l*V, fetched with
-// one V-dword load, so every pass of the wave reads 256*V contiguous bytes.
+// Arithmetic: integer dot products.  The weights sit on the device as signed nibbles (q - 8 in
+// two's complement, converted at upload).  The activation row a (x, or h for the down
+// projection) is written as 24-bit fixed point with one power-of-two scale per row:
+// X_c = rint(a_c * 2^E), with E chosen so that max |a_c| * 2^E < 2^22, and X_c is split into six
+// balanced base-16 digits (each in -8..7, X = sum_n d_n 16^n).  Digit n of eight consecutive
+// columns packs into one dword in the weight's own nibble order (a "digit plane"), so
+// v_dot8_i32_i4 of a weight dword and a plane dword is sum_k (q_k - 8) d_{n,k}, exactly, and six
+// of them give sum_k (q_k - 8) X_k: six instructions per eight weights, no unpacking.  Each
+// lane adds its digit sums in integers, joins them into one float (one rounding), applies the
+// row or group scale, and the lanes are summed in a fixed DPP order; the row's 2^-E comes out
+// after that sum.  The only approximation is the rounding of a to 22-23 significant bits
+// relative to the row's largest |a| (relative error <= 2^-22 of that largest value per element).
 //
-// Dequantisation.  Nibbles stay offset-binary.  For a weight dword w the masks
-// w & 0x0F0F0F0F and w & 0xF0F0F0F0 put the even-column nibbles q and 16 * (odd-column
-// nibbles) in the four bytes, which v_cvt_f32_ubyte{0..3} convert directly; the odd-column
-// activations are pre-divided by 16 (exact) so both give q * x.  The offset is folded in once
-// per span: sum (q - 8) x = sum q x - 8 sum x, with the span sums of x precomputed with the
-// slice.  That is 2.25 VALU ops per weight.  Each span accumulator is multiplied by its
-// scale (the row scale, or the span's group scale when gs is a multiple of 8V), then the
-// lane partials are summed across the wave with DPP in a fixed pattern (deterministic).
-// Group sizes that split a span fall back to a per-byte path.
+// Work decomposition.  One wavefront owns a tile of consecutive output rows of one group row.
+// A row is covered by P passes of the whole wave; in pass p lane l owns V consecutive weight
+// dwords (8V columns) starting at dword p*64*V + l*V, fetched with one V-dword load, so every
+// pass of the wave reads 256*V contiguous bytes.  The workgroup stages the activation row's
+// digit planes in LDS once; every pass reads the lane's planes (six V-dword LDS reads, shared
+// by the step's rows and tensors).
 //
 // Kernels here:
-//   k_proj<V, P, NT, GEN, XB, SEL>  the dual (NT = 2) and long-row down (NT = 1) projections;
-//                                   SEL runs a one-token expert selection first (select.h)
-//   k_rows16<P>                     down projection of short rows, 16 lanes per row
-//   k_down_take<P, W>               down projection of short rows fused with the take (one
-//                                   token, one issue): the weighted, fixed-order sum of the
-//                                   rows is added to the residual in the same launch
+//   k_proj<V, P, NT, GEN, SEL>   the dual (NT = 2) and long-row down (NT = 1) projections;
+//                                SEL runs a one-token expert selection first (select.h)
+//   k_rows16<P>                  down projection of short rows, 16 lanes per row
+//   k_down_take<P>               down projection of short rows fused with the take (one token,
+//                                one issue): the weighted, fixed-order sum of the rows is added to
+//                                the residual in the same launch
 #include <hip/hip_ext.h>
 
 #include "select.h"
@@ -42,67 +47,16 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Keep the compiler from folding the byte masks into each conversion (which would cost a
-// shift+mask per nibble instead of one mask per four nibbles).
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-__device__ __forceinline__ float ub0(uint32_t a) { return (float)(a & 0xffu); }
-__device__ __forceinline__ float ub1(uint32_t a) { return (float)((a >> 8) & 0xffu); }
-__device__ __forceinline__ float ub2(uint32_t a) { return (float)((a >> 16) & 0xffu); }
-__device__ __forceinline__ float ub3(uint32_t a) { return (float)(a >> 24); }
-
-// Eight columns of one weight dword: xe = activations of the even columns, xo = activations
-// of the odd columns divided by 16.
-__device__ __forceinline__ float dot8(uint32_t w, const float (&xe)[4], const float (&xo)[4], float acc) {
-  const uint32_t lo = opaque(w & 0x0F0F0F0Fu);
-  const uint32_t hi = opaque(w & 0xF0F0F0F0u);
-  acc = fmaf(ub0(lo), xe[0], acc);
-  acc = fmaf(ub1(lo), xe[1], acc);
-  acc = fmaf(ub2(lo), xe[2], acc);
-  acc = fmaf(ub3(lo), xe[3], acc);
-  acc = fmaf(ub0(hi), xo[0], acc);
-  acc = fmaf(ub1(hi), xo[1], acc);
-  acc = fmaf(ub2(hi), xo[2], acc);
-  acc = fmaf(ub3(hi), xo[3], acc);
-  return acc;
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) {
-  bf16x2 r;
-  __builtin_memcpy(&r, &u, 4);
-  return r;
-}
-
-// Eight columns of one weight dword against packed bf16 activation pairs.  Nibble k (column
-// 8d+k) sits at bits 4k..4k+3.  t0 = w & 0x0F0F0F0F isolates nibbles 0,2,4,6 in the low bits
-// of its bytes, t1 = (w >> 4) & 0x0F0F0F0F nibbles 1,3,5,7; one v_perm_b32 then puts two of
-// them under the bf16 high byte 0x43, giving the exact bf16 values 128 + q.  v_dot2_f32_bf16
-// takes (128 + q_a) x_a + (128 + q_b) x_b into the f32 accumulator; the pairs are (0,4),
-// (2,6), (1,5), (3,7) and the activations are packed to match.  The 128 + 8 offset comes out
-// once per span through the initial value -136 * sum(x).  7 integer ops + 4 dot2 per 8 weights.
-__device__ __forceinline__ float dot8_bf16(uint32_t w, const uint32_t (&xp)[4], float acc) {
-  const uint32_t t0 = w & 0x0F0F0F0Fu;
-  const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t hi = 0x43434343u;
-  const uint32_t p04 = __builtin_amdgcn_perm(hi, t0, 0x04020400u);
-  const uint32_t p26 = __builtin_amdgcn_perm(hi, t0, 0x04030401u);
-  const uint32_t p15 = __builtin_amdgcn_perm(hi, t1, 0x04020400u);
-  const uint32_t p37 = __builtin_amdgcn_perm(hi, t1, 0x04030401u);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p04), as_bf16x2(xp[0]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p26), as_bf16x2(xp[1]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p15), as_bf16x2(xp[2]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(p37), as_bf16x2(xp[3]), acc, false);
-  return acc;
-}
+constexpr int kPlanes = 6;                 // base-16 digits of the 24-bit fixed-point activations
+constexpr uint32_t kDigitBias = 0x888888u; // sum_n 8 * 16^n: shifts every digit into 0..15
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
 // Sum over the 64 lanes in a fixed order; the total lands in lane 63 and is returned
@@ -117,64 +71,193 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+// Largest value over the 64 lanes, returned wave-uniform (lanes a step does not reach keep
+// their own value, and max with 0 leaves it unchanged).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1, 0xF>(v));
+  v = max(v, dpp_u<0x4E, 0xF>(v));
+  v = max(v, dpp_u<0x141, 0xF>(v));
+  v = max(v, dpp_u<0x140, 0xF>(v));
+  v = max(v, dpp_u<0x142, 0xA>(v));
+  v = max(v, dpp_u<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 
-// Eight activations of columns c0..c0+7 (zero past C).  f32 rows are 8-byte aligned and bf16
-// rows 4-byte aligned because C is even.
-__device__ __forceinline__ void load8(const void *act, int bf16, size_t row_off, int c0, int C, float (&t)[8]) {
-  if (c0 + 8 <= C) {
-    if (bf16) {
-      const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(act) + row_off + c0);
+// ---- Activation digit planes --------------------------------------------------------------
+
+// |a| as bits: for non-negative floats the integer order is the float order.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+// E for a row whose largest |a| has the bit pattern m: |a| < 2^(e - 126) for the biased exponent
+// e = m >> 23, so max |a| * 2^E < 2^22 with E = 148 - e (a zero row gets E = 148 and all-zero
+// digits).
+__device__ __forceinline__ int row_exponent(uint32_t m) { return 148 - (int)(m >> 23); }
+
+// The six digits of X = rint(a * 2^E), |X| <= 2^22, packed in nibbles 0..5: adding the bias turns
+// the balanced digits d_n into d_n + 8 in 0..15, and the xor turns those into the digits' 4-bit
+// two's-complement codes.
+__device__ __forceinline__ uint32_t digits24(float a, int E) {
+  const int X = (int)__builtin_rintf(__builtin_ldexpf(a, E));
+  return ((uint32_t)X + kDigitBias) ^ kDigitBias;
+}
+
+// 8 x 8 nibble transpose: on return nibble k of z[n] is what nibble n of z[k] was.  Three block
+// swaps: 4 x 4 blocks (bytes 2-3 of z[k] with bytes 0-1 of z[k+4]), 2 x 2 blocks inside those
+// (byte pairs of z[k] and z[k+2]), then single nibbles (high nibbles of z[k] with low nibbles of
+// z[k+1]).
+__device__ __forceinline__ void nibble_transpose8(uint32_t (&z)[8]) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t u = p[k];
-        t[2 * k] = bf16_to_f32(u & 0xffffu);
-        t[2 * k + 1] = bf16_to_f32(u >> 16);
-      }
-    } else {
-      const float2 *p = reinterpret_cast<const float2 *>(static_cast<const float *>(act) + row_off + c0);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t a = z[k], b = z[k + 4];
+    z[k] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    z[k + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float2 u = p[k];
-        t[2 * k] = u.x;
-        t[2 * k + 1] = u.y;
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int k = (i & 1) + 4 * (i >> 1);  // 0, 1, 4, 5
+    const uint32_t a = z[k], b = z[k + 2];
+    z[k] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+    z[k + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    const uint32_t t = ((z[k] >> 4) ^ z[k + 1]) & 0x0F0F0F0Fu;
+    z[k + 1] ^= t;
+    z[k] ^= t << 4;
+  }
+}
+
+// One digit-plane position: the eight columns 8j .. 8j+7 of the row, in a thread's registers.
+// Loads are 4-byte (f32 columns, or bf16 column pairs), clamped into the row and unconditional,
+// so their count never depends on the data; columns past C read as zero.
+__device__ __forceinline__ void load_position(float (&v)[8], const void *act, int bf16, size_t row_off, int j,
+                                              int positions, int C) {
+  const bool ok = j < positions;
+  if (bf16) {
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(act) + row_off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 8 * j + 2 * k;  // C is even: a pair is whole or past the row
+      const bool in = ok && c < C;
+      const uint32_t u = row[in ? c / 2 : 0];
+      v[2 * k] = in ? __uint_as_float(u << 16) : 0.f;
+      v[2 * k + 1] = in ? __uint_as_float(u & 0xffff0000u) : 0.f;
     }
   } else {
+    const float *row = static_cast<const float *>(act) + row_off;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t[k] = 0.f;
-    for (int c = c0; c < C && c < c0 + 8; ++c) {
-      t[c - c0] = bf16 ? bf16_to_f32(static_cast<const uint16_t *>(act)[row_off + c])
-                       : static_cast<const float *>(act)[row_off + c];
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * j + k;
+      const bool in = ok && c < C;
+      const float x = row[in ? c : 0];
+      v[k] = in ? x : 0.f;
     }
   }
 }
 
-// Per-byte path for group sizes that split a lane's span (any even gs): each byte's two
-// columns share one group because gs is even.
+// The planes of one position from its eight values.
+__device__ __forceinline__ void position_planes(uint32_t (&z)[8], const float (&v)[8], int E) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) z[k] = digits24(v[k], E);
+  nibble_transpose8(z);
+}
+
+// Workgroup staging of one activation row as digit planes: planes[n * positions + j] holds digit
+// n of columns 8j .. 8j+7 (zero past the row).  `v` holds the thread's positions
+// j = threadIdx.x + m * kBlock, loaded earlier (load_position).  All threads of the workgroup
+// call it; two barriers.  Returns E.
+template <int NPOS>
+__device__ __forceinline__ int stage_planes(uint32_t *planes, int positions, const float (&v)[NPOS][8],
+                                            uint32_t *s_max) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, abs_bits(v[i][k]));
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  const int E = row_exponent(m);
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i) {
+    const int j = threadIdx.x + i * kBlock;
+    if (j < positions) {
+      uint32_t z[8];
+      position_planes(z, v[i], E);
+#pragma unroll
+      for (int n = 0; n < kPlanes; ++n) planes[n * positions + j] = z[n];
+    }
+  }
+  __syncthreads();
+  return E;
+}
+
+// The lane's planes of one span: V dwords at position d0 of each plane.
+template <int V>
+__device__ __forceinline__ void read_planes(uint32_t (&X)[kPlanes][V], const uint32_t *planes, int positions, int d0) {
+#pragma unroll
+  for (int n = 0; n < kPlanes; ++n) {
+    const uint32_t *p = planes + n * positions + d0;
+    if constexpr (V == 4) {
+      const u32x4 q = *reinterpret_cast<const u32x4 *>(p);
+      X[n][0] = q.x; X[n][1] = q.y; X[n][2] = q.z; X[n][3] = q.w;
+    } else if constexpr (V == 2) {
+      const u32x2 q = *reinterpret_cast<const u32x2 *>(p);
+      X[n][0] = q.x; X[n][1] = q.y;
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) X[n][v] = p[v];
+    }
+  }
+}
+
+// sum_n acc[n] * 16^n as a float with one rounding.  Each digit sum is at most 512 per weight
+// dword in magnitude, so for up to 16 dwords per lane the two halves stay below 2^22 and convert
+// exactly.
+__device__ __forceinline__ float join_digits(const int (&acc)[kPlanes]) {
+  const int hi = (acc[5] * 16 + acc[4]) * 16 + acc[3];
+  const int lo = (acc[2] * 16 + acc[1]) * 16 + acc[0];
+  return fmaf((float)hi, 4096.f, (float)lo);
+}
+
+// Signed value of nibble k of w.
+__device__ __forceinline__ int nibble_s(uint32_t w, int k) { return ((int)(w << (28 - 4 * k))) >> 28; }
+
+// Per-byte path for group sizes that split a lane's span (any even gs): each column's integer
+// activation is rebuilt from the planes and takes its own group's scale.  Only odd layouts
+// (gs not a multiple of 8) take it, so it is written for size, not speed: the column loop stays
+// rolled.
+__device__ __noinline__ float dword_dot_generic(const float *srow, int gs, int C, uint32_t w, const uint32_t *planes,
+                                                int positions, int d) {
+  uint32_t X[kPlanes];
+#pragma unroll
+  for (int n = 0; n < kPlanes; ++n) X[n] = planes[n * positions + d];
+  float acc = 0.f;
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    const int col = 8 * d + k;
+    if (col < C) {
+      int x = 0;
+#pragma unroll
+      for (int n = kPlanes - 1; n >= 0; --n) x = x * 16 + nibble_s(X[n], k);
+      acc = fmaf(srow[col / gs], (float)(nibble_s(w, k) * x), acc);
+    }
+  }
+  return acc;
+}
+
 template <int V, int P>
-__device__ float row_dot_generic(const TensorDesc &T, int o, const uint32_t (&w)[P][V], const float (&xe)[P][V][4],
-                                 const float (&xo)[P][V][4], int lane, int RD) {
+__device__ float row_dot_generic(const TensorDesc &T, int o, const uint32_t (&w)[P][V], const uint32_t *planes,
+                                 int positions, int lane, int RD) {
   float acc = 0.f;
   const float *srow = T.s + (size_t)o * T.ng;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int ds = p * 64 * V + lane * V;
-    if (ds >= RD) continue;
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int d = ds + v;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int col = 8 * d + 2 * k;
-        if (col < T.C) {
-          const float s = srow[col / T.gs];
-          const float lo = (float)(int)((w[p][v] >> (8 * k)) & 15u) - 8.f;
-          const float hi = (float)(int)((w[p][v] >> (8 * k + 4)) & 15u) - 8.f;
-          acc = fmaf(s, fmaf(lo, xe[p][v][k], hi * (16.f * xo[p][v][k])), acc);
-        }
-      }
-    }
+    for (int v = 0; v < V; ++v)
+      if (ds + v < RD) acc += dword_dot_generic(srow, T.gs, T.C, w[p][v], planes, positions, ds + v);
   }
   return acc;
 }
@@ -191,131 +274,6 @@ __device__ __forceinline__ TensorDesc ld_desc(const TensorDesc I4MOE_AS4 &d) {
   t.ng = d.ng;
   t.live = d.live;
   return t;
-}
-
-// Activation slice of one lane.  f32 path: x of the even columns and x/16 of the odd columns,
-// offset term -8 * sum(x) per span.  bf16 path: packed pairs (x_k, x_{k+4}) in the order the
-// weight pairs are built, offset term -136 * sum(x) per span.
-template <int V, int P, bool XB>
-struct Act {
-  float xe[P][V][4], xo[P][V][4];
-  float xm[P];
-};
-template <int V, int P>
-struct Act<V, P, true> {
-  uint32_t xp[P][V][4];
-  float xm[P];
-};
-
-// Words of the staged activation row: the row padded with zeros to the columns all lanes of
-// all passes cover (8V columns per lane per pass); bf16 pairs for XB, f32 otherwise.
-template <int V, int P, bool XB>
-constexpr int act_words() {
-  return XB ? P * 64 * V * 4 : P * 64 * V * 8;
-}
-
-// The workgroup copies its activation row into LDS with coalesced 4-byte loads (every wave of
-// the workgroup works on the same group row).  A lane's slice is contiguous in the row but
-// 16V (bf16) or 32V (f32) bytes from its neighbour's, so reading it from global memory directly
-// would touch a separate cache line per lane and load; LDS takes that access pattern for free.
-// The copy is split in two so the kernel can issue these loads before its first weight loads:
-// the LDS writes then wait only for the (older) activation loads, not for weights in flight.
-template <int V, int P, bool XB>
-constexpr int stage_words() {
-  return act_words<V, P, XB>() / kBlock;
-}
-
-template <bool XB, int N>
-__device__ __forceinline__ void stage_load(uint32_t (&xs)[N], const void *act, int bf16, size_t row_off, int C) {
-  if (XB) {
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(act) + row_off);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int w = threadIdx.x + i * kBlock;
-      xs[i] = row[2 * w < C ? w : 0];
-    }
-  } else if (bf16) {
-    const uint16_t *row = static_cast<const uint16_t *>(act) + row_off;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int w = threadIdx.x + i * kBlock;
-      xs[i] = row[w < C ? w : 0];
-    }
-  } else {
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const float *>(act) + row_off);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int w = threadIdx.x + i * kBlock;
-      xs[i] = row[w < C ? w : 0];
-    }
-  }
-}
-
-// Zeros past the row's C columns; bf16 values widened to f32 bits except for XB (pairs).
-template <bool XB, int N>
-__device__ __forceinline__ void stage_store(uint32_t *lds, const uint32_t (&xs)[N], int bf16, int C) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int w = threadIdx.x + i * kBlock;
-    uint32_t v;
-    if (XB)
-      v = 2 * w < C ? xs[i] : 0u;
-    else
-      v = w < C ? (bf16 ? xs[i] << 16 : xs[i]) : 0u;
-    lds[w] = v;
-  }
-}
-
-// The lane's slice of the staged row: dword spans p * LR * V + lane * V + [0, V) for LR lanes
-// per row.
-template <int V, int P, bool XB, int LR = kWave>
-__device__ __forceinline__ void read_act(uint32_t (&raw)[P][V][XB ? 4 : 8], const uint32_t *lds, int lane) {
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int d = p * LR * V + lane * V + v;
-      if constexpr (XB) {
-        const u4 q = *reinterpret_cast<const u4 *>(lds + 4 * d);
-        raw[p][v][0] = q.x; raw[p][v][1] = q.y; raw[p][v][2] = q.z; raw[p][v][3] = q.w;
-      } else {
-        const u4 q0 = *reinterpret_cast<const u4 *>(lds + 8 * d);
-        const u4 q1 = *reinterpret_cast<const u4 *>(lds + 8 * d + 4);
-        raw[p][v][0] = q0.x; raw[p][v][1] = q0.y; raw[p][v][2] = q0.z; raw[p][v][3] = q0.w;
-        raw[p][v][4] = q1.x; raw[p][v][5] = q1.y; raw[p][v][6] = q1.z; raw[p][v][7] = q1.w;
-      }
-    }
-  }
-}
-
-template <int V, int P, bool XB>
-__device__ __forceinline__ void finish_act(Act<V, P, XB> &A, const uint32_t (&raw)[P][V][XB ? 4 : 8]) {
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    float span = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      if constexpr (XB) {
-        const uint32_t *u = raw[p][v];  // u[k] holds columns 2k (low half) and 2k+1 (high half)
-        A.xp[p][v][0] = (u[0] & 0xffffu) | (u[2] << 16);          // columns 0, 4
-        A.xp[p][v][1] = (u[1] & 0xffffu) | (u[3] << 16);          // columns 2, 6
-        A.xp[p][v][2] = (u[0] >> 16) | (u[2] & 0xffff0000u);      // columns 1, 5
-        A.xp[p][v][3] = (u[1] >> 16) | (u[3] & 0xffff0000u);      // columns 3, 7
-#pragma unroll
-        for (int k = 0; k < 4; ++k) span += bf16_to_f32(u[k] & 0xffffu) + bf16_to_f32(u[k] >> 16);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float e = __uint_as_float(raw[p][v][2 * k]), o = __uint_as_float(raw[p][v][2 * k + 1]);
-          A.xe[p][v][k] = e;
-          A.xo[p][v][k] = o * 0.0625f;
-          span += e + o;
-        }
-      }
-    }
-    A.xm[p] = (XB ? -136.f : -8.f) * span;
-  }
 }
 
 // Weights (and their scales) of one pipeline step: RB consecutive rows of NT tensors.
@@ -351,7 +309,7 @@ __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t r, int off, uin
 // buffer range, so its loads return zeros and touch no memory.  Keeping the issue pattern
 // identical on every path keeps the wait counts exact (a load issued on one path only would
 // make the compiler wait for all loads in flight).  A span past the row's padded bytes reads
-// zeros the same way; its activations are zero, so it adds nothing.
+// zeros the same way (weight 0).
 template <int V, int P, int NT, int RB>
 __device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
                                           int o, int o_end, int lane) {
@@ -373,34 +331,67 @@ __device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDe
 }
 
 // Dot products of one step's rows, reduced over the wave; lane (o - o_begin + r) keeps row
-// o + r's result, and the tile's results leave in one coalesced store at the end.
-template <int V, int P, int NT, int RB, bool GEN, bool XB>
+// o + r's result, and the tile's results leave in one coalesced store at the end.  Per pass the
+// lane's planes are read once for every row and tensor of the step.  A group-wise tensor joins
+// its digit sums and applies the span's group scale after every pass; a per-row tensor joins
+// once, after the last pass, and applies the row scale.
+template <int V, int P, int NT, int RB, bool GEN>
 __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT],
-                                             const bool (&gen)[NT], const Act<V, P, XB> &A, int o, int o_end,
-                                             int lane, int RD, int o_begin, float &outv) {
+                                             const bool (&grp)[NT], const bool (&gen)[NT], const uint32_t *planes,
+                                             int positions, int E, int o, int o_end, int lane, int RD, int o_begin,
+                                             float &outv) {
+  int acc[NT][RB][kPlanes];
+  float fa[NT][RB];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      fa[n][r] = 0.f;
+#pragma unroll
+      for (int d = 0; d < kPlanes; ++d) acc[n][r][d] = 0;
+    }
+  // The planes of pass p + 1 are read while pass p computes; a scheduling barrier after each
+  // pass keeps the compiler from hoisting every pass's reads to the top (which would hold all P
+  // passes' planes in registers at once).
+  uint32_t X[2][kPlanes][V];
+  read_planes<V>(X[0], planes, positions, lane * V);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (p + 1 < P) read_planes<V>(X[(p + 1) & 1], planes, positions, (p + 1) * 64 * V + lane * V);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (gen[n]) continue;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+#pragma unroll
+          for (int d = 0; d < kPlanes; ++d)
+            acc[n][r][d] = __builtin_amdgcn_sdot8((int)st.w[n][r][p][v], (int)X[p & 1][d][v], acc[n][r][d], false);
+        }
+        if (grp[n]) {
+          fa[n][r] = fmaf(join_digits(acc[n][r]), st.s[n][r][p], fa[n][r]);
+#pragma unroll
+          for (int d = 0; d < kPlanes; ++d) acc[n][r][d] = 0;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     float sum[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      float acc = 0.f;
-      if (!gen[n]) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          float ap = A.xm[p];
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-            if constexpr (XB)
-              ap = dot8_bf16(st.w[n][r][p][v], A.xp[p][v], ap);
-            else
-              ap = dot8(st.w[n][r][p][v], A.xe[p][v], A.xo[p][v], ap);
-          }
-          acc = fmaf(st.s[n][r][p], ap, acc);
+      float a = fa[n][r];
+      if (gen[n]) {
+        if constexpr (GEN) {
+          if (o + r < o_end) a = row_dot_generic<V, P>(T[n], o + r, st.w[n][r], planes, positions, lane, RD);
         }
-      } else if constexpr (GEN && !XB) {
-        if (o + r < o_end) acc = row_dot_generic<V, P>(T[n], o + r, st.w[n][r], A.xe, A.xo, lane, RD);
+      } else if (!grp[n]) {
+        a = join_digits(acc[n][r]) * st.s[n][r][0];
       }
-      sum[n] = wave_sum(acc);
+      sum[n] = __builtin_ldexpf(wave_sum(a), -E);
     }
     float res = sum[0];
     if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
@@ -408,17 +399,25 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
   }
 }
 
-// NT = 2: dual gate/up with the SiLU-gated product; NT = 1: down projection.  XB: bf16
-// activations through v_dot2_f32_bf16 (dual only).  SEL (dual, one token, E <= 64): every
-// workgroup first runs the expert selection itself from the router's finished scores, so no
-// selection launch sits between the router GEMV and the experts; workgroup 0 publishes the
-// route and group records, the first workgroup of each row that row's descriptor (for the
-// down projection, the take and the taps).  A tile holds at most 64 rows (one result per
-// lane).
-template <int V, int P, int NT, bool GEN, bool XB, bool SEL = false>
+// Positions (dwords) of the staged row for V-dword spans in P passes.
+template <int V, int P>
+constexpr int proj_positions() {
+  return P * 64 * V;
+}
+
+// NT = 2: dual gate/up with the SiLU-gated product; NT = 1: down projection.  SEL (dual, one
+// token, E <= 64): every workgroup first runs the expert selection itself from the router's
+// finished scores, so no selection launch sits between the router GEMV and the experts;
+// workgroup 0 publishes the route and group records, the first workgroup of each row that row's
+// descriptor (for the down projection, the take and the taps).  A tile holds at most 64 rows
+// (one result per lane).
+template <int V, int P, int NT, bool GEN, bool SEL = false>
 __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   constexpr int RB = rows_per_step(V, P, NT, 16);
-  extern __shared__ uint32_t s_act[];
+  constexpr int POS = proj_positions<V, P>();
+  constexpr int NPOS = (POS + kBlock - 1) / kBlock;
+  extern __shared__ uint32_t s_planes[];  // [kPlanes][POS]
+  __shared__ uint32_t s_max[kBlock / kWave];
   const int lane = threadIdx.x & 63;
   // Every workgroup works on one group row; its four waves take consecutive tiles.  The wave
   // index is uniform by construction and readfirstlane lets the compiler keep it (and the row,
@@ -530,12 +529,13 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   const int C = a.C;
   const int RD = (C + 7) >> 3;
   int gi[NT][P];
-  bool gen[NT];
+  bool gen[NT], grp[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
 #pragma unroll
     for (int p = 0; p < P; ++p) gi[n][p] = 0;
-    if (T[n].ng > 1) {
+    grp[n] = T[n].ng > 1;
+    if (grp[n]) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int ds = p * 64 * V + lane * V;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
       }
     }
     // GEN launches carry the per-byte path; others hold only tensors whose groups align with spans.
-    gen[n] = GEN && T[n].ng > 1 && (T[n].gs % (8 * V)) != 0;
+    gen[n] = GEN && grp[n] && (T[n].gs % (8 * V)) != 0;
   }
 
   const int o_begin = tile * a.tile_rows;
@@ -551,35 +551,33 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   const bool work = o_begin < o_end;
 
   // Activation loads first, then the first two steps of weights (empty ranges for a wave
-  // without rows); the activation row goes to LDS as soon as its own loads have landed.
+  // without rows); the digit planes are built once the activation loads have landed.
   // Scheduling barriers keep the issue order: the wait counts below assume it.
-  uint32_t xs[stage_words<V, P, XB>()];
-  stage_load<XB>(xs, a.act, a.act_bf16, (size_t)arow * a.act_ld, C);
+  float xv[NPOS][8];
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i)
+    load_position(xv[i], a.act, a.act_bf16, (size_t)arow * a.act_ld, threadIdx.x + i * kBlock, POS, C);
   __builtin_amdgcn_sched_barrier(0);
   Step<V, P, NT, RB> b0, b1;
   load_step<V, P, NT, RB>(b0, T, gi, o_begin, o_end, lane);
   __builtin_amdgcn_sched_barrier(0);
   load_step<V, P, NT, RB>(b1, T, gi, o_begin + RB, o_end, lane);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<XB>(s_act, xs, a.act_bf16, C);
-  __syncthreads();
+  const int E = stage_planes<NPOS>(s_planes, POS, xv, s_max);
   if (!work) {
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  uint32_t raw[P][V][XB ? 4 : 8];
-  read_act<V, P, XB>(raw, s_act, lane);
-  Act<V, P, XB> A;
-  finish_act<V, P, XB>(A, raw);
 
   // Two-stage pipeline: while one step computes, the other step's weights are in flight.  The
   // loop has one exit, at the bottom; the last pass issues loads of empty ranges.
   float outv = 0.f;
   int o = o_begin;
   do {
-    compute_step<V, P, NT, RB, GEN, XB>(b0, T, gen, A, o, o_end, lane, RD, o_begin, outv);
+    compute_step<V, P, NT, RB, GEN>(b0, T, grp, gen, s_planes, POS, E, o, o_end, lane, RD, o_begin, outv);
     load_step<V, P, NT, RB>(b0, T, gi, o + 2 * RB, o_end, lane);
-    if (o + RB < o_end) compute_step<V, P, NT, RB, GEN, XB>(b1, T, gen, A, o + RB, o_end, lane, RD, o_begin, outv);
+    if (o + RB < o_end)
+      compute_step<V, P, NT, RB, GEN>(b1, T, grp, gen, s_planes, POS, E, o + RB, o_end, lane, RD, o_begin, outv);
     load_step<V, P, NT, RB>(b1, T, gi, o + 3 * RB, o_end, lane);
     o += 2 * RB;
   } while (o < o_end);
@@ -590,7 +588,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
 // ---- Short rows (the down projection, C <= 2048 columns): 16 lanes per row, so one wave
 // instruction covers four rows.  A row's dot product is then summed over 16 lanes (four DPP
 // steps, all four rows at once) instead of 64, and no lane idles when a row is shorter than
-// 64 lanes x 16 bytes.  f32 activations, per-row or span-aligned group scales.
+// 64 lanes x 16 bytes.  Per-row or span-aligned (gs a multiple of 32) group scales.
 constexpr int kLR = 16;                  // lanes per row
 constexpr int kGR = kWave / kLR;         // rows per wave instruction
 
@@ -623,31 +621,42 @@ __device__ __forceinline__ void load_step16(Step16<P> &st, __amdgpu_buffer_rsrc_
   }
 }
 
-// LDS word of column pair-half `half` of dword span (p, v) for lane li: the 16 lanes' 16-byte
-// chunks of one (p, v, half) are contiguous, so each read is conflict-free.
-__device__ __forceinline__ int act16_word(int p, int v, int half, int li) { return (((p * 4 + v) * 2 + half) * kLR + li) * 4; }
-
-// The activations are read from LDS per step (two ds_read_b128 per weight dword) rather than
-// held in registers: a 96-column slice would take 96 VGPRs, and with it the kernel fits
-// three waves per SIMD instead of six.  Odd columns are staged already divided by 16.
+// Positions of a short row staged for P passes of 16 lanes x 4 dwords.
 template <int P>
-__device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32_t *lds, int li, const float (&xm)[P],
+constexpr int rows16_positions() {
+  return P * kLR * 4;
+}
+
+// One step's four rows: the lane's digit sums over its P spans, joined (per pass for group-wise
+// scales, once for a per-row scale), summed over the row's 16 lanes; lane (o - o_begin + g)
+// keeps row o + g.
+template <int P>
+__device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32_t *planes, int li, bool grp, int E,
                                                int o, int o_begin, int lane, float &outv) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  float acc = 0.f;
+  constexpr int POS = rows16_positions<P>();
+  int acc[kPlanes];
+#pragma unroll
+  for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
+  float fa = 0.f;
+  uint32_t X[2][kPlanes][4];
+  read_planes<4>(X[0], planes, POS, li * 4);
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    float ap = xm[p];
+    if (p + 1 < P) read_planes<4>(X[(p + 1) & 1], planes, POS, (p + 1) * kLR * 4 + li * 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const f4 q0 = *reinterpret_cast<const f4 *>(lds + act16_word(p, v, 0, li));
-      const f4 q1 = *reinterpret_cast<const f4 *>(lds + act16_word(p, v, 1, li));
-      const float xe[4] = {q0.x, q0.z, q1.x, q1.z}, xo[4] = {q0.y, q0.w, q1.y, q1.w};
-      ap = dot8(st.w[p][v], xe, xo, ap);
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int d = 0; d < kPlanes; ++d)
+        acc[d] = __builtin_amdgcn_sdot8((int)st.w[p][v], (int)X[p & 1][d][v], acc[d], false);
+    if (grp) {
+      fa = fmaf(join_digits(acc), st.s[p], fa);
+#pragma unroll
+      for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
     }
-    acc = fmaf(st.s[p], ap, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const float sum = row16_sum(acc);
+  if (!grp) fa = join_digits(acc) * st.s[0];
+  const float sum = __builtin_ldexpf(row16_sum(fa), -E);
 #pragma unroll
   for (int g = 0; g < kGR; ++g) {
     const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), g * kLR));
@@ -655,46 +664,13 @@ __device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32
   }
 }
 
-// Stage column w (value x; 0 past the row) of a short row: odd columns divided by 16 (exact),
-// as dot8 takes them.
-__device__ __forceinline__ void stage16(uint32_t *lds, int w, float x) {
-  const int d = w >> 3, j = w & 7;  // dword span d = p * 64 + li * 4 + v, column j in it
-  lds[act16_word(d >> 6, d & 3, j >> 2, (d >> 2) & (kLR - 1)) + (j & 3)] = __float_as_uint((w & 1) ? x * 0.0625f : x);
-}
-
-// The same for columns c4 .. c4 + 3 (c4 a multiple of 4): one 16-byte LDS write.
-__device__ __forceinline__ void stage16x4(uint32_t *lds, int c4, float4 x) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  const int d = c4 >> 3;
-  f4 v = {x.x, x.y * 0.0625f, x.z, x.w * 0.0625f};
-  *reinterpret_cast<f4 *>(lds + act16_word(d >> 6, d & 3, (c4 & 7) >> 2, (d >> 2) & (kLR - 1))) = v;
-}
-
-// Offset term of each of the lane's spans: -8 * (sum of its activations), summed in
-// column-pair order.
-template <int P>
-__device__ __forceinline__ void span_offsets16(float (&xm)[P], const uint32_t *lds, int li) {
-  constexpr int V = 4;
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    float span = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = 2 * k;
-        span += __uint_as_float(lds[act16_word(p, v, j >> 2, li) + (j & 3)]) +
-                16.f * __uint_as_float(lds[act16_word(p, v, (j + 1) >> 2, li) + ((j + 1) & 3)]);
-      }
-    }
-    xm[p] = -8.f * span;
-  }
-}
-
 template <int P>
 __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   constexpr int V = 4;
-  extern __shared__ uint32_t s_act[];
+  constexpr int POS = rows16_positions<P>();
+  static_assert(POS <= kBlock, "one staged position per thread");
+  extern __shared__ uint32_t s_planes[];  // [kPlanes][POS]
+  __shared__ uint32_t s_max[kBlock / kWave];
   const int lane = threadIdx.x & 63;
   const int li = lane & (kLR - 1), g = lane / kLR;
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -710,11 +686,12 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
 
   const int C = a.C;
   const int RD = (C + 7) >> 3;
+  const bool grp = T.ng > 1;
   int gi[P], woff[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int ds = p * kLR * V + li * V;
-    gi[p] = (T.ng > 1 && ds < RD) ? (8 * ds) / T.gs : 0;
+    gi[p] = (grp && ds < RD) ? (8 * ds) / T.gs : 0;
     woff[p] = ds < RD ? 4 * ds : -1;
   }
   const int o_begin = tile * a.tile_rows;
@@ -724,33 +701,26 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
   const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
 
-  uint32_t xs[stage_words<V, P, false>() * kLR / kWave];
-  stage_load<false>(xs, a.act, 0, (size_t)jr * a.act_ld, C);
+  float xv[1][8];
+  load_position(xv[0], a.act, 0, (size_t)jr * a.act_ld, threadIdx.x, POS, C);
   __builtin_amdgcn_sched_barrier(0);
   Step16<P> b0, b1;
   load_step16<P>(b0, wr, sr, T, woff, gi, o_begin, g);
   __builtin_amdgcn_sched_barrier(0);
   load_step16<P>(b1, wr, sr, T, woff, gi, o_begin + kGR, g);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(xs) / sizeof(xs[0])); ++i) {
-    const int w = threadIdx.x + i * kBlock;  // column
-    stage16(s_act, w, w < C ? __uint_as_float(xs[i]) : 0.f);
-  }
-  __syncthreads();
+  const int E = stage_planes<1>(s_planes, POS, xv, s_max);
   if (!work) {
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
-  float xm[P];
-  span_offsets16<P>(xm, s_act, li);
 
   float outv = 0.f;
   int o = o_begin;
   do {
-    compute_step16<P>(b0, s_act, li, xm, o, o_begin, lane, outv);
+    compute_step16<P>(b0, s_planes, li, grp, E, o, o_begin, lane, outv);
     load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
-    if (o + kGR < o_end) compute_step16<P>(b1, s_act, li, xm, o + kGR, o_begin, lane, outv);
+    if (o + kGR < o_end) compute_step16<P>(b1, s_planes, li, grp, E, o + kGR, o_begin, lane, outv);
     load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
     o += 2 * kGR;
   } while (o < o_end);
@@ -768,33 +738,32 @@ const void *rows16_ptr(int P) {
   }
 }
 
-size_t rows16_lds_bytes(int P) { return 4u * (size_t)P * kLR * 4 * 8; }
+size_t rows16_lds_bytes(int P) { return 4u * kPlanes * (size_t)P * kLR * 4; }
 
 // ---- Down projection and take in one launch (one token, one issue, at most kDTRows rows,
 // short down rows).  A workgroup owns TL = 16 output columns of the residual and has one wave
-// per group row: the wave stages its row's h in its own LDS region and computes its expert's
-// TL outputs exactly as k_rows16 does; the rows then meet in LDS and are summed in row
-// (route) order with the take's arithmetic, fmaf over the live rows, added to the residual.
-// No y rows go through memory and no take launch follows.  (Measured on the medium decode
-// layer: 8-column tiles double the h staging traffic and 32-column tiles leave half the CUs
-// idle; both are slower.)  W > 1 splits a row's outputs over W waves that share its staged h.
-template <int P, int W>
-__global__ __launch_bounds__(kDTRows * W * kWave) void k_down_take(ProjArgs a) {
+// per group row: the wave stages its row's h as digit planes in its own LDS region (its own
+// row scale, from a wave reduction) and computes its expert's TL outputs exactly as k_rows16
+// does; the rows then meet in LDS and are summed in row (route) order with the take's
+// arithmetic, fmaf over the live rows, added to the residual.  No y rows go through memory and
+// no take launch follows.  (Measured on the medium decode layer: 8-column tiles double the h
+// staging traffic and 32-column tiles leave half the CUs idle; both are slower.)
+template <int P>
+__global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
   constexpr int V = 4;
   constexpr int TL = kDTTile;
-  constexpr int RW = TL / W;  // outputs per wave
-  static_assert(RW % (2 * kGR) == 0 && RW <= kWave, "whole pipeline passes, one output per lane");
-  extern __shared__ uint32_t s_act[];  // [kDTRows][P * 512] staged h rows
+  constexpr int POS = rows16_positions<P>();
+  constexpr int NX = POS / kWave;  // positions per lane
+  static_assert(TL % (2 * kGR) == 0 && TL <= kWave, "whole pipeline passes, one output per lane");
+  extern __shared__ uint32_t s_planes[];  // [kDTRows][kPlanes][POS]
   __shared__ float s_y[kDTRows][TL];
   __shared__ float s_w[kDTRows];
   __shared__ int s_live[kDTRows];
   const int lane = threadIdx.x & 63;
   const int li = lane & (kLR - 1), g = lane / kLR;
-  const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = wi / W;          // group row of this wave
-  const int part = wi - r * W;   // its share of the tile's outputs and of the row's staging
-  const int i0 = blockIdx.x * TL + part * RW;
-  const int i_end = min(i0 + RW, a.O);
+  const int r = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // group row of this wave
+  const int i0 = blockIdx.x * TL;
+  const int i_end = min(i0 + TL, a.O);
   const CGroupBuf G = (CGroupBuf)a.grp;
   const int rr = min(r, a.grid_rows - 1);
   const TensorDesc T = ld_desc(G->rows[rr].t[2]);
@@ -803,98 +772,101 @@ __global__ __launch_bounds__(kDTRows * W * kWave) void k_down_take(ProjArgs a) {
   asm volatile("" ::"s"(T.q), "s"(T.s), "s"(T.O), "s"(T.C), "s"(T.row_bytes), "s"(T.gs), "s"(T.ng));
   asm volatile("" ::"s"(live));
   // the residual of the tile, in flight from the start
-  const float r_in = a.out[min(i0 + (lane % RW), a.O - 1)];
+  const float r_in = a.out[min(i0 + (lane % TL), a.O - 1)];
 
   const int C = a.C;
   const int RD = (C + 7) >> 3;
+  const bool grp = T.ng > 1;
   int gi[P], woff[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int ds = p * kLR * V + li * V;
-    gi[p] = (T.ng > 1 && ds < RD) ? (8 * ds) / T.gs : 0;
+    gi[p] = (grp && ds < RD) ? (8 * ds) / T.gs : 0;
     woff[p] = ds < RD ? 4 * ds : -1;
   }
   const int rows_in = live && i0 < a.O ? i_end : 0;  // a dead row's loads read nothing
   const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
   const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
 
-  // the wave's share of its row's h, four columns per lane and load (clamped, unconditional;
-  // rows are 16-byte aligned and padded to a multiple of 64 columns)
-  constexpr int NX = P * 512 / (4 * kWave * W);
+  // the wave's row of h: eight columns per position, NX positions per lane (clamped,
+  // unconditional loads; rows are 16-byte aligned and padded to a multiple of 64 columns)
   const float *hrow = static_cast<const float *>(a.act) + (size_t)rr * a.act_ld;
-  float4 xs[NX];
+  float xv[NX][8];
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
-    const int c4 = 4 * (lane + (i * W + part) * kWave);
-    xs[i] = *reinterpret_cast<const float4 *>(hrow + (c4 < C ? c4 : 0));
+    const int j = lane + i * kWave;
+    const float4 *src = reinterpret_cast<const float4 *>(hrow + (8 * j < C ? 8 * j : 0));
+    const float4 u0 = src[0], u1 = src[1];
+    xv[i][0] = u0.x; xv[i][1] = u0.y; xv[i][2] = u0.z; xv[i][3] = u0.w;
+    xv[i][4] = u1.x; xv[i][5] = u1.y; xv[i][6] = u1.z; xv[i][7] = u1.w;
   }
   __builtin_amdgcn_sched_barrier(0);
   Step16<P> b0, b1;
   load_step16<P>(b0, wr, sr, T, woff, gi, i0, g);
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t *lds = s_act + r * (P * 512);
+  uint32_t *planes = s_planes + r * (kPlanes * POS);
+  uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
-    const int c4 = 4 * (lane + (i * W + part) * kWave);
-    float4 x = xs[i];
-    // C is even: a group of four is whole, half or empty
-    if (c4 + 2 > C) x.x = x.y = 0.f;
-    if (c4 + 4 > C) x.z = x.w = 0.f;
-    stage16x4(lds, c4, x);
+    const int j = lane + i * kWave;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (8 * j + k >= C) xv[i][k] = 0.f;  // the zeros of the row's padding (and the clamped reads)
+      m = max(m, abs_bits(xv[i][k]));
+    }
   }
-  if constexpr (W == 1) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
-    __syncthreads();
+  const int E = row_exponent(wave_max_u32(m));
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    uint32_t z[8];
+    position_planes(z, xv[i], E);
+#pragma unroll
+    for (int n = 0; n < kPlanes; ++n) planes[n * POS + lane + i * kWave] = z[n];
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // the second step only now: a smaller first burst lands h and the first step sooner
-  // (measured 0.25 us per layer faster than issuing both steps with h)
   load_step16<P>(b1, wr, sr, T, woff, gi, i0 + kGR, g);
   __builtin_amdgcn_sched_barrier(0);
-  float xm[P];
-  span_offsets16<P>(xm, lds, li);
 
   float outv = 0.f;
   int o = i0;
   do {
-    compute_step16<P>(b0, lds, li, xm, o, i0, lane, outv);
+    compute_step16<P>(b0, planes, li, grp, E, o, i0, lane, outv);
     load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
-    if (o + kGR < i_end) compute_step16<P>(b1, lds, li, xm, o + kGR, i0, lane, outv);
+    if (o + kGR < i_end) compute_step16<P>(b1, planes, li, grp, E, o + kGR, i0, lane, outv);
     load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
     o += 2 * kGR;
   } while (o < i_end);
-  if (lane < RW) s_y[r][part * RW + lane] = outv;
-  if (lane == 0 && part == 0) {
+  if (lane < TL) s_y[r][lane] = outv;
+  if (lane == 0) {
     s_w[r] = wr_row;
     s_live[r] = live;
   }
   __syncthreads();
-  if (r == 0 && lane < RW && i0 + lane < a.O) {
+  if (r == 0 && lane < TL && i0 + lane < a.O) {
     float acc = 0.f;
     for (int q = 0; q < a.grid_rows; ++q)
-      if (s_live[q]) acc = fmaf(s_w[q], s_y[q][part * RW + lane], acc);
+      if (s_live[q]) acc = fmaf(s_w[q], s_y[q][lane], acc);
     a.out[i0 + lane] = r_in + acc;
   }
 }
 
-// Waves per group row.  Measured on the medium decode layer: one wave of 16 outputs per row
-// 9.7 us, two waves of 8 outputs per row (16 waves per workgroup) 11.4 us.
-constexpr int kDTWaves = 1;
 const void *down_take_ptr(int P) {
   switch (P) {
-    case 1: return reinterpret_cast<const void *>(&k_down_take<1, kDTWaves>);
-    case 2: return reinterpret_cast<const void *>(&k_down_take<2, kDTWaves>);
-    case 3: return reinterpret_cast<const void *>(&k_down_take<3, kDTWaves>);
-    case 4: return reinterpret_cast<const void *>(&k_down_take<4, kDTWaves>);
+    case 1: return reinterpret_cast<const void *>(&k_down_take<1>);
+    case 2: return reinterpret_cast<const void *>(&k_down_take<2>);
+    case 3: return reinterpret_cast<const void *>(&k_down_take<3>);
+    case 4: return reinterpret_cast<const void *>(&k_down_take<4>);
     default: return nullptr;
   }
 }
-template <int NT, bool GEN, bool XB, bool SEL = false>
+
+template <int NT, bool GEN, bool SEL = false>
 const void *kernel_ptr_t(int V, int P) {
 #define I4MOE_PTR(v, p) \
-  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, XB, SEL>);
+  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj<v, p, NT, GEN, SEL>);
   I4MOE_PTR(1, 1) I4MOE_PTR(1, 2) I4MOE_PTR(1, 3) I4MOE_PTR(1, 4)
   I4MOE_PTR(2, 1) I4MOE_PTR(2, 2) I4MOE_PTR(2, 3) I4MOE_PTR(2, 4)
   I4MOE_PTR(4, 1) I4MOE_PTR(4, 2) I4MOE_PTR(4, 3) I4MOE_PTR(4, 4)
@@ -902,38 +874,36 @@ const void *kernel_ptr_t(int V, int P) {
   return nullptr;
 }
 
-// The instantiation a launch uses: bf16 pairs only for dual launches over bf16 activations
-// without per-byte group tensors.
-const void *kernel_ptr(int V, int P, int NT, bool gen, bool xb, bool sel = false) {
-  if (NT == 1) return gen ? kernel_ptr_t<1, true, false>(V, P) : kernel_ptr_t<1, false, false>(V, P);
-  if (gen) return sel ? nullptr : kernel_ptr_t<2, true, false>(V, P);
-  if (sel) return xb ? kernel_ptr_t<2, false, true, true>(V, P) : kernel_ptr_t<2, false, false, true>(V, P);
-  return xb ? kernel_ptr_t<2, false, true>(V, P) : kernel_ptr_t<2, false, false>(V, P);
+// The instantiation a launch uses.
+const void *kernel_ptr(int V, int P, int NT, bool gen, bool sel = false) {
+  if (NT == 1) return gen ? kernel_ptr_t<1, true>(V, P) : kernel_ptr_t<1, false>(V, P);
+  if (gen) return sel ? nullptr : kernel_ptr_t<2, true>(V, P);
+  return sel ? kernel_ptr_t<2, false, true>(V, P) : kernel_ptr_t<2, false>(V, P);
 }
 
-size_t lds_bytes(int V, int P, bool xb) { return 4u * (size_t)(xb ? P * 64 * V * 4 : P * 64 * V * 8); }
+size_t lds_bytes(int V, int P) { return 4u * kPlanes * (size_t)P * 64 * V; }
 
-hipError_t launch(int V, int P, int NT, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
+hipError_t launch(int V, int P, int NT, bool gen, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
                   hipEvent_t t0, hipEvent_t t1) {
-  const void *k = kernel_ptr(V, P, NT, gen, xb, sel);
+  const void *k = kernel_ptr(V, P, NT, gen, sel);
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
-  const size_t lds = lds_bytes(V, P, xb);
+  const size_t lds = lds_bytes(V, P);
   if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st, t0, t1, 0);
   return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st);
 }
 
 }  // namespace
 
-int proj_blocks_per_cu(int V, int P, int NT, bool gen, bool xb) {
-  static int cache[5][5][3][2][2] = {};
+int proj_blocks_per_cu(int V, int P, int NT, bool gen) {
+  static int cache[5][5][3][2] = {};
   if (V < 1 || V > 4 || V == 3 || P < 1 || P > 4 || NT < 1 || NT > 2) return 1;
-  int &c = cache[V][P][NT][gen ? 1 : 0][xb ? 1 : 0];
+  int &c = cache[V][P][NT][gen ? 1 : 0];
   if (c == 0) {
-    const void *k = kernel_ptr(V, P, NT, gen, xb);
+    const void *k = kernel_ptr(V, P, NT, gen);
     int n = 0;
-    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kBlock, lds_bytes(V, P, xb)) != hipSuccess || n < 1) {
+    if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kBlock, lds_bytes(V, P)) != hipSuccess || n < 1) {
       (void)hipGetLastError();
       n = 1;
     }
@@ -946,12 +916,13 @@ bool dual_sel_ok(const RouteArgs &ra, bool gen) {
   return !gen && ra.S == 1 && ra.E <= kTabPrefetchE && ra.table != nullptr && ra.K <= kRows;
 }
 
-hipError_t launch_dual(int V, int P, bool gen, bool xb, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
-                       hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_dual(int V, int P, bool gen, bool sel, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
+                       hipEvent_t t1) {
   if (sel && !dual_sel_ok(a.ra, gen)) return hipErrorInvalidValue;
-  hipError_t e = launch(V, P, 2, gen, xb && !gen, sel, a, blocks, st, t0, t1);
+  hipError_t e = launch(V, P, 2, gen, sel, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
+
 int rows16_blocks_per_cu(int P) {
   static int cache[5] = {};
   if (P < 1 || P > 4) return 1;
@@ -989,7 +960,7 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
   }
   ProjArgs args = a;
   void *params[] = {&args};
-  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kDTWaves * kWave);
+  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kWave);
   hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, grid, block, params, lds, st, t0, t1, 0)
                             : hipLaunchKernel(k, grid, block, params, lds, st);
   return e != hipSuccess ? e : hipGetLastError();
@@ -997,7 +968,7 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
 
 hipError_t launch_down(int V, int P, bool gen, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0,
                        hipEvent_t t1) {
-  hipError_t e = launch(V, P, 1, gen, false, false, a, blocks, st, t0, t1);
+  hipError_t e = launch(V, P, 1, gen, false, a, blocks, st, t0, t1);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

@@ -23,15 +23,15 @@ def test_more_than_one_gpu_is_refused():
 def test_traffic_record_matches_sources_only(tmp_path, monkeypatch):
     sys.path.insert(0, ROOT)
     import bench
-    rec_path = os.path.join(bench.PROFILES, "pmc_dual_medium.json")
+    rec_path = os.path.join(bench.PROFILES, "pmc_dual_sustained.json")
     if not os.path.exists(rec_path):
         return
     with open(rec_path) as f:
         rec = json.load(f)
-    got = bench.load_traffic("dual", "medium")
+    got = bench.load_traffic("dual", "sustained")
     assert got in (None, rec["hbm_bytes_per_launch"])
     # a record naming other sources (or a changed hash) is never used
     bad = dict(rec, sources_sha256="0" * 64)
-    (tmp_path / "pmc_dual_medium.json").write_text(json.dumps(bad))
+    (tmp_path / "pmc_dual_sustained.json").write_text(json.dumps(bad))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.load_traffic("dual", "medium") is None
+    assert bench.load_traffic("dual", "sustained") is None

@@ -129,6 +129,8 @@ RAGGED = [
     (512, 256, 128, 2, 32, "group", 64, "bf16"),    # up to 64 distinct experts in one group
     (1024, 512, 256, 8, 1, "group", 64, "bf16"),    # one token, 256 experts: the select kernel at S=1
     (256, 128, 130, 4, 2, "row", 0, "f32"),         # 130 experts: a lane's third column holds two
+    (1024, 2304, 8, 2, 1, "group", 64, "f32"),      # down rows of 2304 columns: the long-row down kernel
+    (512, 4096, 4, 2, 2, "row", 0, "bf16"),         # 4096-column down rows, per-row scales
 ]
 
 
