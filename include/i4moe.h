@@ -212,6 +212,48 @@ int i4moe_expert_group_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int d
  * dropped silently, so every later compute call returns I4MOE_EPOISONED [PR434]. */
 int i4moe_expert_group_take(i4moe_ctx *ctx, float *residual_dev, int S);
 
+/* ---- the steps around the routed experts --------------------------------------------------- */
+/* Sources, same page ("Commit history of c/backend_cuda.cu"):
+ *   [LOG-pipe] the "GPU resident pipeline" commit: device primitives rmsnorm over strided rows,
+ *              silu-mul, residual add and a fixed-order row merge without atomics, checked
+ *              against the engine's CPU math.
+ *   [LOG-mla]  the "CUDA batch MLA attention, ..., W4A16 kernels" commit: W4A16 kernels for the
+ *              shared expert beside the per-device expert groups. */
+
+/* Bind the shared expert of `layer` (gate and up I x D, down D x I, as i4moe_set_expert) [LOG-mla].
+ * It runs on every token with weight 1; it is not part of the router's E experts. */
+int i4moe_set_shared_expert(i4moe_ctx *ctx, int layer, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down);
+
+/* Upload the rmsnorm weights of `layer`: gamma is D float32 (finite), eps >= 0.  Synchronous. */
+int i4moe_upload_norm(i4moe_ctx *ctx, int layer, int D, const float *gamma, float eps);
+
+/* rmsnorm of S rows of x_dev (float32, row stride ld_x >= D) into out_dev (row stride ld_out >= D,
+ * out_dtype F32 or BF16) [LOG-pipe]:
+ *   out[t][i] = round( x[t][i] / sqrt(sum_i x[t][i]^2 / D + eps) * gamma[i] )
+ * in f64 (exact squares, a fixed summation order), rounded once from the f64 value to the output
+ * dtype (round to nearest, ties to even; bf16 directly, not through a float32 rounding).
+ * Limits: 1 <= S <= I4MOE_MAX_TOKENS.  Fault-hook gated. */
+int i4moe_rmsnorm(i4moe_ctx *ctx, int layer, const float *x_dev, int ld_x, int S, void *out_dev, int ld_out,
+                  int out_dtype);
+
+/* Issue the layer's shared expert over the S rows of x_dev ([S][D], F32 or BF16): one group row per
+ * token, weight 1, into the next free slot, reduced by the next take after the slots issued before
+ * it [LOG-mla].  Returns the slot index, or a negative code with nothing enqueued.  Fault-hook gated. */
+int i4moe_shared_expert_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S);
+
+/* One whole MoE block on the residual stream, on the device, in one call: for the S float32 rows
+ * of residual_dev ([S][D], 16-byte aligned, updated in place),
+ *   a   = i4moe_rmsnorm of the rows into act_dtype (context scratch)
+ *   route a (as i4moe_route with K, topp, norm_topk, routed_scale), issue the routed experts,
+ *   issue the shared expert if one is bound, and take:
+ *   residual[t] += (sum over the routed rows of t, route order, of w * y) + y_shared
+ * with the slots added in issue order (routed first).  Needs the layer's router, norm weights and
+ * every routed expert.  Fault-hook gated as one compute call.  A failure after the first launch
+ * poisons the context, as a failed take does.  The first call on a context allocates its scratch
+ * for the normalised rows; later calls with the same or a smaller D allocate nothing. */
+int i4moe_moe_block(i4moe_ctx *ctx, int layer, float *residual_dev, int S, int act_dtype, int K, float topp,
+                    int norm_topk, float routed_scale);
+
 /* ---- test hooks ----------------------------------------------------------------------------- */
 
 /* Fault hook [LOG-fix]: after n more successful compute calls (route, issue, take), every

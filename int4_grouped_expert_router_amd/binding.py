@@ -55,6 +55,12 @@ SIGNATURES = {
                                       C.c_float, C.c_void_p]),
     "i4moe_expert_group_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.POINTER(i4moe_group)]),
     "i4moe_expert_group_take": (C.c_int, [_ctx_p, C.c_void_p, C.c_int]),
+    "i4moe_set_shared_expert": (C.c_int, [_ctx_p, C.c_int, C.c_uint32, C.c_uint32, C.c_uint32]),
+    "i4moe_upload_norm": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_void_p, C.c_float]),
+    "i4moe_rmsnorm": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_int]),
+    "i4moe_shared_expert_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int]),
+    "i4moe_moe_block": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int,
+                                  C.c_float]),
     "i4moe_set_fail_after": (C.c_int, [_ctx_p, C.c_longlong]),
     "i4moe_debug_read": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t]),
     "i4moe_debug_size": (C.c_size_t, [_ctx_p, C.c_int, C.c_int]),
@@ -106,6 +112,11 @@ i4moe_route = _fn("i4moe_route")
 i4moe_route_noalloc = _fn("i4moe_route_noalloc")
 i4moe_expert_group_issue = _fn("i4moe_expert_group_issue")
 i4moe_expert_group_take = _fn("i4moe_expert_group_take")
+i4moe_set_shared_expert = _fn("i4moe_set_shared_expert")
+i4moe_upload_norm = _fn("i4moe_upload_norm")
+i4moe_rmsnorm = _fn("i4moe_rmsnorm")
+i4moe_shared_expert_issue = _fn("i4moe_shared_expert_issue")
+i4moe_moe_block = _fn("i4moe_moe_block")
 i4moe_set_fail_after = _fn("i4moe_set_fail_after")
 i4moe_debug_read = _fn("i4moe_debug_read")
 i4moe_debug_size = _fn("i4moe_debug_size")

@@ -30,11 +30,18 @@ struct Tensor {
   int fmt = 0;
 };
 
+// The layer's shared expert sits in the expert table right after the routed experts' cap.
+constexpr int kShared = kMaxE;
+
 struct Layer {
   int E = 0, D = 0, I = 0;             // router experts; model dim; expert intermediate
   float *W = nullptr, *b = nullptr;    // router
   std::vector<i4moe_tensor> gate, up, down;
-  ExpertRec *d_tab = nullptr;          // [kMaxE]: gate, up, down descriptors per expert
+  i4moe_tensor shared[3] = {0, 0, 0};  // shared expert: gate, up, down
+  bool shared_set = false;
+  float *gamma = nullptr;              // rmsnorm weights [D]
+  float eps = 0.f;
+  ExpertRec *d_tab = nullptr;          // [kMaxE + 1]: gate, up, down descriptors per expert, then the shared one
   std::vector<ExpertRec> h_tab;        // host copy of d_tab
   int route_buf = -1;                  // ring entry holding this layer's latest route
   bool routed = false;
@@ -79,6 +86,8 @@ struct i4moe_ctx {
   double2 *d_score = nullptr;  // [kTokens][kMaxE] router scores (choice score, sigma)
   double *d_logits = nullptr;  // [kTokens][kMaxE]
 
+  float *d_xn = nullptr;   // [kTokens][xn_ld] the block's normalised rows (f32 or bf16)
+  int xn_ld = 0;
   float *d_h = nullptr;    // [kRows][h_ld]
   int h_ld = 0;
   float *d_y = nullptr;    // [kSlots][kRows][y_ld]
@@ -290,9 +299,9 @@ int ensure_route_scratch(i4moe_ctx *c) {
 int ensure_layer_tables(i4moe_ctx *c, Layer &L) {
   if (L.d_tab) return I4MOE_OK;
   hipError_t e;
-  if ((e = dalloc(&L.d_tab, sizeof(ExpertRec) * kMaxE)) != hipSuccess) return hip_fail(c, e, "hipMalloc(table)");
-  L.h_tab.assign(kMaxE, ExpertRec{});
-  e = hipMemcpyAsync(L.d_tab, L.h_tab.data(), sizeof(ExpertRec) * kMaxE, hipMemcpyHostToDevice, c->stream);
+  if ((e = dalloc(&L.d_tab, sizeof(ExpertRec) * (kMaxE + 1))) != hipSuccess) return hip_fail(c, e, "hipMalloc(table)");
+  L.h_tab.assign(kMaxE + 1, ExpertRec{});
+  e = hipMemcpyAsync(L.d_tab, L.h_tab.data(), sizeof(ExpertRec) * (kMaxE + 1), hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return hip_fail(c, e, "table init");
   return I4MOE_OK;
@@ -511,8 +520,10 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
     Layer &L = kv.second;
     dfree(L.W);
     dfree(L.b);
+    dfree(L.gamma);
     dfree(L.d_tab);
   }
+  dfree(c->d_xn);
   dfree(c->d_score);
   dfree(c->d_logits);
   dfree(c->d_ring);
@@ -655,6 +666,13 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
       int rc = write_table_entry(c, L, (int)x);
       if (rc) return rc;
     }
+    if (L.shared_set && (L.shared[0] == h || L.shared[1] == h || L.shared[2] == h)) {
+      L.shared[0] = L.shared[1] = L.shared[2] = 0;
+      L.shared_set = false;
+      L.h_tab[kShared] = ExpertRec{};
+      int rc = write_table_entry(c, L, kShared);
+      if (rc) return rc;
+    }
   }
   dfree(it->second.q);
   dfree(it->second.s);
@@ -751,11 +769,11 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
   return I4MOE_OK;
 }
 
-int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
-                float routed_scale, i4moe_route_host *host_out) {
-  if (!c) return I4MOE_EINVAL;
-  int rc = gate_compute(c);
-  if (rc) return rc;
+// The compute entry points are the fault hook's gate and call count around these bodies; a
+// composite call (i4moe_moe_block) gates and counts once around several of them.
+static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
+                      float routed_scale, i4moe_route_host *host_out) {
+  int rc = I4MOE_OK;
   Layer *L = find_layer(c, layer);
   if (!L || !L->W) return fail(c, I4MOE_EINVAL, "layer %d has no router", layer);
   if (!x_dev) return fail(c, I4MOE_EINVAL, "x_dev is NULL");
@@ -810,13 +828,22 @@ int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, in
   L->route_K = K;
   c->last_route_S = S;
   c->last_route_E = L->E;
-  c->calls++;
   if (host_out) {
     e = hipMemcpyAsync(host_out, c->d_ring[ring].route, sizeof(RouteTok) * S, hipMemcpyDeviceToHost, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "route copy back");
   }
   return I4MOE_OK;
+}
+
+int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
+                float routed_scale, i4moe_route_host *host_out) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  rc = route_impl(c, layer, x_dev, dtype, S, K, topp, norm_topk, routed_scale, host_out);
+  if (rc == I4MOE_OK) c->calls++;
+  return rc;
 }
 
 int i4moe_route_noalloc(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
@@ -871,10 +898,10 @@ int i4moe_route_noalloc(i4moe_ctx *c, int layer, const void *x_dev, int dtype, i
   return I4MOE_OK;
 }
 
-int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group) {
-  if (!c) return I4MOE_EINVAL;
-  int rc = gate_compute(c);
-  if (rc) return rc;
+// allow_shared: the group may name the layer's shared expert (kShared).
+static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group,
+                      bool allow_shared) {
+  int rc = I4MOE_OK;
   Layer *L = find_layer(c, layer);
   if (!L || !L->D || !L->I || !L->d_tab) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
   if (!x_dev) return fail(c, I4MOE_EINVAL, "x_dev is NULL");
@@ -921,7 +948,8 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
     int n_ent = 0, ent_of[kRows];
     for (int r = 0; r < n; ++r) {
       const int e = group->expert[r], t = group->token[r];
-      if (e < 0 || e >= (int)L->gate.size() || !L->gate[e])
+      const bool shared = allow_shared && e == kShared && L->shared_set;
+      if (!shared && (e < 0 || e >= (int)L->gate.size() || !L->gate[e]))
         return fail(c, I4MOE_EINVAL, "group row %d: expert %d is not set", r, e);
       if (t < 0 || t >= S) return fail(c, I4MOE_EINVAL, "group row %d: token %d outside 0..%d", r, t, S - 1);
       if (!std::isfinite(group->weight[r])) return fail(c, I4MOE_EINVAL, "group row %d: weight not finite", r);
@@ -1026,22 +1054,22 @@ int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dty
   c->nslots = s + 1;
   c->last_issue_rows = max_rows;
   c->last_issue_I = L->I;
-  c->calls++;
   return s;
 }
 
-int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
+int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group) {
   if (!c) return I4MOE_EINVAL;
-  if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
   int rc = gate_compute(c);
-  if (rc) {
-    c->poisoned = true;
-    return rc;
-  }
-  if (c->nslots == 0) {
-    c->calls++;
-    return I4MOE_OK;
-  }
+  if (rc) return rc;
+  rc = issue_impl(c, layer, x_dev, dtype, S, group, false);
+  if (rc >= 0) c->calls++;
+  return rc;
+}
+
+// A failure here poisons the context (the routed experts would be dropped silently).
+static int take_impl(i4moe_ctx *c, float *residual_dev, int S) {
+  int rc = I4MOE_OK;
+  if (c->nslots == 0) return I4MOE_OK;
   if (!residual_dev || S != c->slots[0].S) {
     c->poisoned = true;
     return fail(c, I4MOE_EINVAL, "take: residual NULL or S=%d differs from the issued S=%d", S, c->slots[0].S);
@@ -1061,7 +1089,6 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
     }
     si.down_pending = false;
     c->nslots = 0;
-    c->calls++;
     return I4MOE_OK;
   }
   if ((rc = flush_down(c))) {
@@ -1089,6 +1116,198 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
     return hip_fail(c, e, "take launch");
   }
   c->nslots = 0;
+  return I4MOE_OK;
+}
+
+int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
+  if (!c) return I4MOE_EINVAL;
+  if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
+  int rc = gate_compute(c);
+  if (rc) {
+    c->poisoned = true;
+    return rc;
+  }
+  rc = take_impl(c, residual_dev, S);
+  if (rc == I4MOE_OK) c->calls++;
+  return rc;
+}
+
+int i4moe_set_shared_expert(i4moe_ctx *c, int layer, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
+  if (!c) return I4MOE_EINVAL;
+  ensure_device(c);
+  if (int rc = flush_all(c)) return rc;
+  if (layer < 0) return fail(c, I4MOE_EINVAL, "bad layer %d", layer);
+  auto tg = c->tensors.find(gate), tu = c->tensors.find(up), td = c->tensors.find(down);
+  if (tg == c->tensors.end() || tu == c->tensors.end() || td == c->tensors.end())
+    return fail(c, I4MOE_EINVAL, "unknown tensor handle");
+  const TensorDesc &G = tg->second.desc, &U = tu->second.desc, &Dn = td->second.desc;
+  const int I = G.O, D = G.C;
+  if (U.O != I || U.C != D || Dn.O != D || Dn.C != I)
+    return fail(c, I4MOE_EINVAL, "shared expert shapes: gate %dx%d, up %dx%d, down %dx%d (need I x D, I x D, D x I)",
+                G.O, G.C, U.O, U.C, Dn.O, Dn.C);
+  Layer &L = c->layers[layer];
+  if ((L.D && L.D != D) || (L.I && L.I != I))
+    return fail(c, I4MOE_EINVAL, "layer %d has D=%d I=%d, shared expert has D=%d I=%d", layer, L.D, L.I, D, I);
+  int rc = ensure_rows_scratch(c, D, I);
+  if (rc) return rc;
+  if ((rc = ensure_layer_tables(c, L))) return rc;
+  L.D = D;
+  L.I = I;
+  L.shared[0] = gate;
+  L.shared[1] = up;
+  L.shared[2] = down;
+  L.shared_set = true;
+  L.h_tab[kShared].t[0] = G;
+  L.h_tab[kShared].t[1] = U;
+  L.h_tab[kShared].t[2] = Dn;
+  return write_table_entry(c, L, kShared);
+}
+
+int i4moe_upload_norm(i4moe_ctx *c, int layer, int D, const float *gamma, float eps) {
+  if (!c) return I4MOE_EINVAL;
+  if (layer < 0 || D < 1 || !gamma) return fail(c, I4MOE_EINVAL, "bad norm arguments");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(c, I4MOE_EINVAL, "eps must be finite and >= 0");
+  if (!all_finite(gamma, (size_t)D)) return fail(c, I4MOE_EINVAL, "gamma must be finite");
+  ensure_device(c);
+  if (int rc = flush_all(c)) return rc;
+  Layer &L = c->layers[layer];
+  if (L.D && L.D != D) return fail(c, I4MOE_EINVAL, "norm D=%d but layer %d has D=%d", D, layer, L.D);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  float *g = nullptr;
+  if ((e = dalloc(&g, sizeof(float) * D)) != hipSuccess) return hip_fail(c, e, "hipMalloc(gamma)");
+  e = hipMemcpyAsync(g, gamma, sizeof(float) * D, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    dfree(g);
+    return hip_fail(c, e, "norm copy");
+  }
+  dfree(L.gamma);
+  L.gamma = g;
+  L.eps = eps;
+  if (!L.D) L.D = D;
+  return I4MOE_OK;
+}
+
+// The block's normalised rows, [kTokens][D] of float32 (bf16 uses half of it).  Grows only with
+// no issue pending (an issue may still read the old buffer).
+static int ensure_xn(i4moe_ctx *c, int D) {
+  const int need = round_up(D, 64);
+  if (need <= c->xn_ld) return I4MOE_OK;
+  if (c->nslots > 0) return fail(c, I4MOE_EINVAL, "cannot grow the block scratch while %d issue(s) are pending", c->nslots);
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  float *p = nullptr;
+  if ((e = dalloc(&p, sizeof(float) * (size_t)kTokens * need)) != hipSuccess) return hip_fail(c, e, "hipMalloc(xn)");
+  dfree(c->d_xn);
+  c->d_xn = p;
+  c->xn_ld = need;
+  return I4MOE_OK;
+}
+
+static int rmsnorm_impl(i4moe_ctx *c, const Layer &L, const float *x_dev, int ld_x, int S, void *out_dev, int ld_out,
+                        int out_dtype) {
+  NormArgs a{};
+  a.x = x_dev;
+  a.gamma = L.gamma;
+  a.out = out_dev;
+  a.ld_x = ld_x;
+  a.ld_out = ld_out;
+  a.S = S;
+  a.D = L.D;
+  a.out_bf16 = out_dtype == I4MOE_DTYPE_BF16;
+  a.eps = L.eps;
+  hipError_t e = launch_rmsnorm(a, c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "rmsnorm launch");
+  return I4MOE_OK;
+}
+
+int i4moe_rmsnorm(i4moe_ctx *c, int layer, const float *x_dev, int ld_x, int S, void *out_dev, int ld_out,
+                  int out_dtype) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->gamma) return fail(c, I4MOE_EINVAL, "layer %d has no norm weights", layer);
+  if (!x_dev || !out_dev) return fail(c, I4MOE_EINVAL, "x_dev and out_dev must be device pointers");
+  if (out_dtype != I4MOE_DTYPE_F32 && out_dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", out_dtype);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  if (ld_x < L->D || ld_out < L->D) return fail(c, I4MOE_EINVAL, "row strides %d, %d below D=%d", ld_x, ld_out, L->D);
+  if (reinterpret_cast<uintptr_t>(x_dev) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(out_dev) % (out_dtype == I4MOE_DTYPE_F32 ? 4 : 2) != 0)
+    return fail(c, I4MOE_EINVAL, "misaligned rows");
+  ensure_device(c);
+  rc = rmsnorm_impl(c, *L, x_dev, ld_x, S, out_dev, ld_out, out_dtype);
+  if (rc == I4MOE_OK) c->calls++;
+  return rc;
+}
+
+// The shared expert's group: one row per token, weight 1, listed in token order.
+static int shared_issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S) {
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->shared_set) return fail(c, I4MOE_EINVAL, "layer %d has no shared expert", layer);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  int32_t ex[kTokens], tok[kTokens];
+  float w[kTokens];
+  for (int t = 0; t < S; ++t) {
+    ex[t] = kShared;
+    tok[t] = t;
+    w[t] = 1.f;
+  }
+  const i4moe_group g{S, ex, tok, w};
+  return issue_impl(c, layer, x_dev, dtype, S, &g, true);
+}
+
+int i4moe_shared_expert_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S) {
+  if (!c) return I4MOE_EINVAL;
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  rc = shared_issue_impl(c, layer, x_dev, dtype, S);
+  if (rc >= 0) c->calls++;
+  return rc;
+}
+
+int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act_dtype, int K, float topp,
+                    int norm_topk, float routed_scale) {
+  if (!c) return I4MOE_EINVAL;
+  if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->W || !L->gamma || !L->I || !L->d_tab)
+    return fail(c, I4MOE_EINVAL, "layer %d needs a router, norm weights and experts", layer);
+  if (!residual_dev || reinterpret_cast<uintptr_t>(residual_dev) % 16 != 0)
+    return fail(c, I4MOE_EINVAL, "residual_dev must be a 16-byte aligned device pointer");
+  if (act_dtype != I4MOE_DTYPE_F32 && act_dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", act_dtype);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  if (K < 1 || K > L->E || K > kMaxK || S * K > kRows)
+    return fail(c, I4MOE_EINVAL, "K=%d with S=%d outside the route's limits", K, S);
+  if (c->nslots + (L->shared_set ? 2 : 1) > kSlots) return fail(c, I4MOE_EINVAL, "no free issue slots");
+  if (c->nslots > 0 && (c->slots[0].S != S || c->slots[0].D != L->D))
+    return fail(c, I4MOE_EINVAL, "pending issues have another S or D");
+  if ((int)L->gate.size() < L->E) return fail(c, I4MOE_EINVAL, "layer %d: experts 0..%d must all be set", layer, L->E - 1);
+  for (int e = 0; e < L->E; ++e)
+    if (!L->gate[e]) return fail(c, I4MOE_EINVAL, "layer %d: expert %d is not set", layer, e);
+  ensure_device(c);
+  if ((rc = ensure_xn(c, L->D))) return rc;
+  // From the first launch on, a failure leaves the residual without its experts: poison, as a
+  // failed take does.
+  // the normalised rows are packed [S][D] (what the route and the issues read)
+  rc = rmsnorm_impl(c, *L, residual_dev, L->D, S, c->d_xn, L->D, act_dtype);
+  if (!rc) rc = route_impl(c, layer, c->d_xn, act_dtype, S, K, topp, norm_topk, routed_scale, nullptr);
+  if (!rc) {
+    const int s = issue_impl(c, layer, c->d_xn, act_dtype, S, nullptr, false);
+    if (s < 0) rc = s;
+  }
+  if (!rc && L->shared_set) {
+    const int s = shared_issue_impl(c, layer, c->d_xn, act_dtype, S);
+    if (s < 0) rc = s;
+  }
+  if (!rc) rc = take_impl(c, residual_dev, S);
+  if (rc) {
+    c->poisoned = true;
+    return rc;
+  }
   c->calls++;
   return I4MOE_OK;
 }

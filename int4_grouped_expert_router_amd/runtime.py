@@ -131,6 +131,31 @@ class Context:
             raise TypeError("residual must be a contiguous float32 device tensor")
         self.check(B.i4moe_expert_group_take(self.p, C.c_void_p(residual.data_ptr()), residual.shape[0]))
 
+    def set_shared_expert(self, layer: int, gate: int, up: int, down: int):
+        self.check(B.i4moe_set_shared_expert(self.p, layer, gate, up, down))
+
+    def upload_norm(self, layer: int, gamma: np.ndarray, eps: float):
+        gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+        self.check(B.i4moe_upload_norm(self.p, layer, gamma.shape[0], _ptr(gamma), eps))
+
+    def rmsnorm(self, layer: int, x, out, ld_x: int = 0, ld_out: int = 0):
+        """x: float32 device rows [S][>= D]; out: float32 or bfloat16 device rows [S][>= D]."""
+        S = x.shape[0]
+        self.check(B.i4moe_rmsnorm(self.p, layer, C.c_void_p(x.data_ptr()), ld_x or x.shape[1], S,
+                                   C.c_void_p(out.data_ptr()), ld_out or out.shape[1], _dtype_code(out)))
+
+    def shared_issue(self, layer: int, x) -> int:
+        return self.check(B.i4moe_shared_expert_issue(self.p, layer, C.c_void_p(x.data_ptr()), _dtype_code(x),
+                                                      x.shape[0]))
+
+    def moe_block(self, layer: int, residual, act_dtype: int, K: int, topp: float = 0.0, norm_topk: bool = True,
+                  routed_scale: float = 1.0):
+        import torch
+        if residual.dtype != torch.float32 or not residual.is_contiguous():
+            raise TypeError("residual must be a contiguous float32 device tensor")
+        self.check(B.i4moe_moe_block(self.p, layer, C.c_void_p(residual.data_ptr()), residual.shape[0], act_dtype, K,
+                                     topp, 1 if norm_topk else 0, routed_scale))
+
     def set_fail_after(self, n: int):
         self.check(B.i4moe_set_fail_after(self.p, n))
 

@@ -23,6 +23,8 @@ Sources (the web pages the method is described on), cited in each module as:
 * [PR342]   "cuda: COLI_GROUP_ASYNC=1 - overlap the CPU expert rows with the GPU
             groups at decode", section "What": S<=4 small-batch grouped decode,
             issue/take split.
+* [LOG-mla] same page, the "CUDA batch MLA attention, ..., W4A16 kernels" commit: the
+            shared expert runs as a W4A16 MLP beside the expert groups.
 * [PR434]   "cuda: COLI_CUDA_RESID=1 - expert-group results stay on device",
             section "What": per-expert weighting, fixed-order reduce into a
             per-issue slot, take reduces slots in issue order into the residual.
@@ -32,7 +34,7 @@ against brute force, closed forms, invariants or library routines; none is
 "parity unpinned".
 """
 
-from . import brute, experts, int4, router  # noqa: F401
+from . import block, brute, experts, int4, router  # noqa: F401
 from .experts import (  # noqa: F401
     build_group,
     expert_forward,

@@ -15,7 +15,9 @@ from .gen import (  # noqa: F401
     gen_activations,
     gen_expert,
     gen_layer,
+    gen_norm,
     gen_residual,
     gen_router,
+    gen_shared_expert,
     round_f32_to_bf16_bits,
 )

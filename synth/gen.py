@@ -30,6 +30,8 @@ ROLE_ROUTER = 0
 ROLE_EXPERT = 1
 ROLE_ACT = 2
 ROLE_RESID = 3
+ROLE_SHARED = 4
+ROLE_NORM = 5
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -103,6 +105,23 @@ def gen_expert(cfg: Config, layer: int, e: int) -> ExpertWeights:
     up = _tensor(rng, cfg, fmt, gs, cfg.I, cfg.D)
     down = _tensor(rng, cfg, fmt, gs, cfg.D, cfg.I)
     return ExpertWeights(gate, up, down)
+
+
+def gen_shared_expert(cfg: Config, layer: int) -> ExpertWeights:
+    """The layer's shared expert: the same shapes as a routed expert; group-wise when the workload
+    has group-wise experts at all, else per-row."""
+    fmt, gs = (FMT_ROW, 0) if cfg.formats == "row" else (FMT_GROUP, cfg.gs)
+    rng = _rng(cfg.seed, layer, ROLE_SHARED)
+    gate = _tensor(rng, cfg, fmt, gs, cfg.I, cfg.D)
+    up = _tensor(rng, cfg, fmt, gs, cfg.I, cfg.D)
+    down = _tensor(rng, cfg, fmt, gs, cfg.D, cfg.I)
+    return ExpertWeights(gate, up, down)
+
+
+def gen_norm(cfg: Config, layer: int) -> np.ndarray:
+    """rmsnorm weights gamma ~ N(1, 0.1), float32 [D]."""
+    rng = _rng(cfg.seed, layer, ROLE_NORM)
+    return rng.normal(1.0, 0.1, cfg.D).astype(np.float32)
 
 
 def gen_router(cfg: Config, layer: int):

@@ -404,4 +404,125 @@ def pin_worked_example():
     assert np.allclose(delta[0], [2.5 * v for v in y1], rtol=1e-15, atol=1e-16)
 
 
+
+
+# ---------------------------------------------------------------- the block around the experts
+
+def _bf16_table():
+    """Every finite bf16 value, ascending, with its bit pattern: brute force for the rounding."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    keep = np.isfinite(f)
+    vals = np.where(keep, f, 0).astype(np.float64)
+    vals, bits = vals[keep], bits[keep]
+    order = np.lexsort((bits, vals))
+    vals, bits = vals[order], bits[order]
+    # -0 and +0 compare equal: keep +0 only
+    first = np.concatenate([[True], vals[1:] != vals[:-1]])
+    return vals[first], bits[first]
+
+
+def pin_round_bf16_brute():
+    """Nearest bf16, ties to the even pattern, by search over the whole bf16 table; exact ties,
+    values just off a tie (where an intermediate float32 rounding would fall on the tie and go
+    to even), subnormals, and the overflow edge."""
+    vals, bits = _bf16_table()
+    rng = np.random.default_rng(21)
+    cases = list(rng.standard_normal(3000) * np.exp(rng.uniform(-20, 20, 3000)))
+    for i in rng.integers(1, len(vals) - 2, 400):
+        lo, hi = vals[i], vals[i + 1]
+        if np.isfinite(lo) and np.isfinite(hi):
+            mid = (lo + hi) / 2
+            cases += [mid, mid + abs(mid) * 2.0 ** -40, mid - abs(mid) * 2.0 ** -40]
+    cases += [2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 1e-45, 2.0 ** 127 * 1.99, 3.3e38, 3.4e38, -3.39e38]
+    for v in cases:
+        v = float(v)
+        got = oracle.block.round_bf16(v)
+        j = np.searchsorted(vals, v)
+        if j >= len(vals):
+            assert math.isinf(got) and got > 0, v
+            continue
+        cand = [vals[j]] + ([vals[j - 1]] if j > 0 else [])
+        d = [abs(c - v) for c in cand]
+        if len(cand) == 2 and d[0] == d[1]:
+            want = cand[0] if bits[j] % 2 == 0 else cand[1]
+        else:
+            want = cand[int(np.argmin(d))]
+        # past the largest finite value: ties and beyond go to infinity
+        if abs(v) >= 2.0 ** 128 - 2.0 ** 119:
+            assert math.isinf(got), v
+            continue
+        assert got == want, (v, got, want)
+
+
+def pin_round_bf16_vs_bits():
+    """For float32 inputs the rounding equals the integer round-to-nearest-even on the bit
+    pattern (the synthetic inputs' own conversion)."""
+    from synth import round_f32_to_bf16_bits
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal(5000) * np.exp(rng.uniform(-30, 30, 5000))).astype(np.float32)
+    # exact float32 ties of bf16: low half 0x8000
+    t = (rng.integers(0, 1 << 16, 500).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, t[np.isfinite(t)]])
+    got = oracle.block.round_activations(x.astype(np.float64), "bf16")
+    assert np.array_equal(got, round_f32_to_bf16_bits(x))
+
+
+def pin_rmsnorm_forms():
+    rng = np.random.default_rng(23)
+    D = 64
+    g1 = np.ones(D, np.float32)
+    # a constant row c: every output is c / sqrt(c^2 + eps)
+    for c, eps in [(3.0, 1e-5), (-0.25, 1e-6), (1e-4, 1e-5)]:
+        out = oracle.block.rmsnorm(np.full((1, D), c), g1, eps)
+        e = float(np.float32(eps))
+        assert np.allclose(out, c / math.sqrt(c * c + e), rtol=1e-15, atol=0)
+    # eps = 0: the output's mean square is exactly 1 (to rounding), and scaling the row changes nothing
+    x = rng.standard_normal((3, D))
+    out = oracle.block.rmsnorm(x, g1, 0.0)
+    assert np.allclose((out ** 2).mean(axis=1), 1.0, rtol=1e-14)
+    assert np.allclose(oracle.block.rmsnorm(7.5 * x, g1, 0.0), out, rtol=1e-14)
+    # gamma multiplies column by column
+    g = rng.normal(1.0, 0.2, D).astype(np.float32)
+    assert np.allclose(oracle.block.rmsnorm(x, g, 1e-5), oracle.block.rmsnorm(x, g1, 1e-5) * g.astype(np.float64),
+                       rtol=1e-15)
+    # against a second formulation: the Euclidean norm
+    e = float(np.float32(1e-5))
+    ref = x / np.sqrt(np.linalg.norm(x, axis=1) ** 2 / D + e)[:, None]
+    assert np.allclose(oracle.block.rmsnorm(x, g1, 1e-5), ref, rtol=1e-13)
+
+
+def pin_block_identities():
+    """The block is rmsnorm -> rounding -> the layer of the routed experts, plus the shared
+    expert with weight 1, plus the residual."""
+    rng = np.random.default_rng(24)
+    D, I, E, K = 16, 8, 4, 2
+    ex = [SimpleNamespace(gate=rand_tensor(rng, 2, 0, I, D), up=rand_tensor(rng, 2, 0, I, D),
+                          down=rand_tensor(rng, 4, 4, D, I)) for _ in range(E)]
+    sh = SimpleNamespace(gate=rand_tensor(rng, 4, 4, I, D), up=rand_tensor(rng, 2, 0, I, D),
+                         down=rand_tensor(rng, 2, 0, D, I))
+    W = rng.normal(0, 0.5, (E, D)).astype(np.float32)
+    b = rng.normal(0, 0.1, E).astype(np.float32)
+    r = rng.standard_normal((2, D)).astype(np.float32)
+    gam = rng.normal(1, 0.1, D).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        a, routes, delta, out = oracle.block.moe_block(r, gam, 1e-5, dt, W, b, lambda e: ex[e], K, 0.0, True, 2.0,
+                                                       shared=sh)
+        n = oracle.block.rmsnorm(r, gam, 1e-5)
+        a64 = router.widen_activations(a, dt)
+        assert np.max(np.abs(a64 - n)) <= (2.0 ** -8 if dt == "bf16" else 2.0 ** -24) * np.max(np.abs(n))
+        _, _, d_routed, _ = experts.moe_layer(W, b, a64, lambda e: ex[e], K, 0.0, True, 2.0)
+        for t in range(2):
+            ys = brute.expert(sh.gate, sh.up, sh.down, a64[t].tolist())
+            assert np.allclose(delta[t], d_routed[t] + np.array(ys), rtol=1e-12, atol=1e-14)
+            assert np.allclose(out[t], r[t].astype(np.float64) + delta[t], rtol=0, atol=0)
+    # a shared expert of zero weights (all nibbles 8) adds nothing
+    z = SimpleNamespace(gate=T(2, 0, I, D, np.full((I, D // 2), 0x88), np.ones(I)),
+                        up=T(2, 0, I, D, np.full((I, D // 2), 0x88), np.ones(I)),
+                        down=T(2, 0, D, I, np.full((D, I // 2), 0x88), np.ones(D)))
+    _, _, d0, _ = oracle.block.moe_block(r, gam, 1e-5, "f32", W, b, lambda e: ex[e], K, 0.0, True, 2.0, shared=z)
+    _, _, d1, _ = oracle.block.moe_block(r, gam, 1e-5, "f32", W, b, lambda e: ex[e], K, 0.0, True, 2.0)
+    assert np.array_equal(d0, d1)
+
+
 PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

@@ -7,10 +7,12 @@ wrong activation, a dropped residual.  If some mutant survived every pin, the
 pins would not be pinning that part of the oracle.
 """
 
+import math
+
 import numpy as np
 import pytest
 
-from oracle import experts, int4, router
+from oracle import block, experts, int4, router
 from pins_oracle import PINS
 
 _orig_unpack = int4.unpack_nibbles
@@ -245,7 +247,81 @@ def m_dequant_unchecked(packed, scales, fmt, gs, O, C, rows):
     return q * _orig_scale(scales, fmt, gs, O, C, rows)
 
 
+_orig_rmsnorm = block.rmsnorm
+_orig_round_bf16 = block.round_bf16
+_orig_block = block.moe_block
+
+
+def m_rms_no_eps(x, gamma, eps):
+    return _orig_rmsnorm(x, gamma, 0.0)
+
+
+def m_rms_eps_outside(x, gamma, eps):
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        ms = math.fsum(float(v) * float(v) for v in x[t]) / x.shape[1]
+        out[t] = x[t] / (math.sqrt(ms) + float(np.float32(eps))) * g
+    return out
+
+
+def m_rms_mean_over_d_minus_1(x, gamma, eps):
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        ms = math.fsum(float(v) * float(v) for v in x[t]) / (x.shape[1] - 1)
+        out[t] = x[t] / math.sqrt(ms + float(np.float32(eps))) * g
+    return out
+
+
+def m_round_via_f32(v):
+    # double rounding: to float32 first, then to bf16
+    f = float(np.float32(v))
+    return _orig_round_bf16(f)
+
+
+def m_round_half_up(v):
+    if v == 0.0 or not math.isfinite(v):
+        return v
+    m, e = math.frexp(v)
+    q = max(e - 8, -133)
+    scaled = math.ldexp(v, -q)
+    return math.ldexp(math.floor(abs(scaled) + 0.5) * (1 if v > 0 else -1), q)
+
+
+def m_shared_half_weight(residual, gamma, eps, act_dtype, W, bias, expert_of, K, topp, norm_topk, routed_scale,
+                         shared=None):
+    a, routes, delta, out = _orig_block(residual, gamma, eps, act_dtype, W, bias, expert_of, K, topp, norm_topk,
+                                        routed_scale, shared=None)
+    a64 = router.widen_activations(a, act_dtype)
+    if shared is not None:
+        for t in range(a64.shape[0]):
+            delta[t] += 0.5 * experts.expert_forward(shared.gate, shared.up, shared.down, a64[t])[3]
+    r = np.atleast_2d(np.asarray(residual, dtype=np.float32)).astype(np.float64)
+    return a, routes, delta, r + delta
+
+
+def m_shared_on_raw_residual(residual, gamma, eps, act_dtype, W, bias, expert_of, K, topp, norm_topk, routed_scale,
+                             shared=None):
+    a, routes, delta, out = _orig_block(residual, gamma, eps, act_dtype, W, bias, expert_of, K, topp, norm_topk,
+                                        routed_scale, shared=None)
+    r = np.atleast_2d(np.asarray(residual, dtype=np.float32)).astype(np.float64)
+    if shared is not None:
+        for t in range(r.shape[0]):
+            delta[t] += experts.expert_forward(shared.gate, shared.up, shared.down, r[t])[3]
+    return a, routes, delta, r + delta
+
+
 MUTANTS = {
+    "rmsnorm_without_eps": (block, "rmsnorm", m_rms_no_eps),
+    "rmsnorm_eps_outside_sqrt": (block, "rmsnorm", m_rms_eps_outside),
+    "rmsnorm_mean_over_d_minus_1": (block, "rmsnorm", m_rms_mean_over_d_minus_1),
+    "bf16_double_rounding": (block, "round_bf16", m_round_via_f32),
+    "bf16_ties_away": (block, "round_bf16", m_round_half_up),
+    "shared_expert_half_weight": (block, "moe_block", m_shared_half_weight),
+    "shared_expert_on_raw_residual": (block, "moe_block", m_shared_on_raw_residual),
     "check_accepts_odd_gs": (int4, "check_format", m_check_accepts_odd_gs),
     "dequant_unchecked": (int4, "dequantize_rows", m_dequant_unchecked),
     "swap_nibbles": (int4, "unpack_nibbles", m_swap_nibbles),
