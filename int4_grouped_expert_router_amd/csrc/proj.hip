@@ -309,10 +309,10 @@ __device__ __forceinline__ void load_span(__amdgpu_buffer_rsrc_t r, int off, uin
 // buffer range, so its loads return zeros and touch no memory.  Keeping the issue pattern
 // identical on every path keeps the wait counts exact (a load issued on one path only would
 // make the compiler wait for all loads in flight).  A span past the row's padded bytes reads
-// zeros the same way (weight 0).
+// zeros the same way (weight 0).  One pass of a step: the pass-p spans (and scales) of its rows.
 template <int V, int P, int NT, int RB>
-__device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
-                                          int o, int o_end, int lane) {
+__device__ __forceinline__ void load_pass(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
+                                          int o, int o_end, int lane, int p) {
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const bool ok = o + r < o_end;
@@ -321,13 +321,17 @@ __device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDe
     for (int n = 0; n < NT; ++n) {
       const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T[n].q + (size_t)row * T[n].row_bytes, ok ? T[n].row_bytes : 0);
       const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T[n].s + (size_t)row * T[n].ng, ok ? 4 * T[n].ng : 0);
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        load_span<V>(wr, 4 * (p * 64 * V + lane * V), st.w[n][r][p]);
-        st.s[n][r][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * gi[n][p], 0, 0));
-      }
+      load_span<V>(wr, 4 * (p * 64 * V + lane * V), st.w[n][r][p]);
+      st.s[n][r][p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * gi[n][p], 0, 0));
     }
   }
+}
+
+template <int V, int P, int NT, int RB>
+__device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
+                                          int o, int o_end, int lane) {
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_pass<V, P, NT, RB>(st, T, gi, o, o_end, lane, p);
 }
 
 // Dot products of one step's rows, reduced over the wave; lane (o - o_begin + r) keeps row
@@ -335,13 +339,22 @@ __device__ __forceinline__ void load_step(Step<V, P, NT, RB> &st, const TensorDe
 // lane's planes are read once for every row and tensor of the step.  A group-wise tensor joins
 // its digit sums and applies the span's group scale after every pass; a per-row tensor joins
 // once, after the last pass, and applies the row scale.
-template <int V, int P, int NT, int RB, bool GEN>
-__device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT],
+//
+// ROLL: as soon as a pass of the step is consumed, its registers are reloaded with the same pass
+// of rows o_next .. (the step after next), so loads are issued throughout the computation rather
+// than after it, and a wave always has close to two steps of weights in flight.
+template <int V, int P, int NT, int RB, bool GEN, bool ROLL>
+__device__ __forceinline__ void compute_step(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT], const int (&gi)[NT][P],
                                              const bool (&grp)[NT], const bool (&gen)[NT], const uint32_t *planes,
                                              int positions, int E, int o, int o_end, int lane, int RD, int o_begin,
-                                             float &outv) {
+                                             int o_next, float &outv) {
   int acc[NT][RB][kPlanes];
   float fa[NT][RB];
+  float srow[NT][RB];  // per-row scales, kept before pass 0 is reloaded
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) srow[n][r] = st.s[n][r][0];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -376,6 +389,7 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
         }
       }
     }
+    if constexpr (ROLL) load_pass<V, P, NT, RB>(st, T, gi, o_next, o_end, lane, p);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -389,7 +403,7 @@ __device__ __forceinline__ void compute_step(const Step<V, P, NT, RB> &st, const
           if (o + r < o_end) a = row_dot_generic<V, P>(T[n], o + r, st.w[n][r], planes, positions, lane, RD);
         }
       } else if (!grp[n]) {
-        a = join_digits(acc[n][r]) * st.s[n][r][0];
+        a = join_digits(acc[n][r]) * srow[n][r];
       }
       sum[n] = __builtin_ldexpf(wave_sum(a), -E);
     }
@@ -574,11 +588,24 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   float outv = 0.f;
   int o = o_begin;
   do {
-    compute_step<V, P, NT, RB, GEN>(b0, T, grp, gen, s_planes, POS, E, o, o_end, lane, RD, o_begin, outv);
-    load_step<V, P, NT, RB>(b0, T, gi, o + 2 * RB, o_end, lane);
-    if (o + RB < o_end)
-      compute_step<V, P, NT, RB, GEN>(b1, T, grp, gen, s_planes, POS, E, o + RB, o_end, lane, RD, o_begin, outv);
-    load_step<V, P, NT, RB>(b1, T, gi, o + 3 * RB, o_end, lane);
+    if constexpr (!GEN) {
+      // rolling reloads inside the computation; the second step runs even past the tile (its
+      // rows read zeros and its results land on lanes that are never stored), so the issue
+      // pattern never depends on the tile length
+      compute_step<V, P, NT, RB, GEN, true>(b0, T, gi, grp, gen, s_planes, POS, E, o, o_end, lane, RD, o_begin,
+                                            o + 2 * RB, outv);
+      compute_step<V, P, NT, RB, GEN, true>(b1, T, gi, grp, gen, s_planes, POS, E, o + RB, o_end, lane, RD, o_begin,
+                                            o + 3 * RB, outv);
+    } else {
+      // the per-byte path reads a step's weights after its last pass: reload afterwards
+      compute_step<V, P, NT, RB, GEN, false>(b0, T, gi, grp, gen, s_planes, POS, E, o, o_end, lane, RD, o_begin, 0,
+                                             outv);
+      load_step<V, P, NT, RB>(b0, T, gi, o + 2 * RB, o_end, lane);
+      if (o + RB < o_end)
+        compute_step<V, P, NT, RB, GEN, false>(b1, T, gi, grp, gen, s_planes, POS, E, o + RB, o_end, lane, RD,
+                                               o_begin, 0, outv);
+      load_step<V, P, NT, RB>(b1, T, gi, o + 3 * RB, o_end, lane);
+    }
     o += 2 * RB;
   } while (o < o_end);
   if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
@@ -608,17 +635,22 @@ struct Step16 {
 
 // One step: four consecutive rows o .. o+3, lane group g on row o + g.  The buffer ranges end
 // at row o_end, so rows past the tile read zeros without a memory access; spans past the row
-// get an offset past every range for the same effect.
+// get an offset past every range for the same effect.  One pass at a time.
+template <int P>
+__device__ __forceinline__ void load_pass16(Step16<P> &st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                            const TensorDesc &T, const int (&woff)[P], const int (&gi)[P], int o, int g,
+                                            int p) {
+  const int row = o + g;
+  load_span<4>(wr, woff[p] < 0 ? 0x7ffffff0 : row * T.row_bytes + woff[p], st.w[p]);
+  st.s[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * (row * T.ng + gi[p]), 0, 0));
+}
+
 template <int P>
 __device__ __forceinline__ void load_step16(Step16<P> &st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
                                             const TensorDesc &T, const int (&woff)[P], const int (&gi)[P], int o,
                                             int g) {
-  const int row = o + g;
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load_span<4>(wr, woff[p] < 0 ? 0x7ffffff0 : row * T.row_bytes + woff[p], st.w[p]);
-    st.s[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * (row * T.ng + gi[p]), 0, 0));
-  }
+  for (int p = 0; p < P; ++p) load_pass16<P>(st, wr, sr, T, woff, gi, o, g, p);
 }
 
 // Positions of a short row staged for P passes of 16 lanes x 4 dwords.
@@ -630,14 +662,19 @@ constexpr int rows16_positions() {
 // One step's four rows: the lane's digit sums over its P spans, joined (per pass for group-wise
 // scales, once for a per-row scale), summed over the row's 16 lanes; lane (o - o_begin + g)
 // keeps row o + g.
+// After each pass its registers are reloaded with the same pass of rows o_next .. (the step
+// after next), as in k_proj.
 template <int P>
-__device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32_t *planes, int li, bool grp, int E,
-                                               int o, int o_begin, int lane, float &outv) {
+__device__ __forceinline__ void compute_step16(Step16<P> &st, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                               const TensorDesc &T, const int (&woff)[P], const int (&gi)[P],
+                                               const uint32_t *planes, int li, int g, bool grp, int E, int o,
+                                               int o_begin, int o_next, int lane, float &outv) {
   constexpr int POS = rows16_positions<P>();
   int acc[kPlanes];
 #pragma unroll
   for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
   float fa = 0.f;
+  const float srow = st.s[0];
   uint32_t X[2][kPlanes][4];
   read_planes<4>(X[0], planes, POS, li * 4);
 #pragma unroll
@@ -653,9 +690,10 @@ __device__ __forceinline__ void compute_step16(const Step16<P> &st, const uint32
 #pragma unroll
       for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
     }
+    load_pass16<P>(st, wr, sr, T, woff, gi, o_next, g, p);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (!grp) fa = join_digits(acc) * st.s[0];
+  if (!grp) fa = join_digits(acc) * srow;
   const float sum = __builtin_ldexpf(row16_sum(fa), -E);
 #pragma unroll
   for (int g = 0; g < kGR; ++g) {
@@ -718,10 +756,9 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   float outv = 0.f;
   int o = o_begin;
   do {
-    compute_step16<P>(b0, s_planes, li, grp, E, o, o_begin, lane, outv);
-    load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
-    if (o + kGR < o_end) compute_step16<P>(b1, s_planes, li, grp, E, o + kGR, o_begin, lane, outv);
-    load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
+    // the second step runs even past the tile (zeros in, results on lanes never stored)
+    compute_step16<P>(b0, wr, sr, T, woff, gi, s_planes, li, g, grp, E, o, o_begin, o + 2 * kGR, lane, outv);
+    compute_step16<P>(b1, wr, sr, T, woff, gi, s_planes, li, g, grp, E, o + kGR, o_begin, o + 3 * kGR, lane, outv);
     o += 2 * kGR;
   } while (o < o_end);
   if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
@@ -833,10 +870,8 @@ __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
   float outv = 0.f;
   int o = i0;
   do {
-    compute_step16<P>(b0, planes, li, grp, E, o, i0, lane, outv);
-    load_step16<P>(b0, wr, sr, T, woff, gi, o + 2 * kGR, g);
-    if (o + kGR < i_end) compute_step16<P>(b1, planes, li, grp, E, o + kGR, i0, lane, outv);
-    load_step16<P>(b1, wr, sr, T, woff, gi, o + 3 * kGR, g);
+    compute_step16<P>(b0, wr, sr, T, woff, gi, planes, li, g, grp, E, o, i0, o + 2 * kGR, lane, outv);
+    compute_step16<P>(b1, wr, sr, T, woff, gi, planes, li, g, grp, E, o + kGR, i0, o + 3 * kGR, lane, outv);
     o += 2 * kGR;
   } while (o < i_end);
   if (lane < TL) s_y[r][lane] = outv;
