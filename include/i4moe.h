@@ -92,7 +92,9 @@ typedef struct {
 
 /* Explicit group for issue (host arrays of n_rows entries): each row runs expert[r] on token
  * row token[r] of x and is weighted by weight[r].  Per token, rows are summed in the order
- * listed.  Rows of one expert share one pass over its weights. */
+ * listed.  The rows of one expert run together: up to 4 of them share each pass over its
+ * weights when enough rows share (see I4MOE_ENTRY_ROWS at i4moe_ctx_create), and an expert with
+ * at least 16 rows runs on the matrix cores (I4MOE_MFMA_MIN_ROWS). */
 typedef struct {
   int32_t n_rows;
   const int32_t *expert;
@@ -107,6 +109,15 @@ typedef struct {
  * I4MOE_WAVE_FACTOR (0.05 .. 64, default 1) scales the number of waves the projections aim
  * for per CU; it changes how output rows are tiled over waves, never the results (each row
  * is still reduced by one wave in a fixed order).
+ * I4MOE_ENTRY_ROWS sets how rows of one expert (S > 1) share weight passes: 0 never, 2..4 always
+ * (at most that many rows per pass), unset automatic (when at least a quarter of the rows would
+ * ride on another row's pass).  It changes only the order of additions: a group-wise tensor's
+ * results are the same bits either way, a per-row tensor's may differ in the last bits (both
+ * within the documented tolerance of the f64 result).
+ * I4MOE_MFMA_MIN_ROWS (0 = off, else 2 .. 64; default 16) is the row count from which an
+ * expert's rows in one issue run on the matrix cores (int8 products of digit rows, exact like
+ * the vector kernels; gate/up/down of every expert of the issue per-row or with group sizes
+ * that are multiples of 64); smaller entries keep the vector kernels.
  * Errors: EINVAL (bad device, out == NULL), EDEVICE, ENOMEM. */
 int i4moe_ctx_create(int device, i4moe_ctx **out);
 
@@ -288,8 +299,9 @@ size_t i4moe_debug_size(i4moe_ctx *ctx, int what, int index);
 
 /* Kernel families timed when profiling is on.  A selection run inside the dual projection
  * (see i4moe_route) is timed as part of I4MOE_K_DUAL, a down projection run inside the take
- * (see i4moe_expert_group_issue) as part of I4MOE_K_TAKE. */
-enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_COUNT = 4 };
+ * (see i4moe_expert_group_issue) as part of I4MOE_K_TAKE.  I4MOE_K_MFMA: the matrix-core
+ * projections of experts with many rows, with the digit rows they read. */
+enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_MFMA = 4, I4MOE_K_COUNT = 5 };
 
 /* on != 0: bracket every later kernel launch with a pair of HIP events on the context's
  * stream; on == 0 stops.  Switching resets the accumulated figures. */

@@ -25,7 +25,7 @@ I4MOE_DTYPE_F32, I4MOE_DTYPE_BF16 = 0, 1
 I4MOE_OK, I4MOE_EINVAL, I4MOE_ENOMEM, I4MOE_EDEVICE = 0, -1, -2, -3
 I4MOE_EUNSUPPORTED, I4MOE_EINJECTED, I4MOE_EPOISONED = -4, -5, -6
 I4MOE_TAP_LOGITS, I4MOE_TAP_ROUTE, I4MOE_TAP_GROUP, I4MOE_TAP_H, I4MOE_TAP_Y = 1, 2, 3, 4, 5
-I4MOE_K_ROUTE, I4MOE_K_DUAL, I4MOE_K_DOWN, I4MOE_K_TAKE, I4MOE_K_COUNT = 0, 1, 2, 3, 4
+I4MOE_K_ROUTE, I4MOE_K_DUAL, I4MOE_K_DOWN, I4MOE_K_TAKE, I4MOE_K_MFMA, I4MOE_K_COUNT = 0, 1, 2, 3, 4, 5
 
 
 class i4moe_route_host(C.Structure):

@@ -6,6 +6,7 @@
 // later healthy call, uploaded tensors never look at the caller's host buffers again, and the
 // fail-after hook gates compute entry points only.  The take is fatal on failure, as in the
 // COLI_CUDA_RESID page: a take that did not run would silently drop routed experts.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -59,7 +60,9 @@ struct SlotInfo {
   ProjArgs down{};
 };
 
-constexpr int kRing = 32;  // route buffers: a layer may be re-routed up to 31 times before a take
+constexpr int kRing = 32;
+constexpr double kEntryMinShare = 0.25;  // rows sharing another row's weight pass, to share passes
+constexpr int kMfmaMinRows = 16;          // rows of one expert from which the matrix cores pay  // route buffers: a layer may be re-routed up to 31 times before a take
 
 struct ProfRec {
   int kernel;
@@ -98,6 +101,10 @@ struct i4moe_ctx {
   SlotInfo slots[kSlots];
   int n_cu = 256;
   double wave_factor = 1.0;
+  int entry_mode = -1;     // rows of one expert per weight pass: -1 automatic, 0 never, 2..4 always
+  int mfma_min = kMfmaMinRows;  // rows from which an entry runs on the matrix cores (0: never)
+  int8_t *d_dig = nullptr;      // [kRows][3][kMaxCols] digit rows of the matrix-core projections
+  int *d_dig_E = nullptr;       // [kRows] their row exponents
   int nslots = 0;
 
   int last_route_S = 0, last_route_E = 0;
@@ -118,8 +125,8 @@ struct i4moe_ctx {
   bool profiling = false;
   std::vector<hipEvent_t> ev_pool;
   std::vector<ProfRec> recs;
-  double prof_ms[I4MOE_K_COUNT] = {0, 0, 0, 0};
-  long long prof_n[I4MOE_K_COUNT] = {0, 0, 0, 0};
+  double prof_ms[I4MOE_K_COUNT] = {};
+  long long prof_n[I4MOE_K_COUNT] = {};
 };
 
 namespace {
@@ -277,6 +284,23 @@ int ensure_rows_scratch(i4moe_ctx *c, int D, int I) {
   c->d_y = y;
   c->h_ld = h_ld;
   c->y_ld = y_ld;
+  return I4MOE_OK;
+}
+
+// Digit rows for the matrix-core projections at their cap (1.5 MB), allocated by the first
+// issue that uses them.
+int ensure_digit_scratch(i4moe_ctx *c) {
+  if (c->d_dig) return I4MOE_OK;
+  hipError_t e;
+  int8_t *d = nullptr;
+  int *E = nullptr;
+  if ((e = dalloc(&d, (size_t)kRows * 3 * kMaxCols)) != hipSuccess) return hip_fail(c, e, "hipMalloc(digit rows)");
+  if ((e = dalloc(&E, sizeof(int) * kRows)) != hipSuccess) {
+    dfree(d);
+    return hip_fail(c, e, "hipMalloc(digit exponents)");
+  }
+  c->d_dig = d;
+  c->d_dig_E = E;
   return I4MOE_OK;
 }
 
@@ -499,6 +523,16 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
     const double v = std::atof(wf);
     if (v >= 0.05 && v <= 64.0) c->wave_factor = v;
   }
+  if (const char *mm = std::getenv("I4MOE_MFMA_MIN_ROWS")) {
+    char *end = nullptr;
+    const long v = std::strtol(mm, &end, 10);
+    if (end && end != mm && *end == '\0' && (v == 0 || (v >= 2 && v <= kRows))) c->mfma_min = (int)v;
+  }
+  if (const char *er = std::getenv("I4MOE_ENTRY_ROWS")) {
+    char *end = nullptr;
+    const long v = std::strtol(er, &end, 10);
+    if (end && end != er && *end == '\0' && (v == 0 || (v >= 2 && v <= kEntryRows))) c->entry_mode = (int)v;
+  }
   if (const char *fa = std::getenv("I4MOE_FAIL_AFTER")) {
     char *end = nullptr;
     const long long v = std::strtoll(fa, &end, 10);
@@ -530,6 +564,8 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   dfree(c->d_slot_bufs);
   dfree(c->d_h);
   dfree(c->d_y);
+  dfree(c->d_dig);
+  dfree(c->d_dig_E);
   for (auto &r : c->recs) {
     c->ev_pool.push_back(r.a);
     c->ev_pool.push_back(r.b);
@@ -1013,6 +1049,62 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   an.tile_groups = pn.tile_groups;
   an.grid_rows = max_rows;
   an.tile_rows = pn.tile_rows;
+  // Several tokens: the rows of one expert may share each weight pass.  Automatic mode shares
+  // when at least a quarter of the rows would ride on another row's pass: counted exactly for an
+  // explicit group, and for a device route estimated from S tokens picking K of E experts
+  // uniformly (E (1 - (1 - K/E)^S) distinct experts expected).  Below that the shared passes
+  // cost more than they save: a workgroup running nr rows does nr times the dot products per
+  // weight byte.
+  if (S > 1 && c->entry_mode != 0) {
+    int most = S;  // a device route gives an expert at most one row per token
+    double share;
+    if (group) {
+      most = 0;
+      for (int j = 0; j < hg.n_entries; ++j) most = std::max(most, hg.entry_row0[j + 1] - hg.entry_row0[j]);
+      const int er = std::min(most, kEntryRows);
+      int chunks = 0;
+      for (int j = 0; j < hg.n_entries; ++j) chunks += (hg.entry_row0[j + 1] - hg.entry_row0[j] + er - 1) / er;
+      share = 1.0 - (double)chunks / hg.n_rows;
+    } else {
+      const double E = L->E, K = L->route_K;
+      share = 1.0 - E * (1.0 - std::pow(1.0 - K / E, S)) / (S * K);
+    }
+    if (c->entry_mode > 0 || share >= kEntryMinShare) {
+      const int want = c->entry_mode > 0 ? std::min(most, c->entry_mode) : most;
+      const int ed = entry_rows_fit(pd.V, pd.P, false, want);
+      const int en = entry_rows_fit(pn.V, pn.P, pn.rows16, want);
+      if (ed > 1 && !pd.gen) ad.entry_rows = ed;
+      if (en > 1 && (pn.rows16 || !pn.gen)) an.entry_rows = en;
+    }
+  }
+
+  // Entries of at least mfma_min rows run on the matrix cores (every tensor of the issue per-row
+  // or with group sizes that are multiples of 64); the vector kernels then take the chunked path,
+  // which skips those entries.
+  int mfma_min = 0, mfma_slots = 0, mfma_tiles = 0;
+  if (S > 1 && c->mfma_min > 0) {
+    bool fmt_ok = true;
+    for (int gs : gs_in) fmt_ok = fmt_ok && gs % 64 == 0;
+    for (int gs : gs_dn) fmt_ok = fmt_ok && gs % 64 == 0;
+    int most = S, n_big = max_rows / c->mfma_min;  // a device route: at most one row per token
+    if (group) {
+      most = n_big = 0;
+      for (int j = 0; j < hg.n_entries; ++j) {
+        const int n = hg.entry_row0[j + 1] - hg.entry_row0[j];
+        most = std::max(most, n);
+        if (n >= c->mfma_min) ++n_big;
+      }
+    }
+    if (fmt_ok && most >= c->mfma_min && n_big > 0) {
+      mfma_min = c->mfma_min;
+      mfma_slots = n_big;
+      mfma_tiles = (std::min(most, kRows) + 15) / 16;
+      if ((rc = ensure_digit_scratch(c))) return rc;
+      ad.mfma_min = an.mfma_min = mfma_min;
+      if (ad.entry_rows == 0) ad.entry_rows = 1;
+      if (an.entry_rows == 0) an.entry_rows = 1;
+    }
+  }
 
   // This layer's latest route still owes its selection: run it inside the dual projection
   // when that variant can, else as its own kernel first.
@@ -1031,14 +1123,48 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   const bool defer_down = S == 1 && !group && s == 0 && pn.rows16 && max_rows <= kDTRows;
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
+  // matrix-core launches of one projection: the digit rows of its activations, then the
+  // projection of the big entries (after the vector kernels of the same projection)
+  auto mfma = [&](bool dual) -> hipError_t {
+    DigitArgs da{};
+    da.act = dual ? x_dev : c->d_h;
+    da.grp = dual ? nullptr : grp;
+    da.dig = c->d_dig;
+    da.E = c->d_dig_E;
+    da.act_ld = dual ? L->D : c->h_ld;
+    da.bf16 = dual && dtype == I4MOE_DTYPE_BF16;
+    da.rows = dual ? S : max_rows;
+    da.C = dual ? L->D : L->I;
+    da.C64 = round_up(da.C, 64);
+    MfmaArgs ma{};
+    ma.grp = grp;
+    ma.dig = c->d_dig;
+    ma.E = c->d_dig_E;
+    ma.out = dual ? c->d_h : an.out;
+    ma.out_ld = dual ? c->h_ld : c->y_ld;
+    ma.dig_rows = da.rows;
+    ma.dual = dual ? 1 : 0;
+    ma.O = dual ? L->I : L->D;
+    ma.C64 = da.C64;
+    ma.mfma_min = mfma_min;
+    ma.slots = mfma_slots;
+    ma.token_tiles = mfma_tiles;
+    return timed(c, I4MOE_K_MFMA, [&](hipEvent_t t0, hipEvent_t t1) {
+      // the event pair spans both launches: start of the digit rows, end of the projection
+      hipError_t r = launch_digits8(da, c->stream, t0, nullptr);
+      return r != hipSuccess ? r : launch_mfma(dual ? 2 : 1, ma, c->stream, nullptr, t1);
+    });
+  };
   if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_dual(pd.V, pd.P, pd.gen, sel, ad, pd.blocks, c->stream, t0, t1);
     });
   if (e == hipSuccess && sel) c->sel_pending = false;
+  if (e == hipSuccess && mfma_min) e = mfma(true);
   if (e == hipSuccess && !defer_down) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
       return pn.rows16 ? launch_down16(pn.P, an, pn.blocks, c->stream, t0, t1)
                        : launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
     });
+  if (e == hipSuccess && mfma_min) e = mfma(false);
   if (e != hipSuccess) return hip_fail(c, e, "issue launch");
   c->slots[s].down_pending = defer_down;
   if (defer_down) {

@@ -54,7 +54,8 @@ static_assert(sizeof(GroupDev) == I4MOE_GROUP_WORDS * 4, "group record layout");
 
 // Everything a projection wave needs about its group row, in one 128-byte record (t[0].live
 // marks the rows of the current group; every row of the buffer is rewritten per group): the
-// expert's gate / up / down tensors, the token row of x and the route weight.
+// expert's gate / up / down tensors, the token row of x and the route weight.  In a live row,
+// t[1].live is the row's rank among its entry's rows and t[2].live the entry's row count.
 struct RowDesc {
   TensorDesc t[3];
   int32_t token;
@@ -103,7 +104,40 @@ struct ProjArgs {
   int O, C;                  // rows and columns of every tensor in the launch
   int tile_groups, tile_rows;  // workgroups per group row (4 tiles each), rows per tile
   int grid_rows;             // group rows the grid covers (grid = grid_rows * tile_groups)
+  // entry_rows > 0 (several tokens): the rows of one expert share each weight pass, at most
+  // entry_rows (<= kEntryRows) at a time, and the dynamic LDS holds that many staged rows.
+  int entry_rows;
+  // mfma_min > 0: entries of at least this many rows belong to the matrix-core kernels and the
+  // vector kernels skip them
+  int mfma_min;
   RouteArgs ra;              // dual with the fused selection: the route whose scores it ranks
+};
+
+constexpr int kEntryRows = 4;  // rows of one expert per weight pass in the vector kernels
+
+// Digit rows for the matrix-core projections: rows of f32 or bf16 activations (row stride
+// act_ld) as three int8 planes of C64 bytes each (row r at dig + 3 r C64), and each row's E.
+// grp non-null: rows at or past the group's n_rows are skipped.
+struct DigitArgs {
+  const void *act;
+  const GroupBuf *grp;
+  int8_t *dig;
+  int *E;
+  int act_ld, bf16, rows, C, C64;
+};
+
+// Matrix-core projection of the entries with at least mfma_min rows (slot k: the k-th such
+// entry in entry order).  dual: gate/up + SiLU into h rows, digit rows indexed by token; else the
+// down projection into y rows, digit rows indexed by group row.
+struct MfmaArgs {
+  const GroupBuf *grp;
+  const int8_t *dig;
+  const int *E;
+  float *out;
+  int out_ld, dig_rows, dual;
+  int O, C64;
+  int mfma_min, slots, token_tiles;
+  int weight_tiles, tiles;  // set by the launcher
 };
 
 struct TakeArgs {
@@ -152,9 +186,14 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
 hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0 = nullptr,
                          hipEvent_t t1 = nullptr);
 int rows16_blocks_per_cu(int P);
+// Rows of one expert a launch shape stages per workgroup: at most `want` and kEntryRows, and few
+// enough that three workgroups' staged rows fit a CU's LDS.
+int entry_rows_fit(int V, int P, bool rows16, int want);
 int proj_blocks_per_cu(int V, int P, int NT, bool gen);  // resident 256-thread workgroups per CU
 hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBuf *dst, hipStream_t st);
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.
 constexpr int rows_per_step(int V, int P, int tensors, int budget) {

@@ -493,8 +493,10 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
       // this row's descriptor for the down projection and the take (zeros for a dead row)
       uint32_t val = 0u;
       if (live) {
-        if (lane == kLiveWord)
-          val = 1u;
+        if (lane == kLiveWord || lane == kSizeWord)
+          val = 1u;  // live; an entry of one row (rank 0)
+        else if (lane == kRankWord)
+          val = 0u;
         else if (lane < kTabWords)
           val = s_tab[e * kDescWords + lane];
         else if (lane == kTabWords)
@@ -610,6 +612,215 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
   } while (o < o_end);
   if (lane < o_end - o_begin) a.out[(size_t)jr * a.out_ld + o_begin + lane] = outv;
   asm volatile("" ::"v"(touch));
+}
+
+// ---- Several rows of one expert per weight pass (S > 1).  The rows of a group are ordered
+// expert by expert, so an entry's rows are consecutive and split into chunks of up to entry_rows
+// rows.  The nr workgroups of a chunk's rows all run every row of the chunk, each over its own
+// nr-th of the output tile: every weight row is read once for the whole chunk (each load feeds
+// nr dot products, one per staged activation row), and each workgroup does the work of one row
+// over a whole tile, as in k_proj, so no workgroup runs longer than the others.  The row record
+// carries the row's rank in its entry and the entry's size, so the chunk is known from the same
+// scalar loads as the tensors.  Each lane joins its digit sums per pass and row (for a per-row
+// tensor too; its scale is applied after the last pass).
+
+// The chunk of a row with this rank in an entry of `size` rows: its row count nr (0 for an entry
+// the matrix-core kernels take, at least mfma_min rows) and the row's index k in it.
+struct ChunkPos {
+  int nr, k;
+};
+__device__ __forceinline__ ChunkPos chunk_of(int rank, int size, int chunk, int mfma_min) {
+  ChunkPos c;
+  c.k = rank % chunk;
+  c.nr = (mfma_min > 0 && size >= mfma_min) ? 0 : min(chunk, size - (rank - c.k));
+  return c;
+}
+
+// Output rows [b, e) of sub-tile k of nr, inside the tile [t0, t1), in steps of RB rows.
+__device__ __forceinline__ void sub_tile(int t0, int t1, int tile_rows, int nr, int k, int RB, int &b, int &e) {
+  const int sub = ((tile_rows + nr - 1) / nr + RB - 1) / RB * RB;
+  b = min(t0 + k * sub, t1);
+  e = min(b + sub, t1);
+}
+
+template <int V, int P, int NT, int RB>
+__device__ __forceinline__ void compute_step_entry(Step<V, P, NT, RB> &st, const TensorDesc (&T)[NT],
+                                                   const int (&gi)[NT][P], const bool (&grp)[NT],
+                                                   const uint32_t *planes, int positions, const int (&E)[kEntryRows],
+                                                   int nr, int o, int o_end, int lane, int o_begin, int o_next,
+                                                   float (&outv)[kEntryRows]) {
+  float fa[NT][RB][kEntryRows];
+  float srow[NT][RB];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      srow[n][r] = st.s[n][r][0];
+#pragma unroll
+      for (int i = 0; i < kEntryRows; ++i) fa[n][r][i] = 0.f;
+    }
+  // per pass, row by row: the row's planes, then its dot products (the guard on the chunk's
+  // row count, uniform over the wave, also keeps the compiler from holding several rows' planes)
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int i = 0; i < kEntryRows; ++i) {
+      if (i < nr) {
+        uint32_t X[kPlanes][V];
+        read_planes<V>(X, planes + i * kPlanes * positions, positions, p * 64 * V + lane * V);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int r = 0; r < RB; ++r) {
+            int acc[kPlanes];
+#pragma unroll
+            for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+              for (int d = 0; d < kPlanes; ++d)
+                acc[d] = __builtin_amdgcn_sdot8((int)st.w[n][r][p][v], (int)X[d][v], acc[d], false);
+            const float jd = join_digits(acc);
+            fa[n][r][i] = grp[n] ? fmaf(jd, st.s[n][r][p], fa[n][r][i]) : fa[n][r][i] + jd;
+          }
+      }
+    }
+    load_pass<V, P, NT, RB>(st, T, gi, o_next, o_end, lane, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int i = 0; i < kEntryRows; ++i) {
+      if (i < nr) {
+        float sum[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float a = grp[n] ? fa[n][r][i] : fa[n][r][i] * srow[n][r];
+          sum[n] = __builtin_ldexpf(wave_sum(a), -E[i]);
+        }
+        float res = sum[0];
+        if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
+        if (lane == o - o_begin + r) outv[i] = res;
+      }
+    }
+}
+
+// k_proj for the chunks of entries (span-aligned group sizes only).  The staged rows arrive
+// one after another: row i + 1's activation loads are in flight while row i is staged.
+template <int V, int P, int NT>
+__global__ __launch_bounds__(kBlock) void k_proj_entry(ProjArgs a) {
+  constexpr int RB = rows_per_step(V, P, NT, 16);
+  constexpr int POS = proj_positions<V, P>();
+  constexpr int NPOS = (POS + kBlock - 1) / kBlock;
+  extern __shared__ uint32_t s_planes[];  // [entry_rows][kPlanes][POS]
+  __shared__ uint32_t s_max[kBlock / kWave];
+  const int lane = threadIdx.x & 63;
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int jr = blockIdx.x / a.tile_groups;
+  const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
+  const CGroupBuf G = (CGroupBuf)a.grp;
+  TensorDesc T[NT];
+  if constexpr (NT == 2) {
+    T[0] = ld_desc(G->rows[jr].t[0]);
+    T[1] = ld_desc(G->rows[jr].t[1]);
+  } else {
+    T[0] = ld_desc(G->rows[jr].t[2]);
+  }
+  const int live = G->rows[jr].t[0].live;
+  const int rank = G->rows[jr].t[1].live, size = G->rows[jr].t[2].live;
+  // the tokens of rows jr - 3 .. jr + 3, the rows a chunk holding jr may span (dual)
+  constexpr int kSpan = 2 * kEntryRows - 1;
+  int tok[kSpan];
+#pragma unroll
+  for (int d = 0; d < kSpan; ++d)
+    tok[d] = NT == 2 ? G->rows[min(max(jr + d - (kEntryRows - 1), 0), kRows - 1)].token : 0;
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    asm volatile("" ::"s"(T[n].q), "s"(T[n].s), "s"(T[n].O), "s"(T[n].C), "s"(T[n].row_bytes), "s"(T[n].gs),
+                 "s"(T[n].ng));
+  asm volatile("" ::"s"(live), "s"(rank), "s"(size));
+#pragma unroll
+  for (int d = 0; d < kSpan; ++d) asm volatile("" ::"s"(tok[d]));
+  if (!live) return;
+  const ChunkPos cp = chunk_of(rank, size, a.entry_rows, a.mfma_min);
+  const int nr = cp.nr;
+  if (nr == 0) return;
+  const int head = jr - cp.k;  // the chunk's first row
+  int arow[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) {
+    const int c = min(i, nr - 1);  // rows past the chunk repeat its last row
+    if constexpr (NT == 2) {
+      int t = tok[0];
+#pragma unroll
+      for (int d = 1; d < kSpan; ++d)
+        if (d == c - cp.k + kEntryRows - 1) t = tok[d];
+      arow[i] = t;
+    } else {
+      arow[i] = head + c;
+    }
+  }
+
+  const int C = a.C;
+  const int RD = (C + 7) >> 3;
+  int gi[NT][P];
+  bool grp[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    grp[n] = T[n].ng > 1;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int ds = p * 64 * V + lane * V;
+      gi[n][p] = grp[n] && ds < RD ? (8 * ds) / T[n].gs : 0;
+    }
+  }
+  int o_begin, o_end;
+  sub_tile(tile * a.tile_rows, min(tile * a.tile_rows + a.tile_rows, a.O), a.tile_rows, nr, cp.k, RB, o_begin, o_end);
+  const bool work = o_begin < o_end;
+
+  float xv[2][NPOS][8];
+#pragma unroll
+  for (int k = 0; k < NPOS; ++k)
+    load_position(xv[0][k], a.act, a.act_bf16, (size_t)arow[0] * a.act_ld, threadIdx.x + k * kBlock, POS, C);
+  __builtin_amdgcn_sched_barrier(0);
+  Step<V, P, NT, RB> b0, b1;
+  load_step<V, P, NT, RB>(b0, T, gi, o_begin, o_end, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step<V, P, NT, RB>(b1, T, gi, o_begin + RB, o_end, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  int E[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) {
+    if (i + 1 < kEntryRows) {
+#pragma unroll
+      for (int k = 0; k < NPOS; ++k)
+        load_position(xv[(i + 1) & 1][k], a.act, a.act_bf16, (size_t)arow[i + 1] * a.act_ld, threadIdx.x + k * kBlock,
+                      POS, C);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    E[i] = 0;
+    if (i < nr) E[i] = stage_planes<NPOS>(s_planes + i * kPlanes * POS, POS, xv[i & 1], s_max);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!work) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  float outv[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) outv[i] = 0.f;
+  int o = o_begin;
+  do {
+    compute_step_entry<V, P, NT, RB>(b0, T, gi, grp, s_planes, POS, E, nr, o, o_end, lane, o_begin, o + 2 * RB, outv);
+    compute_step_entry<V, P, NT, RB>(b1, T, gi, grp, s_planes, POS, E, nr, o + RB, o_end, lane, o_begin, o + 3 * RB,
+                                     outv);
+    o += 2 * RB;
+  } while (o < o_end);
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i)
+    if (i < nr && lane < o_end - o_begin) a.out[(size_t)(head + i) * a.out_ld + o_begin + lane] = outv[i];
 }
 
 // ---- Short rows (the down projection, C <= 2048 columns): 16 lanes per row, so one wave
@@ -765,6 +976,132 @@ __global__ __launch_bounds__(kBlock) void k_rows16(ProjArgs a) {
   asm volatile("" ::"v"(touch));
 }
 
+// k_rows16 for the chunks of entries: the staged h rows of the chunk share every weight pass.
+template <int P>
+__device__ __forceinline__ void compute_step16_entry(Step16<P> &st, __amdgpu_buffer_rsrc_t wr,
+                                                     __amdgpu_buffer_rsrc_t sr, const TensorDesc &T,
+                                                     const int (&woff)[P], const int (&gi)[P], const uint32_t *planes,
+                                                     int li, int g, bool grp, const int (&E)[kEntryRows], int nr, int o,
+                                                     int o_begin, int o_next, int lane, float (&outv)[kEntryRows]) {
+  constexpr int POS = rows16_positions<P>();
+  float fa[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) fa[i] = 0.f;
+  const float srow = st.s[0];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int i = 0; i < kEntryRows; ++i) {
+      if (i < nr) {
+        uint32_t X[kPlanes][4];
+        read_planes<4>(X, planes + i * kPlanes * POS, POS, p * kLR * 4 + li * 4);
+        int acc[kPlanes];
+#pragma unroll
+        for (int d = 0; d < kPlanes; ++d) acc[d] = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int d = 0; d < kPlanes; ++d)
+            acc[d] = __builtin_amdgcn_sdot8((int)st.w[p][v], (int)X[d][v], acc[d], false);
+        const float jd = join_digits(acc);
+        fa[i] = grp ? fmaf(jd, st.s[p], fa[i]) : fa[i] + jd;
+      }
+    }
+    load_pass16<P>(st, wr, sr, T, woff, gi, o_next, g, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) {
+    if (i < nr) {
+      const float sum = __builtin_ldexpf(row16_sum(grp ? fa[i] : fa[i] * srow), -E[i]);
+#pragma unroll
+      for (int q = 0; q < kGR; ++q) {
+        const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), q * kLR));
+        if (lane == o - o_begin + q) outv[i] = r;
+      }
+    }
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_rows16_entry(ProjArgs a) {
+  constexpr int V = 4;
+  constexpr int POS = rows16_positions<P>();
+  static_assert(POS <= kBlock, "one staged position per thread");
+  extern __shared__ uint32_t s_planes[];  // [entry_rows][kPlanes][POS]
+  __shared__ uint32_t s_max[kBlock / kWave];
+  const int lane = threadIdx.x & 63;
+  const int li = lane & (kLR - 1), g = lane / kLR;
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const CGroupBuf G = (CGroupBuf)a.grp;
+  const int jr = blockIdx.x / a.tile_groups;
+  const int tile = (blockIdx.x - jr * a.tile_groups) * (kBlock / kWave) + wib;
+  const TensorDesc T = ld_desc(G->rows[jr].t[2]);
+  const int live = G->rows[jr].t[0].live;
+  const int rank = G->rows[jr].t[1].live, size = G->rows[jr].t[2].live;
+  asm volatile("" ::"s"(T.q), "s"(T.s), "s"(T.O), "s"(T.C), "s"(T.row_bytes), "s"(T.gs), "s"(T.ng));
+  asm volatile("" ::"s"(live), "s"(rank), "s"(size));
+  if (!live) return;
+  const ChunkPos cp = chunk_of(rank, size, a.entry_rows, a.mfma_min);
+  const int nr = cp.nr;
+  if (nr == 0) return;
+  const int head = jr - cp.k;
+
+  const int C = a.C;
+  const int RD = (C + 7) >> 3;
+  const bool grp = T.ng > 1;
+  int gi[P], woff[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int ds = p * kLR * V + li * V;
+    gi[p] = (grp && ds < RD) ? (8 * ds) / T.gs : 0;
+    woff[p] = ds < RD ? 4 * ds : -1;
+  }
+  int o_begin, o_end;
+  sub_tile(tile * a.tile_rows, min(tile * a.tile_rows + a.tile_rows, a.O), a.tile_rows, nr, cp.k, kGR, o_begin,
+           o_end);
+  const bool work = o_begin < o_end;
+  const int rows_in = work ? o_end : 0;
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(T.q, rows_in * T.row_bytes);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(T.s, rows_in * T.ng * 4);
+
+  // every row's position, loaded unconditionally (rows past the chunk repeat its last row)
+  float xv[kEntryRows][1][8];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i)
+    load_position(xv[i][0], a.act, 0, (size_t)(head + min(i, nr - 1)) * a.act_ld, threadIdx.x, POS, C);
+  __builtin_amdgcn_sched_barrier(0);
+  Step16<P> b0, b1;
+  load_step16<P>(b0, wr, sr, T, woff, gi, o_begin, g);
+  __builtin_amdgcn_sched_barrier(0);
+  load_step16<P>(b1, wr, sr, T, woff, gi, o_begin + kGR, g);
+  __builtin_amdgcn_sched_barrier(0);
+  int E[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) {
+    E[i] = 0;
+    if (i < nr) E[i] = stage_planes<1>(s_planes + i * kPlanes * POS, POS, xv[i], s_max);
+  }
+  if (!work) {
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  float outv[kEntryRows];
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i) outv[i] = 0.f;
+  int o = o_begin;
+  do {
+    compute_step16_entry<P>(b0, wr, sr, T, woff, gi, s_planes, li, g, grp, E, nr, o, o_begin, o + 2 * kGR, lane, outv);
+    compute_step16_entry<P>(b1, wr, sr, T, woff, gi, s_planes, li, g, grp, E, nr, o + kGR, o_begin, o + 3 * kGR, lane,
+                            outv);
+    o += 2 * kGR;
+  } while (o < o_end);
+#pragma unroll
+  for (int i = 0; i < kEntryRows; ++i)
+    if (i < nr && lane < o_end - o_begin) a.out[(size_t)(head + i) * a.out_ld + o_begin + lane] = outv[i];
+}
+
 const void *rows16_ptr(int P) {
   switch (P) {
     case 1: return reinterpret_cast<const void *>(&k_rows16<1>);
@@ -918,13 +1255,54 @@ const void *kernel_ptr(int V, int P, int NT, bool gen, bool sel = false) {
 
 size_t lds_bytes(int V, int P) { return 4u * kPlanes * (size_t)P * 64 * V; }
 
+template <int NT>
+const void *entry_ptr_t(int V, int P) {
+#define I4MOE_PTR(v, p) \
+  if (V == v && P == p) return reinterpret_cast<const void *>(&k_proj_entry<v, p, NT>);
+  I4MOE_PTR(1, 1) I4MOE_PTR(1, 2) I4MOE_PTR(1, 3) I4MOE_PTR(1, 4)
+  I4MOE_PTR(2, 1) I4MOE_PTR(2, 2) I4MOE_PTR(2, 3) I4MOE_PTR(2, 4)
+  I4MOE_PTR(4, 1) I4MOE_PTR(4, 2) I4MOE_PTR(4, 3) I4MOE_PTR(4, 4)
+#undef I4MOE_PTR
+  return nullptr;
+}
+
+const void *rows16_entry_ptr(int P) {
+  switch (P) {
+    case 1: return reinterpret_cast<const void *>(&k_rows16_entry<1>);
+    case 2: return reinterpret_cast<const void *>(&k_rows16_entry<2>);
+    case 3: return reinterpret_cast<const void *>(&k_rows16_entry<3>);
+    case 4: return reinterpret_cast<const void *>(&k_rows16_entry<4>);
+    default: return nullptr;
+  }
+}
+
+// Dynamic LDS beyond 48 KB needs the kernel's limit raised (once per kernel and device).
+hipError_t raise_lds(const void *k, size_t lds) {
+  if (lds <= 48 * 1024) return hipSuccess;
+  constexpr int kKeys = 64;
+  static const void *keys[kKeys];
+  static bool done[kKeys][kMaxDevices];
+  static int nk = 0;
+  int i = 0;
+  while (i < nk && keys[i] != k) ++i;
+  if (i == nk) {
+    if (nk == kKeys) return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    keys[nk++] = k;
+  }
+  return raise_lds_once(k, (int)lds, done[i]);
+}
+
 hipError_t launch(int V, int P, int NT, bool gen, bool sel, const ProjArgs &a, int blocks, hipStream_t st,
                   hipEvent_t t0, hipEvent_t t1) {
-  const void *k = kernel_ptr(V, P, NT, gen, sel);
+  const bool entry = a.entry_rows > 0;
+  if (entry && (gen || sel || a.entry_rows > kEntryRows)) return hipErrorInvalidValue;
+  const void *k = entry ? (NT == 2 ? entry_ptr_t<2>(V, P) : entry_ptr_t<1>(V, P)) : kernel_ptr(V, P, NT, gen, sel);
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
-  const size_t lds = lds_bytes(V, P);
+  const size_t lds = lds_bytes(V, P) * (entry ? a.entry_rows : 1);
+  const hipError_t e = raise_lds(k, lds);
+  if (e != hipSuccess) return e;
   if (t0 || t1) return hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st, t0, t1, 0);
   return hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st);
 }
@@ -958,6 +1336,16 @@ hipError_t launch_dual(int V, int P, bool gen, bool sel, const ProjArgs &a, int 
   return e != hipSuccess ? e : hipGetLastError();
 }
 
+int entry_rows_fit(int V, int P, bool rows16, int want) {
+  // keep three workgroups' staged rows within a CU's 160 KB of LDS
+  constexpr size_t kBudget = 160 * 1024 / 3;
+  const size_t per_row = rows16 ? rows16_lds_bytes(P) : lds_bytes(V, P);
+  int n = (int)(kBudget / per_row);
+  n = n < 1 ? 1 : n;
+  n = n < want ? n : want;
+  return n < kEntryRows ? n : kEntryRows;
+}
+
 int rows16_blocks_per_cu(int P) {
   static int cache[5] = {};
   if (P < 1 || P > 4) return 1;
@@ -974,12 +1362,17 @@ int rows16_blocks_per_cu(int P) {
 }
 
 hipError_t launch_down16(int P, const ProjArgs &a, int blocks, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
-  const void *k = rows16_ptr(P);
+  const bool entry = a.entry_rows > 0;
+  if (a.entry_rows > kEntryRows) return hipErrorInvalidValue;
+  const void *k = entry ? rows16_entry_ptr(P) : rows16_ptr(P);
   if (!k) return hipErrorInvalidValue;
   ProjArgs args = a;
   void *params[] = {&args};
-  hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st, t0, t1, 0)
-                            : hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, rows16_lds_bytes(P), st);
+  const size_t lds = rows16_lds_bytes(P) * (entry ? a.entry_rows : 1);
+  hipError_t e = raise_lds(k, lds);
+  if (e != hipSuccess) return e;
+  e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st, t0, t1, 0)
+                 : hipLaunchKernel(k, dim3(blocks), dim3(kBlock), params, lds, st);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

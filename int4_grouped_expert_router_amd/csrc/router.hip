@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   __shared__ int s_pidx[kRows];
   __shared__ float s_pw[kRows];
   __shared__ int s_n[kTokens];
-  __shared__ int s_row_e[kRows], s_row_t[kRows];
+  __shared__ int s_row_e[kRows], s_row_t[kRows], s_row_rank[kRows], s_row_size[kRows];
   __shared__ float s_row_w[kRows];
   __shared__ int s_rows;
   __shared__ __attribute__((aligned(16))) uint32_t s_tab[kSelTabE * kDescWords];  // expert records, E <= 256
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_route_select(RouteArgs a) {
   // the scores, so the row descriptors need no further memory round trip at the end.
   const bool tab_pre = a.table != nullptr && a.E <= kSelTabE;
   uint32_t tv[kSelTabPerThread];
-  SelShared sh{s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, &s_rows, tab_pre ? s_tab : nullptr};
+  SelShared sh{s_pidx, s_pw, s_n, s_row_e, s_row_t, s_row_w, s_row_rank, s_row_size, &s_rows, tab_pre ? s_tab : nullptr};
   // behind each pass's first scores (the same records every pass, so the loads and the wait
   // counts do not depend on the pass)
   const int tab_bytes = tab_pre ? a.E * (int)sizeof(ExpertRec) : 0;

@@ -11,6 +11,8 @@ namespace i4moe {
 constexpr int kWavesPerBlock = kBlock / kWave;                 // 4
 constexpr int kTabWords = 3 * sizeof(TensorDesc) / 4;          // tensor words of a row descriptor
 constexpr int kLiveWord = offsetof(TensorDesc, live) / 4;     // t[0].live inside a row descriptor
+constexpr int kRankWord = kLiveWord + sizeof(TensorDesc) / 4;  // t[1].live: the row's rank in its entry
+constexpr int kSizeWord = kRankWord + sizeof(TensorDesc) / 4;  // t[2].live: its entry's row count
 constexpr int kDescWords = sizeof(RowDesc) / 4;               // 32
 constexpr int kTabPrefetchE = 64;                             // fused selection: records staged early
 constexpr int kTabPerThread = kTabPrefetchE * kDescWords / kBlock;
@@ -36,6 +38,7 @@ struct SelShared {
   int *n;                // [t]: kept count after top-p
   int *row_e, *row_t;    // per group row: expert, token
   float *row_w;          // per group row: weight
+  int *row_rank, *row_size;  // per group row: rank in its entry, the entry's row count
   int *rows;             // group rows
   const uint32_t *tab;   // staged expert records [E][32], or null
 };
@@ -304,6 +307,7 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
   const float *s_pw = sh.pw;
   const int *s_n = sh.n;
   int *s_row_e = sh.row_e, *s_row_t = sh.row_t;
+  int *s_row_rank = sh.row_rank, *s_row_size = sh.row_size;
   float *s_row_w = sh.row_w;
   int &s_rows = *sh.rows;
   const bool tab_pre = sh.tab != nullptr;
@@ -328,6 +332,8 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_row_e[lane] = e;
         s_row_t[lane] = 0;
         s_row_w[lane] = w;
+        s_row_rank[lane] = 0;
+        s_row_size[lane] = 1;
       }
       if (lane == 0) {
         G->entry_row0[n] = n;
@@ -395,6 +401,8 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_row_e[my_row] = my_e;
         s_row_t[my_row] = my_t;
         s_row_w[my_row] = my_w;
+        s_row_rank[my_row] = rank;
+        s_row_size[my_row] = __popcll(same);
       }
       if (lane < S) G->tok_row0[lane] = tok0;
       if (lane == 0) {
@@ -436,6 +444,8 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
     if (row < rows) {
       val = v[j];
       if (c == kLiveWord / 4) val[kLiveWord % 4] = 1u;
+      if (c == kRankWord / 4) val[kRankWord % 4] = (uint32_t)s_row_rank[row];
+      if (c == kSizeWord / 4) val[kSizeWord % 4] = (uint32_t)s_row_size[row];
       if (c == kChunks - 1) {
         val.z = (uint32_t)s_row_t[row];
         val.w = __float_as_uint(s_row_w[row]);

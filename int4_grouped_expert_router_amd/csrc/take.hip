@@ -115,10 +115,14 @@ __global__ void k_group_store(GroupDev g, const ExpertRec *table, GroupBuf *dst)
     RowDesc &rd = dst->rows[r];
     if (r < g.n_rows) {
       const int e = g.row_expert[r];
+      int j = 0;  // the row's entry (entries list their rows consecutively, in row order)
+      while (j + 1 < g.n_entries && g.entry_row0[j + 1] <= r) ++j;
       rd.t[0] = table[e].t[0];
       rd.t[1] = table[e].t[1];
       rd.t[2] = table[e].t[2];
       rd.t[0].live = 1;
+      rd.t[1].live = r - g.entry_row0[j];                    // rank in the entry
+      rd.t[2].live = g.entry_row0[j + 1] - g.entry_row0[j];  // the entry's rows
       rd.token = g.row_token[r];
       rd.weight = g.row_weight[r];
     } else {
