@@ -187,7 +187,10 @@ def measure(name, layers, steps, warmup, torch, B, eager=False):
             step(i)
     torch.cuda.synchronize()
     kt = {k: ctx.profile(v) for k, v in
-          [("route", B.I4MOE_K_ROUTE), ("dual", B.I4MOE_K_DUAL), ("down", B.I4MOE_K_DOWN), ("take", B.I4MOE_K_TAKE)]}
+          [("route", B.I4MOE_K_ROUTE), ("dual", B.I4MOE_K_DUAL), ("down", B.I4MOE_K_DOWN), ("take", B.I4MOE_K_TAKE),
+           ("mfma", B.I4MOE_K_MFMA)]}
+    if kt["mfma"][1] == 0:
+        del kt["mfma"]
     launch = "graph" if graph is not None else "eager stream"
     del graph
     torch.cuda.synchronize()
@@ -227,6 +230,77 @@ def measure(name, layers, steps, warmup, torch, B, eager=False):
         res["down_GBps"] = round(dn_bytes / (down_ms * 1e-3) / 1e9, 1)
         res["down_pct_hbm_peak"] = round(100 * dn_bytes / (down_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
     return res, cfg
+
+
+# Rows per expert in one issue: the vector kernels one row at a time, the vector kernels with
+# rows sharing weight passes, the matrix cores (every entry of 2 rows or more), and the library's
+# own choice.
+CROSS_ROWS = (1, 2, 3, 4, 8, 12, 16, 24, 32, 48, 64)
+CROSS_MODES = {"per_row": {"I4MOE_ENTRY_ROWS": "0", "I4MOE_MFMA_MIN_ROWS": "0"},
+               "shared_passes": {"I4MOE_ENTRY_ROWS": "4", "I4MOE_MFMA_MIN_ROWS": "0"},
+               "matrix_cores": {"I4MOE_ENTRY_ROWS": "0", "I4MOE_MFMA_MIN_ROWS": "2"},
+               "automatic": {}}
+
+
+def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, modes=tuple(CROSS_MODES)):
+    """Device time of one issue + take for explicit groups of R rows per expert (S = 64 tokens,
+    min(8, 64 // R) experts per issue, rotating over 32 experts of the small-batch shape so the
+    weights stream from HBM), under each launch mode; prints one JSON line per R."""
+    from int4_grouped_expert_router_amd import Context
+    from synth import gen_layer, get_config
+    from synth.gen import gen_expert
+    cfg = get_config("small_batch", S=64, E=n_experts)
+    L = gen_layer(cfg, 0)
+    with cf.ThreadPoolExecutor(WORKERS) as pool:
+        ews = list(pool.map(lambda e: gen_expert(cfg, 0, e), range(n_experts)))
+    per_expert = tensor_bytes(ews[0].gate) + tensor_bytes(ews[0].up) + tensor_bytes(ews[0].down)
+    x = torch.from_numpy(L.x.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
+    out = torch.zeros((cfg.S, cfg.D), dtype=torch.float32, device="cuda:0")
+    table = {R: {"rows_per_expert": R, "experts_per_issue": max(1, min(8, cfg.S // R))} for R in rows}
+    for mode in modes:
+        env = CROSS_MODES[mode]
+        saved = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        ctx = Context(0, torch.cuda.current_stream())
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k)
+            else:
+                os.environ[k] = v
+        for e, ew in enumerate(ews):
+            ctx.set_expert(0, e, ctx.upload_host_tensor(ew.gate), ctx.upload_host_tensor(ew.up),
+                           ctx.upload_host_tensor(ew.down))
+        for R in rows:
+            n = table[R]["experts_per_issue"]
+
+            def group(it):
+                ex = [(it * n + k) % n_experts for k in range(n)]
+                return [(e, (k * R + j) % cfg.S, 0.5) for k, e in enumerate(ex) for j in range(R)]
+
+            for it in range(3):
+                ctx.issue(0, x, rows=group(it))
+                ctx.take(out)
+            torch.cuda.synchronize()
+            ctx.set_profiling(True)
+            for it in range(reps):
+                ctx.issue(0, x, rows=group(it))
+                ctx.take(out)
+            torch.cuda.synchronize()
+            kt = {k: ctx.profile(v) for k, v in [("dual", B.I4MOE_K_DUAL), ("down", B.I4MOE_K_DOWN),
+                                                 ("mfma", B.I4MOE_K_MFMA), ("take", B.I4MOE_K_TAKE)]}
+            ctx.set_profiling(False)
+            dev_us = sum(v[0] for v in kt.values()) * 1e3 / reps
+            table[R][mode] = {"device_us_per_issue": round(dev_us, 2),
+                              "device_us_per_expert": round(dev_us / n, 3),
+                              "weight_GBps": round(per_expert * n / (dev_us * 1e-6) / 1e9, 1),
+                              "kernel_us": {k: round(v[0] * 1e3 / reps, 2) for k, v in kt.items() if v[1]}}
+            log(f"crossover {mode} R={R}: {dev_us:.1f} us per issue")
+        ctx.close()
+        torch.cuda.empty_cache()
+    for R in rows:
+        best = min(modes, key=lambda m: table[R][m]["device_us_per_issue"])
+        table[R]["fastest"] = best
+        print(json.dumps(table[R]), flush=True)
 
 
 def blas_threads():
@@ -294,6 +368,10 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="measure the headline workload only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (scale for the HBM byte counters)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only time explicit groups of 1..64 rows per expert under each launch mode")
+    ap.add_argument("--crossover-rows", default="", help="comma-separated rows per expert (default: all)")
+    ap.add_argument("--crossover-modes", default="", help="comma-separated launch modes (default: all)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -310,6 +388,11 @@ def main():
     from synth import get_config
 
     torch.cuda.set_device(0)
+    if args.crossover:
+        rows = tuple(int(v) for v in args.crossover_rows.split(",")) if args.crossover_rows else CROSS_ROWS
+        modes = tuple(args.crossover_modes.split(",")) if args.crossover_modes else tuple(CROSS_MODES)
+        crossover(torch, B, rows=rows, modes=modes)
+        return
     layers = args.layers or get_config(args.workload).layers
     head, cfg = measure(args.workload, layers, args.steps, args.warmup, torch, B, eager=args.eager)
     log(f"{args.workload}: {head['us_per_layer']} us/layer")

@@ -92,9 +92,9 @@ typedef struct {
 
 /* Explicit group for issue (host arrays of n_rows entries): each row runs expert[r] on token
  * row token[r] of x and is weighted by weight[r].  Per token, rows are summed in the order
- * listed.  The rows of one expert run together: up to 4 of them share each pass over its
- * weights when enough rows share (see I4MOE_ENTRY_ROWS at i4moe_ctx_create), and an expert with
- * at least 16 rows runs on the matrix cores (I4MOE_MFMA_MIN_ROWS). */
+ * listed.  An expert with at least 16 rows in the group runs on the matrix cores
+ * (I4MOE_MFMA_MIN_ROWS at i4moe_ctx_create), the others on the vector kernels, one row per
+ * workgroup (or up to 4 rows per weight pass with I4MOE_ENTRY_ROWS). */
 typedef struct {
   int32_t n_rows;
   const int32_t *expert;
@@ -109,11 +109,12 @@ typedef struct {
  * I4MOE_WAVE_FACTOR (0.05 .. 64, default 1) scales the number of waves the projections aim
  * for per CU; it changes how output rows are tiled over waves, never the results (each row
  * is still reduced by one wave in a fixed order).
- * I4MOE_ENTRY_ROWS sets how rows of one expert (S > 1) share weight passes: 0 never, 2..4 always
- * (at most that many rows per pass), unset automatic (when at least a quarter of the rows would
- * ride on another row's pass).  It changes only the order of additions: a group-wise tensor's
- * results are the same bits either way, a per-row tensor's may differ in the last bits (both
- * within the documented tolerance of the f64 result).
+ * I4MOE_ENTRY_ROWS (2..4; unset or 0: one row per workgroup) lets up to that many rows of one
+ * expert (S > 1) share each pass over its weights in the vector kernels.  Off by default: it
+ * measured slower than one row per workgroup at every row count (rows of one expert running
+ * together re-read its weights mostly from cache).  It changes only the order of additions: a
+ * group-wise tensor's results are the same bits either way, a per-row tensor's may differ in the
+ * last bits (both within the documented tolerance of the f64 result).
  * I4MOE_MFMA_MIN_ROWS (0 = off, else 2 .. 64; default 16) is the row count from which an
  * expert's rows in one issue run on the matrix cores (int8 products of digit rows, exact like
  * the vector kernels; gate/up/down of every expert of the issue per-row or with group sizes

@@ -61,7 +61,6 @@ struct SlotInfo {
 };
 
 constexpr int kRing = 32;
-constexpr double kEntryMinShare = 0.25;  // rows sharing another row's weight pass, to share passes
 constexpr int kMfmaMinRows = 16;          // rows of one expert from which the matrix cores pay  // route buffers: a layer may be re-routed up to 31 times before a take
 
 struct ProfRec {
@@ -101,7 +100,7 @@ struct i4moe_ctx {
   SlotInfo slots[kSlots];
   int n_cu = 256;
   double wave_factor = 1.0;
-  int entry_mode = -1;     // rows of one expert per weight pass: -1 automatic, 0 never, 2..4 always
+  int entry_mode = 0;      // rows of one expert per weight pass: 0 one, 2..4 up to that many
   int mfma_min = kMfmaMinRows;  // rows from which an entry runs on the matrix cores (0: never)
   int8_t *d_dig = nullptr;      // [kRows][3][kMaxCols] digit rows of the matrix-core projections
   int *d_dig_E = nullptr;       // [kRows] their row exponents
@@ -1049,39 +1048,29 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   an.tile_groups = pn.tile_groups;
   an.grid_rows = max_rows;
   an.tile_rows = pn.tile_rows;
-  // Several tokens: the rows of one expert may share each weight pass.  Automatic mode shares
-  // when at least a quarter of the rows would ride on another row's pass: counted exactly for an
-  // explicit group, and for a device route estimated from S tokens picking K of E experts
-  // uniformly (E (1 - (1 - K/E)^S) distinct experts expected).  Below that the shared passes
-  // cost more than they save: a workgroup running nr rows does nr times the dot products per
-  // weight byte.
-  if (S > 1 && c->entry_mode != 0) {
+  // Several tokens: the rows of one expert may share each weight pass (I4MOE_ENTRY_ROWS).  Not
+  // by default: measured on the small-batch shape at 1 to 64 rows per expert, the shared passes
+  // were slower than one row per workgroup at every row count (rows of one expert that run
+  // together re-read its weights mostly from L2 and the Infinity Cache, while a workgroup running
+  // nr rows does nr times the dot products per weight byte); from 16 rows the matrix cores win.
+  if (S > 1 && c->entry_mode > 0) {
     int most = S;  // a device route gives an expert at most one row per token
-    double share;
     if (group) {
       most = 0;
       for (int j = 0; j < hg.n_entries; ++j) most = std::max(most, hg.entry_row0[j + 1] - hg.entry_row0[j]);
-      const int er = std::min(most, kEntryRows);
-      int chunks = 0;
-      for (int j = 0; j < hg.n_entries; ++j) chunks += (hg.entry_row0[j + 1] - hg.entry_row0[j] + er - 1) / er;
-      share = 1.0 - (double)chunks / hg.n_rows;
-    } else {
-      const double E = L->E, K = L->route_K;
-      share = 1.0 - E * (1.0 - std::pow(1.0 - K / E, S)) / (S * K);
     }
-    if (c->entry_mode > 0 || share >= kEntryMinShare) {
-      const int want = c->entry_mode > 0 ? std::min(most, c->entry_mode) : most;
-      const int ed = entry_rows_fit(pd.V, pd.P, false, want);
-      const int en = entry_rows_fit(pn.V, pn.P, pn.rows16, want);
-      if (ed > 1 && !pd.gen) ad.entry_rows = ed;
-      if (en > 1 && (pn.rows16 || !pn.gen)) an.entry_rows = en;
-    }
+    const int want = std::min(most, c->entry_mode);
+    const int ed = entry_rows_fit(pd.V, pd.P, false, want);
+    const int en = entry_rows_fit(pn.V, pn.P, pn.rows16, want);
+    if (ed > 1 && !pd.gen) ad.entry_rows = ed;
+    if (en > 1 && (pn.rows16 || !pn.gen)) an.entry_rows = en;
   }
 
   // Entries of at least mfma_min rows run on the matrix cores (every tensor of the issue per-row
   // or with group sizes that are multiples of 64); the vector kernels then take the chunked path,
   // which skips those entries.
   int mfma_min = 0, mfma_slots = 0, mfma_tiles = 0;
+  bool vec_rows = true;  // some entry runs on the vector kernels (always possible for a device route)
   if (S > 1 && c->mfma_min > 0) {
     bool fmt_ok = true;
     for (int gs : gs_in) fmt_ok = fmt_ok && gs % 64 == 0;
@@ -1094,6 +1083,7 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
         most = std::max(most, n);
         if (n >= c->mfma_min) ++n_big;
       }
+      vec_rows = n_big < hg.n_entries;
     }
     if (fmt_ok && most >= c->mfma_min && n_big > 0) {
       mfma_min = c->mfma_min;
@@ -1103,6 +1093,8 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
       ad.mfma_min = an.mfma_min = mfma_min;
       if (ad.entry_rows == 0) ad.entry_rows = 1;
       if (an.entry_rows == 0) an.entry_rows = 1;
+    } else {
+      vec_rows = true;
     }
   }
 
@@ -1155,12 +1147,12 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
       return r != hipSuccess ? r : launch_mfma(dual ? 2 : 1, ma, c->stream, nullptr, t1);
     });
   };
-  if (e == hipSuccess) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
+  if (e == hipSuccess && vec_rows) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {
       return launch_dual(pd.V, pd.P, pd.gen, sel, ad, pd.blocks, c->stream, t0, t1);
     });
   if (e == hipSuccess && sel) c->sel_pending = false;
   if (e == hipSuccess && mfma_min) e = mfma(true);
-  if (e == hipSuccess && !defer_down) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
+  if (e == hipSuccess && !defer_down && vec_rows) e = timed(c, I4MOE_K_DOWN, [&](hipEvent_t t0, hipEvent_t t1) {
       return pn.rows16 ? launch_down16(pn.P, an, pn.blocks, c->stream, t0, t1)
                        : launch_down(pn.V, pn.P, pn.gen, an, pn.blocks, c->stream, t0, t1);
     });

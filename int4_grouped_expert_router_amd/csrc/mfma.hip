@@ -13,9 +13,10 @@
 // scaled after every 64 columns (group sizes are multiples of 64); a per-row tensor keeps its
 // integer sums to the end.  The result is (join) 2^-E / 16.
 //
-// Tiling: a workgroup owns 16 output rows x 16 rows of one entry (an expert's group rows, its
-// token tile); its 8 waves split the columns, and their partial results meet in LDS, summed in
-// wave order.  MFMA operands: A = 16 activation rows x 64 columns (lane l: row l % 16, bytes of
+// Tiling: a workgroup owns 32 output rows x 16 rows of one entry (an expert's group rows, its
+// token tile); its waves (up to 8, each with at least 8 steps of 64 columns) split the columns,
+// and their partial results meet in LDS, summed in wave order.  Each wave keeps two steps of
+// loads in flight.  MFMA operands: A = 16 activation rows x 64 columns (lane l: row l % 16, bytes of
 // columns 16 (l / 16) .. +15 of the step), B = 64 columns x 16 weight rows (lane l: weight row
 // l % 16, the same columns), so the 4 result dwords of lane l are rows 4 (l / 16) + v of the
 // activation tile against weight row l % 16: one lane holds one weight row, and the row's scale
@@ -102,21 +103,26 @@ __device__ __forceinline__ float join3(const v4i (&acc)[kDigits], int v) {
   return fmaf((float)acc[2][v], 65536.f, fmaf((float)acc[1][v], 256.f, (float)acc[0][v]));
 }
 
+constexpr int kWT = 2;  // weight tiles (16 rows each) per wave
+
+constexpr int kWaveGroups = 16;  // scale groups of one wave's columns: at most 16 steps of 64
+
 template <int NT>
 struct MStep {
-  uint32_t w[NT][2];
+  uint32_t w[kWT][NT][2];
   v4i x[kDigits];
-  float s[NT];
 };
 
 template <int NT>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
-  __shared__ float s_part[kMfmaWaves][NT][kWave * 4];
+  __shared__ float s_part[kMfmaWaves][kWT][NT][kWave * 4];
+  __shared__ float s_scale[kMfmaWaves][kWT][NT][16][kWaveGroups];  // each wave's group scales
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Logical tiles (entry slot, weight tile, token tile), token tile fastest; the blocks of one
-  // XCD (block index mod 8) take one contiguous run of them, so the token tiles of a weight tile
-  // re-read its weights from the same L2.
+  const int KW = blockDim.x >> 6;  // waves splitting the columns
+  // Logical tiles (entry slot, weight tile pair, token tile), token tile fastest; the blocks of
+  // one XCD (block index mod 8) take one contiguous run of them, so the token tiles of a weight
+  // tile re-read its weights from the same L2.
   const int L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   if (L >= a.tiles) return;
   const int tt = L % a.token_tiles;
@@ -143,14 +149,11 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
     const TensorDesc I4MOE_AS4 &d = G->rows[start].t[NT == 2 ? n : 2];
     T[n].q = d.q;
     T[n].s = d.s;
-    T[n].O = d.O;
-    T[n].C = d.C;
     T[n].row_bytes = d.row_bytes;
     T[n].gs = d.gs;
     T[n].ng = d.ng;
   }
   const int O = a.O;
-  const int o0 = 16 * wt;
   const int li = lane & 15, q = lane >> 4;
 
   // A operand rows: lane row li of the token tile; rows past the entry read zeros
@@ -158,11 +161,16 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
   const bool a_ok = 16 * tt + li < size;
   const int drow = a_ok ? (a.dual ? a.grp->rows[arow_g].token : arow_g) : 0;
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.dig, a.dig_rows * kDigits * a.C64);
-  const int xoff0 = a_ok ? drow * kDigits * a.C64 + 16 * q : 0x7ffffff0;
+  const int xoff0 = a_ok ? drow * kDigits * a.C64 + 16 * q : -1;  // -1: no row
 
-  // B operand: weight row o0 + li of each tensor; rows past O read zeros
-  const int orow = o0 + li;
-  const bool o_ok = orow < O;
+  // B operands: weight rows 16 (kWT wt + t) + li of each tensor; rows past O read zeros
+  int orow[kWT];
+  bool o_ok[kWT];
+#pragma unroll
+  for (int t = 0; t < kWT; ++t) {
+    orow[t] = 16 * (kWT * wt + t) + li;
+    o_ok[t] = orow[t] < O;
+  }
   __amdgpu_buffer_rsrc_t wr[NT], sr[NT];
   bool grp[NT];
 #pragma unroll
@@ -173,73 +181,117 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
   }
 
   const int KS = a.C64 / 64;
-  const int s0 = (w * KS) / kMfmaWaves, s1 = ((w + 1) * KS) / kMfmaWaves;
+  const int s0 = (w * KS) / KW, s1 = ((w + 1) * KS) / KW;
+  // Per-lane base offsets, fixed for the whole loop; a step adds a wave-uniform term, so the
+  // loads carry no conditions (a row past O, or an activation row past the entry, gets a base
+  // beyond its buffer and reads zeros).  A weight step reaching past a row's padded bytes reads
+  // the next row's first bytes, but those columns (C and up) have zero digits; loads of steps
+  // past this wave's range are issued and never used.
+  constexpr int kFar = 0x40000000;
+  int wbase[kWT][NT];
+#pragma unroll
+  for (int t = 0; t < kWT; ++t)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      wbase[t][n] = o_ok[t] ? orow[t] * T[n].row_bytes + 8 * q : kFar;
+    }
+  // The group scales of this wave's columns, staged in the wave's own LDS region once (a step
+  // then reads its scale there instead of issuing a load per row): lane (row li, quarter q) loads
+  // groups g0 + 4q .. g0 + 4q + 3 of its row (past the row's scales: unused values).
+  int g0[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) g0[n] = grp[n] ? (64 * s0) / T[n].gs : 0;
+#pragma unroll
+  for (int t = 0; t < kWT; ++t)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int off = (o_ok[t] && grp[n]) ? 4 * (orow[t] * T[n].ng + g0[n] + 4 * q) : kFar;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(sr[n], off, 0, 0);
+      *reinterpret_cast<u32x4 *>(&s_scale[w][t][n][li][4 * q]) = v;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int xbase = xoff0 >= 0 ? xoff0 : kFar;
   auto load = [&](MStep<NT> &st, int s) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int b = 32 * s + 8 * q;  // this lane's 8 bytes of the step in the weight row
-      const int off = (o_ok && b < T[n].row_bytes) ? orow * T[n].row_bytes + b : 0x7ffffff0;
-      const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(wr[n], off, 0, kNontemporal);
-      st.w[n][0] = u.x;
-      st.w[n][1] = u.y;
-      const int soff = o_ok ? 4 * (orow * T[n].ng + (grp[n] ? (64 * s) / T[n].gs : 0)) : 0x7ffffff0;
-      st.s[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr[n], soff, 0, 0));
-    }
+    for (int t = 0; t < kWT; ++t)
 #pragma unroll
-    for (int d = 0; d < kDigits; ++d) {
-      const int off = xoff0 == 0x7ffffff0 ? xoff0 : xoff0 + d * a.C64 + 64 * s;
-      st.x[d] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
+      for (int n = 0; n < NT; ++n) {
+        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(wr[n], wbase[t][n] + 32 * s, 0, kNontemporal);
+        st.w[t][n][0] = u.x;
+        st.w[t][n][1] = u.y;
+      }
+#pragma unroll
+    for (int d = 0; d < kDigits; ++d)
+      st.x[d] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, xbase + d * a.C64 + 64 * s, 0, 0));
   };
 
-  v4i acc[NT][kDigits];
-  float F[NT][4];
-  float srow[NT];
+  v4i acc[kWT][NT][kDigits];
+  float F[kWT][NT][4];
+  float srow[kWT][NT];  // a per-row tensor's row scale
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    srow[n] = 0.f;
-#pragma unroll
-    for (int d = 0; d < kDigits; ++d) acc[n][d] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) F[n][v] = 0.f;
-  }
-  MStep<NT> cur, nxt;
-  if (s0 < s1) load(cur, s0);
-  for (int s = s0; s < s1; ++s) {
-    if (s + 1 < s1) load(nxt, s + 1);
+  for (int t = 0; t < kWT; ++t)
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const v4i B = weight_operand(cur.w[n][0], cur.w[n][1]);
+      srow[t][n] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(sr[n], o_ok[t] && !grp[n] ? 4 * orow[t] : 0x7ffffff0, 0, 0));
 #pragma unroll
-      for (int d = 0; d < kDigits; ++d) acc[n][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.x[d], B, acc[n][d], 0, 0, 0);
-      if (grp[n]) {
+      for (int d = 0; d < kDigits; ++d) acc[t][n][d] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) F[n][v] = fmaf(join3(acc[n], v), cur.s[n], F[n][v]);
-#pragma unroll
-        for (int d = 0; d < kDigits; ++d) acc[n][d] = v4i{0, 0, 0, 0};
-      } else {
-        srow[n] = cur.s[n];
-      }
+      for (int v = 0; v < 4; ++v) F[t][n][v] = 0.f;
     }
-    cur = nxt;
+  auto compute = [&](const MStep<NT> &st, int s) {
+#pragma unroll
+    for (int t = 0; t < kWT; ++t)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const v4i B = weight_operand(st.w[t][n][0], st.w[t][n][1]);
+#pragma unroll
+        for (int d = 0; d < kDigits; ++d)
+          acc[t][n][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.x[d], B, acc[t][n][d], 0, 0, 0);
+        if (grp[n]) {
+          const float sc = s_scale[w][t][n][li][(64 * s) / T[n].gs - g0[n]];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) F[t][n][v] = fmaf(join3(acc[t][n], v), sc, F[t][n][v]);
+#pragma unroll
+          for (int d = 0; d < kDigits; ++d) acc[t][n][d] = v4i{0, 0, 0, 0};
+        }
+      }
+  };
+  // two steps in flight: each step's registers are refilled with the step after next as soon as
+  // it is consumed; the loop runs in pairs
+  MStep<NT> b0, b1;
+  load(b0, s0);
+  load(b1, s0 + 1);
+  for (int s = s0; s < s1; s += 2) {
+    compute(b0, s);
+    load(b0, s + 2);
+    if (s + 1 < s1) compute(b1, s + 1);  // an odd last step
+    load(b1, s + 3);
   }
+  __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-    if (!grp[n])
+  for (int t = 0; t < kWT; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) F[n][v] = join3(acc[n], v) * srow[n];
+    for (int n = 0; n < NT; ++n)
+      if (!grp[n])
+#pragma unroll
+        for (int v = 0; v < 4; ++v) F[t][n][v] = join3(acc[t][n], v) * srow[t][n];
 
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int t = 0; t < kWT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s_part[w][n][lane * 4 + v] = F[n][v];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_part[w][t][n][lane * 4 + v] = F[t][n][v];
   __syncthreads();
-  // one output per thread of the first four waves: lane l2 = t / 4 of the result layout, v = t % 4
-  const int t = threadIdx.x;
-  if (t < kWave * 4) {
-    const int l2 = t >> 2, v = t & 3;
-    const int m = 4 * (l2 >> 4) + v;  // row of the token tile
-    const int o = o0 + (l2 & 15);     // weight row
+  // one output per thread: weight tile t, lane l2 = i / 4 of the result layout, v = i % 4
+  for (int i = threadIdx.x; i < kWT * kWave * 4; i += blockDim.x) {
+    const int t = i / (kWave * 4), e = i % (kWave * 4);
+    const int l2 = e >> 2, v = e & 3;
+    const int m = 4 * (l2 >> 4) + v;               // row of the token tile
+    const int o = 16 * (kWT * wt + t) + (l2 & 15);  // weight row
     if (16 * tt + m < size && o < O) {
       const int rg = start + 16 * tt + m;
       const int dr = a.dual ? a.grp->rows[rg].token : rg;
@@ -248,8 +300,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         float acc_w = 0.f;
-#pragma unroll
-        for (int k = 0; k < kMfmaWaves; ++k) acc_w += s_part[k][n][t];
+        for (int k = 0; k < KW; ++k) acc_w += s_part[k][t][n][e];
         sum[n] = __builtin_ldexpf(acc_w, -E - 4);
       }
       float res = sum[0];
@@ -275,14 +326,18 @@ hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEve
   if ((NT != 1 && NT != 2) || a.mfma_min < 1 || a.C64 % 64 != 0 || a.C64 > kMaxCols || a.dig_rows < 1 ||
       a.dig_rows > kRows || a.slots < 0 || a.slots > kRows || a.token_tiles < 1 || a.token_tiles > kRows / 16)
     return hipErrorInvalidValue;
-  a.weight_tiles = (a.O + 15) / 16;
+  a.weight_tiles = (a.O + 16 * kWT - 1) / (16 * kWT);
   a.tiles = a.slots * a.weight_tiles * a.token_tiles;
   if (a.tiles < 1) return hipSuccess;
+  // waves splitting the columns: at least 8 steps of 64 columns each, at most kMfmaWaves
+  const int KS = a.C64 / 64;
+  int kw = KS / 8;
+  kw = kw < 1 ? 1 : (kw > kMfmaWaves ? kMfmaWaves : kw);
   const int blocks = (a.tiles + 7) / 8 * 8;
   const void *k = NT == 2 ? reinterpret_cast<const void *>(&k_mfma<2>) : reinterpret_cast<const void *>(&k_mfma<1>);
   void *params[] = {&a};
-  const hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMfmaWaves * kWave), params, 0, st, t0, t1, 0)
-                                  : hipLaunchKernel(k, dim3(blocks), dim3(kMfmaWaves * kWave), params, 0, st);
+  const hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kw * kWave), params, 0, st, t0, t1, 0)
+                                  : hipLaunchKernel(k, dim3(blocks), dim3(kw * kWave), params, 0, st);
   return e != hipSuccess ? e : hipGetLastError();
 }
 
