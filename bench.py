@@ -303,6 +303,67 @@ def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, mo
         print(json.dumps(table[R]), flush=True)
 
 
+def tiered(torch, B, reps: int = 20):
+    """The CPU tier's overlap: experts of the small-batch shape (D=6144, I=2048, g64, bf16; 64
+    experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1 and 4.
+    Per S: wall time of the device rows alone, the host rows alone, and both in one tiered issue
+    (route copy to the host excluded: the routes are computed once); prints one JSON line per S."""
+    from int4_grouped_expert_router_amd import Context
+    from synth import gen_layer, get_config
+    from synth.gen import gen_expert
+    for S in (1, 4):
+        cfg = get_config("small_batch", S=S, E=64)
+        L = gen_layer(cfg, 0)
+        ctx = Context(0, torch.cuda.current_stream())
+        ctx.upload_router(0, L.router_W, L.router_b)
+        with cf.ThreadPoolExecutor(WORKERS) as pool:
+            for e, ew in enumerate(pool.map(lambda e: gen_expert(cfg, 0, e), range(cfg.E))):
+                if e % 2:
+                    ctx.set_host_expert(0, e, ew.gate, ew.up, ew.down)
+                else:
+                    ctx.set_expert(0, e, ctx.upload_host_tensor(ew.gate), ctx.upload_host_tensor(ew.up),
+                                   ctx.upload_host_tensor(ew.down))
+        x = torch.from_numpy(L.x.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
+        out = torch.zeros((S, cfg.D), dtype=torch.float32, device="cuda:0")
+        rec = list(ctx.route(0, x, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True))
+
+        def only(keep):
+            rs = [B.i4moe_route_host() for _ in range(S)]
+            for t in range(S):
+                ks = [k for k in range(rec[t].n) if keep(rec[t].idx[k])]
+                rs[t].n = len(ks)
+                for j, k in enumerate(ks):
+                    rs[t].idx[j], rs[t].w[j] = rec[t].idx[k], rec[t].w[k]
+            return rs
+
+        arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": only(lambda e: e % 2 == 1), "tiered": rec}
+        res = {"S": S, "threads": None}
+        for name, routes in arms.items():
+            for _ in range(3):
+                ctx.tiered_issue(0, x, routes)
+                ctx.take(out)
+            torch.cuda.synchronize()
+            walls, cpus = [], []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                _, tt = ctx.tiered_issue(0, x, routes)
+                ctx.take(out)
+                torch.cuda.synchronize()
+                walls.append(time.perf_counter() - t0)
+                cpus.append(tt.cpu_ms)
+            res[name + "_ms"] = round(float(np.median(walls)) * 1e3, 3)
+            if name == "tiered":
+                res["device_rows"], res["host_rows"] = tt.device_rows, tt.host_rows
+                res["tiered_cpu_ms"] = round(float(np.median(cpus)), 3)
+        res["serial_ms"] = round(res["device_only_ms"] + res["host_only_ms"], 3)
+        res["hidden_ms"] = round(res["serial_ms"] - res["tiered_ms"], 3)
+        res["threads"] = int(os.environ.get("I4MOE_HOST_THREADS", "0")) or min(16, os.cpu_count() or 1)
+        log(f"tiered S={S}: {res}")
+        print(json.dumps(res), flush=True)
+        ctx.close()
+        torch.cuda.empty_cache()
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -371,6 +432,8 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="only time explicit groups of 1..64 rows per expert under each launch mode")
     ap.add_argument("--crossover-rows", default="", help="comma-separated rows per expert (default: all)")
+    ap.add_argument("--tiered", action="store_true",
+                    help="only time the CPU tier: device rows, host rows, and both overlapped")
     ap.add_argument("--crossover-modes", default="", help="comma-separated launch modes (default: all)")
     args = ap.parse_args()
 
@@ -388,6 +451,9 @@ def main():
     from synth import get_config
 
     torch.cuda.set_device(0)
+    if args.tiered:
+        tiered(torch, B)
+        return
     if args.crossover:
         rows = tuple(int(v) for v in args.crossover_rows.split(",")) if args.crossover_rows else CROSS_ROWS
         modes = tuple(args.crossover_modes.split(",")) if args.crossover_modes else tuple(CROSS_MODES)

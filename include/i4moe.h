@@ -296,6 +296,49 @@ size_t i4moe_debug_size(i4moe_ctx *ctx, int what, int index);
  * red_rows[tok_row0[t] .. tok_row0[t+1]-1]. */
 #define I4MOE_GROUP_WORDS (4 + 64 + 65 + 64 + 64 + 64 + 65 + 64)
 
+/* ---- the CPU tier [PR342] ------------------------------------------------------------------ */
+
+/* One int4 tensor in host memory, in the layout of i4moe_upload_expert_tensor. */
+typedef struct {
+  int32_t fmt, gs, O, C;
+  const uint8_t *packed;
+  const float *scales;
+} i4moe_host_tensor;
+
+/* Keep expert `expert` of `layer` on the host (gate and up I x D, down D x I, formats and layout
+ * as i4moe_upload_expert_tensor; D and I equal to the layer's device experts' when there are
+ * any).  The library copies the three tensors into host memory it owns, so the buffers may be
+ * freed when the call returns.  A host expert is computed on the CPU by i4moe_tiered_issue; an
+ * expert also bound on the device (i4moe_set_expert) runs on the device. */
+int i4moe_set_host_expert(i4moe_ctx *ctx, int layer, int expert, const i4moe_host_tensor *gate,
+                          const i4moe_host_tensor *up, const i4moe_host_tensor *down);
+
+/* Host wall-clock split of one tiered issue, in milliseconds (cf. the overlap window of [PR342]):
+ * enqueueing the device group, waiting for x to reach the host, the CPU rows, and the whole call. */
+typedef struct {
+  double issue_ms, x_wait_ms, cpu_ms, total_ms;
+  int32_t device_rows, host_rows;
+} i4moe_tier_times;
+
+/* The experts of a host route (S records, e.g. from i4moe_route with host_out) split by tier
+ * [PR342]: the rows (t, k < n_t) whose expert is bound on the device run as one explicit group on
+ * the GPU (a slot, as i4moe_expert_group_issue); the rows whose expert is kept on the host are
+ * computed on the CPU while that group runs, in float32 (each weight row summed over its columns
+ * in order, group by group), and their weighted sum per token (rows in route order) goes to the
+ * next slot as one row per token with weight 1.  i4moe_expert_group_take then joins both slots in
+ * issue order (the device slot first), so the sum order is fixed and the result bitwise
+ * reproducible [PR434].
+ * x_dev ([S][D], F32 or BF16) is copied to the host on the stream before the device group's
+ * kernels are enqueued; the CPU starts when that copy has landed, and the call returns when the
+ * CPU rows are done and their sum is enqueued for upload (the device group may still be running).
+ * Uses up to 2 slots; returns the number of slots issued (0 when no token has an expert), or a
+ * negative code.  Every expert the routes name must be bound on the device or kept on the host.
+ * On failure nothing is left pending except possibly the copy of x.  times may be NULL.
+ * Host threads: I4MOE_HOST_THREADS at context creation (1..256; default the host's cores, at
+ * most 16).  Fault-hook gated (one compute call). */
+int i4moe_tiered_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S,
+                       const i4moe_route_host *routes, i4moe_tier_times *times);
+
 /* ---- profiling ---------------------------------------------------------------------------- */
 
 /* Kernel families timed when profiling is on.  A selection run inside the dual projection

@@ -37,6 +37,16 @@ class i4moe_group(C.Structure):
                 ("weight", C.POINTER(C.c_float))]
 
 
+class i4moe_host_tensor(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("gs", C.c_int32), ("O", C.c_int32), ("C", C.c_int32),
+                ("packed", C.c_void_p), ("scales", C.c_void_p)]
+
+
+class i4moe_tier_times(C.Structure):
+    _fields_ = [("issue_ms", C.c_double), ("x_wait_ms", C.c_double), ("cpu_ms", C.c_double),
+                ("total_ms", C.c_double), ("device_rows", C.c_int32), ("host_rows", C.c_int32)]
+
+
 _ctx_p = C.c_void_p
 
 # name -> (restype, argtypes); exactly the declarations of include/i4moe.h
@@ -61,6 +71,10 @@ SIGNATURES = {
     "i4moe_shared_expert_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int]),
     "i4moe_moe_block": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int,
                                   C.c_float]),
+    "i4moe_set_host_expert": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.POINTER(i4moe_host_tensor),
+                                        C.POINTER(i4moe_host_tensor), C.POINTER(i4moe_host_tensor)]),
+    "i4moe_tiered_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.POINTER(i4moe_route_host),
+                                     C.POINTER(i4moe_tier_times)]),
     "i4moe_set_fail_after": (C.c_int, [_ctx_p, C.c_longlong]),
     "i4moe_debug_read": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t]),
     "i4moe_debug_size": (C.c_size_t, [_ctx_p, C.c_int, C.c_int]),
@@ -117,6 +131,8 @@ i4moe_upload_norm = _fn("i4moe_upload_norm")
 i4moe_rmsnorm = _fn("i4moe_rmsnorm")
 i4moe_shared_expert_issue = _fn("i4moe_shared_expert_issue")
 i4moe_moe_block = _fn("i4moe_moe_block")
+i4moe_set_host_expert = _fn("i4moe_set_host_expert")
+i4moe_tiered_issue = _fn("i4moe_tiered_issue")
 i4moe_set_fail_after = _fn("i4moe_set_fail_after")
 i4moe_debug_read = _fn("i4moe_debug_read")
 i4moe_debug_size = _fn("i4moe_debug_size")

@@ -7,6 +7,7 @@
 // fail-after hook gates compute entry points only.  The take is fatal on failure, as in the
 // COLI_CUDA_RESID page: a take that did not run would silently drop routed experts.
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -16,9 +17,11 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "common.h"
+#include "host_tier.h"
 
 using namespace i4moe;
 
@@ -47,6 +50,8 @@ struct Layer {
   int route_buf = -1;                  // ring entry holding this layer's latest route
   bool routed = false;
   int route_S = 0, route_K = 0;
+  std::map<int, std::unique_ptr<HostExpert>> host;  // experts kept on the host (the CPU tier)
+  int host_D = 0, host_I = 0;
 };
 
 struct SlotInfo {
@@ -60,8 +65,8 @@ struct SlotInfo {
   ProjArgs down{};
 };
 
-constexpr int kRing = 32;
-constexpr int kMfmaMinRows = 16;          // rows of one expert from which the matrix cores pay  // route buffers: a layer may be re-routed up to 31 times before a take
+constexpr int kRing = 32;  // route buffers: a layer may be re-routed up to 31 times before a take
+constexpr int kMfmaMinRows = 16;  // rows of one expert from which the matrix cores pay
 
 struct ProfRec {
   int kernel;
@@ -104,6 +109,15 @@ struct i4moe_ctx {
   int mfma_min = kMfmaMinRows;  // rows from which an entry runs on the matrix cores (0: never)
   int8_t *d_dig = nullptr;      // [kRows][3][kMaxCols] digit rows of the matrix-core projections
   int *d_dig_E = nullptr;       // [kRows] their row exponents
+
+  // the CPU tier: worker threads, pinned copies of x and of the host rows' sum, and the events
+  // that say when the x copy has landed and when the sum's upload has been read
+  int host_threads = 0;
+  std::unique_ptr<HostPool> pool;
+  void *h_x = nullptr;          // [kTokens][kMaxCols] float32 or bf16, pinned
+  float *h_P = nullptr;         // [kTokens][kMaxCols] float32, pinned
+  hipEvent_t ev_x = nullptr, ev_p = nullptr;
+  bool ev_p_recorded = false;
   int nslots = 0;
 
   int last_route_S = 0, last_route_E = 0;
@@ -522,6 +536,15 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
     const double v = std::atof(wf);
     if (v >= 0.05 && v <= 64.0) c->wave_factor = v;
   }
+  {
+    const unsigned hw = std::thread::hardware_concurrency();
+    c->host_threads = hw == 0 ? 1 : (hw > 16 ? 16 : (int)hw);
+  }
+  if (const char *ht = std::getenv("I4MOE_HOST_THREADS")) {
+    char *end = nullptr;
+    const long v = std::strtol(ht, &end, 10);
+    if (end && end != ht && *end == '\0' && v >= 1 && v <= 256) c->host_threads = (int)v;
+  }
   if (const char *mm = std::getenv("I4MOE_MFMA_MIN_ROWS")) {
     char *end = nullptr;
     const long v = std::strtol(mm, &end, 10);
@@ -565,6 +588,11 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   dfree(c->d_y);
   dfree(c->d_dig);
   dfree(c->d_dig_E);
+  c->pool.reset();
+  if (c->h_x) (void)hipHostFree(c->h_x);
+  if (c->h_P) (void)hipHostFree(c->h_P);
+  if (c->ev_x) (void)hipEventDestroy(c->ev_x);
+  if (c->ev_p) (void)hipEventDestroy(c->ev_p);
   for (auto &r : c->recs) {
     c->ev_pool.push_back(r.a);
     c->ev_pool.push_back(r.b);
@@ -1483,6 +1511,220 @@ int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t b
   }
   if (e != hipSuccess) return hip_fail(c, e, "tap copy");
   return I4MOE_OK;
+}
+
+// ---- the CPU tier ----------------------------------------------------------------------------
+
+static int host_tensor_copy(i4moe_ctx *c, const i4moe_host_tensor *h, const char *what, HostTensor &t) {
+  if (!h) return fail(c, I4MOE_EINVAL, "%s: NULL tensor", what);
+  if (h->fmt != I4MOE_FMT_ROW && h->fmt != I4MOE_FMT_GROUP)
+    return fail(c, I4MOE_EUNSUPPORTED, "%s: unsupported weight format %d", what, h->fmt);
+  if ((h->fmt == I4MOE_FMT_ROW && h->gs != 0) || (h->fmt == I4MOE_FMT_GROUP && (h->gs < 0 || h->gs % 2 != 0)))
+    return fail(c, I4MOE_EINVAL, "%s: bad group size %d for format %d", what, h->gs, h->fmt);
+  if (h->O < 1 || h->C < 2 || h->C % 2 != 0 || h->C > kMaxCols)
+    return fail(c, I4MOE_EINVAL, "%s: bad shape %d x %d", what, h->O, h->C);
+  if (!h->packed || !h->scales) return fail(c, I4MOE_EINVAL, "%s: packed and scales must be non-NULL", what);
+  t.O = h->O;
+  t.C = h->C;
+  t.gs = h->fmt == I4MOE_FMT_GROUP ? h->gs : 0;
+  t.ng = t.gs > 0 ? (h->C + t.gs - 1) / t.gs : 1;
+  if (!all_finite(h->scales, (size_t)t.O * t.ng)) return fail(c, I4MOE_EINVAL, "%s: scales must be finite", what);
+  try {
+    t.packed.assign(h->packed, h->packed + (size_t)t.O * (t.C / 2));
+    t.scales.assign(h->scales, h->scales + (size_t)t.O * t.ng);
+  } catch (const std::bad_alloc &) {
+    return fail(c, I4MOE_ENOMEM, "%s: host memory", what);
+  }
+  return I4MOE_OK;
+}
+
+int i4moe_set_host_expert(i4moe_ctx *c, int layer, int expert, const i4moe_host_tensor *gate,
+                          const i4moe_host_tensor *up, const i4moe_host_tensor *down) {
+  if (!c) return I4MOE_EINVAL;
+  if (layer < 0 || expert < 0 || expert >= kMaxE) return fail(c, I4MOE_EINVAL, "bad layer %d / expert %d", layer, expert);
+  std::unique_ptr<HostExpert> he(new (std::nothrow) HostExpert());
+  if (!he) return fail(c, I4MOE_ENOMEM, "host memory");
+  int rc;
+  if ((rc = host_tensor_copy(c, gate, "gate", he->gate)) || (rc = host_tensor_copy(c, up, "up", he->up)) ||
+      (rc = host_tensor_copy(c, down, "down", he->down)))
+    return rc;
+  const int I = he->gate.O, D = he->gate.C;
+  if (he->up.O != I || he->up.C != D || he->down.O != D || he->down.C != I)
+    return fail(c, I4MOE_EINVAL, "host expert shapes: need gate I x D, up I x D, down D x I");
+  Layer &L = c->layers[layer];
+  if ((L.D && L.D != D) || (L.I && L.I != I) || (L.host_D && L.host_D != D) || (L.host_I && L.host_I != I))
+    return fail(c, I4MOE_EINVAL, "layer %d: host expert D=%d I=%d differs from the layer's", layer, D, I);
+  if (L.E && expert >= L.E) return fail(c, I4MOE_EINVAL, "expert %d >= router E=%d", expert, L.E);
+  L.host_D = D;
+  L.host_I = I;
+  L.host[expert] = std::move(he);
+  return I4MOE_OK;
+}
+
+static int tier_buffers(i4moe_ctx *c) {
+  hipError_t e = hipSuccess;
+  const size_t bytes = sizeof(float) * (size_t)kTokens * kMaxCols;
+  if (!c->h_x && (e = hipHostMalloc(&c->h_x, bytes, hipHostMallocDefault)) != hipSuccess) {
+    c->h_x = nullptr;
+    return hip_fail(c, e, "hipHostMalloc(x)");
+  }
+  if (!c->h_P && (e = hipHostMalloc(reinterpret_cast<void **>(&c->h_P), bytes, hipHostMallocDefault)) != hipSuccess) {
+    c->h_P = nullptr;
+    return hip_fail(c, e, "hipHostMalloc(host rows)");
+  }
+  if (!c->ev_x && (e = hipEventCreateWithFlags(&c->ev_x, hipEventDisableTiming)) != hipSuccess) {
+    c->ev_x = nullptr;
+    return hip_fail(c, e, "hipEventCreate");
+  }
+  if (!c->ev_p && (e = hipEventCreateWithFlags(&c->ev_p, hipEventDisableTiming)) != hipSuccess) {
+    c->ev_p = nullptr;
+    return hip_fail(c, e, "hipEventCreate");
+  }
+  if (!c->pool) {
+    c->pool.reset(new (std::nothrow) HostPool(c->host_threads));
+    if (!c->pool) return fail(c, I4MOE_ENOMEM, "host worker pool");
+  }
+  return I4MOE_OK;
+}
+
+int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_route_host *routes,
+                       i4moe_tier_times *times) {
+  if (!c) return I4MOE_EINVAL;
+  using clk = std::chrono::steady_clock;
+  const auto t_start = clk::now();
+  int rc = gate_compute(c);
+  if (rc) return rc;
+  Layer *L = find_layer(c, layer);
+  if (!L) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
+  if (!x_dev || !routes) return fail(c, I4MOE_EINVAL, "x_dev and routes must be non-NULL");
+  if (dtype != I4MOE_DTYPE_F32 && dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", dtype);
+  if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
+  const int D = L->D ? L->D : L->host_D, I = L->I ? L->I : L->host_I;
+  if (!D || !I) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
+
+  // the rows of each tier, in route order (token-major, selection order)
+  std::vector<int32_t> de, dt;
+  std::vector<float> dw;
+  std::vector<HostRow> hrows;
+  for (int t = 0; t < S; ++t) {
+    const i4moe_route_host &r = routes[t];
+    if (r.n < 0 || r.n > kMaxK) return fail(c, I4MOE_EINVAL, "route %d: n=%d outside 0..%d", t, r.n, kMaxK);
+    for (int k = 0; k < r.n; ++k) {
+      const int e = r.idx[k];
+      const float w = r.w[k];
+      if (!std::isfinite(w)) return fail(c, I4MOE_EINVAL, "route %d: weight %d not finite", t, k);
+      if (e >= 0 && e < (int)L->gate.size() && L->gate[e]) {
+        de.push_back(e);
+        dt.push_back(t);
+        dw.push_back(w);
+        continue;
+      }
+      auto it = L->host.find(e);
+      if (it == L->host.end()) return fail(c, I4MOE_EINVAL, "route %d: expert %d is neither on the device nor on the host", t, e);
+      hrows.push_back(HostRow{t, it->second.get(), w});
+    }
+  }
+  const bool dev = !de.empty(), host = !hrows.empty();
+  if ((int)de.size() > kRows) return fail(c, I4MOE_EINVAL, "%zu device rows exceed the %d-row cap", de.size(), kRows);
+  if (c->nslots + (dev ? 1 : 0) + (host ? 1 : 0) > kSlots)
+    return fail(c, I4MOE_EINVAL, "%d issues pending; take before issuing more", c->nslots);
+  if (c->nslots > 0 && (c->slots[0].S != S || c->slots[0].D != D))
+    return fail(c, I4MOE_EINVAL, "pending issues have S=%d D=%d; this issue has S=%d D=%d", c->slots[0].S,
+                c->slots[0].D, S, D);
+  if (host && reinterpret_cast<uintptr_t>(x_dev) % (dtype == I4MOE_DTYPE_F32 ? 4 : 2) != 0)
+    return fail(c, I4MOE_EINVAL, "x_dev misaligned");
+  ensure_device(c);
+  if ((rc = ensure_rows_scratch(c, D, I))) return rc;
+  if ((rc = ensure_layer_tables(c, *L))) return rc;
+  if (host && (rc = tier_buffers(c))) return rc;
+  if ((rc = flush_all(c))) return rc;
+
+  // x to the host first, so the CPU can start while the device group's kernels run
+  const size_t esz = dtype == I4MOE_DTYPE_F32 ? 4 : 2;
+  hipError_t e = hipSuccess;
+  if (host) {
+    e = hipMemcpyAsync(c->h_x, x_dev, esz * S * D, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_x, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "copy of x to the host");
+  }
+  int issued = 0;
+  if (dev) {
+    i4moe_group g{(int32_t)de.size(), de.data(), dt.data(), dw.data()};
+    const int s = issue_impl(c, layer, x_dev, dtype, S, &g, false);
+    if (s < 0) return s;
+    ++issued;
+  }
+  const auto t_issued = clk::now();
+  auto t_x = t_issued, t_cpu = t_issued;
+  if (host) {
+    if ((e = hipEventSynchronize(c->ev_x)) != hipSuccess) return hip_fail(c, e, "wait for x");
+    t_x = clk::now();
+    std::vector<float> xf((size_t)S * D);
+    if (dtype == I4MOE_DTYPE_F32) {
+      std::memcpy(xf.data(), c->h_x, sizeof(float) * xf.size());
+    } else {
+      const uint16_t *xb = static_cast<const uint16_t *>(c->h_x);
+      for (size_t i = 0; i < xf.size(); ++i) {
+        const uint32_t u = (uint32_t)xb[i] << 16;
+        std::memcpy(&xf[i], &u, 4);
+      }
+    }
+    // the previous tiered issue's upload of the host sum must have read it
+    if (c->ev_p_recorded && (e = hipEventSynchronize(c->ev_p)) != hipSuccess) return hip_fail(c, e, "wait for upload");
+    std::memset(c->h_P, 0, sizeof(float) * (size_t)S * D);
+    host_rows_forward(*c->pool, hrows, xf.data(), D, I, c->h_P);
+    t_cpu = clk::now();
+    // the host slot: one row per token, weight 1, holding the token's sum of host rows
+    const int s = c->nslots;
+    GroupDev hg;
+    std::memset(&hg, 0, sizeof hg);
+    hg.n_entries = 1;
+    hg.entry_expert[0] = 0;
+    hg.entry_row0[0] = 0;
+    hg.entry_row0[1] = S;
+    for (int t = 0; t < S; ++t) {
+      hg.row_token[t] = t;
+      hg.row_expert[t] = 0;
+      hg.row_weight[t] = 1.f;
+      hg.tok_row0[t] = t;
+      hg.red_rows[t] = t;
+    }
+    hg.tok_row0[S] = S;
+    hg.n_rows = S;
+    hg.S = S;
+    GroupBuf *gb = c->d_slot_bufs + s;
+    e = launch_group_store(hg, L->d_tab, gb, c->stream);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(c->d_y + (size_t)s * kRows * c->y_ld, sizeof(float) * c->y_ld, c->h_P, sizeof(float) * D,
+                           sizeof(float) * D, S, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_p, c->stream);
+    if (e != hipSuccess) {
+      c->poisoned = true;  // the device slot is issued but the host rows would be lost
+      return hip_fail(c, e, "upload of the host rows");
+    }
+    c->ev_p_recorded = true;
+    SlotInfo &si = c->slots[s];
+    si = SlotInfo{};
+    si.S = S;
+    si.D = D;
+    si.rows = S;
+    si.grp = gb;
+    si.ring = -1;
+    c->nslots = s + 1;
+    ++issued;
+  }
+  c->calls++;
+  if (times) {
+    auto ms = [](clk::time_point a, clk::time_point b) { return std::chrono::duration<double, std::milli>(b - a).count(); };
+    const auto t_end = clk::now();
+    times->issue_ms = ms(t_start, t_issued);
+    times->x_wait_ms = host ? ms(t_issued, t_x) : 0.0;
+    times->cpu_ms = host ? ms(t_x, t_cpu) : 0.0;
+    times->total_ms = ms(t_start, t_end);
+    times->device_rows = (int32_t)de.size();
+    times->host_rows = (int32_t)hrows.size();
+  }
+  return issued;
 }
 
 int i4moe_set_profiling(i4moe_ctx *c, int on) {

@@ -156,6 +156,32 @@ class Context:
         self.check(B.i4moe_moe_block(self.p, layer, C.c_void_p(residual.data_ptr()), residual.shape[0], act_dtype, K,
                                      topp, 1 if norm_topk else 0, routed_scale))
 
+    def set_host_expert(self, layer: int, e: int, gate, up, down):
+        """Keep expert e of `layer` on the host: gate/up/down are host tensors (fmt, gs, O, C,
+        packed uint8 [O][C/2], scales float32), copied by the library."""
+        keep = []
+
+        def desc(t):
+            packed = np.ascontiguousarray(t.packed, dtype=np.uint8)
+            scales = np.ascontiguousarray(t.scales, dtype=np.float32)
+            keep.append((packed, scales))
+            return B.i4moe_host_tensor(t.fmt, t.gs, t.O, t.C, _ptr(packed), _ptr(scales))
+
+        g, u, d = desc(gate), desc(up), desc(down)
+        self.check(B.i4moe_set_host_expert(self.p, layer, e, C.byref(g), C.byref(u), C.byref(d)))
+
+    def tiered_issue(self, layer: int, x, routes):
+        """Device rows as a device group, host rows on the CPU meanwhile (see i4moe_tiered_issue);
+        routes: S route records (i4moe_route_host).  Returns (slots issued, timings)."""
+        S = x.shape[0]
+        if len(routes) < S:
+            raise ValueError("need S route records")
+        arr = (B.i4moe_route_host * S)(*routes[:S])
+        times = B.i4moe_tier_times()
+        n = self.check(B.i4moe_tiered_issue(self.p, layer, C.c_void_p(x.data_ptr()), _dtype_code(x), S, arr,
+                                            C.byref(times)))
+        return n, times
+
     def set_fail_after(self, n: int):
         self.check(B.i4moe_set_fail_after(self.p, n))
 

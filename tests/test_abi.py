@@ -103,6 +103,8 @@ def test_null_context_rejected_before_any_device_call(lib_path):
     assert B.i4moe_rmsnorm(None, 0, None, 8, 1, None, 8, 0) == EINVAL
     assert B.i4moe_shared_expert_issue(None, 0, None, 0, 1) == EINVAL
     assert B.i4moe_moe_block(None, 0, None, 1, 0, 1, 0.0, 1, 1.0) == EINVAL
+    assert B.i4moe_set_host_expert(None, 0, 0, None, None, None) == EINVAL
+    assert B.i4moe_tiered_issue(None, 0, None, 0, 1, None, None) == EINVAL
     assert B.i4moe_set_fail_after(None, 0) == EINVAL
     buf = (C.c_char * 8)()
     assert B.i4moe_debug_read(None, 0, 0, C.cast(buf, C.c_void_p), 8) == EINVAL
