@@ -92,7 +92,7 @@ typedef struct {
 
 /* Explicit group for issue (host arrays of n_rows entries): each row runs expert[r] on token
  * row token[r] of x and is weighted by weight[r].  Per token, rows are summed in the order
- * listed.  An expert with at least 16 rows in the group runs on the matrix cores
+ * listed.  An expert with at least 8 rows in the group runs on the matrix cores
  * (I4MOE_MFMA_MIN_ROWS at i4moe_ctx_create), the others on the vector kernels, one row per
  * workgroup (or up to 4 rows per weight pass with I4MOE_ENTRY_ROWS). */
 typedef struct {
@@ -115,10 +115,11 @@ typedef struct {
  * together re-read its weights mostly from cache).  It changes only the order of additions: a
  * group-wise tensor's results are the same bits either way, a per-row tensor's may differ in the
  * last bits (both within the documented tolerance of the f64 result).
- * I4MOE_MFMA_MIN_ROWS (0 = off, else 2 .. 64; default 16) is the row count from which an
- * expert's rows in one issue run on the matrix cores (int8 products of digit rows, exact like
- * the vector kernels; gate/up/down of every expert of the issue per-row or with group sizes
- * that are multiples of 64); smaller entries keep the vector kernels.
+ * I4MOE_MFMA_MIN_ROWS (0 = off, else 2 .. 64; default 8, the crossover measured on MI355X; the
+ * pages report ~16 on their GPU) is the row count from which an expert's rows in one issue run on
+ * the matrix cores (int8 products of digit rows, exact like the vector kernels; gate/up/down of
+ * every expert of the issue per-row or with group sizes that are multiples of 64); smaller
+ * entries keep the vector kernels.
  * Errors: EINVAL (bad device, out == NULL), EDEVICE, ENOMEM. */
 int i4moe_ctx_create(int device, i4moe_ctx **out);
 

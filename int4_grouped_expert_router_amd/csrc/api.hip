@@ -66,7 +66,7 @@ struct SlotInfo {
 };
 
 constexpr int kRing = 32;  // route buffers: a layer may be re-routed up to 31 times before a take
-constexpr int kMfmaMinRows = 16;  // rows of one expert from which the matrix cores pay
+constexpr int kMfmaMinRows = 8;  // rows of one expert from which the matrix cores pay (measured)
 
 struct ProfRec {
   int kernel;
@@ -109,6 +109,8 @@ struct i4moe_ctx {
   int mfma_min = kMfmaMinRows;  // rows from which an entry runs on the matrix cores (0: never)
   int8_t *d_dig = nullptr;      // [kRows][3][kMaxCols] digit rows of the matrix-core projections
   int *d_dig_E = nullptr;       // [kRows] their row exponents
+  float *d_part = nullptr;      // partial sums of the matrix-core column slices
+  size_t part_floats = 0;
 
   // the CPU tier: worker threads, pinned copies of x and of the host rows' sum, and the events
   // that say when the x copy has landed and when the sum's upload has been read
@@ -314,6 +316,19 @@ int ensure_digit_scratch(i4moe_ctx *c) {
   }
   c->d_dig = d;
   c->d_dig_E = E;
+  return I4MOE_OK;
+}
+
+// Partial sums of the matrix-core column slices; grows (with the stream drained) only.
+int ensure_part_scratch(i4moe_ctx *c, size_t floats) {
+  if (floats <= c->part_floats) return I4MOE_OK;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  float *p = nullptr;
+  if ((e = dalloc(&p, sizeof(float) * floats)) != hipSuccess) return hip_fail(c, e, "hipMalloc(partial sums)");
+  dfree(c->d_part);
+  c->d_part = p;
+  c->part_floats = floats;
   return I4MOE_OK;
 }
 
@@ -588,6 +603,7 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   dfree(c->d_y);
   dfree(c->d_dig);
   dfree(c->d_dig_E);
+  dfree(c->d_part);
   c->pool.reset();
   if (c->h_x) (void)hipHostFree(c->h_x);
   if (c->h_P) (void)hipHostFree(c->h_P);
@@ -1097,7 +1113,7 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   // Entries of at least mfma_min rows run on the matrix cores (every tensor of the issue per-row
   // or with group sizes that are multiples of 64); the vector kernels then take the chunked path,
   // which skips those entries.
-  int mfma_min = 0, mfma_slots = 0, mfma_tiles = 0;
+  int mfma_min = 0, mfma_slots = 0, ks_dual = 1, ks_down = 1;
   bool vec_rows = true;  // some entry runs on the vector kernels (always possible for a device route)
   if (S > 1 && c->mfma_min > 0) {
     bool fmt_ok = true;
@@ -1116,8 +1132,12 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
     if (fmt_ok && most >= c->mfma_min && n_big > 0) {
       mfma_min = c->mfma_min;
       mfma_slots = n_big;
-      mfma_tiles = (std::min(most, kRows) + 15) / 16;
+      ks_dual = mfma_ksplit(L->I, round_up(L->D, 64), n_big, c->n_cu);
+      ks_down = mfma_ksplit(L->D, round_up(L->I, 64), n_big, c->n_cu);
       if ((rc = ensure_digit_scratch(c))) return rc;
+      if ((rc = ensure_part_scratch(c, std::max(mfma_part_floats(2, L->I, n_big, ks_dual),
+                                                 mfma_part_floats(1, L->D, n_big, ks_down)))))
+        return rc;
       ad.mfma_min = an.mfma_min = mfma_min;
       if (ad.entry_rows == 0) ad.entry_rows = 1;
       if (an.entry_rows == 0) an.entry_rows = 1;
@@ -1168,7 +1188,8 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
     ma.C64 = da.C64;
     ma.mfma_min = mfma_min;
     ma.slots = mfma_slots;
-    ma.token_tiles = mfma_tiles;
+    ma.ksplit = dual ? ks_dual : ks_down;
+    ma.part = c->d_part;
     return timed(c, I4MOE_K_MFMA, [&](hipEvent_t t0, hipEvent_t t1) {
       // the event pair spans both launches: start of the digit rows, end of the projection
       hipError_t r = launch_digits8(da, c->stream, t0, nullptr);

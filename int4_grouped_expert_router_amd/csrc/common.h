@@ -128,15 +128,18 @@ struct DigitArgs {
 
 // Matrix-core projection of the entries with at least mfma_min rows (slot k: the k-th such
 // entry in entry order).  dual: gate/up + SiLU into h rows, digit rows indexed by token; else the
-// down projection into y rows, digit rows indexed by group row.
+// down projection into y rows, digit rows indexed by group row.  The columns are split into
+// ksplit slices whose partial sums go to part ([ksplit][NT][slots][64][O] floats) and are added
+// in slice order by the reduction launch.
 struct MfmaArgs {
   const GroupBuf *grp;
   const int8_t *dig;
   const int *E;
   float *out;
+  float *part;
   int out_ld, dig_rows, dual;
   int O, C64;
-  int mfma_min, slots, token_tiles;
+  int mfma_min, slots, ksplit;
   int weight_tiles, tiles;  // set by the launcher
 };
 
@@ -194,6 +197,9 @@ hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBu
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Column slices of a matrix-core launch (about two workgroups per CU) and its partial-sum floats.
+int mfma_ksplit(int O, int C64, int slots, int n_cu);
+size_t mfma_part_floats(int NT, int O, int slots, int ksplit);
 
 // Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.
 constexpr int rows_per_step(int V, int P, int tensors, int budget) {

@@ -9,9 +9,9 @@
 // balanced base-256 digits d_n in -128..127 (X = d_0 + 256 d_1 + 65536 d_2): three int8 "digit
 // rows".  A weight nibble q (signed, -8..7) becomes the int8 16 q by masking it into the high half
 // of its byte, so one v_mfma_i32_16x16x64_i8 per digit gives sum_k 16 q_k d_{n,k} over 64
-// columns exactly in int32.  A group-wise tensor's three digit sums are joined into a float and
-// scaled after every 64 columns (group sizes are multiples of 64); a per-row tensor keeps its
-// integer sums to the end.  The result is (join) 2^-E / 16.
+// columns exactly in int32.  The three digit sums of every 64 columns are joined into a float
+// and scaled (a group-wise tensor's group scale, group sizes being multiples of 64; a per-row
+// tensor's row scale after the last step).  The result is (join) 2^-E / 16.
 //
 // Tiling: a workgroup owns 32 output rows x 16 rows of one entry (an expert's group rows, its
 // token tile); its waves (up to 8, each with at least 8 steps of 64 columns) split the columns,
@@ -50,35 +50,65 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 // One workgroup per activation row: E from the row's largest |a|, then 16 columns per thread
 // and step, written as three 16-byte digit chunks in the byte order of the weight operand.
-__global__ __launch_bounds__(kBlock) void k_digits8(DigitArgs a) {
-  __shared__ uint32_t s_max[kBlock / kWave];
+constexpr int kDigBlock = 1024;  // threads per activation row
+
+__global__ __launch_bounds__(kDigBlock) void k_digits8(DigitArgs a) {
+  __shared__ uint32_t s_max[kDigBlock / kWave];
   const int row = blockIdx.x;
   if (a.grp && row >= ((CGroupBuf)a.grp)->g.n_rows) return;  // rows past the group: not used
   const int C = a.C;
   const size_t off = (size_t)row * a.act_ld;
   const uint16_t *xb = static_cast<const uint16_t *>(a.act) + off;
   const float *xf = static_cast<const float *>(a.act) + off;
-  auto val = [&](int c) -> float {
-    if (c >= C) return 0.f;
-    return a.bf16 ? __uint_as_float((uint32_t)xb[c] << 16) : xf[c];
+  // 16 columns per thread and step: whole aligned 4-byte words (C and the row offset are even,
+  // rows are 4-byte aligned), clamped into the row, zero past C
+  auto load16 = [&](int b, float (&v)[16]) {
+    const int c0 = 16 * b;
+    if (a.bf16) {
+      const uint32_t *w = reinterpret_cast<const uint32_t *>(xb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = c0 + 2 * k;
+        const uint32_t u = w[c < C ? c / 2 : 0];
+        v[2 * k] = c < C ? __uint_as_float(u << 16) : 0.f;
+        v[2 * k + 1] = c < C ? __uint_as_float(u & 0xffff0000u) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = c0 + k;
+        const float x = xf[c < C ? c : 0];
+        v[k] = c < C ? x : 0.f;
+      }
+    }
   };
+  const int nb = a.C64 / 16;
   uint32_t m = 0;
-  for (int c = threadIdx.x; c < C; c += kBlock) m = max(m, __float_as_uint(val(c)) & 0x7fffffffu);
+  for (int b = threadIdx.x; b < nb; b += kDigBlock) {
+    float v[16];
+    load16(b, v);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(v[k]) & 0x7fffffffu);
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
   __syncthreads();
-  m = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  m = s_max[0];
+#pragma unroll
+  for (int k = 1; k < kDigBlock / kWave; ++k) m = max(m, s_max[k]);
   const int E = 148 - (int)(m >> 23);  // max |a| 2^E < 2^22 (a zero row: E = 148, zero digits)
   if (threadIdx.x == 0) a.E[row] = E;
   int8_t *dst = a.dig + (size_t)row * kDigits * a.C64;
-  for (int b = threadIdx.x; b < a.C64 / 16; b += kBlock) {
+  for (int b = threadIdx.x; b < nb; b += kDigBlock) {
+    float v[16];
+    load16(b, v);
     uint32_t d[kDigits][4] = {};
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       // byte p of the chunk holds column 16 b + col(p): within each half, even columns first
       const int h = p >> 3, r = p & 7;
-      const int col = 16 * b + 8 * h + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
-      const int X = (int)__builtin_rintf(__builtin_ldexpf(val(col), E));
+      const int col = 8 * h + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
+      const int X = (int)__builtin_rintf(__builtin_ldexpf(v[col], E));
       const uint32_t u = ((uint32_t)X + 0x808080u) ^ 0x808080u;  // balanced digits as int8
 #pragma unroll
       for (int n = 0; n < kDigits; ++n) d[n][p >> 2] |= ((u >> (8 * n)) & 0xffu) << (8 * (p & 3));
@@ -98,52 +128,79 @@ __device__ __forceinline__ v4i weight_operand(uint32_t w0, uint32_t w1) {
              (int)(w1 & 0xF0F0F0F0u)};
 }
 
-// sum_n acc[n] 256^n per element as a float (exact digit sums; two roundings).
-__device__ __forceinline__ float join3(const v4i (&acc)[kDigits], int v) {
-  return fmaf((float)acc[2][v], 65536.f, fmaf((float)acc[1][v], 256.f, (float)acc[0][v]));
-}
 
-constexpr int kWT = 2;  // weight tiles (16 rows each) per wave
-
-constexpr int kWaveGroups = 16;  // scale groups of one wave's columns: at most 16 steps of 64
-
-template <int NT>
-struct MStep {
-  uint32_t w[kWT][NT][2];
-  v4i x[kDigits];
-};
-
-template <int NT>
-__global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
-  __shared__ float s_part[kMfmaWaves][kWT][NT][kWave * 4];
-  __shared__ float s_scale[kMfmaWaves][kWT][NT][16][kWaveGroups];  // each wave's group scales
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int KW = blockDim.x >> 6;  // waves splitting the columns
-  // Logical tiles (entry slot, weight tile pair, token tile), token tile fastest; the blocks of
-  // one XCD (block index mod 8) take one contiguous run of them, so the token tiles of a weight
-  // tile re-read its weights from the same L2.
-  const int L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  if (L >= a.tiles) return;
-  const int tt = L % a.token_tiles;
-  const int wt = (L / a.token_tiles) % a.weight_tiles;
-  const int slot = L / (a.token_tiles * a.weight_tiles);
-
-  // the slot-th entry with at least mfma_min rows
-  const CGroupBuf G = (CGroupBuf)a.grp;
+// The slot-th entry of the group with at least mfma_min rows: its first row and row count
+// (size 0: no such entry).  Wave-level; every lane gets the result.
+__device__ __forceinline__ void big_entry(const GroupBuf *grp, int mfma_min, int slot, int lane, int &start, int &size) {
+  const CGroupBuf G = (CGroupBuf)grp;
   const int ne = G->g.n_entries;
-  const int r0 = lane < ne ? a.grp->g.entry_row0[lane] : 0;
-  const int r1 = lane < ne ? a.grp->g.entry_row0[lane + 1] : 0;  // entry_row0[ne] = n_rows
-  const bool big = lane < ne && r1 - r0 >= a.mfma_min;
+  const int r0 = lane < ne ? grp->g.entry_row0[lane] : 0;
+  const int r1 = lane < ne ? grp->g.entry_row0[lane + 1] : 0;  // entry_row0[ne] = n_rows
+  const bool big = lane < ne && r1 - r0 >= mfma_min;
   const unsigned long long bigs = __ballot(big);
   const unsigned long long pick = __ballot(big && __popcll(bigs & ((1ull << lane) - 1ull)) == slot);
-  if (pick == 0) return;
+  if (pick == 0) {
+    start = size = 0;
+    return;
+  }
   const int j = __ffsll((long long)pick) - 1;
-  const int start = __builtin_amdgcn_readlane(r0, j);
-  const int size = __builtin_amdgcn_readlane(r1, j) - start;
-  if (16 * tt >= size) return;
+  start = __builtin_amdgcn_readlane(r0, j);
+  size = __builtin_amdgcn_readlane(r1, j) - start;
+}
 
+// LDS stage: kCh steps of 64 columns.  Weight rows of 32 bytes per step, digit rows of 64 bytes
+// per step and digit; rows padded so that the 16 rows one MFMA operand reads fall in distinct
+// banks.
+constexpr int kMW = 4;                       // waves per workgroup: one 16-row weight tile each
+constexpr int kMRows = 16 * kMW;             // weight rows per workgroup
+constexpr int kCh = 2;                       // steps per stage
+constexpr int kWRow = kCh * 32 + 8;          // LDS bytes per weight row
+constexpr int kXRow = kDigits * kCh * 64 + 16;  // LDS bytes per activation row (3 digits)
+constexpr int kXLoads = 64 * kDigits * kCh * 64 / 16 / (kMW * kWave);  // 16-byte loads per thread
+static_assert(kMRows * kCh * 32 / 16 == kMW * kWave, "one 16-byte weight load per thread and tensor");
+static_assert(kXLoads * kMW * kWave * 16 == 64 * kDigits * kCh * 64, "digit rows split evenly");
+
+template <int NT>
+constexpr int stage_bytes() {
+  return NT * kMRows * kWRow + 64 * kXRow + NT * kMRows * kCh * 4;
+}
+template <int NT>
+constexpr size_t mfma_lds_bytes() {
+  return 2 * (size_t)stage_bytes<NT>();
+}
+
+template <int NT>
+struct MLoads {
+  u32x4 w[NT];
+  u32x4 x[kXLoads];
+  float sc;
+};
+
+// Matrix-core projection of one entry's rows: a workgroup owns kMRows weight rows x all token
+// tiles of the entry x one slice of the columns; wave w owns weight tile w.  Each stage is loaded
+// by the whole workgroup with 16-byte loads (a weight row's kCh x 32 bytes, a digit row's
+// kCh x 64 bytes) while the previous stage computes.  The partial sums of the slice go to
+// a.part[slice][n][slot][m][o]; k_mfma_reduce adds the slices in order.
+template <int NT>
+__global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
+  __shared__ int s_drow[64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // blocks: (slot, weight block, column slice), slice fastest; one XCD takes a contiguous run,
+  // so the slices of a weight block share an L2 for the digit rows
+  const int L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  if (L >= a.tiles) return;
+  const int ks = L % a.ksplit;
+  const int wb = (L / a.ksplit) % a.weight_tiles;
+  const int slot = L / (a.ksplit * a.weight_tiles);
+  int start, size;
+  big_entry(a.grp, a.mfma_min, slot, lane, start, size);
+  if (size == 0) return;
+  const int TT = (size + 15) >> 4;
+  const CGroupBuf G = (CGroupBuf)a.grp;
   TensorDesc T[NT];
+  bool grp[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const TensorDesc I4MOE_AS4 &d = G->rows[start].t[NT == 2 ? n : 2];
@@ -152,162 +209,195 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void k_mfma(MfmaArgs a) {
     T[n].row_bytes = d.row_bytes;
     T[n].gs = d.gs;
     T[n].ng = d.ng;
-  }
-  const int O = a.O;
-  const int li = lane & 15, q = lane >> 4;
-
-  // A operand rows: lane row li of the token tile; rows past the entry read zeros
-  const int arow_g = min(start + 16 * tt + li, kRows - 1);
-  const bool a_ok = 16 * tt + li < size;
-  const int drow = a_ok ? (a.dual ? a.grp->rows[arow_g].token : arow_g) : 0;
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.dig, a.dig_rows * kDigits * a.C64);
-  const int xoff0 = a_ok ? drow * kDigits * a.C64 + 16 * q : -1;  // -1: no row
-
-  // B operands: weight rows 16 (kWT wt + t) + li of each tensor; rows past O read zeros
-  int orow[kWT];
-  bool o_ok[kWT];
-#pragma unroll
-  for (int t = 0; t < kWT; ++t) {
-    orow[t] = 16 * (kWT * wt + t) + li;
-    o_ok[t] = orow[t] < O;
-  }
-  __amdgpu_buffer_rsrc_t wr[NT], sr[NT];
-  bool grp[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    wr[n] = rsrc(T[n].q, O * T[n].row_bytes);
-    sr[n] = rsrc(T[n].s, O * T[n].ng * 4);
     grp[n] = T[n].ng > 1;
   }
+  if (tid < 64) s_drow[tid] = tid < size ? (a.dual ? a.grp->rows[start + tid].token : start + tid) : -1;
+  __syncthreads();
 
+  const int O = a.O, o0 = kMRows * wb;
   const int KS = a.C64 / 64;
-  const int s0 = (w * KS) / KW, s1 = ((w + 1) * KS) / KW;
-  // Per-lane base offsets, fixed for the whole loop; a step adds a wave-uniform term, so the
-  // loads carry no conditions (a row past O, or an activation row past the entry, gets a base
-  // beyond its buffer and reads zeros).  A weight step reaching past a row's padded bytes reads
-  // the next row's first bytes, but those columns (C and up) have zero digits; loads of steps
-  // past this wave's range are issued and never used.
+  const int k0 = (ks * KS) / a.ksplit, k1 = ((ks + 1) * KS) / a.ksplit;  // this slice's steps
   constexpr int kFar = 0x40000000;
-  int wbase[kWT][NT];
+  __amdgpu_buffer_rsrc_t wr[NT], sr[NT];
 #pragma unroll
-  for (int t = 0; t < kWT; ++t)
+  for (int n = 0; n < NT; ++n) {
+    wr[n] = rsrc(T[n].q, O * T[n].row_bytes + 64);
+    sr[n] = rsrc(T[n].s, O * T[n].ng * 4);
+  }
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.dig, a.dig_rows * kDigits * a.C64);
+  // this thread's loads: weight row tid / 4, 16-byte chunk tid % 4 (every tensor); digit loads
+  // j: activation row m, digit d, chunk c of the stage's 128 bytes; one scale (thread < NT x 128)
+  const int wrow = tid >> 2, wch = tid & 3;
+  const bool w_ok = o0 + wrow < O;
+  int xbase[kXLoads], xlds[kXLoads];
+#pragma unroll
+  for (int j = 0; j < kXLoads; ++j) {
+    const int idx = tid + j * kMW * kWave;
+    const int m = idx / (kDigits * kCh * 4), rem = idx % (kDigits * kCh * 4);
+    const int d = rem / (kCh * 4), c = rem % (kCh * 4);
+    const int dr = s_drow[m];
+    xbase[j] = dr >= 0 ? (dr * kDigits + d) * a.C64 + 16 * c : kFar;
+    xlds[j] = m * kXRow + d * (kCh * 64) + 16 * c;
+  }
+  // scale loads: tensor sn (wave-uniform: 128 threads per tensor), row srow, step sc_c of the stage
+  const int sn = __builtin_amdgcn_readfirstlane(tid / (kMRows * kCh));
+  const int srow = (tid / kCh) % kMRows, sc_c = tid % kCh;
+  const int sn_c = sn < NT ? sn : 0;
+  const bool s_ok = sn < NT && o0 + srow < O;
+  auto load = [&](MLoads<NT> &r, int s0) {  // the stage starting at step s0
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      wbase[t][n] = o_ok[t] ? orow[t] * T[n].row_bytes + 8 * q : kFar;
+      // a stage may reach up to 48 bytes past a row's padded end: the next row's first bytes (or
+      // the tensor's 64-byte tail slack), multiplied by zero digits (columns C and up) or unused
+      const int off = w_ok ? (o0 + wrow) * T[n].row_bytes + 32 * s0 + 16 * wch : kFar;
+      r.w[n] = __builtin_amdgcn_raw_buffer_load_b128(wr[n], off, 0, kNontemporal);
     }
-  // The group scales of this wave's columns, staged in the wave's own LDS region once (a step
-  // then reads its scale there instead of issuing a load per row): lane (row li, quarter q) loads
-  // groups g0 + 4q .. g0 + 4q + 3 of its row (past the row's scales: unused values).
-  int g0[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) g0[n] = grp[n] ? (64 * s0) / T[n].gs : 0;
+    for (int j = 0; j < kXLoads; ++j)
+      r.x[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xbase[j] < kFar ? xbase[j] + 64 * s0 : kFar, 0, 0);
+    const int gs = NT == 2 ? (sn_c ? T[1 % NT].gs : T[0].gs) : T[0].gs;
+    const int ng = NT == 2 ? (sn_c ? T[1 % NT].ng : T[0].ng) : T[0].ng;
+    const bool gg = ng > 1;
+    const int g = gg ? (64 * (s0 + sc_c)) / gs : 0;
+    const int soff = s_ok ? 4 * ((o0 + srow) * ng + g) : kFar;
+    const __amdgpu_buffer_rsrc_t srs = NT == 2 ? (sn_c ? sr[1 % NT] : sr[0]) : sr[0];
+    r.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0));
+  };
+  auto store = [&](const MLoads<NT> &r, int stage) {
+    uint8_t *base = s_lds + stage * stage_bytes<NT>();
 #pragma unroll
-  for (int t = 0; t < kWT; ++t)
+    for (int n = 0; n < NT; ++n)
+      *reinterpret_cast<u32x4 *>(base + n * kMRows * kWRow + wrow * kWRow + 16 * wch) = r.w[n];
+    uint8_t *xb = base + NT * kMRows * kWRow;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int off = (o_ok[t] && grp[n]) ? 4 * (orow[t] * T[n].ng + g0[n] + 4 * q) : kFar;
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(sr[n], off, 0, 0);
-      *reinterpret_cast<u32x4 *>(&s_scale[w][t][n][li][4 * q]) = v;
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int xbase = xoff0 >= 0 ? xoff0 : kFar;
-  auto load = [&](MStep<NT> &st, int s) {
-#pragma unroll
-    for (int t = 0; t < kWT; ++t)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(wr[n], wbase[t][n] + 32 * s, 0, kNontemporal);
-        st.w[t][n][0] = u.x;
-        st.w[t][n][1] = u.y;
-      }
-#pragma unroll
-    for (int d = 0; d < kDigits; ++d)
-      st.x[d] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(xr, xbase + d * a.C64 + 64 * s, 0, 0));
+    for (int j = 0; j < kXLoads; ++j) *reinterpret_cast<u32x4 *>(xb + xlds[j]) = r.x[j];
+    float *scb = reinterpret_cast<float *>(xb + 64 * kXRow);
+    if (sn < NT) scb[(sn * kMRows + srow) * kCh + sc_c] = r.sc;
   };
 
-  v4i acc[kWT][NT][kDigits];
-  float F[kWT][NT][4];
-  float srow[kWT][NT];  // a per-row tensor's row scale
+  // Every step's three digit products start from zero and are joined into F at once: the
+  // step's scale (group-wise) or 1 (per-row, its row scale applied after the last step).  Low
+  // digits first in int32 (|r| <= 2^20 per step, so r1 * 256 + r0 is exact), then one float.
+  float F[4][NT][4];
 #pragma unroll
-  for (int t = 0; t < kWT; ++t)
+  for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      srow[t][n] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(sr[n], o_ok[t] && !grp[n] ? 4 * orow[t] : 0x7ffffff0, 0, 0));
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int d = 0; d < kDigits; ++d) acc[t][n][d] = v4i{0, 0, 0, 0};
+      for (int v = 0; v < 4; ++v) F[tt][n][v] = 0.f;
+  const int li = lane & 15, q = lane >> 4;
+  // a per-row tensor's scale: one value per lane (its weight row)
+  float srow_s[NT];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) F[t][n][v] = 0.f;
-    }
-  auto compute = [&](const MStep<NT> &st, int s) {
+  for (int n = 0; n < NT; ++n) {
+    const int orow = o0 + 16 * w + li;
+    srow_s[n] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(sr[n], (!grp[n] && orow < O) ? 4 * orow : kFar, 0, 0));
+  }
+  auto compute = [&](int stage, int nsteps, int s0) {
+    const uint8_t *base = s_lds + stage * stage_bytes<NT>();
+    const uint8_t *xb = base + NT * kMRows * kWRow;
+    const float *scb = reinterpret_cast<const float *>(xb + 64 * kXRow);
 #pragma unroll
-    for (int t = 0; t < kWT; ++t)
+    for (int cs = 0; cs < kCh; ++cs) {
+      if (cs >= nsteps) break;
+      v4i B[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const v4i B = weight_operand(st.w[t][n][0], st.w[t][n][1]);
+        const u32x2 u = *reinterpret_cast<const u32x2 *>(base + n * kMRows * kWRow + (16 * w + li) * kWRow + cs * 32 + 8 * q);
+        B[n] = weight_operand(u.x, u.y);
+      }
+      float sc[NT];
 #pragma unroll
-        for (int d = 0; d < kDigits; ++d)
-          acc[t][n][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.x[d], B, acc[t][n][d], 0, 0, 0);
-        if (grp[n]) {
-          const float sc = s_scale[w][t][n][li][(64 * s) / T[n].gs - g0[n]];
+      for (int n = 0; n < NT; ++n) sc[n] = grp[n] ? scb[(n * kMRows + 16 * w + li) * kCh + cs] : 1.f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) F[t][n][v] = fmaf(join3(acc[t][n], v), sc, F[t][n][v]);
+      for (int tt = 0; tt < 4; ++tt) {
+        if (tt < TT) {
+          v4i A[kDigits];
 #pragma unroll
-          for (int d = 0; d < kDigits; ++d) acc[t][n][d] = v4i{0, 0, 0, 0};
+          for (int d = 0; d < kDigits; ++d)
+            A[d] = *reinterpret_cast<const v4i *>(xb + (16 * tt + li) * kXRow + d * (kCh * 64) + cs * 64 + 16 * q);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            v4i r[kDigits];
+#pragma unroll
+            for (int d = 0; d < kDigits; ++d)
+              r[d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d], B[n], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int lo = (r[1][v] << 8) + r[0][v];
+              F[tt][n][v] = fmaf(fmaf((float)r[2][v], 65536.f, (float)lo), sc[n], F[tt][n][v]);
+            }
+          }
         }
       }
-  };
-  // two steps in flight: each step's registers are refilled with the step after next as soon as
-  // it is consumed; the loop runs in pairs
-  MStep<NT> b0, b1;
-  load(b0, s0);
-  load(b1, s0 + 1);
-  for (int s = s0; s < s1; s += 2) {
-    compute(b0, s);
-    load(b0, s + 2);
-    if (s + 1 < s1) compute(b1, s + 1);  // an odd last step
-    load(b1, s + 3);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-  for (int t = 0; t < kWT; ++t)
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      if (!grp[n])
-#pragma unroll
-        for (int v = 0; v < 4; ++v) F[t][n][v] = join3(acc[t][n], v) * srow[t][n];
-
-#pragma unroll
-  for (int t = 0; t < kWT; ++t)
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s_part[w][t][n][lane * 4 + v] = F[t][n][v];
-  __syncthreads();
-  // one output per thread: weight tile t, lane l2 = i / 4 of the result layout, v = i % 4
-  for (int i = threadIdx.x; i < kWT * kWave * 4; i += blockDim.x) {
-    const int t = i / (kWave * 4), e = i % (kWave * 4);
-    const int l2 = e >> 2, v = e & 3;
-    const int m = 4 * (l2 >> 4) + v;               // row of the token tile
-    const int o = 16 * (kWT * wt + t) + (l2 & 15);  // weight row
-    if (16 * tt + m < size && o < O) {
-      const int rg = start + 16 * tt + m;
-      const int dr = a.dual ? a.grp->rows[rg].token : rg;
-      const int E = a.E[dr];
-      float sum[NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float acc_w = 0.f;
-        for (int k = 0; k < KW; ++k) acc_w += s_part[k][t][n][e];
-        sum[n] = __builtin_ldexpf(acc_w, -E - 4);
-      }
-      float res = sum[0];
-      if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
-      a.out[(size_t)rg * a.out_ld + o] = res;
     }
+  };
+
+  // stages over this slice: load stage i + 1 while stage i computes
+  MLoads<NT> r;
+  if (k0 < k1) {
+    load(r, k0);
+    store(r, 0);
   }
+  __syncthreads();
+  int stage = 0;
+  for (int s0 = k0; s0 < k1; s0 += kCh) {
+    const bool more = s0 + kCh < k1;
+    if (more) load(r, s0 + kCh);
+    compute(stage, min(kCh, k1 - s0), s0);
+    if (more) store(r, stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    if (!grp[n])
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) F[tt][n][v] *= srow_s[n];
+  // partial sums of this slice: lane (li, q), element v = activation row 16 tt + 4 q + v,
+  // weight row o0 + 16 w + li
+  const int o = o0 + 16 * w + li;
+  if (o < O) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 16 * tt + 4 * q + v;
+          if (m < size)
+            a.part[((((size_t)ks * NT + n) * a.slots + slot) * 64 + m) * O + o] = F[tt][n][v];
+        }
+  }
+}
+
+// The slices' partial sums in slice order, then 2^(-E-4) and (dual) SiLU(gate) x up, into the
+// entry's rows of h or y.  Grid: (column blocks of 256, activation row m < 64, slot).
+template <int NT>
+__global__ __launch_bounds__(kBlock) void k_mfma_reduce(MfmaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.y, slot = blockIdx.z;
+  int start, size;
+  big_entry(a.grp, a.mfma_min, slot, lane, start, size);
+  if (m >= size) return;
+  const int o = blockIdx.x * kBlock + threadIdx.x;
+  if (o >= a.O) return;
+  const int rg = start + m;
+  const int dr = a.dual ? a.grp->rows[rg].token : rg;
+  const int E = a.E[dr];
+  float sum[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float acc = 0.f;
+    for (int ks = 0; ks < a.ksplit; ++ks) acc += a.part[((((size_t)ks * NT + n) * a.slots + slot) * 64 + m) * a.O + o];
+    sum[n] = __builtin_ldexpf(acc, -E - 4);
+  }
+  float res = sum[0];
+  if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
+  a.out[(size_t)rg * a.out_ld + o] = res;
 }
 
 }  // namespace
@@ -316,28 +406,44 @@ hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0, hip
   if (a.rows < 1 || a.rows > kRows || a.C < 1 || a.C64 % 64 != 0 || a.C64 < a.C || a.C64 > kMaxCols)
     return hipErrorInvalidValue;
   if (t0 || t1)
-    hipExtLaunchKernelGGL(k_digits8, dim3(a.rows), dim3(kBlock), 0, st, t0, t1, 0, a);
+    hipExtLaunchKernelGGL(k_digits8, dim3(a.rows), dim3(kDigBlock), 0, st, t0, t1, 0, a);
   else
-    hipLaunchKernelGGL(k_digits8, dim3(a.rows), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(k_digits8, dim3(a.rows), dim3(kDigBlock), 0, st, a);
   return hipGetLastError();
+}
+
+size_t mfma_part_floats(int NT, int O, int slots, int ksplit) { return (size_t)ksplit * NT * slots * 64 * O; }
+
+int mfma_ksplit(int O, int C64, int slots, int n_cu) {
+  const int blocks = slots * ((O + kMRows - 1) / kMRows);
+  const int KS = C64 / 64;
+  int k = (2 * n_cu + blocks - 1) / blocks;      // about two workgroups per CU
+  const int kmax = KS / (2 * kCh) > 0 ? KS / (2 * kCh) : 1;  // at least two stages per slice
+  k = k < 1 ? 1 : (k > kmax ? kmax : k);
+  return k > 32 ? 32 : k;
 }
 
 hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if ((NT != 1 && NT != 2) || a.mfma_min < 1 || a.C64 % 64 != 0 || a.C64 > kMaxCols || a.dig_rows < 1 ||
-      a.dig_rows > kRows || a.slots < 0 || a.slots > kRows || a.token_tiles < 1 || a.token_tiles > kRows / 16)
+      a.dig_rows > kRows || a.slots < 1 || a.slots > kRows || a.ksplit < 1 || !a.part)
     return hipErrorInvalidValue;
-  a.weight_tiles = (a.O + 16 * kWT - 1) / (16 * kWT);
-  a.tiles = a.slots * a.weight_tiles * a.token_tiles;
-  if (a.tiles < 1) return hipSuccess;
-  // waves splitting the columns: at least 8 steps of 64 columns each, at most kMfmaWaves
-  const int KS = a.C64 / 64;
-  int kw = KS / 8;
-  kw = kw < 1 ? 1 : (kw > kMfmaWaves ? kMfmaWaves : kw);
+  a.weight_tiles = (a.O + kMRows - 1) / kMRows;
+  a.tiles = a.slots * a.weight_tiles * a.ksplit;
   const int blocks = (a.tiles + 7) / 8 * 8;
   const void *k = NT == 2 ? reinterpret_cast<const void *>(&k_mfma<2>) : reinterpret_cast<const void *>(&k_mfma<1>);
+  const size_t lds = NT == 2 ? mfma_lds_bytes<2>() : mfma_lds_bytes<1>();
+  static bool raised[2][kMaxDevices] = {};
+  hipError_t e = raise_lds_once(k, (int)lds, raised[NT - 1]);
+  if (e != hipSuccess) return e;
   void *params[] = {&a};
-  const hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kw * kWave), params, 0, st, t0, t1, 0)
-                                  : hipLaunchKernel(k, dim3(blocks), dim3(kw * kWave), params, 0, st);
+  e = (t0) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st, t0, nullptr, 0)
+           : hipLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st);
+  if (e != hipSuccess) return e;
+  const void *kr = NT == 2 ? reinterpret_cast<const void *>(&k_mfma_reduce<2>)
+                           : reinterpret_cast<const void *>(&k_mfma_reduce<1>);
+  const dim3 rg((a.O + kBlock - 1) / kBlock, 64, a.slots);
+  e = (t1) ? hipExtLaunchKernel(kr, rg, dim3(kBlock), params, 0, st, nullptr, t1, 0)
+           : hipLaunchKernel(kr, rg, dim3(kBlock), params, 0, st);
   return e != hipSuccess ? e : hipGetLastError();
 }
 

@@ -22,10 +22,13 @@ static_assert(kRows == kWave, "take stages one slot per wave");
 // One token whose rows reduce in row order (a device route at S = 1: its selections are
 // distinct experts, one row each, in route order): every read is independent of the group
 // record (live flags and weights come from the row descriptors, y rows are read
-// speculatively up to the slot's capacity), so the whole take is one memory round trip.
-// The arithmetic is the general path's: fmaf over the live rows in order, slots in order.
-__device__ __forceinline__ void take_in_order(const TakeArgs &a) {
-  const int i = blockIdx.x * kBlock + threadIdx.x;
+// speculatively up to the slot's capacity), so the take is one or two memory round trips: one
+// wave per 64 columns (so the reads spread over many CUs) and 32 rows' loads in flight at a
+// time.  The arithmetic is the general path's: fmaf over the live rows in order, slots in order.
+constexpr int kTakeBatch = 32;
+
+__global__ __launch_bounds__(kWave) void k_take_in_order(TakeArgs a) {
+  const int i = blockIdx.x * kWave + threadIdx.x;
   if (i >= a.D) return;
   float *rp = a.resid + i;
   const float r_in = *rp;  // in flight with the rows' loads
@@ -35,18 +38,18 @@ __device__ __forceinline__ void take_in_order(const TakeArgs &a) {
     const float *__restrict__ y = a.y[s];
     const int rows = a.rows[s];
     float acc = 0.f;
-    for (int r0 = 0; r0 < rows; r0 += 8) {
-      float v[8], w[8];
-      int live[8];
+    for (int r0 = 0; r0 < rows; r0 += kTakeBatch) {
+      float v[kTakeBatch], w[kTakeBatch];
+      int live[kTakeBatch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < kTakeBatch; ++j) {
         const int r = min(r0 + j, rows - 1);
         v[j] = y[(size_t)r * a.y_ld + i];
         w[j] = G->rows[r].weight;
         live[j] = G->rows[r].t[0].live;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < kTakeBatch; ++j)
         if (r0 + j < rows && live[j]) acc = fmaf(w[j], v[j], acc);
     }
     total = (s == 0) ? acc : total + acc;
@@ -55,10 +58,6 @@ __device__ __forceinline__ void take_in_order(const TakeArgs &a) {
 }
 
 __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
-  if (a.in_order) {
-    take_in_order(a);
-    return;
-  }
   __shared__ int s_rr[kSlots][kRows];    // reduce order of each slot (group rows, token-major)
   __shared__ float s_rw[kSlots][kRows];  // route weight of each group row
   __shared__ int s_r0[kSlots], s_cnt[kSlots];
@@ -134,6 +133,14 @@ __global__ void k_group_store(GroupDev g, const ExpertRec *table, GroupBuf *dst)
 }  // namespace
 
 hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  if (a.in_order) {
+    const dim3 grid((a.D + kWave - 1) / kWave);
+    if (t0 || t1)
+      hipExtLaunchKernelGGL(k_take_in_order, grid, dim3(kWave), 0, st, t0, t1, 0, a);
+    else
+      hipLaunchKernelGGL(k_take_in_order, grid, dim3(kWave), 0, st, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.D + kBlock - 1) / kBlock, a.S);
   if (t0 || t1)
     hipExtLaunchKernelGGL(k_take, grid, dim3(kBlock), 0, st, t0, t1, 0, a);
