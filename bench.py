@@ -303,7 +303,7 @@ def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, mo
         print(json.dumps(table[R]), flush=True)
 
 
-def tiered(torch, B, reps: int = 20):
+def tiered(torch, B, reps: int = 30):
     """The CPU tier's overlap: experts of the small-batch shape (D=6144, I=2048, g64, bf16; 64
     experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1 and 4.
     Per S: wall time of the device rows alone, the host rows alone, and both in one tiered issue
@@ -338,26 +338,26 @@ def tiered(torch, B, reps: int = 20):
 
         arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": only(lambda e: e % 2 == 1), "tiered": rec}
         res = {"S": S, "threads": None}
-        for name, routes in arms.items():
-            for _ in range(3):
-                ctx.tiered_issue(0, x, routes)
-                ctx.take(out)
-            torch.cuda.synchronize()
-            walls, cpus = [], []
-            for _ in range(reps):
+        walls = {k: [] for k in arms}
+        cpus = []
+        for rep in range(reps + 3):  # the arms interleaved, so they see the same machine state
+            for name, routes in arms.items():
                 t0 = time.perf_counter()
                 _, tt = ctx.tiered_issue(0, x, routes)
                 ctx.take(out)
                 torch.cuda.synchronize()
-                walls.append(time.perf_counter() - t0)
-                cpus.append(tt.cpu_ms)
-            res[name + "_ms"] = round(float(np.median(walls)) * 1e3, 3)
-            if name == "tiered":
-                res["device_rows"], res["host_rows"] = tt.device_rows, tt.host_rows
-                res["tiered_cpu_ms"] = round(float(np.median(cpus)), 3)
+                if rep >= 3:
+                    walls[name].append(time.perf_counter() - t0)
+                    if name == "tiered":
+                        cpus.append(tt.cpu_ms)
+                        res["device_rows"], res["host_rows"] = tt.device_rows, tt.host_rows
+        for name in arms:
+            res[name + "_ms"] = round(float(np.median(walls[name])) * 1e3, 3)
+        res["tiered_cpu_ms"] = round(float(np.median(cpus)), 3)
         res["serial_ms"] = round(res["device_only_ms"] + res["host_only_ms"], 3)
         res["hidden_ms"] = round(res["serial_ms"] - res["tiered_ms"], 3)
-        res["threads"] = int(os.environ.get("I4MOE_HOST_THREADS", "0")) or min(16, os.cpu_count() or 1)
+        hw = len(os.sched_getaffinity(0))
+        res["threads"] = int(os.environ.get("I4MOE_HOST_THREADS", "0")) or (1 if hw <= 2 else min(16, hw - 1))
         log(f"tiered S={S}: {res}")
         print(json.dumps(res), flush=True)
         ctx.close()

@@ -314,8 +314,9 @@ typedef struct {
 int i4moe_set_host_expert(i4moe_ctx *ctx, int layer, int expert, const i4moe_host_tensor *gate,
                           const i4moe_host_tensor *up, const i4moe_host_tensor *down);
 
-/* Host wall-clock split of one tiered issue, in milliseconds (cf. the overlap window of [PR342]):
- * enqueueing the device group, waiting for x to reach the host, the CPU rows, and the whole call. */
+/* Host wall-clock split of one tiered issue, in milliseconds (cf. the overlap window of [PR342]),
+ * each from the start of the call: until the device group is enqueued (issue_ms), until x has
+ * reached the host (x_wait_ms); then the CPU rows themselves (cpu_ms) and the whole call. */
 typedef struct {
   double issue_ms, x_wait_ms, cpu_ms, total_ms;
   int32_t device_rows, host_rows;
@@ -330,15 +331,27 @@ typedef struct {
  * issue order (the device slot first), so the sum order is fixed and the result bitwise
  * reproducible [PR434].
  * x_dev ([S][D], F32 or BF16) is copied to the host on the stream before the device group's
- * kernels are enqueued; the CPU starts when that copy has landed, and the call returns when the
- * CPU rows are done and their sum is enqueued for upload (the device group may still be running).
+ * kernels are enqueued; the CPU rows start on a helper thread of the context when that copy has
+ * landed, while the calling thread enqueues the device group, and the call returns when the CPU
+ * rows are done and their sum is enqueued for upload (the device group may still be running).
  * Uses up to 2 slots; returns the number of slots issued (0 when no token has an expert), or a
  * negative code.  Every expert the routes name must be bound on the device or kept on the host.
  * On failure nothing is left pending except possibly the copy of x.  times may be NULL.
- * Host threads: I4MOE_HOST_THREADS at context creation (1..256; default the host's cores, at
- * most 16).  Fault-hook gated (one compute call). */
+ * Host threads: I4MOE_HOST_THREADS at context creation (1..256; default the host's cores but
+ * one, at most 16).  Fault-hook gated (one compute call). */
 int i4moe_tiered_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S,
                        const i4moe_route_host *routes, i4moe_tier_times *times);
+
+/* The CPU tier's arithmetic alone (host only, no device and no context; what i4moe_tiered_issue
+ * runs for its host rows) [PR342]: for r < n_rows, in order,
+ *   P[token[r]][d] += weight[r] * (down[r] . (silu(gate[r] . x_t) * (up[r] . x_t)))[d]
+ * with x: S x D float32 rows and P: S x D float32 (accumulated into), gate/up/down[r] host tensors
+ * (I x D, I x D, D x I, layouts as i4moe_upload_expert_tensor), in float32 as described at
+ * i4moe_tiered_issue.  threads >= 1 workers (the results do not depend on the count).
+ * Errors: EINVAL (bad shapes, tokens, NULL pointers, non-finite scales or weights), ENOMEM. */
+int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const float *weight,
+                    const i4moe_host_tensor *gate, const i4moe_host_tensor *up, const i4moe_host_tensor *down,
+                    const float *x, float *P, int threads);
 
 /* ---- profiling ---------------------------------------------------------------------------- */
 

@@ -5,4 +5,4 @@ The compute lives in libi4moe.so (HIP kernels behind the C ABI of include/i4moe.
 """
 
 from . import binding  # noqa: F401
-from .runtime import Context, I4moeError  # noqa: F401
+from .runtime import Context, I4moeError, host_rows  # noqa: F401

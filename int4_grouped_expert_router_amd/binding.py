@@ -75,6 +75,9 @@ SIGNATURES = {
                                         C.POINTER(i4moe_host_tensor), C.POINTER(i4moe_host_tensor)]),
     "i4moe_tiered_issue": (C.c_int, [_ctx_p, C.c_int, C.c_void_p, C.c_int, C.c_int, C.POINTER(i4moe_route_host),
                                      C.POINTER(i4moe_tier_times)]),
+    "i4moe_host_rows": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                  C.POINTER(i4moe_host_tensor), C.POINTER(i4moe_host_tensor),
+                                  C.POINTER(i4moe_host_tensor), C.c_void_p, C.c_void_p, C.c_int]),
     "i4moe_set_fail_after": (C.c_int, [_ctx_p, C.c_longlong]),
     "i4moe_debug_read": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t]),
     "i4moe_debug_size": (C.c_size_t, [_ctx_p, C.c_int, C.c_int]),
@@ -133,6 +136,7 @@ i4moe_shared_expert_issue = _fn("i4moe_shared_expert_issue")
 i4moe_moe_block = _fn("i4moe_moe_block")
 i4moe_set_host_expert = _fn("i4moe_set_host_expert")
 i4moe_tiered_issue = _fn("i4moe_tiered_issue")
+i4moe_host_rows = _fn("i4moe_host_rows")
 i4moe_set_fail_after = _fn("i4moe_set_fail_after")
 i4moe_debug_read = _fn("i4moe_debug_read")
 i4moe_debug_size = _fn("i4moe_debug_size")

@@ -6,6 +6,8 @@
 // later healthy call, uploaded tensors never look at the caller's host buffers again, and the
 // fail-after hook gates compute entry points only.  The take is fatal on failure, as in the
 // COLI_CUDA_RESID page: a take that did not run would silently drop routed experts.
+#include <sched.h>
+
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -116,6 +118,7 @@ struct i4moe_ctx {
   // that say when the x copy has landed and when the sum's upload has been read
   int host_threads = 0;
   std::unique_ptr<HostPool> pool;
+  std::unique_ptr<HostHelper> helper;  // runs the host rows while the calling thread issues the device group
   void *h_x = nullptr;          // [kTokens][kMaxCols] float32 or bf16, pinned
   float *h_P = nullptr;         // [kTokens][kMaxCols] float32, pinned
   hipEvent_t ev_x = nullptr, ev_p = nullptr;
@@ -552,8 +555,12 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
     if (v >= 0.05 && v <= 64.0) c->wave_factor = v;
   }
   {
-    const unsigned hw = std::thread::hardware_concurrency();
-    c->host_threads = hw == 0 ? 1 : (hw > 16 ? 16 : (int)hw);
+    // the cores this process may run on but one (the calling thread issues the device group
+    // meanwhile), at most 16
+    unsigned hw = std::thread::hardware_concurrency();
+    cpu_set_t cs;
+    if (sched_getaffinity(0, sizeof cs, &cs) == 0 && CPU_COUNT(&cs) > 0) hw = (unsigned)CPU_COUNT(&cs);
+    c->host_threads = hw <= 2 ? 1 : (hw - 1 > 16 ? 16 : (int)hw - 1);
   }
   if (const char *ht = std::getenv("I4MOE_HOST_THREADS")) {
     char *end = nullptr;
@@ -604,6 +611,7 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   dfree(c->d_dig);
   dfree(c->d_dig_E);
   dfree(c->d_part);
+  c->helper.reset();
   c->pool.reset();
   if (c->h_x) (void)hipHostFree(c->h_x);
   if (c->h_P) (void)hipHostFree(c->h_P);
@@ -1559,6 +1567,55 @@ static int host_tensor_copy(i4moe_ctx *c, const i4moe_host_tensor *h, const char
   return I4MOE_OK;
 }
 
+int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const float *weight,
+                    const i4moe_host_tensor *gate, const i4moe_host_tensor *up, const i4moe_host_tensor *down,
+                    const float *x, float *P, int threads) {
+  if (S < 1 || D < 2 || I < 2 || n_rows < 0 || threads < 1 || threads > 256 || !x || !P) return I4MOE_EINVAL;
+  if (n_rows > 0 && (!token || !weight || !gate || !up || !down)) return I4MOE_EINVAL;
+  std::vector<HostExpert> ex;
+  std::vector<HostRow> rows;
+  try {
+    ex.resize(n_rows);
+    rows.reserve(n_rows);
+  } catch (const std::bad_alloc &) {
+    return I4MOE_ENOMEM;
+  }
+  // the same checks as i4moe_set_host_expert, without a context to report them on
+  auto copy = [](const i4moe_host_tensor &h, int O, int C, HostTensor &t) -> int {
+    if (h.O != O || h.C != C || h.C % 2 != 0 || h.C > kMaxCols || !h.packed || !h.scales) return I4MOE_EINVAL;
+    if (h.fmt != I4MOE_FMT_ROW && h.fmt != I4MOE_FMT_GROUP) return I4MOE_EUNSUPPORTED;
+    if ((h.fmt == I4MOE_FMT_ROW && h.gs != 0) || (h.fmt == I4MOE_FMT_GROUP && (h.gs < 0 || h.gs % 2 != 0)))
+      return I4MOE_EINVAL;
+    t.O = O;
+    t.C = C;
+    t.gs = h.fmt == I4MOE_FMT_GROUP ? h.gs : 0;
+    t.ng = t.gs > 0 ? (C + t.gs - 1) / t.gs : 1;
+    if (!all_finite(h.scales, (size_t)O * t.ng)) return I4MOE_EINVAL;
+    try {
+      t.packed.assign(h.packed, h.packed + (size_t)O * (C / 2));
+      t.scales.assign(h.scales, h.scales + (size_t)O * t.ng);
+    } catch (const std::bad_alloc &) {
+      return I4MOE_ENOMEM;
+    }
+    return I4MOE_OK;
+  };
+  for (int r = 0; r < n_rows; ++r) {
+    if (token[r] < 0 || token[r] >= S || !std::isfinite(weight[r])) return I4MOE_EINVAL;
+    int rc;
+    if ((rc = copy(gate[r], I, D, ex[r].gate)) || (rc = copy(up[r], I, D, ex[r].up)) ||
+        (rc = copy(down[r], D, I, ex[r].down)))
+      return rc;
+    rows.push_back(HostRow{token[r], &ex[r], weight[r]});
+  }
+  try {
+    HostPool pool(threads);
+    host_rows_forward(pool, rows, x, D, I, P);
+  } catch (const std::exception &) {
+    return I4MOE_ENOMEM;
+  }
+  return I4MOE_OK;
+}
+
 int i4moe_set_host_expert(i4moe_ctx *c, int layer, int expert, const i4moe_host_tensor *gate,
                           const i4moe_host_tensor *up, const i4moe_host_tensor *down) {
   if (!c) return I4MOE_EINVAL;
@@ -1604,6 +1661,10 @@ static int tier_buffers(i4moe_ctx *c) {
   if (!c->pool) {
     c->pool.reset(new (std::nothrow) HostPool(c->host_threads));
     if (!c->pool) return fail(c, I4MOE_ENOMEM, "host worker pool");
+  }
+  if (!c->helper) {
+    c->helper.reset(new (std::nothrow) HostHelper());
+    if (!c->helper) return fail(c, I4MOE_ENOMEM, "host helper thread");
   }
   return I4MOE_OK;
 }
@@ -1668,33 +1729,49 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
     if (e == hipSuccess) e = hipEventRecord(c->ev_x, c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "copy of x to the host");
   }
+  // The host rows start on the helper thread as soon as x has landed, while this thread issues
+  // the device group (its host-side work and launches overlap them too).
+  hipError_t host_err = hipSuccess;
+  auto t_x = clk::now(), t_cpu = t_x;
+  if (host) {
+    // the previous tiered issue's upload of the host sum must have read it
+    if (c->ev_p_recorded && (e = hipEventSynchronize(c->ev_p)) != hipSuccess) return hip_fail(c, e, "wait for upload");
+    c->helper->post([&, S, D, I] {
+      host_err = hipEventSynchronize(c->ev_x);
+      t_x = clk::now();
+      if (host_err != hipSuccess) return;
+      std::vector<float> xf((size_t)S * D);
+      if (dtype == I4MOE_DTYPE_F32) {
+        std::memcpy(xf.data(), c->h_x, sizeof(float) * xf.size());
+      } else {
+        const uint16_t *xb = static_cast<const uint16_t *>(c->h_x);
+        for (size_t i = 0; i < xf.size(); ++i) {
+          const uint32_t u = (uint32_t)xb[i] << 16;
+          std::memcpy(&xf[i], &u, 4);
+        }
+      }
+      std::memset(c->h_P, 0, sizeof(float) * (size_t)S * D);
+      host_rows_forward(*c->pool, hrows, xf.data(), D, I, c->h_P);
+      t_cpu = clk::now();
+    });
+  }
   int issued = 0;
   if (dev) {
     i4moe_group g{(int32_t)de.size(), de.data(), dt.data(), dw.data()};
     const int s = issue_impl(c, layer, x_dev, dtype, S, &g, false);
-    if (s < 0) return s;
+    if (s < 0) {
+      if (host) c->helper->wait();
+      return s;
+    }
     ++issued;
   }
   const auto t_issued = clk::now();
-  auto t_x = t_issued, t_cpu = t_issued;
   if (host) {
-    if ((e = hipEventSynchronize(c->ev_x)) != hipSuccess) return hip_fail(c, e, "wait for x");
-    t_x = clk::now();
-    std::vector<float> xf((size_t)S * D);
-    if (dtype == I4MOE_DTYPE_F32) {
-      std::memcpy(xf.data(), c->h_x, sizeof(float) * xf.size());
-    } else {
-      const uint16_t *xb = static_cast<const uint16_t *>(c->h_x);
-      for (size_t i = 0; i < xf.size(); ++i) {
-        const uint32_t u = (uint32_t)xb[i] << 16;
-        std::memcpy(&xf[i], &u, 4);
-      }
+    c->helper->wait();
+    if (host_err != hipSuccess) {
+      if (dev) c->poisoned = true;  // the device slot is issued but the host rows would be lost
+      return hip_fail(c, host_err, "wait for x");
     }
-    // the previous tiered issue's upload of the host sum must have read it
-    if (c->ev_p_recorded && (e = hipEventSynchronize(c->ev_p)) != hipSuccess) return hip_fail(c, e, "wait for upload");
-    std::memset(c->h_P, 0, sizeof(float) * (size_t)S * D);
-    host_rows_forward(*c->pool, hrows, xf.data(), D, I, c->h_P);
-    t_cpu = clk::now();
     // the host slot: one row per token, weight 1, holding the token's sum of host rows
     const int s = c->nslots;
     GroupDev hg;
@@ -1739,7 +1816,7 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
     auto ms = [](clk::time_point a, clk::time_point b) { return std::chrono::duration<double, std::milli>(b - a).count(); };
     const auto t_end = clk::now();
     times->issue_ms = ms(t_start, t_issued);
-    times->x_wait_ms = host ? ms(t_issued, t_x) : 0.0;
+    times->x_wait_ms = host ? ms(t_start, t_x) : 0.0;
     times->cpu_ms = host ? ms(t_x, t_cpu) : 0.0;
     times->total_ms = ms(t_start, t_end);
     times->device_rows = (int32_t)de.size();

@@ -51,6 +51,25 @@ class HostPool {
   bool stop_ = false;
 };
 
+// One job at a time on a thread of its own: post(fn) hands fn over and returns at once, wait()
+// returns when it has finished.
+class HostHelper {
+ public:
+  HostHelper();
+  ~HostHelper();
+  HostHelper(const HostHelper &) = delete;
+  HostHelper &operator=(const HostHelper &) = delete;
+  void post(std::function<void()> fn);
+  void wait();
+
+ private:
+  std::thread t_;
+  std::mutex m_;
+  std::condition_variable cv_;
+  std::function<void()> job_;
+  bool busy_ = false, stop_ = false;
+};
+
 // One host row: (token, expert, weight).
 struct HostRow {
   int token;
@@ -62,7 +81,8 @@ struct HostRow {
 //   P[t][d] += sum over the rows r of token t, in order, of w_r * y_r[d],
 //   y_r = down . (silu(gate . x_t) * (up . x_t))
 // x: S x D float32 rows, P: S x D float32 (accumulated into).  Each weight row's dot product is
-// summed over its columns in order, group by group (a group's products summed, then scaled).
+// summed group by group (a group's products summed, then scaled): in column order, or, on a host
+// with AVX2 and FMA, 32 columns at a time in four 8-wide partial sums added in a fixed order.
 void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const float *x, int D, int I, float *P);
 
 }  // namespace i4moe

@@ -29,6 +29,31 @@ def _dtype_code(t) -> int:
     raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
 
 
+def host_rows(S: int, D: int, I: int, rows, x: np.ndarray, threads: int = 1) -> np.ndarray:
+    """The CPU tier's arithmetic alone (i4moe_host_rows; host only): rows is a list of
+    (token, weight, gate, up, down) with host tensors; x is S x D float32.  Returns P (S x D)."""
+    n = len(rows)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    P = np.zeros((S, D), dtype=np.float32)
+    keep = []
+
+    def desc(t):
+        packed = np.ascontiguousarray(t.packed, dtype=np.uint8)
+        scales = np.ascontiguousarray(t.scales, dtype=np.float32)
+        keep.append((packed, scales))
+        return B.i4moe_host_tensor(t.fmt, t.gs, t.O, t.C, _ptr(packed), _ptr(scales))
+
+    tok = np.array([r[0] for r in rows] or [0], dtype=np.int32)
+    wt = np.array([r[1] for r in rows] or [0.0], dtype=np.float32)
+    g = (B.i4moe_host_tensor * max(n, 1))(*[desc(r[2]) for r in rows])
+    u = (B.i4moe_host_tensor * max(n, 1))(*[desc(r[3]) for r in rows])
+    d = (B.i4moe_host_tensor * max(n, 1))(*[desc(r[4]) for r in rows])
+    rc = B.i4moe_host_rows(S, D, I, n, _ptr(tok), _ptr(wt), g, u, d, _ptr(x), _ptr(P), threads)
+    if rc < 0:
+        raise I4moeError(rc, "i4moe_host_rows refused its arguments")
+    return P
+
+
 class Context:
     def __init__(self, device: int = 0, stream=None):
         B.load()
