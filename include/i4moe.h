@@ -211,6 +211,9 @@ int i4moe_route_noalloc(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype,
  * enqueues only the dual projection: the take then runs the down projection and the
  * reduction in one kernel.  A y tap, another issue, a stream switch or a change of the
  * layer's experts runs the down projection on its own first; the results are bitwise the same.
+ * The first issue whose entries reach the matrix cores (I4MOE_MFMA_MIN_ROWS) allocates their
+ * scratch (digit rows, column-slice partial sums; the latter grows for larger shapes), which
+ * synchronises the stream: under graph capture, run one issue of the same shape eagerly first.
  * Fault-hook gated. */
 int i4moe_expert_group_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, int S,
                              const i4moe_group *group);

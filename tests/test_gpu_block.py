@@ -99,6 +99,9 @@ CASES = {
     "medium_like": ("medium", {"E": 16}),
     "small_batch_like": ("small_batch", {"D": 2048, "I": 768, "E": 32, "K": 4}),
     "sustained_like": ("sustained", {"E": 16, "K": 8}),
+    # 16 tokens: the shared expert's entry (16 rows) and the routed entries of 8 rows or more run on
+    # the matrix cores, the others on the vector kernels, in one block
+    "prefill_like": ("small_batch", {"D": 2048, "I": 768, "E": 8, "K": 2, "S": 16}),
 }
 
 
