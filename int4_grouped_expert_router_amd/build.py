@@ -29,6 +29,9 @@ CFLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs: the join that follows each MFMA then needs no
+    # v_accvgpr_read per result dword
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

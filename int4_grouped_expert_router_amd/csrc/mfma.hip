@@ -13,15 +13,18 @@
 // and scaled (a group-wise tensor's group scale, group sizes being multiples of 64; a per-row
 // tensor's row scale after the last step).  The result is (join) 2^-E / 16.
 //
-// Tiling: a workgroup owns 32 output rows x 16 rows of one entry (an expert's group rows, its
-// token tile); its waves (up to 8, each with at least 8 steps of 64 columns) split the columns,
-// and their partial results meet in LDS, summed in wave order.  Each wave keeps two steps of
-// loads in flight.  MFMA operands: A = 16 activation rows x 64 columns (lane l: row l % 16, bytes of
-// columns 16 (l / 16) .. +15 of the step), B = 64 columns x 16 weight rows (lane l: weight row
-// l % 16, the same columns), so the 4 result dwords of lane l are rows 4 (l / 16) + v of the
-// activation tile against weight row l % 16: one lane holds one weight row, and the row's scale
-// is one value per lane.  Inside every 16 columns the bytes run in the order the nibble masks
-// produce them (0 2 4 6 1 3 5 7, then 8 .. 15 likewise); the digit rows are written in that order.
+// Tiling: a workgroup of four waves owns 64 weight rows (one 16-row tile per wave) x every
+// 16-row token tile of one entry (an expert's group rows) x one slice of the columns; the slices
+// spread an entry over about two workgroups per CU.  Each stage (two steps of 64 columns: the
+// weight rows and the digit rows) is loaded by the whole workgroup with 16-byte loads into LDS
+// while the previous stage computes.  A slice's partial sums go to memory and a second launch
+// adds the slices in slice order.  MFMA operands: A = 16 activation rows x 64 columns (lane l:
+// row l % 16, bytes of columns 16 (l / 16) .. +15 of the step), B = 64 columns x 16 weight rows
+// (lane l: weight row l % 16, the same columns), so the 4 result dwords of lane l are rows
+// 4 (l / 16) + v of the activation tile against weight row l % 16: one lane holds one weight
+// row, and the row's scale is one value per lane.  Inside every 16 columns the bytes run in the
+// order the nibble masks produce them (0 2 4 6 1 3 5 7, then 8 .. 15 likewise); the digit rows
+// are written in that order.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -34,7 +37,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDigits = 3;
-constexpr int kMfmaWaves = 8;
 constexpr int kNontemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {

@@ -21,40 +21,38 @@ static_assert(kRows == kWave, "take stages one slot per wave");
 
 // One token whose rows reduce in row order (a device route at S = 1: its selections are
 // distinct experts, one row each, in route order): every read is independent of the group
-// record (live flags and weights come from the row descriptors, y rows are read
-// speculatively up to the slot's capacity), so the take is one or two memory round trips: one
-// wave per 64 columns (so the reads spread over many CUs) and 32 rows' loads in flight at a
-// time.  The arithmetic is the general path's: fmaf over the live rows in order, slots in order.
-constexpr int kTakeBatch = 32;
-
+// record (live flags and weights come from the row descriptors), so the take is one memory round
+// trip: one wave per 64 columns (so the reads spread over many CUs); lane j loads row j's weight
+// and live flag while every lane loads its column of all of a slot's y rows (a slot has at most
+// kRows = 64), then the FMAs run in row order with each row's weight read from its lane.  The
+// arithmetic is the general path's: fmaf over the live rows in order, slots in order.
 __global__ __launch_bounds__(kWave) void k_take_in_order(TakeArgs a) {
-  const int i = blockIdx.x * kWave + threadIdx.x;
-  if (i >= a.D) return;
-  float *rp = a.resid + i;
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x * kWave + lane;
+  const int ic = min(i, a.D - 1);  // every lane stays for the broadcasts; lanes past D store nothing
+  float *rp = a.resid + ic;
   const float r_in = *rp;  // in flight with the rows' loads
   float total = 0.f;
   for (int s = 0; s < a.nslots; ++s) {
     const CGroupBuf G = (CGroupBuf)a.groups[s];
     const float *__restrict__ y = a.y[s];
-    const int rows = a.rows[s];
+    const int rows = min(a.rows[s], kRows);
+    const int rl = min(lane, max(rows - 1, 0));
+    const float wl = G->rows[rl].weight;
+    const int livel = lane < rows ? G->rows[rl].t[0].live : 0;
+    float v[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) v[j] = j < rows ? y[(size_t)j * a.y_ld + ic] : 0.f;
     float acc = 0.f;
-    for (int r0 = 0; r0 < rows; r0 += kTakeBatch) {
-      float v[kTakeBatch], w[kTakeBatch];
-      int live[kTakeBatch];
 #pragma unroll
-      for (int j = 0; j < kTakeBatch; ++j) {
-        const int r = min(r0 + j, rows - 1);
-        v[j] = y[(size_t)r * a.y_ld + i];
-        w[j] = G->rows[r].weight;
-        live[j] = G->rows[r].t[0].live;
-      }
-#pragma unroll
-      for (int j = 0; j < kTakeBatch; ++j)
-        if (r0 + j < rows && live[j]) acc = fmaf(w[j], v[j], acc);
+    for (int j = 0; j < kRows; ++j) {
+      const int live = __builtin_amdgcn_readlane(livel, j);
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+      if (live) acc = fmaf(w, v[j], acc);
     }
     total = (s == 0) ? acc : total + acc;
   }
-  *rp = r_in + total;
+  if (i < a.D) *rp = r_in + total;
 }
 
 __global__ __launch_bounds__(kBlock) void k_take(TakeArgs a) {
