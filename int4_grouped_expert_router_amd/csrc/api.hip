@@ -313,7 +313,7 @@ int ensure_digit_scratch(i4moe_ctx *c) {
   int8_t *d = nullptr;
   int *E = nullptr;
   if ((e = dalloc(&d, (size_t)kRows * 3 * kMaxCols)) != hipSuccess) return hip_fail(c, e, "hipMalloc(digit rows)");
-  if ((e = dalloc(&E, sizeof(int) * kRows)) != hipSuccess) {
+  if ((e = dalloc(&E, sizeof(int) * 2 * kRows)) != hipSuccess) {  // x rows by token, then h rows
     dfree(d);
     return hip_fail(c, e, "hipMalloc(digit exponents)");
   }
@@ -1171,37 +1171,40 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   const bool defer_down = S == 1 && !group && s == 0 && pn.rows16 && max_rows <= kDTRows;
   hipError_t e = hipSuccess;
   if (group) e = launch_group_store(hg, L->d_tab, c->d_slot_bufs + s, c->stream);
-  // matrix-core launches of one projection: the digit rows of its activations, then the
-  // projection of the big entries (after the vector kernels of the same projection)
+  // matrix-core launches of one projection: the dual's digit rows of x, the projection of the
+  // big entries (after the vector kernels of the same projection) and its reduction, which for
+  // the dual also writes the digit rows of h that the down projection reads
   auto mfma = [&](bool dual) -> hipError_t {
     DigitArgs da{};
-    da.act = dual ? x_dev : c->d_h;
-    da.grp = dual ? nullptr : grp;
+    da.act = x_dev;
     da.dig = c->d_dig;
     da.E = c->d_dig_E;
-    da.act_ld = dual ? L->D : c->h_ld;
-    da.bf16 = dual && dtype == I4MOE_DTYPE_BF16;
-    da.rows = dual ? S : max_rows;
-    da.C = dual ? L->D : L->I;
-    da.C64 = round_up(da.C, 64);
+    da.act_ld = L->D;
+    da.bf16 = dtype == I4MOE_DTYPE_BF16;
+    da.rows = S;
+    da.C = L->D;
+    da.C64 = round_up(L->D, 64);
     MfmaArgs ma{};
     ma.grp = grp;
     ma.dig = c->d_dig;
-    ma.E = c->d_dig_E;
+    ma.E = dual ? c->d_dig_E : c->d_dig_E + kRows;
     ma.out = dual ? c->d_h : an.out;
     ma.out_ld = dual ? c->h_ld : c->y_ld;
-    ma.dig_rows = da.rows;
+    ma.dig_out = dual ? c->d_dig : nullptr;
+    ma.E_out = dual ? c->d_dig_E + kRows : nullptr;
+    ma.dig_rows = dual ? S : max_rows;
     ma.dual = dual ? 1 : 0;
     ma.O = dual ? L->I : L->D;
-    ma.C64 = da.C64;
+    ma.C64 = dual ? da.C64 : round_up(L->I, 64);
     ma.mfma_min = mfma_min;
     ma.slots = mfma_slots;
     ma.ksplit = dual ? ks_dual : ks_down;
     ma.part = c->d_part;
     return timed(c, I4MOE_K_MFMA, [&](hipEvent_t t0, hipEvent_t t1) {
-      // the event pair spans both launches: start of the digit rows, end of the projection
+      // the event pair spans the projection's launches
+      if (!dual) return launch_mfma(1, ma, c->stream, t0, t1);
       hipError_t r = launch_digits8(da, c->stream, t0, nullptr);
-      return r != hipSuccess ? r : launch_mfma(dual ? 2 : 1, ma, c->stream, nullptr, t1);
+      return r != hipSuccess ? r : launch_mfma(2, ma, c->stream, nullptr, t1);
     });
   };
   if (e == hipSuccess && vec_rows) e = timed(c, I4MOE_K_DUAL, [&](hipEvent_t t0, hipEvent_t t1) {

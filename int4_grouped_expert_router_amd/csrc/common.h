@@ -127,16 +127,19 @@ struct DigitArgs {
 };
 
 // Matrix-core projection of the entries with at least mfma_min rows (slot k: the k-th such
-// entry in entry order).  dual: gate/up + SiLU into h rows, digit rows indexed by token; else the
-// down projection into y rows, digit rows indexed by group row.  The columns are split into
-// ksplit slices whose partial sums go to part ([ksplit][NT][slots][64][O] floats) and are added
-// in slice order by the reduction launch.
+// entry in entry order).  dual: gate/up + SiLU into h rows, digit rows indexed by token, and the
+// digit rows of those h rows (dig_out, E_out, indexed by group row) for the down projection;
+// else the down projection into y rows, digit rows indexed by group row.  The columns are split
+// into ksplit slices whose partial sums go to part ([ksplit][NT][slots][64][O] floats) and are
+// added in slice order by the reduction launch.
 struct MfmaArgs {
   const GroupBuf *grp;
   const int8_t *dig;
   const int *E;
   float *out;
   float *part;
+  int8_t *dig_out;  // dual: digit rows of h
+  int *E_out;       // dual: their exponents
   int out_ld, dig_rows, dual;
   int O, C64;
   int mfma_min, slots, ksplit;

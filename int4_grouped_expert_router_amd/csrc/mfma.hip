@@ -50,6 +50,42 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 // ---- Digit rows ----------------------------------------------------------------------------
 
+// A row's exponent from the bits of its largest |a|: max |a| 2^E < 2^22 (a zero row: E = 148,
+// zero digits).
+__device__ __forceinline__ int row_exponent_bits(uint32_t m) { return 148 - (int)(m >> 23); }
+
+// The three digit chunks of columns 16 b .. 16 b + 15 of a row (values v, zeros past its end)
+// whose exponent is E, in the byte order of the weight operand, into the row's digit rows at dst
+// (C64 bytes per digit).
+__device__ __forceinline__ void store_digit_chunk(const float (&v)[16], int E, int8_t *dst, int C64, int b) {
+  uint32_t d[kDigits][4] = {};
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    // byte p of the chunk holds column 16 b + col(p): within each half, even columns first
+    const int h = p >> 3, r = p & 7;
+    const int col = 8 * h + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
+    const int X = (int)__builtin_rintf(__builtin_ldexpf(v[col], E));
+    const uint32_t u = ((uint32_t)X + 0x808080u) ^ 0x808080u;  // balanced digits as int8
+#pragma unroll
+    for (int n = 0; n < kDigits; ++n) d[n][p >> 2] |= ((u >> (8 * n)) & 0xffu) << (8 * (p & 3));
+  }
+#pragma unroll
+  for (int n = 0; n < kDigits; ++n)
+    *reinterpret_cast<u32x4 *>(dst + (size_t)n * C64 + 16 * b) = u32x4{d[n][0], d[n][1], d[n][2], d[n][3]};
+}
+
+// The largest of the workgroup's values (all threads; holds a workgroup barrier).
+template <int NW>
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t (&s_max)[NW]) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = s_max[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) m = max(m, s_max[k]);
+  return m;
+}
+
 // One workgroup per activation row: E from the row's largest |a|, then 16 columns per thread
 // and step, written as three 16-byte digit chunks in the byte order of the weight operand.
 constexpr int kDigBlock = 1024;  // threads per activation row
@@ -92,32 +128,13 @@ __global__ __launch_bounds__(kDigBlock) void k_digits8(DigitArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(v[k]) & 0x7fffffffu);
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = s_max[0];
-#pragma unroll
-  for (int k = 1; k < kDigBlock / kWave; ++k) m = max(m, s_max[k]);
-  const int E = 148 - (int)(m >> 23);  // max |a| 2^E < 2^22 (a zero row: E = 148, zero digits)
+  const int E = row_exponent_bits(block_max(m, s_max));
   if (threadIdx.x == 0) a.E[row] = E;
   int8_t *dst = a.dig + (size_t)row * kDigits * a.C64;
   for (int b = threadIdx.x; b < nb; b += kDigBlock) {
     float v[16];
     load16(b, v);
-    uint32_t d[kDigits][4] = {};
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      // byte p of the chunk holds column 16 b + col(p): within each half, even columns first
-      const int h = p >> 3, r = p & 7;
-      const int col = 8 * h + (r < 4 ? 2 * r : 2 * (r - 4) + 1);
-      const int X = (int)__builtin_rintf(__builtin_ldexpf(v[col], E));
-      const uint32_t u = ((uint32_t)X + 0x808080u) ^ 0x808080u;  // balanced digits as int8
-#pragma unroll
-      for (int n = 0; n < kDigits; ++n) d[n][p >> 2] |= ((u >> (8 * n)) & 0xffu) << (8 * (p & 3));
-    }
-#pragma unroll
-    for (int n = 0; n < kDigits; ++n)
-      *reinterpret_cast<u32x4 *>(dst + (size_t)n * a.C64 + 16 * b) = u32x4{d[n][0], d[n][1], d[n][2], d[n][3]};
+    store_digit_chunk(v, E, dst, a.C64, b);
   }
 }
 
@@ -182,7 +199,7 @@ struct MLoads {
 // tiles of the entry x one slice of the columns; wave w owns weight tile w.  Each stage is loaded
 // by the whole workgroup with 16-byte loads (a weight row's kCh x 32 bytes, a digit row's
 // kCh x 64 bytes) while the previous stage computes.  The partial sums of the slice go to
-// a.part[slice][n][slot][m][o]; k_mfma_reduce adds the slices in order.
+// a.part[slice][n][slot][m][o]; k_mfma_h (dual) or k_mfma_reduce (down) adds the slices in order.
 template <int NT>
 __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
@@ -376,9 +393,25 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   }
 }
 
-// The slices' partial sums in slice order, then 2^(-E-4) and (dual) SiLU(gate) x up, into the
-// entry's rows of h or y.  Grid: (column blocks of 256, activation row m < 64, slot).
-template <int NT>
+// Sum over the slices ks < ksplit (<= KB) of p[ks * stride], in slice order.  The KB loads are
+// unconditional (slice indices clamped into the partials) so that all of them are in flight
+// together; the slices past ksplit add +0, which leaves the sum's bits unchanged (a sum that
+// starts at +0 is never -0).
+constexpr int kMaxSlices = 32;
+template <int KB>
+__device__ __forceinline__ float slice_sum(const float *p, size_t stride, int ksplit) {
+  float v[KB];
+#pragma unroll
+  for (int k = 0; k < KB; ++k) v[k] = p[min(k, ksplit - 1) * stride];
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) acc += k < ksplit ? v[k] : 0.f;
+  return acc;
+}
+
+// The down projection's slice reduction: the slices' partial sums in slice order, then
+// 2^(-E-4), into the entry's rows of y.  Grid: (column blocks of 256, activation row m < 64, slot).
+template <int KB>
 __global__ __launch_bounds__(kBlock) void k_mfma_reduce(MfmaArgs a) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.y, slot = blockIdx.z;
@@ -388,18 +421,66 @@ __global__ __launch_bounds__(kBlock) void k_mfma_reduce(MfmaArgs a) {
   const int o = blockIdx.x * kBlock + threadIdx.x;
   if (o >= a.O) return;
   const int rg = start + m;
-  const int dr = a.dual ? a.grp->rows[rg].token : rg;
-  const int E = a.E[dr];
-  float sum[NT];
+  const float acc = slice_sum<KB>(a.part + ((size_t)slot * 64 + m) * a.O + o, (size_t)a.slots * 64 * a.O, a.ksplit);
+  a.out[(size_t)rg * a.out_ld + o] = __builtin_ldexpf(acc, -a.E[rg] - 4);
+}
+
+// The dual projection's slice reduction fused with the digit rows of h, one workgroup per row m
+// of a matrix-core entry: the slices' partial sums in slice order, 2^(-E-4) and SiLU(gate) x up
+// into the entry's row of h, then the row's exponent from
+// its largest |h| and its three digit rows (the arithmetic of k_digits8 on that row of h),
+// indexed by group row, for the down projection.  Grid: (row m < 64, slot).
+template <int KB>
+__global__ __launch_bounds__(kDigBlock) void k_mfma_h(MfmaArgs a) {
+  __shared__ float s_h[kMaxCols];
+  __shared__ uint32_t s_max[kDigBlock / kWave];
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x, slot = blockIdx.y;
+  int start, size;
+  big_entry(a.grp, a.mfma_min, slot, lane, start, size);
+  if (m >= size) return;
+  const int O = a.O, O64 = (O + 63) & ~63;
+  const int rg = start + m;
+  const int E = a.E[a.grp->rows[rg].token];
+  uint32_t mx = 0;
+  for (int o = threadIdx.x; o < O64; o += kDigBlock) {
+    float res = 0.f;
+    if (o < O) {
+      // gate and up partials of every slice in flight together (clamped slices add +0, as in
+      // slice_sum)
+      const size_t stride = (size_t)2 * a.slots * 64 * O;  // one slice
+      const float *p0 = a.part + ((size_t)slot * 64 + m) * O + o;
+      const float *p1 = p0 + (size_t)a.slots * 64 * O;
+      float vg[KB], vu[KB];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float acc = 0.f;
-    for (int ks = 0; ks < a.ksplit; ++ks) acc += a.part[((((size_t)ks * NT + n) * a.slots + slot) * 64 + m) * a.O + o];
-    sum[n] = __builtin_ldexpf(acc, -E - 4);
+      for (int k = 0; k < KB; ++k) {
+        const size_t off = min(k, a.ksplit - 1) * stride;
+        vg[k] = p0[off];
+        vu[k] = p1[off];
+      }
+      float sum[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        sum[0] += k < a.ksplit ? vg[k] : 0.f;
+        sum[1] += k < a.ksplit ? vu[k] : 0.f;
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) sum[n] = __builtin_ldexpf(sum[n], -E - 4);
+      res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
+      a.out[(size_t)rg * a.out_ld + o] = res;
+    }
+    s_h[o] = res;
+    mx = max(mx, __float_as_uint(res) & 0x7fffffffu);
   }
-  float res = sum[0];
-  if constexpr (NT == 2) res = sum[0] / (1.f + expf(-sum[0])) * sum[1];
-  a.out[(size_t)rg * a.out_ld + o] = res;
+  const int Eh = row_exponent_bits(block_max(mx, s_max));  // its barrier also publishes s_h
+  if (threadIdx.x == 0) a.E_out[rg] = Eh;
+  int8_t *dst = a.dig_out + (size_t)rg * kDigits * O64;
+  for (int b = threadIdx.x; b < O64 / 16; b += kDigBlock) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = s_h[16 * b + k];
+    store_digit_chunk(v, Eh, dst, O64, b);
+  }
 }
 
 }  // namespace
@@ -422,12 +503,12 @@ int mfma_ksplit(int O, int C64, int slots, int n_cu) {
   int k = (2 * n_cu + blocks - 1) / blocks;      // about two workgroups per CU
   const int kmax = KS / (2 * kCh) > 0 ? KS / (2 * kCh) : 1;  // at least two stages per slice
   k = k < 1 ? 1 : (k > kmax ? kmax : k);
-  return k > 32 ? 32 : k;
+  return k > kMaxSlices ? kMaxSlices : k;
 }
 
 hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   if ((NT != 1 && NT != 2) || a.mfma_min < 1 || a.C64 % 64 != 0 || a.C64 > kMaxCols || a.dig_rows < 1 ||
-      a.dig_rows > kRows || a.slots < 1 || a.slots > kRows || a.ksplit < 1 || !a.part)
+      a.dig_rows > kRows || a.slots < 1 || a.slots > kRows || a.ksplit < 1 || a.ksplit > kMaxSlices || !a.part)
     return hipErrorInvalidValue;
   a.weight_tiles = (a.O + kMRows - 1) / kMRows;
   a.tiles = a.slots * a.weight_tiles * a.ksplit;
@@ -441,11 +522,27 @@ hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEve
   e = (t0) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st, t0, nullptr, 0)
            : hipLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st);
   if (e != hipSuccess) return e;
-  const void *kr = NT == 2 ? reinterpret_cast<const void *>(&k_mfma_reduce<2>)
-                           : reinterpret_cast<const void *>(&k_mfma_reduce<1>);
-  const dim3 rg((a.O + kBlock - 1) / kBlock, 64, a.slots);
-  e = (t1) ? hipExtLaunchKernel(kr, rg, dim3(kBlock), params, 0, st, nullptr, t1, 0)
-           : hipLaunchKernel(kr, rg, dim3(kBlock), params, 0, st);
+  // the reduction, with as many slice loads in flight as the smallest power of two >= ksplit
+  const int kb = a.ksplit <= 4 ? 0 : a.ksplit <= 8 ? 1 : a.ksplit <= 16 ? 2 : 3;
+  if (NT == 2) {
+    // the dual's reduction also writes the digit rows of h for the down projection
+    if (!a.dig_out || !a.E_out || a.O > kMaxCols) return hipErrorInvalidValue;
+    static const void *const kh[4] = {reinterpret_cast<const void *>(&k_mfma_h<4>),
+                                      reinterpret_cast<const void *>(&k_mfma_h<8>),
+                                      reinterpret_cast<const void *>(&k_mfma_h<16>),
+                                      reinterpret_cast<const void *>(&k_mfma_h<32>)};
+    const dim3 hg(64, a.slots);
+    e = (t1) ? hipExtLaunchKernel(kh[kb], hg, dim3(kDigBlock), params, 0, st, nullptr, t1, 0)
+             : hipLaunchKernel(kh[kb], hg, dim3(kDigBlock), params, 0, st);
+  } else {
+    static const void *const kr[4] = {reinterpret_cast<const void *>(&k_mfma_reduce<4>),
+                                      reinterpret_cast<const void *>(&k_mfma_reduce<8>),
+                                      reinterpret_cast<const void *>(&k_mfma_reduce<16>),
+                                      reinterpret_cast<const void *>(&k_mfma_reduce<32>)};
+    const dim3 rg((a.O + kBlock - 1) / kBlock, 64, a.slots);
+    e = (t1) ? hipExtLaunchKernel(kr[kb], rg, dim3(kBlock), params, 0, st, nullptr, t1, 0)
+             : hipLaunchKernel(kr[kb], rg, dim3(kBlock), params, 0, st);
+  }
   return e != hipSuccess ? e : hipGetLastError();
 }
 
