@@ -115,12 +115,10 @@ struct ProjArgs {
 
 constexpr int kEntryRows = 4;  // rows of one expert per weight pass in the vector kernels
 
-// Digit rows for the matrix-core projections: rows of f32 or bf16 activations (row stride
+// Digit rows for the matrix-core dual projection: rows of f32 or bf16 activations (row stride
 // act_ld) as three int8 planes of C64 bytes each (row r at dig + 3 r C64), and each row's E.
-// grp non-null: rows at or past the group's n_rows are skipped.
 struct DigitArgs {
   const void *act;
-  const GroupBuf *grp;
   int8_t *dig;
   int *E;
   int act_ld, bf16, rows, C, C64;

@@ -86,14 +86,13 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t (&s_max)[NW])
   return m;
 }
 
-// One workgroup per activation row: E from the row's largest |a|, then 16 columns per thread
-// and step, written as three 16-byte digit chunks in the byte order of the weight operand.
+// One workgroup per activation row: E from the row's largest |a|, then each thread's 16
+// columns written as three 16-byte digit chunks in the byte order of the weight operand.
 constexpr int kDigBlock = 1024;  // threads per activation row
 
 __global__ __launch_bounds__(kDigBlock) void k_digits8(DigitArgs a) {
   __shared__ uint32_t s_max[kDigBlock / kWave];
   const int row = blockIdx.x;
-  if (a.grp && row >= ((CGroupBuf)a.grp)->g.n_rows) return;  // rows past the group: not used
   const int C = a.C;
   const size_t off = (size_t)row * a.act_ld;
   const uint16_t *xb = static_cast<const uint16_t *>(a.act) + off;
@@ -120,22 +119,18 @@ __global__ __launch_bounds__(kDigBlock) void k_digits8(DigitArgs a) {
       }
     }
   };
-  const int nb = a.C64 / 16;
+  // one 16-column chunk per thread (C64 / 16 <= kMaxCols / 16 <= kDigBlock), loaded once
+  static_assert(kMaxCols / 16 <= kDigBlock, "one chunk per thread");
+  const int b = threadIdx.x;
+  const bool has = b < a.C64 / 16;
+  float v[16];
+  load16(has ? b : 0, v);
   uint32_t m = 0;
-  for (int b = threadIdx.x; b < nb; b += kDigBlock) {
-    float v[16];
-    load16(b, v);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(v[k]) & 0x7fffffffu);
-  }
+  for (int k = 0; k < 16; ++k) m = max(m, has ? __float_as_uint(v[k]) & 0x7fffffffu : 0u);
   const int E = row_exponent_bits(block_max(m, s_max));
   if (threadIdx.x == 0) a.E[row] = E;
-  int8_t *dst = a.dig + (size_t)row * kDigits * a.C64;
-  for (int b = threadIdx.x; b < nb; b += kDigBlock) {
-    float v[16];
-    load16(b, v);
-    store_digit_chunk(v, E, dst, a.C64, b);
-  }
+  if (has) store_digit_chunk(v, E, a.dig + (size_t)row * kDigits * a.C64, a.C64, b);
 }
 
 // ---- Matrix-core projection ----------------------------------------------------------------
