@@ -242,21 +242,24 @@ CROSS_MODES = {"per_row": {"I4MOE_ENTRY_ROWS": "0", "I4MOE_MFMA_MIN_ROWS": "0"},
                "automatic": {}}
 
 
-def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, modes=tuple(CROSS_MODES)):
+def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, modes=tuple(CROSS_MODES),
+              formats: str = "group"):
     """Device time of one issue + take for explicit groups of R rows per expert (S = 64 tokens,
     min(8, 64 // R) experts per issue, rotating over 32 experts of the small-batch shape so the
-    weights stream from HBM), under each launch mode; prints one JSON line per R."""
+    weights stream from HBM; group-wise g64 experts, or per-row with formats="row"), under each
+    launch mode; prints one JSON line per R."""
     from int4_grouped_expert_router_amd import Context
     from synth import gen_layer, get_config
     from synth.gen import gen_expert
-    cfg = get_config("small_batch", S=64, E=n_experts)
+    cfg = get_config("small_batch", S=64, E=n_experts, formats=formats, gs=64 if formats == "group" else 0)
     L = gen_layer(cfg, 0)
     with cf.ThreadPoolExecutor(WORKERS) as pool:
         ews = list(pool.map(lambda e: gen_expert(cfg, 0, e), range(n_experts)))
     per_expert = tensor_bytes(ews[0].gate) + tensor_bytes(ews[0].up) + tensor_bytes(ews[0].down)
     x = torch.from_numpy(L.x.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
     out = torch.zeros((cfg.S, cfg.D), dtype=torch.float32, device="cuda:0")
-    table = {R: {"rows_per_expert": R, "experts_per_issue": max(1, min(8, cfg.S // R))} for R in rows}
+    table = {R: {"rows_per_expert": R, "experts_per_issue": max(1, min(8, cfg.S // R)), "formats": formats}
+             for R in rows}
     for mode in modes:
         env = CROSS_MODES[mode]
         saved = {k: os.environ.get(k) for k in env}
@@ -435,6 +438,8 @@ def main():
     ap.add_argument("--tiered", action="store_true",
                     help="only time the CPU tier: device rows, host rows, and both overlapped")
     ap.add_argument("--crossover-modes", default="", help="comma-separated launch modes (default: all)")
+    ap.add_argument("--crossover-formats", default="group", choices=("group", "row"),
+                    help="crossover experts: group-wise g64 (default) or per-row int4")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -457,7 +462,7 @@ def main():
     if args.crossover:
         rows = tuple(int(v) for v in args.crossover_rows.split(",")) if args.crossover_rows else CROSS_ROWS
         modes = tuple(args.crossover_modes.split(",")) if args.crossover_modes else tuple(CROSS_MODES)
-        crossover(torch, B, rows=rows, modes=modes)
+        crossover(torch, B, rows=rows, modes=modes, formats=args.crossover_formats)
         return
     layers = args.layers or get_config(args.workload).layers
     head, cfg = measure(args.workload, layers, args.steps, args.warmup, torch, B, eager=args.eager)

@@ -1199,6 +1199,7 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
     ma.mfma_min = mfma_min;
     ma.slots = mfma_slots;
     ma.ksplit = dual ? ks_dual : ks_down;
+    ma.row_acc = (dual ? gs_in : gs_dn).empty() ? 1 : 0;
     ma.part = c->d_part;
     return timed(c, I4MOE_K_MFMA, [&](hipEvent_t t0, hipEvent_t t1) {
       // the event pair spans the projection's launches

@@ -141,6 +141,7 @@ struct MfmaArgs {
   int out_ld, dig_rows, dual;
   int O, C64;
   int mfma_min, slots, ksplit;
+  int row_acc;              // every tensor of the launch is per-row: int32 digit sums over a slice
   int weight_tiles, tiles;  // set by the launcher
 };
 

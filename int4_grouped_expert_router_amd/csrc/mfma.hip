@@ -195,7 +195,9 @@ struct MLoads {
 // by the whole workgroup with 16-byte loads (a weight row's kCh x 32 bytes, a digit row's
 // kCh x 64 bytes) while the previous stage computes.  The partial sums of the slice go to
 // a.part[slice][n][slot][m][o]; k_mfma_h (dual) or k_mfma_reduce (down) adds the slices in order.
-template <int NT>
+// ACC: every tensor of the launch is per-row, so each digit's sums accumulate in int32 over the
+// whole slice (at most 2^20 per step, 2^27 over kMaxCols columns) and are joined once at the end.
+template <int NT, bool ACC>
 __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
   __shared__ int s_drow[64];
@@ -269,13 +271,15 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j)
       r.x[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xbase[j] < kFar ? xbase[j] + 64 * s0 : kFar, 0, 0);
-    const int gs = NT == 2 ? (sn_c ? T[1 % NT].gs : T[0].gs) : T[0].gs;
-    const int ng = NT == 2 ? (sn_c ? T[1 % NT].ng : T[0].ng) : T[0].ng;
-    const bool gg = ng > 1;
-    const int g = gg ? (64 * (s0 + sc_c)) / gs : 0;
-    const int soff = s_ok ? 4 * ((o0 + srow) * ng + g) : kFar;
-    const __amdgpu_buffer_rsrc_t srs = NT == 2 ? (sn_c ? sr[1 % NT] : sr[0]) : sr[0];
-    r.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0));
+    if constexpr (!ACC) {
+      const int gs = NT == 2 ? (sn_c ? T[1 % NT].gs : T[0].gs) : T[0].gs;
+      const int ng = NT == 2 ? (sn_c ? T[1 % NT].ng : T[0].ng) : T[0].ng;
+      const bool gg = ng > 1;
+      const int g = gg ? (64 * (s0 + sc_c)) / gs : 0;
+      const int soff = s_ok ? 4 * ((o0 + srow) * ng + g) : kFar;
+      const __amdgpu_buffer_rsrc_t srs = NT == 2 ? (sn_c ? sr[1 % NT] : sr[0]) : sr[0];
+      r.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0));
+    }
   };
   auto store = [&](const MLoads<NT> &r, int stage) {
     uint8_t *base = s_lds + stage * stage_bytes<NT>();
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) *reinterpret_cast<u32x4 *>(xb + xlds[j]) = r.x[j];
     float *scb = reinterpret_cast<float *>(xb + 64 * kXRow);
-    if (sn < NT) scb[(sn * kMRows + srow) * kCh + sc_c] = r.sc;
+    if (!ACC && sn < NT) scb[(sn * kMRows + srow) * kCh + sc_c] = r.sc;
   };
 
   // Every step's three digit products start from zero and are joined into F at once: the
@@ -299,6 +303,14 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int v = 0; v < 4; ++v) F[tt][n][v] = 0.f;
+  // ACC: the digit sums of the slice, digit d of tensor n and token tile tt
+  v4i I[ACC ? 4 : 1][NT][kDigits];
+#pragma unroll
+  for (int tt = 0; tt < (ACC ? 4 : 1); ++tt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int d = 0; d < kDigits; ++d) I[tt][n][d] = v4i{0, 0, 0, 0};
   const int li = lane & 15, q = lane >> 4;
   // a per-row tensor's scale: one value per lane (its weight row)
   float srow_s[NT];
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
       }
       float sc[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) sc[n] = grp[n] ? scb[(n * kMRows + 16 * w + li) * kCh + cs] : 1.f;
+      for (int n = 0; n < NT; ++n) sc[n] = (!ACC && grp[n]) ? scb[(n * kMRows + 16 * w + li) * kCh + cs] : 1.f;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         if (tt < TT) {
@@ -333,14 +345,20 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
             A[d] = *reinterpret_cast<const v4i *>(xb + (16 * tt + li) * kXRow + d * (kCh * 64) + cs * 64 + 16 * q);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            v4i r[kDigits];
+            if constexpr (ACC) {
 #pragma unroll
-            for (int d = 0; d < kDigits; ++d)
-              r[d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d], B[n], v4i{0, 0, 0, 0}, 0, 0, 0);
+              for (int d = 0; d < kDigits; ++d)
+                I[tt][n][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d], B[n], I[tt][n][d], 0, 0, 0);
+            } else {
+              v4i r[kDigits];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int lo = (r[1][v] << 8) + r[0][v];
-              F[tt][n][v] = fmaf(fmaf((float)r[2][v], 65536.f, (float)lo), sc[n], F[tt][n][v]);
+              for (int d = 0; d < kDigits; ++d)
+                r[d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[d], B[n], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int lo = (r[1][v] << 8) + r[0][v];
+                F[tt][n][v] = fmaf(fmaf((float)r[2][v], 65536.f, (float)lo), sc[n], F[tt][n][v]);
+              }
             }
           }
         }
@@ -364,9 +382,20 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
     __syncthreads();
     stage ^= 1;
   }
+  if constexpr (ACC) {
+    // the slice's digit sums joined once (exactly, in double), one rounding to f32
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          F[tt][n][v] = (float)(((double)I[tt][n][2][v] * 65536.0 + (double)I[tt][n][1][v] * 256.0) +
+                                (double)I[tt][n][0][v]);
+  }
 #pragma unroll
   for (int n = 0; n < NT; ++n)
-    if (!grp[n])
+    if (ACC || !grp[n])
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -508,10 +537,14 @@ hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEve
   a.weight_tiles = (a.O + kMRows - 1) / kMRows;
   a.tiles = a.slots * a.weight_tiles * a.ksplit;
   const int blocks = (a.tiles + 7) / 8 * 8;
-  const void *k = NT == 2 ? reinterpret_cast<const void *>(&k_mfma<2>) : reinterpret_cast<const void *>(&k_mfma<1>);
+  static const void *const km[2][2] = {
+      {reinterpret_cast<const void *>(&k_mfma<1, false>), reinterpret_cast<const void *>(&k_mfma<1, true>)},
+      {reinterpret_cast<const void *>(&k_mfma<2, false>), reinterpret_cast<const void *>(&k_mfma<2, true>)}};
+  const int acc = a.row_acc ? 1 : 0;
+  const void *k = km[NT - 1][acc];
   const size_t lds = NT == 2 ? mfma_lds_bytes<2>() : mfma_lds_bytes<1>();
-  static bool raised[2][kMaxDevices] = {};
-  hipError_t e = raise_lds_once(k, (int)lds, raised[NT - 1]);
+  static bool raised[2][2][kMaxDevices] = {};
+  hipError_t e = raise_lds_once(k, (int)lds, raised[NT - 1][acc]);
   if (e != hipSuccess) return e;
   void *params[] = {&a};
   e = (t0) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st, t0, nullptr, 0)

@@ -34,6 +34,9 @@ CASES = {
     # matrix-core entries beside vector entries in one issue; f32 x, g64 and per-row experts,
     # the down rows' 16-wide tail group
     "mfma_mixed": ("mix", dict(D=2560, I=2000, E=16), 48, [17, 5, 3, 1, 2, 16, 20]),
+    # per-row experts only: the matrix cores keep each digit's sums in int32 over a slice; f32 x,
+    # down rows of 2000 columns (not a multiple of 64), a vector entry beside them
+    "mfma_row": ("medium", dict(D=2560, I=2000, E=12, x_dtype="f32"), 48, [17, 5, 16, 24]),
 }
 
 
