@@ -1140,8 +1140,8 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
     if (fmt_ok && most >= c->mfma_min && n_big > 0) {
       mfma_min = c->mfma_min;
       mfma_slots = n_big;
-      ks_dual = mfma_ksplit(L->I, round_up(L->D, 64), n_big, c->n_cu);
-      ks_down = mfma_ksplit(L->D, round_up(L->I, 64), n_big, c->n_cu);
+      ks_dual = mfma_ksplit(L->I, round_up(L->D, 64), n_big, c->n_cu, most);
+      ks_down = mfma_ksplit(L->D, round_up(L->I, 64), n_big, c->n_cu, most);
       if ((rc = ensure_digit_scratch(c))) return rc;
       if ((rc = ensure_part_scratch(c, std::max(mfma_part_floats(2, L->I, n_big, ks_dual),
                                                  mfma_part_floats(1, L->D, n_big, ks_down)))))

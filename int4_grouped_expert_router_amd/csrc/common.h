@@ -200,7 +200,7 @@ hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st, hipEvent_t t0 = nul
 hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Column slices of a matrix-core launch (about two workgroups per CU) and its partial-sum floats.
-int mfma_ksplit(int O, int C64, int slots, int n_cu);
+int mfma_ksplit(int O, int C64, int slots, int n_cu, int rows);
 size_t mfma_part_floats(int NT, int O, int slots, int ksplit);
 
 // Rows per pipeline step for a launch shape: about `budget` weight dwords per lane per step.

@@ -422,6 +422,7 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
 // together; the slices past ksplit add +0, which leaves the sum's bits unchanged (a sum that
 // starts at +0 is never -0).
 constexpr int kMaxSlices = 32;
+constexpr int kMfmaOneWgRows = 24;
 template <int KB>
 __device__ __forceinline__ float slice_sum(const float *p, size_t stride, int ksplit) {
   float v[KB];
@@ -521,10 +522,14 @@ hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0, hip
 
 size_t mfma_part_floats(int NT, int O, int slots, int ksplit) { return (size_t)ksplit * NT * slots * 64 * O; }
 
-int mfma_ksplit(int O, int C64, int slots, int n_cu) {
+int mfma_ksplit(int O, int C64, int slots, int n_cu, int rows) {
   const int blocks = slots * ((O + kMRows - 1) / kMRows);
   const int KS = C64 / 64;
-  int k = (2 * n_cu + blocks - 1) / blocks;      // about two workgroups per CU
+  // about two workgroups per CU; one for entries of 24 rows or more, whose stages carry two or
+  // more token tiles (measured on the crossover shape: two per CU faster up to 20 rows, one from
+  // 24 rows, 7-13% at 24-64 rows)
+  const int per_cu = rows >= kMfmaOneWgRows ? 1 : 2;
+  int k = (per_cu * n_cu + blocks - 1) / blocks;
   const int kmax = KS / (2 * kCh) > 0 ? KS / (2 * kCh) : 1;  // at least two stages per slice
   k = k < 1 ? 1 : (k > kmax ? kmax : k);
   return k > kMaxSlices ? kMaxSlices : k;
