@@ -139,3 +139,56 @@ def test_device_route_many_rows_per_expert():
     delta, _ = layer_delta_threads(gpu_routes(rec, cfg.S, cfg.K), L.expert, x64)
     for t in range(cfg.S):
         assert normwise_err(out[t], delta[t]) < TOL, t
+
+
+@pytest.mark.parametrize("mfma", ["8", "0"])
+def test_entries_at_column_cap(mfma, monkeypatch):
+    """D = I = 8192 (the column cap on both projections), group-wise g64 experts with f32 x: two
+    entries of 12 and 9 rows on the matrix cores (or on the vector kernels), every h and y row
+    and the layer delta against the oracle, run twice for bitwise determinism."""
+    import torch
+    from int4_grouped_expert_router_amd import Context
+    from int4_grouped_expert_router_amd import binding as B
+    S, sizes = 16, [12, 9]
+    print(f"[entry] column cap D=I=8192 S={S} entries={sizes} mfma_min={mfma}", flush=True)
+    cfg = get_config("small_batch", D=8192, I=8192, E=4, S=S, layers=1, x_dtype="f32")
+    L = make_layer(cfg, 0)
+    rng = np.random.default_rng(8192)
+    rows = make_rows(rng, S, sizes, cfg.E)
+    monkeypatch.setenv("I4MOE_MFMA_MIN_ROWS", mfma)
+    ctx = Context(0, torch.cuda.current_stream())
+    monkeypatch.delenv("I4MOE_MFMA_MIN_ROWS")
+    upload_layer(ctx, L, 0, experts=sorted({r[0] for r in rows}))
+    x = x_to_device(L.x, L.x_dtype)
+    outs, hs, ys = [], [], []
+    for _ in range(2):
+        slot = ctx.issue(0, x, rows=rows)
+        hs.append(ctx.tap(B.I4MOE_TAP_H).reshape(-1, cfg.I)[: len(rows)].copy())
+        ys.append(ctx.tap(B.I4MOE_TAP_Y, slot).reshape(-1, cfg.D)[: len(rows)].copy())
+        out = torch.zeros((S, cfg.D), dtype=torch.float32, device="cuda:0")
+        ctx.take(out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    ctx.close()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(hs[0], hs[1]) and np.array_equal(ys[0], ys[1])
+
+    # the oracle one expert at a time, its rows as the columns of one matrix
+    x64 = oracle.widen_activations(L.x, L.x_dtype)
+    ordered = expert_major(rows)
+    ref_h, ref_y = {}, {}
+    for e in sorted({r[0] for r in rows}):
+        ew = gen_expert(cfg, 0, e)
+        idx = [i for i, r in enumerate(ordered) if r[0] == e]
+        _, _, h, y = oracle.expert_forward(ew.gate, ew.up, ew.down, x64[[ordered[i][1] for i in idx]].T)
+        for j, i in enumerate(idx):
+            ref_h[i], ref_y[i] = h[:, j], y[:, j]
+    for i, r in enumerate(ordered):
+        assert normwise_err(hs[0][i], ref_h[i]) < TOL, (i, r, "h")
+        assert normwise_err(ys[0][i], ref_y[i]) < TOL, (i, r, "y")
+    ref = np.zeros((S, cfg.D))
+    for i, r in enumerate(ordered):
+        ref[r[1]] += float(np.float32(r[2])) * ref_y[i]
+    for t in range(S):
+        if np.any(ref[t]):
+            assert normwise_err(outs[0][t], ref[t]) < TOL, t
+    print(f"[entry] column cap: {len(rows)} rows ok", flush=True)

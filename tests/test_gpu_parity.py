@@ -131,6 +131,7 @@ RAGGED = [
     (256, 128, 130, 4, 2, "row", 0, "f32"),         # 130 experts: a lane's third column holds two
     (1024, 2304, 8, 2, 1, "group", 64, "f32"),      # down rows of 2304 columns: the long-row down kernel
     (512, 4096, 4, 2, 2, "row", 0, "bf16"),         # 4096-column down rows, per-row scales
+    (8192, 8192, 4, 2, 1, "mix_even_odd", 64, "f32"),  # the column cap (I4MOE_MAX_COLS) on both sides
 ]
 
 
