@@ -4,7 +4,8 @@ entries of 1 to 28 rows (listed out of order, so the library's expert-major row 
 exercised, and with repeated tokens inside an entry), checked row by row against the f64 oracle
 (every h row and every y row, through the taps) and as a layer delta after the take, with pass
 sharing forced on and the matrix cores on and off; every run repeated for bitwise determinism.
-A device route at S = 64, K = 1 over 4 experts (about 16 rows each) is checked as a layer."""
+A device route at S = 64, K = 1 over 4 experts (about 16 rows each) is checked as a layer, and
+entries at the column cap (D = I = 8192) on the matrix cores and on the vector kernels."""
 
 from __future__ import annotations
 
