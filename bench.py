@@ -191,6 +191,19 @@ def measure(name, layers, steps, warmup, torch, B, eager=False):
            ("mfma", B.I4MOE_K_MFMA)]}
     if kt["mfma"][1] == 0:
         del kt["mfma"]
+
+    # The plain-read rate of the same experts' weights on this GPU: the read probe over each
+    # step's distinct experts (gate + up, then down), in the same bursts behind a GPU sleep.
+    probe = {}
+    for key, mask in (("gate_up", 3), ("down", 4)):
+        ctx.set_profiling(True)
+        for b0 in range(0, steps, burst):
+            torch.cuda._sleep(sleep_cycles)
+            for i in range(b0, min(steps, b0 + burst)):
+                ctx.read_probe(i % layers, mask, taken[i % layers][0])
+        torch.cuda.synchronize()
+        probe[key] = ctx.profile(B.I4MOE_K_PROBE)
+    ctx.set_profiling(False)
     launch = "graph" if graph is not None else "eager stream"
     del graph
     torch.cuda.synchronize()
@@ -226,7 +239,19 @@ def measure(name, layers, steps, warmup, torch, B, eager=False):
                      "kernel": "k_proj dual gate/up + SiLU (with the one-token selection when S=1, E<=64)",
                      "bytes_per_launch": round(dual_alg / steps), "avg_launch_us": round(dual_ms * 1e3 / max(dual_n, 1), 3)},
     }
+    pr_gu = gu_bytes / (probe["gate_up"][0] * 1e-3) / 1e9
+    pr_dn = dn_bytes / (probe["down"][0] * 1e-3) / 1e9
+    res["plain_read"] = {
+        "kernel": "k_read_probe: the same experts' nibbles and scales as contiguous 16-row blocks, "
+                  "no arithmetic (HIP events, as the kernels above)",
+        "gate_up_GBps": round(pr_gu, 1), "gate_up_pct_hbm_peak": round(100 * pr_gu / HBM_PEAK_GBPS, 2),
+        "down_GBps": round(pr_dn, 1), "down_pct_hbm_peak": round(100 * pr_dn / HBM_PEAK_GBPS, 2),
+        "dual_frac_of_plain_read": round((gu_bytes / (dual_ms * 1e-3) / 1e9) / pr_gu, 4),
+        "avg_launch_us": {"gate_up": round(probe["gate_up"][0] * 1e3 / max(probe["gate_up"][1], 1), 3),
+                          "down": round(probe["down"][0] * 1e3 / max(probe["down"][1], 1), 3)},
+    }
     if down_n:   # a down projection launched on its own (otherwise it ran inside the take kernel)
+        res["plain_read"]["down_frac_of_plain_read"] = round((dn_bytes / (down_ms * 1e-3) / 1e9) / pr_dn, 4)
         res["down_GBps"] = round(dn_bytes / (down_ms * 1e-3) / 1e9, 1)
         res["down_pct_hbm_peak"] = round(100 * dn_bytes / (down_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)
     return res, cfg
@@ -484,7 +509,7 @@ def main():
                    "weights": "random int4, seeded"},
     }
     for k in ("expert_weight_bytes_per_layer", "expert_weight_GBps_layer", "expert_weight_pct_hbm_peak_layer",
-              "expert_weight_GBps_kernels", "kernel_us", "down_GBps", "down_pct_hbm_peak"):
+              "expert_weight_GBps_kernels", "kernel_us", "down_GBps", "down_pct_hbm_peak", "plain_read"):
         if k in head:
             line[k] = head[k]
     line["roofline"] = head["roofline"]

@@ -362,7 +362,10 @@ int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const
  * (see i4moe_route) is timed as part of I4MOE_K_DUAL, a down projection run inside the take
  * (see i4moe_expert_group_issue) as part of I4MOE_K_TAKE.  I4MOE_K_MFMA: the matrix-core
  * projections of experts with many rows, with the digit rows they read. */
-enum { I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_MFMA = 4, I4MOE_K_COUNT = 5 };
+enum {
+  I4MOE_K_ROUTE = 0, I4MOE_K_DUAL = 1, I4MOE_K_DOWN = 2, I4MOE_K_TAKE = 3, I4MOE_K_MFMA = 4, I4MOE_K_PROBE = 5,
+  I4MOE_K_COUNT = 6
+};
 
 /* on != 0: bracket every later kernel launch with a pair of HIP events on the context's
  * stream; on == 0 stops.  Switching resets the accumulated figures. */
@@ -371,6 +374,17 @@ int i4moe_set_profiling(i4moe_ctx *ctx, int on);
 /* Synchronise, then report the total device milliseconds and launch count accumulated for one
  * kernel family since profiling was switched on. */
 int i4moe_profile_query(i4moe_ctx *ctx, int kernel, double *total_ms, long long *launches);
+
+/* A measuring aid: the plain-read rate of the expert weights, against which the projections'
+ * bandwidth is reported (expert-weight bytes per second, the figure the pages' grouped kernels
+ * are measured by [LOG-tc, PR651]).  One launch on the context's stream that reads every nibble
+ * and scale byte of the listed experts' tensors of the layer (tensor_mask bit 0 gate, 1 up,
+ * 2 down; n_experts 1..I4MOE_MAX_ROWS indices into the layer's table, each bound on the device)
+ * and computes nothing: one wave per 16 rows of a tensor, read as one contiguous block of
+ * nibbles and one of scales with eight 16-byte loads per lane in flight; it writes nothing the
+ * caller reads.  Timed as I4MOE_K_PROBE when profiling is on.  Errors: EINVAL (bad layer, mask,
+ * list or expert), ENOMEM (its 256-byte scratch, allocated on the first call). */
+int i4moe_read_probe(i4moe_ctx *ctx, int layer, int tensor_mask, int n_experts, const int32_t *experts);
 
 #ifdef __cplusplus
 }

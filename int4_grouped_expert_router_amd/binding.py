@@ -25,7 +25,7 @@ I4MOE_DTYPE_F32, I4MOE_DTYPE_BF16 = 0, 1
 I4MOE_OK, I4MOE_EINVAL, I4MOE_ENOMEM, I4MOE_EDEVICE = 0, -1, -2, -3
 I4MOE_EUNSUPPORTED, I4MOE_EINJECTED, I4MOE_EPOISONED = -4, -5, -6
 I4MOE_TAP_LOGITS, I4MOE_TAP_ROUTE, I4MOE_TAP_GROUP, I4MOE_TAP_H, I4MOE_TAP_Y = 1, 2, 3, 4, 5
-I4MOE_K_ROUTE, I4MOE_K_DUAL, I4MOE_K_DOWN, I4MOE_K_TAKE, I4MOE_K_MFMA, I4MOE_K_COUNT = 0, 1, 2, 3, 4, 5
+I4MOE_K_ROUTE, I4MOE_K_DUAL, I4MOE_K_DOWN, I4MOE_K_TAKE, I4MOE_K_MFMA, I4MOE_K_PROBE, I4MOE_K_COUNT = 0, 1, 2, 3, 4, 5, 6
 
 
 class i4moe_route_host(C.Structure):
@@ -83,6 +83,7 @@ SIGNATURES = {
     "i4moe_debug_size": (C.c_size_t, [_ctx_p, C.c_int, C.c_int]),
     "i4moe_set_profiling": (C.c_int, [_ctx_p, C.c_int]),
     "i4moe_profile_query": (C.c_int, [_ctx_p, C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),
+    "i4moe_read_probe": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int32)]),
 }
 
 _lib = None
@@ -142,3 +143,4 @@ i4moe_debug_read = _fn("i4moe_debug_read")
 i4moe_debug_size = _fn("i4moe_debug_size")
 i4moe_set_profiling = _fn("i4moe_set_profiling")
 i4moe_profile_query = _fn("i4moe_profile_query")
+i4moe_read_probe = _fn("i4moe_read_probe")

@@ -112,6 +112,7 @@ struct i4moe_ctx {
   int8_t *d_dig = nullptr;      // [kRows][3][kMaxCols] digit rows of the matrix-core projections
   int *d_dig_E = nullptr;       // [kRows] their row exponents
   float *d_part = nullptr;      // partial sums of the matrix-core column slices
+  uint32_t *d_sink = nullptr;   // the read probe's 64-dword sink
   size_t part_floats = 0;
 
   // the CPU tier: worker threads, pinned copies of x and of the host rows' sum, and the events
@@ -611,6 +612,7 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   dfree(c->d_dig);
   dfree(c->d_dig_E);
   dfree(c->d_part);
+  dfree(c->d_sink);
   c->helper.reset();
   c->pool.reset();
   if (c->h_x) (void)hipHostFree(c->h_x);
@@ -1827,6 +1829,45 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
     times->host_rows = (int32_t)hrows.size();
   }
   return issued;
+}
+
+int i4moe_read_probe(i4moe_ctx *c, int layer, int tensor_mask, int n_experts, const int32_t *experts) {
+  if (!c) return I4MOE_EINVAL;
+  Layer *L = find_layer(c, layer);
+  if (!L || !L->D || !L->I || !L->d_tab) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
+  if (tensor_mask < 1 || tensor_mask > 7) return fail(c, I4MOE_EINVAL, "tensor_mask %d outside 1..7", tensor_mask);
+  if (n_experts < 1 || n_experts > kRows || !experts)
+    return fail(c, I4MOE_EINVAL, "read probe needs 1..%d experts and a non-NULL list", kRows);
+  ProbeArgs a{};
+  for (int i = 0; i < n_experts; ++i) {
+    const int e = experts[i];
+    if (e < 0 || e >= (int)L->gate.size() || !L->gate[e])
+      return fail(c, I4MOE_EINVAL, "read probe: expert %d is not set", e);
+    a.experts[i] = (int16_t)e;
+  }
+  ensure_device(c);
+  if (!c->d_sink) {
+    const hipError_t e = dalloc(&c->d_sink, 64 * sizeof(uint32_t));
+    if (e != hipSuccess) return hip_fail(c, e, "hipMalloc(read probe sink)");
+  }
+  constexpr int kProbeTileRows = 16;
+  a.tab = L->d_tab;
+  a.sink = c->d_sink;
+  a.n_experts = n_experts;
+  a.tile_rows = kProbeTileRows;
+  int per_e = 0;
+  for (int n = 0; n < 3; ++n)
+    if (tensor_mask & (1 << n)) {
+      const int O = n < 2 ? L->I : L->D;
+      a.tensors[a.n_tensors] = n;
+      a.tiles[a.n_tensors] = (O + kProbeTileRows - 1) / kProbeTileRows;
+      per_e += a.tiles[a.n_tensors++];
+    }
+  a.waves = n_experts * per_e;
+  const hipError_t e = timed(c, I4MOE_K_PROBE, [&](hipEvent_t t0, hipEvent_t t1) {
+    return launch_read_probe(a, c->stream, t0, t1);
+  });
+  return e != hipSuccess ? hip_fail(c, e, "read probe launch") : I4MOE_OK;
 }
 
 int i4moe_set_profiling(i4moe_ctx *c, int on) {

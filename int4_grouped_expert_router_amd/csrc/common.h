@@ -199,6 +199,18 @@ hipError_t launch_group_store(const GroupDev &g, const ExpertRec *table, GroupBu
 hipError_t launch_rmsnorm(const NormArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_digits8(const DigitArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+
+// The read probe (a measuring aid): every nibble and scale byte of the listed experts' tensors,
+// read with the projections' access shape and no arithmetic.
+struct ProbeArgs {
+  const ExpertRec *tab;
+  uint32_t *sink;            // 64 dwords, written only when the folded loads equal a constant
+  int16_t experts[kRows];    // expert indices into tab
+  int n_experts;
+  int tensors[3], tiles[3];  // tensor indices (0 gate, 1 up, 2 down) and their row tiles
+  int n_tensors, tile_rows, waves;
+};
+hipError_t launch_read_probe(const ProbeArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Column slices of a matrix-core launch (about two workgroups per CU) and its partial-sum floats.
 int mfma_ksplit(int O, int C64, int slots, int n_cu, int rows);
 size_t mfma_part_floats(int NT, int O, int slots, int ksplit);

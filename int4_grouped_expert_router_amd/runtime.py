@@ -238,3 +238,8 @@ class Context:
         n = C.c_longlong()
         self.check(B.i4moe_profile_query(self.p, kernel, C.byref(ms), C.byref(n)))
         return ms.value, n.value
+
+    def read_probe(self, layer: int, tensor_mask: int, experts):
+        """Enqueue the plain read of the listed experts' tensors (see i4moe_read_probe)."""
+        arr = (C.c_int32 * len(experts))(*[int(e) for e in experts])
+        self.check(B.i4moe_read_probe(self.p, layer, tensor_mask, len(experts), arr))

@@ -112,3 +112,5 @@ def test_null_context_rejected_before_any_device_call(lib_path):
     assert B.i4moe_set_profiling(None, 1) == EINVAL
     ms, n = C.c_double(), C.c_longlong()
     assert B.i4moe_profile_query(None, 0, C.byref(ms), C.byref(n)) == EINVAL
+    ex = (C.c_int32 * 1)(0)
+    assert B.i4moe_read_probe(None, 0, 3, 1, ex) == EINVAL

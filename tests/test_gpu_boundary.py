@@ -364,3 +364,31 @@ def test_wave_factor_changes_tiling_not_bits(name, monkeypatch):
         outs.append(pair[0])
         ctx.close()
     assert outs[0] == outs[1] == outs[2]
+
+
+def test_read_probe_reads_and_rejects_bad_arguments():
+    """The read probe (a measuring aid) launches once per call, is timed as I4MOE_K_PROBE, leaves
+    the layer's results untouched, and refuses a bad layer, mask, list or unbound expert with
+    EINVAL and nothing launched."""
+    from int4_grouped_expert_router_amd import I4moeError
+    from int4_grouped_expert_router_amd import binding as B
+    cfg = get_config("mix", D=1024, I=200, E=6, K=2, S=1, layers=1)
+    L = make_layer(cfg, 0)
+    ctx = new_ctx()
+    upload_layer(ctx, L, 0)
+    x = x_to_device(L.x, L.x_dtype)
+    before = tiny_delta(ctx, cfg, L, x)
+    ctx.set_profiling(True)
+    for mask in (1, 2, 3, 4, 7):
+        ctx.read_probe(0, mask, list(range(cfg.E)))
+    ms, n = ctx.profile(B.I4MOE_K_PROBE)
+    assert n == 5 and ms > 0.0
+    for layer, mask, ex in [(1, 3, [0]), (0, 0, [0]), (0, 8, [0]), (0, 3, []), (0, 3, [cfg.E]), (0, 3, [-1]),
+                            (0, 3, list(range(65)))]:
+        with pytest.raises(I4moeError) as ei:
+            ctx.read_probe(layer, mask, ex)
+        assert ei.value.code == B.I4MOE_EINVAL
+    assert ctx.profile(B.I4MOE_K_PROBE)[1] == 5  # nothing launched by the refused calls
+    ctx.set_profiling(False)
+    assert np.array_equal(tiny_delta(ctx, cfg, L, x), before)
+    ctx.close()
