@@ -1,7 +1,8 @@
 """One captured HIP graph per MoE layer (route -> issue -> take, no host work between the
 kernels): every replay, with eager work of the program between replays, gives the eager
 result bit for bit, and a replay into a zero residual gives the oracle's two-layer delta
-(MI355X only)."""
+(MI355X only).  One case has about 16 rows per expert, so the matrix-core launches are in the
+graph."""
 
 from __future__ import annotations
 
@@ -15,13 +16,17 @@ from synth import get_config
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["medium", "mix", "small_batch_like"])
+@pytest.mark.parametrize("name", ["medium", "mix", "small_batch_like", "prefill_like"])
 def test_graph_replays_match_eager(name):
     import torch
     from int4_grouped_expert_router_amd import Context
     print(f"[graph] {name}", flush=True)
     if name == "small_batch_like":
         cfg = get_config("tiny", D=1024, I=512, E=32, K=4, S=4, formats="group", gs=64, x_dtype="bf16", seed=21)
+    elif name == "prefill_like":
+        # 32 tokens over 4 experts, about 16 rows each: the matrix-core launches inside the graph
+        cfg = get_config("tiny", D=1024, I=512, E=4, K=2, S=32, formats="mix_even_odd", gs=64, x_dtype="bf16",
+                         seed=22)
     else:
         cfg = get_config(name)
     s = torch.cuda.Stream()
@@ -44,6 +49,17 @@ def test_graph_replays_match_eager(name):
         two_layers()
     s.synchronize()
     eager = resid.cpu().numpy()
+    if name == "prefill_like":
+        # the same layers eager with profiling on: the matrix-core launches are part of the step
+        from int4_grouped_expert_router_amd import binding as B
+        ctx.set_profiling(True)
+        with torch.cuda.stream(s):
+            resid.copy_(r0)
+            two_layers()
+        s.synchronize()
+        assert ctx.profile(B.I4MOE_K_MFMA)[1] > 0
+        ctx.set_profiling(False)
+        assert resid.cpu().numpy().tobytes() == eager.tobytes()
     # the routes each layer takes (deterministic, so the graph's routes are these too)
     recs = [ctx.route(l, xs[l], cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True) for l in range(2)]
 

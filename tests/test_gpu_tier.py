@@ -1,8 +1,8 @@
 """The CPU tier through the C ABI: experts kept on the host run on the CPU while the device
 group runs on the GPU, and the take joins both.  Checked against the f64 oracle on the GPU's own
 route (mixed tiers, all on the host, bf16 and f32 activations, per-row / group-wise / tail
-groups), bitwise against the plain explicit issue when every expert is on the device, bitwise
-run to run, and on its error path."""
+groups, device entries on the matrix cores), bitwise against the plain explicit issue when every
+expert is on the device, bitwise run to run, and on its error path."""
 
 from __future__ import annotations
 
@@ -21,6 +21,9 @@ CASES = {
     "mix_f32": ("mix", dict(D=2048, I=2000, E=16, K=6, S=3)),
     # bf16 x, g64 experts
     "group_bf16": ("small_batch", dict(D=3072, I=1024, E=16, K=8, S=4)),
+    # 16 tokens over 4 experts (about 8 rows each): device entries on the matrix cores beside the
+    # host rows
+    "many_rows": ("mix", dict(D=2048, I=1024, E=4, K=2, S=16)),
 }
 
 
@@ -53,18 +56,27 @@ def run_tiered(ctx, cfg, L, x):
 
 @pytest.mark.parametrize("case", sorted(CASES))
 @pytest.mark.parametrize("split", ["odd_on_host", "all_on_host"])
-def test_tiered_matches_oracle(case, split):
+def test_tiered_matches_oracle(case, split, monkeypatch):
     base, over = CASES[case]
     cfg = get_config(base, layers=1, **over)
     print(f"[tier] {case} {split}", flush=True)
     L = make_layer(cfg, 0)
     on_host = set(range(cfg.E)) if split == "all_on_host" else set(range(1, cfg.E, 2))
+    if case == "many_rows":
+        monkeypatch.setenv("I4MOE_MFMA_MIN_ROWS", "4")  # every device entry of 4+ rows on the matrix cores
     ctx = new_ctx()
+    monkeypatch.delenv("I4MOE_MFMA_MIN_ROWS", raising=False)
     bind(ctx, cfg, L, on_host)
     x = x_to_device(L.x, L.x_dtype)
     rec, n, times, out = run_tiered(ctx, cfg, L, x)
+    from int4_grouped_expert_router_amd import binding as B
+    ctx.set_profiling(True)
     _, n2, _, out2 = run_tiered(ctx, cfg, L, x)
+    mfma_launches = ctx.profile(B.I4MOE_K_MFMA)[1]
+    ctx.set_profiling(False)
     ctx.close()
+    if case == "many_rows" and split == "odd_on_host":
+        assert mfma_launches > 0  # the device entries ran on the matrix cores
     assert np.array_equal(out, out2)  # bitwise run to run
     routes = gpu_routes(rec, cfg.S, cfg.K)
     pairs = [(t, routes[t].idx[k]) for t in range(cfg.S) for k in range(routes[t].n)]
