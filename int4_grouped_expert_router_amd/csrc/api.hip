@@ -1106,7 +1106,7 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   // by default: measured on the small-batch shape at 1 to 64 rows per expert, the shared passes
   // were slower than one row per workgroup at every row count (rows of one expert that run
   // together re-read its weights mostly from L2 and the Infinity Cache, while a workgroup running
-  // nr rows does nr times the dot products per weight byte); from 16 rows the matrix cores win.
+  // nr rows does nr times the dot products per weight byte); from 8 rows the matrix cores win.
   if (S > 1 && c->entry_mode > 0) {
     int most = S;  // a device route gives an expert at most one row per token
     if (group) {

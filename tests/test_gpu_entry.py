@@ -1,5 +1,5 @@
 """Several rows of one expert in one issue (S > 1): rows of an entry sharing weight passes in the
-vector kernels, and entries of at least 16 rows on the matrix cores.  Explicit groups with
+vector kernels, and entries of many rows on the matrix cores.  Explicit groups with
 entries of 1 to 28 rows (listed out of order, so the library's expert-major row order is
 exercised, and with repeated tokens inside an entry), checked row by row against the f64 oracle
 (every h row and every y row, through the taps) and as a layer delta after the take, with pass
