@@ -331,6 +331,71 @@ def crossover(torch, B, reps: int = 24, n_experts: int = 32, rows=CROSS_ROWS, mo
         print(json.dumps(table[R]), flush=True)
 
 
+def block(torch, B, name: str = "medium", layers: int = 8, steps: int = 400, warmup: int = 16):
+    """The MoE block around the routed experts at decode: per layer one i4moe_moe_block call
+    (rmsnorm of the residual row, route, routed experts, the layer's shared expert, the join
+    into the residual), over `layers` distinct layers each with its norm weights and shared
+    expert, replayed from one captured graph; then the same calls eager with HIP events around
+    every launch.  Each layer's residual row carries on from block to block (the rmsnorm keeps
+    the activations at scale).  Prints one JSON line."""
+    from int4_grouped_expert_router_amd import Context
+    from synth import gen_norm, gen_shared_expert, get_config
+    cfg = get_config(name)
+    stream = torch.cuda.Stream()   # default priority
+    torch.cuda.set_stream(stream)
+    ctx = Context(0, stream)
+    Ls = setup(cfg, layers, ctx, torch)
+    shared_bytes = 0
+    for l in range(layers):
+        ctx.upload_norm(l, gen_norm(cfg, l), 1e-5)
+        sh = gen_shared_expert(cfg, l)
+        ctx.set_shared_expert(l, ctx.upload_host_tensor(sh.gate), ctx.upload_host_tensor(sh.up),
+                              ctx.upload_host_tensor(sh.down))
+        shared_bytes = tensor_bytes(sh.gate) + tensor_bytes(sh.up) + tensor_bytes(sh.down)
+    dt = B.I4MOE_DTYPE_BF16 if cfg.x_dtype == "bf16" else B.I4MOE_DTYPE_F32
+
+    def step(i):
+        L = Ls[i % layers]
+        ctx.moe_block(i % layers, L.r_dev, dt, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del graph
+    ctx.set_profiling(True)
+    burst = 40
+    sleep_cycles = calibrate_sleep(torch, stream, burst=burst)
+    for b0 in range(0, steps, burst):
+        torch.cuda._sleep(sleep_cycles)
+        for i in range(b0, min(steps, b0 + burst)):
+            step(i)
+    torch.cuda.synchronize()
+    kt = {k: ctx.profile(v) for k, v in [("route", B.I4MOE_K_ROUTE), ("dual", B.I4MOE_K_DUAL),
+                                         ("down", B.I4MOE_K_DOWN), ("take", B.I4MOE_K_TAKE)]}
+    ctx.set_profiling(False)
+    finite = all(bool(torch.isfinite(L.r_dev).all()) for L in Ls)
+    ctx.close()
+    torch.cuda.empty_cache()
+    us = elapsed / steps * 1e6
+    print(json.dumps({
+        "block": workload_text(cfg, layers) + ", S=1 decode, rmsnorm + route + routed experts + shared expert + join",
+        "steps": steps, "launch": "graph", "us_per_block": round(us, 3),
+        "kernel_us_per_block": {k: round(v[0] * 1e3 / steps, 3) for k, v in kt.items()},
+        "launches_per_block": {k: round(v[1] / steps, 2) for k, v in kt.items()},
+        "shared_expert_bytes": shared_bytes,
+        "residual_finite": finite}), flush=True)
+
+
 def tiered(torch, B, reps: int = 30):
     """The CPU tier's overlap: experts of the small-batch shape (D=6144, I=2048, g64, bf16; 64
     experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1 and 4.
@@ -460,6 +525,8 @@ def main():
     ap.add_argument("--crossover", action="store_true",
                     help="only time explicit groups of 1..64 rows per expert under each launch mode")
     ap.add_argument("--crossover-rows", default="", help="comma-separated rows per expert (default: all)")
+    ap.add_argument("--block", action="store_true",
+                    help="only time the MoE block (rmsnorm, route, routed and shared experts, join) on medium")
     ap.add_argument("--tiered", action="store_true",
                     help="only time the CPU tier: device rows, host rows, and both overlapped")
     ap.add_argument("--crossover-modes", default="", help="comma-separated launch modes (default: all)")
@@ -483,6 +550,9 @@ def main():
     torch.cuda.set_device(0)
     if args.tiered:
         tiered(torch, B)
+        return
+    if args.block:
+        block(torch, B)
         return
     if args.crossover:
         rows = tuple(int(v) for v in args.crossover_rows.split(",")) if args.crossover_rows else CROSS_ROWS

@@ -8,8 +8,9 @@
 //
 //   out[t][i] = round( x[t][i] / sqrt(sum_i x[t][i]^2 / D + eps) * gamma[i] )
 //
-// in f64 (every square of a float32 is exact in f64; the sum runs in a fixed order), rounded
-// once, directly from the f64 value, to the output dtype: float32, or bfloat16 through
+// in f64 (every square of a float32 is exact in f64; the sum runs in a fixed order; the division
+// is a multiplication by the row's reciprocal, within an f64 ulp or two of it), rounded once,
+// directly from the f64 value, to the output dtype: float32, or bfloat16 through
 // round-to-odd float32 (which, with 16 spare bits, makes the final round-to-nearest-even to
 // bf16 the same as rounding the f64 value directly).
 #include <hip/hip_ext.h>
@@ -59,8 +60,12 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(uint32_t b) {
   return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
 }
 
-constexpr int kNormBlock = 256;
+constexpr int kNormBlock = 1024;  // threads per row: a decode row of a few thousand values is a few per thread
 
+// One workgroup per row.  The sum of squares: each thread's columns in column order (fma: the
+// square is exact, one rounding per add), a fixed-pattern wave sum, then the waves' sums in wave
+// order.  Each value is then multiplied by the row's 1 / sqrt(mean + eps) and by gamma in f64 and
+// rounded once.
 __global__ __launch_bounds__(kNormBlock) void k_rmsnorm(NormArgs a) {
   __shared__ double s_part[kNormBlock / kWave];
   const int t = blockIdx.x;
@@ -68,15 +73,17 @@ __global__ __launch_bounds__(kNormBlock) void k_rmsnorm(NormArgs a) {
   double ss = 0.0;
   for (int i = threadIdx.x; i < a.D; i += kNormBlock) {
     const double v = (double)x[i];
-    ss = fma(v, v, ss);  // the square is exact; one rounding per add
+    ss = fma(v, v, ss);
   }
   const double w = wave_sum_f64(ss);
   if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = w;
   __syncthreads();
-  const double total = ((s_part[0] + s_part[1]) + s_part[2]) + s_part[3];
-  const double den = sqrt(total / (double)a.D + (double)a.eps);
+  double total = s_part[0];
+#pragma unroll
+  for (int k = 1; k < kNormBlock / kWave; ++k) total += s_part[k];
+  const double rinv = 1.0 / sqrt(total / (double)a.D + (double)a.eps);
   for (int i = threadIdx.x; i < a.D; i += kNormBlock) {
-    const double v = (double)x[i] / den * (double)a.gamma[i];
+    const double v = (double)x[i] * rinv * (double)a.gamma[i];
     if (a.out_bf16)
       static_cast<uint16_t *>(a.out)[(size_t)t * a.ld_out + i] = bf16_rne_bits(f32_round_odd_bits(v));
     else
