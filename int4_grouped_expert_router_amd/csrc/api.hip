@@ -37,7 +37,7 @@ struct Tensor {
 };
 
 // The layer's shared expert sits in the expert table right after the routed experts' cap.
-constexpr int kShared = kMaxE;
+constexpr int kShared = kSharedRec;
 
 struct Layer {
   int E = 0, D = 0, I = 0;             // router experts; model dim; expert intermediate
@@ -52,6 +52,7 @@ struct Layer {
   int route_buf = -1;                  // ring entry holding this layer's latest route
   bool routed = false;
   int route_S = 0, route_K = 0;
+  bool route_shared = false;  // the route's group ends with one shared-expert row per token
   std::map<int, std::unique_ptr<HostExpert>> host;  // experts kept on the host (the CPU tier)
   int host_D = 0, host_I = 0;
 };
@@ -860,8 +861,10 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
 
 // The compute entry points are the fault hook's gate and call count around these bodies; a
 // composite call (i4moe_moe_block) gates and counts once around several of them.
+// with_shared: the route's group also gets the layer's shared expert, one row per token after the
+// routed rows (i4moe_moe_block).
 static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
-                      float routed_scale, i4moe_route_host *host_out) {
+                      float routed_scale, i4moe_route_host *host_out, bool with_shared = false) {
   int rc = I4MOE_OK;
   Layer *L = find_layer(c, layer);
   if (!L || !L->W) return fail(c, I4MOE_EINVAL, "layer %d has no router", layer);
@@ -870,6 +873,8 @@ static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
   if (K < 1 || K > L->E || K > kMaxK) return fail(c, I4MOE_EINVAL, "K=%d outside 1..min(E=%d, %d)", K, L->E, kMaxK);
   if (S * K > kRows) return fail(c, I4MOE_EINVAL, "S*K=%d exceeds the %d-row cap", S * K, kRows);
+  if (with_shared && (!L->shared_set || S * K + S > kRows))
+    return fail(c, I4MOE_EINVAL, "no shared expert, or S*(K+1)=%d exceeds the %d-row cap", S * (K + 1), kRows);
   if (!std::isfinite(topp) || !std::isfinite(routed_scale)) return fail(c, I4MOE_EINVAL, "topp and scale must be finite");
   ensure_device(c);
   const int ring = c->ring_next;
@@ -898,6 +903,7 @@ static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   a.norm_topk = norm_topk ? 1 : 0;
   a.topp = topp;
   a.routed_scale = routed_scale;
+  a.shared_rows = with_shared ? 1 : 0;
   // Without a host copy a one-token route defers its selection to the issue that consumes it.
   const bool defer = !host_out && dual_sel_ok(a, false);
   const int parts = defer ? kRouteGemv : kRouteGemv | kRouteSelect;
@@ -915,6 +921,7 @@ static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   L->routed = true;
   L->route_S = S;
   L->route_K = K;
+  L->route_shared = with_shared;
   c->last_route_S = S;
   c->last_route_E = L->E;
   if (host_out) {
@@ -1025,7 +1032,11 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
       if (!L->gate[e]) return fail(c, I4MOE_EINVAL, "layer %d: expert %d is not set", layer, e);
       note(e);
     }
-    max_rows = S * L->route_K;
+    if (L->route_shared) {
+      if (!L->shared_set) return fail(c, I4MOE_EINVAL, "layer %d: the route's shared expert is gone", layer);
+      note(kShared);
+    }
+    max_rows = S * L->route_K + (L->route_shared ? S : 0);
     ring = L->route_buf;
     grp = c->d_ring + ring;
   } else {
@@ -1461,9 +1472,9 @@ int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act
     return fail(c, I4MOE_EINVAL, "residual_dev must be a 16-byte aligned device pointer");
   if (act_dtype != I4MOE_DTYPE_F32 && act_dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", act_dtype);
   if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
-  if (K < 1 || K > L->E || K > kMaxK || S * K > kRows)
+  if (K < 1 || K > L->E || K > kMaxK || S * K + (L->shared_set ? S : 0) > kRows)
     return fail(c, I4MOE_EINVAL, "K=%d with S=%d outside the route's limits", K, S);
-  if (c->nslots + (L->shared_set ? 2 : 1) > kSlots) return fail(c, I4MOE_EINVAL, "no free issue slots");
+  if (c->nslots + 1 > kSlots) return fail(c, I4MOE_EINVAL, "no free issue slots");
   if (c->nslots > 0 && (c->slots[0].S != S || c->slots[0].D != L->D))
     return fail(c, I4MOE_EINVAL, "pending issues have another S or D");
   if ((int)L->gate.size() < L->E) return fail(c, I4MOE_EINVAL, "layer %d: experts 0..%d must all be set", layer, L->E - 1);
@@ -1475,13 +1486,12 @@ int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act
   // failed take does.
   // the normalised rows are packed [S][D] (what the route and the issues read)
   rc = rmsnorm_impl(c, *L, residual_dev, L->D, S, c->d_xn, L->D, act_dtype);
-  if (!rc) rc = route_impl(c, layer, c->d_xn, act_dtype, S, K, topp, norm_topk, routed_scale, nullptr);
+  // the shared expert rides in the routed group as one more row per token (weight 1, after the
+  // routed rows): one issue and one slot, the same sums as a separate shared issue taken after it
+  if (!rc)
+    rc = route_impl(c, layer, c->d_xn, act_dtype, S, K, topp, norm_topk, routed_scale, nullptr, L->shared_set);
   if (!rc) {
     const int s = issue_impl(c, layer, c->d_xn, act_dtype, S, nullptr, false);
-    if (s < 0) rc = s;
-  }
-  if (!rc && L->shared_set) {
-    const int s = shared_issue_impl(c, layer, c->d_xn, act_dtype, S);
     if (s < 0) rc = s;
   }
   if (!rc) rc = take_impl(c, residual_dev, S);

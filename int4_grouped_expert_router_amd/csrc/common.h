@@ -12,6 +12,7 @@ constexpr int kRows = I4MOE_MAX_ROWS;      // expert-token rows per issue
 constexpr int kTokens = I4MOE_MAX_TOKENS;
 constexpr int kMaxK = I4MOE_MAX_K;
 constexpr int kMaxE = I4MOE_MAX_E;
+constexpr int kSharedRec = kMaxE;  // the layer's shared expert: the table record after the routed experts' cap
 constexpr int kMaxCols = I4MOE_MAX_COLS;
 constexpr int kSlots = I4MOE_MAX_SLOTS;
 constexpr int kWave = 64;
@@ -93,6 +94,10 @@ struct RouteArgs {
   int vec;                   // four-column loads in the GEMV
   int norm_topk;
   float topp, routed_scale;
+  // 1: the group gets one more row per token after the routed rows: the layer's shared expert
+  // (table record kSharedRec) with weight 1, as one more entry (the route records list only the
+  // routed experts)
+  int shared_rows;
 };
 
 struct ProjArgs {
@@ -184,7 +189,7 @@ hipError_t launch_take(const TakeArgs &a, hipStream_t st, hipEvent_t t0 = nullpt
 // rows whose down rows fit k_rows16 (P passes), kDTTile outputs per workgroup: a.act = h,
 // a.grp = the group, a.grid_rows = its rows, a.O = D, a.C = I, a.out = the residual row,
 // updated in place.
-constexpr int kDTRows = 8, kDTTile = 16;
+constexpr int kDTRows = 16, kDTTile = 16;
 hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Down projection over rows of at most 256 weight dwords (C <= 2048): 16 lanes per row, P
 // passes of 4 dwords per lane; f32 activations, per-row or 32-column-aligned group scales.

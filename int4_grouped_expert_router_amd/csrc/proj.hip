@@ -457,34 +457,39 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
     uint32_t tv[kTabPerThread];
     table_prefetch_rsrc(tv, ra.table, writer ? ra.E * (int)sizeof(ExpertRec) : 0);
     const SelOne r = select_one(ra, cs, s_cw, s_cnt, [&] { table_stage(s_tab, tv); });
-    // this row is selection jr of the one token
-    live = jr < r.n ? 1 : 0;
-    const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(r.e_k, jr));
-    const float w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(r.w_k), jr));
+    // this row is selection jr of the one token, or (jr == n, with the shared expert) its row
+    const bool shared_row = ra.shared_rows != 0 && jr == r.n;
+    live = jr < r.n || shared_row ? 1 : 0;
+    const int e = shared_row ? kSharedRec : __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(r.e_k, jr));
+    const float w = shared_row ? 1.f : __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(r.w_k), jr));
     arow = 0;
     GroupBuf *out = ra.out;
     if (blockIdx.x == 0 && wib == 0) {
       // route record and group record of the token: its selections, one row each, in order
+      // (and the shared expert's row after them)
       RouteTok *rt = out->route;
       const int n = r.n;
+      const int nr = n + (ra.shared_rows != 0 ? 1 : 0);
       if (lane == 0) rt->n = n;
       rt->idx[lane] = lane < ra.K ? r.e_k : -1;
       rt->w[lane] = r.w_k;
       GroupDev *G = &out->g;
-      if (lane < n) {
-        G->entry_expert[lane] = r.e_k;
+      if (lane < nr) {
+        const int ge = lane < n ? r.e_k : kSharedRec;
+        const float gw = lane < n ? r.w_k : 1.f;
+        G->entry_expert[lane] = ge;
         G->entry_row0[lane] = lane;
         G->row_token[lane] = 0;
-        G->row_expert[lane] = r.e_k;
-        G->row_weight[lane] = r.w_k;
+        G->row_expert[lane] = ge;
+        G->row_weight[lane] = gw;
         G->red_rows[lane] = lane;
       }
       if (lane == 0) {
-        G->entry_row0[n] = n;
+        G->entry_row0[nr] = nr;
         G->tok_row0[0] = 0;
-        G->tok_row0[1] = n;
-        G->n_entries = n;
-        G->n_rows = n;
+        G->tok_row0[1] = nr;
+        G->n_entries = nr;
+        G->n_rows = nr;
         G->S = 1;
         G->reserved = 0;
       }
@@ -498,7 +503,7 @@ __global__ __launch_bounds__(kBlock) void k_proj(ProjArgs a) {
         else if (lane == kRankWord)
           val = 0u;
         else if (lane < kTabWords)
-          val = s_tab[e * kDescWords + lane];
+          val = shared_row ? reinterpret_cast<const uint32_t *>(ra.table + e)[lane] : s_tab[e * kDescWords + lane];
         else if (lane == kTabWords)
           val = 0u;  // token
         else
@@ -1124,6 +1129,7 @@ size_t rows16_lds_bytes(int P) { return 4u * kPlanes * (size_t)P * kLR * 4; }
 // staging traffic and 32-column tiles leave half the CUs idle; both are slower.)
 template <int P>
 __global__ __launch_bounds__(kDTRows * kWave) void k_down_take(ProjArgs a) {
+  // launched with one wave per group row (a.grid_rows <= kDTRows waves)
   constexpr int V = 4;
   constexpr int TL = kDTTile;
   constexpr int POS = rows16_positions<P>();
@@ -1380,15 +1386,16 @@ hipError_t launch_down_take(int P, const ProjArgs &a, hipStream_t st, hipEvent_t
   const void *k = down_take_ptr(P);
   if (!k || a.grid_rows < 1 || a.grid_rows > kDTRows || a.act_ld % 4 != 0 || reinterpret_cast<uintptr_t>(a.act) % 16 != 0)
     return hipErrorInvalidValue;
-  const size_t lds = (size_t)kDTRows * rows16_lds_bytes(P);
+  // one wave per group row, each with its own staged h row
+  const size_t lds = (size_t)a.grid_rows * rows16_lds_bytes(P);
   static bool raised[5][kMaxDevices] = {};
-  if (lds > 48 * 1024) {
-    const hipError_t e = raise_lds_once(k, (int)lds, raised[P]);
+  if (lds > 48 * 1024) {  // raised once, to what the most rows need
+    const hipError_t e = raise_lds_once(k, (int)(kDTRows * rows16_lds_bytes(P)), raised[P]);
     if (e != hipSuccess) return e;
   }
   ProjArgs args = a;
   void *params[] = {&args};
-  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(kDTRows * kWave);
+  const dim3 grid((a.O + kDTTile - 1) / kDTTile), block(a.grid_rows * kWave);
   hipError_t e = (t0 || t1) ? hipExtLaunchKernel(k, grid, block, params, lds, st, t0, t1, 0)
                             : hipLaunchKernel(k, grid, block, params, lds, st);
   return e != hipSuccess ? e : hipGetLastError();

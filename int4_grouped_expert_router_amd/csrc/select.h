@@ -317,12 +317,15 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
   // first-appearance order; an expert's rows are its tokens in ascending order.
   if (wid == 0) {
     GroupDev *G = &a.out->g;
+    const bool sh = a.shared_rows != 0;
     if (S == 1) {
-      // one token: the selections are already distinct, one row each, in route order
+      // one token: the selections are already distinct, one row each, in route order (and the
+      // shared expert's row after them)
       const int n = s_n[0];
-      if (lane < n) {
-        const int e = s_pidx[lane];
-        const float w = s_pw[lane];
+      const int nr = n + (sh ? 1 : 0);
+      if (lane < nr) {
+        const int e = lane < n ? s_pidx[lane] : kSharedRec;
+        const float w = lane < n ? s_pw[lane] : 1.f;
         G->entry_expert[lane] = e;
         G->entry_row0[lane] = lane;
         G->row_token[lane] = 0;
@@ -336,14 +339,14 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         s_row_size[lane] = 1;
       }
       if (lane == 0) {
-        G->entry_row0[n] = n;
+        G->entry_row0[nr] = nr;
         G->tok_row0[0] = 0;
-        G->tok_row0[1] = n;
-        G->n_entries = n;
-        G->n_rows = n;
+        G->tok_row0[1] = nr;
+        G->n_entries = nr;
+        G->n_rows = nr;
         G->S = 1;
         G->reserved = 0;
-        s_rows = n;
+        s_rows = nr;
       }
     } else {
       // lane p < npairs holds pair p = (token t, selection k < n_t), token-major.  Token t's
@@ -393,25 +396,45 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
         G->entry_row0[my_entry] = row0;
       }
       if (lane == 0) G->entry_row0[n_ent] = npairs;  // n_ent may be 64
+      // with the shared expert: its rows npairs + t (one per token t) form the last entry, and
+      // each token's reduce list is its routed rows in route order, then its shared row (so a
+      // pair's reduce position moves up by one per earlier token)
       if (pl && my_row < kRows) {  // always: the rows are a permutation of the pairs
         G->row_token[my_row] = my_t;
         G->row_expert[my_row] = my_e;
         G->row_weight[my_row] = my_w;
-        G->red_rows[lane] = my_row;
+        G->red_rows[lane + (sh ? my_t : 0)] = my_row;
         s_row_e[my_row] = my_e;
         s_row_t[my_row] = my_t;
         s_row_w[my_row] = my_w;
         s_row_rank[my_row] = rank;
         s_row_size[my_row] = __popcll(same);
       }
-      if (lane < S) G->tok_row0[lane] = tok0;
+      if (sh && lane < S) {  // the host keeps npairs + S <= kRows
+        const int r = npairs + lane;
+        G->row_token[r] = lane;
+        G->row_expert[r] = kSharedRec;
+        G->row_weight[r] = 1.f;
+        G->red_rows[tok_end + lane] = r;
+        s_row_e[r] = kSharedRec;
+        s_row_t[r] = lane;
+        s_row_w[r] = 1.f;
+        s_row_rank[r] = lane;
+        s_row_size[r] = S;
+      }
+      if (sh && lane == 0) {
+        G->entry_expert[n_ent] = kSharedRec;
+        G->entry_row0[n_ent + 1] = npairs + S;
+      }
+      if (lane < S) G->tok_row0[lane] = tok0 + (sh ? lane : 0);
       if (lane == 0) {
-        G->tok_row0[S] = npairs;  // S may be 64
-        G->n_entries = n_ent;
-        G->n_rows = npairs;
+        const int nr = npairs + (sh ? S : 0);
+        G->tok_row0[S] = nr;  // S may be 64
+        G->n_entries = n_ent + (sh ? 1 : 0);
+        G->n_rows = nr;
         G->S = S;
         G->reserved = 0;
-        s_rows = npairs;
+        s_rows = nr;
       }
     }
   }
@@ -431,7 +454,7 @@ static __device__ __forceinline__ void publish_group(const RouteArgs &a, const S
     const int q = tid + j * kBlock;
     const int row = q / kChunks, c = q % kChunks;
     const int e = row < rows ? s_row_e[row] : 0;
-    if (tab_pre)
+    if (tab_pre && e != kSharedRec)  // the shared expert's record is not among the staged ones
       v[j] = *reinterpret_cast<const u4 *>(s_tab + e * kDescWords + 4 * c);
     else
       v[j] = a.table ? reinterpret_cast<const u4 *>(a.table + e)[c] : u4{0u, 0u, 0u, 0u};
