@@ -260,10 +260,12 @@ int i4moe_shared_expert_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int 
 /* One whole MoE block on the residual stream, on the device, in one call: for the S float32 rows
  * of residual_dev ([S][D], 16-byte aligned, updated in place),
  *   a   = i4moe_rmsnorm of the rows into act_dtype (context scratch)
- *   route a (as i4moe_route with K, topp, norm_topk, routed_scale), issue the routed experts,
- *   issue the shared expert if one is bound, and take:
+ *   route a (as i4moe_route with K, topp, norm_topk, routed_scale), issue the routed experts and,
+ *   if one is bound, the shared expert, and take:
  *   residual[t] += (sum over the routed rows of t, route order, of w * y) + y_shared
- * with the slots added in issue order (routed first).  Needs the layer's router, norm weights and
+ * The shared expert runs as one more row per token of the routed group (weight 1, after the routed
+ * rows; S * (K + 1) <= I4MOE_MAX_ROWS), in the same launches and the same take slot: the same bits
+ * as issuing it separately after the routed experts.  Needs the layer's router, norm weights and
  * every routed expert.  Fault-hook gated as one compute call.  A failure after the first launch
  * poisons the context, as a failed take does.  The first call on a context allocates its scratch
  * for the normalised rows; later calls with the same or a smaller D allocate nothing. */
