@@ -264,8 +264,8 @@ int i4moe_shared_expert_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int 
  *   if one is bound, the shared expert, and take:
  *   residual[t] += (sum over the routed rows of t, route order, of w * y) + y_shared
  * The shared expert runs as one more row per token of the routed group (weight 1, after the routed
- * rows; S * (K + 1) <= I4MOE_MAX_ROWS), in the same launches and the same take slot: the same bits
- * as issuing it separately after the routed experts.  Needs the layer's router, norm weights and
+ * rows) when S * (K + 1) <= I4MOE_MAX_ROWS, in the same launches and the same take slot, else as
+ * its own issue after the routed one: the same bits either way.  Needs the layer's router, norm weights and
  * every routed expert.  Fault-hook gated as one compute call.  A failure after the first launch
  * poisons the context, as a failed take does.  The first call on a context allocates its scratch
  * for the normalised rows; later calls with the same or a smaller D allocate nothing. */

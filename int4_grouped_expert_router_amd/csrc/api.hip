@@ -1472,9 +1472,11 @@ int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act
     return fail(c, I4MOE_EINVAL, "residual_dev must be a 16-byte aligned device pointer");
   if (act_dtype != I4MOE_DTYPE_F32 && act_dtype != I4MOE_DTYPE_BF16) return fail(c, I4MOE_EINVAL, "bad dtype %d", act_dtype);
   if (S < 1 || S > kTokens) return fail(c, I4MOE_EINVAL, "S=%d outside 1..%d", S, kTokens);
-  if (K < 1 || K > L->E || K > kMaxK || S * K + (L->shared_set ? S : 0) > kRows)
+  if (K < 1 || K > L->E || K > kMaxK || S * K > kRows)
     return fail(c, I4MOE_EINVAL, "K=%d with S=%d outside the route's limits", K, S);
-  if (c->nslots + 1 > kSlots) return fail(c, I4MOE_EINVAL, "no free issue slots");
+  // the shared expert rides in the routed group when its rows fit beside the routed ones
+  const bool merge = L->shared_set && S * K + S <= kRows;
+  if (c->nslots + (L->shared_set && !merge ? 2 : 1) > kSlots) return fail(c, I4MOE_EINVAL, "no free issue slots");
   if (c->nslots > 0 && (c->slots[0].S != S || c->slots[0].D != L->D))
     return fail(c, I4MOE_EINVAL, "pending issues have another S or D");
   if ((int)L->gate.size() < L->E) return fail(c, I4MOE_EINVAL, "layer %d: experts 0..%d must all be set", layer, L->E - 1);
@@ -1487,11 +1489,15 @@ int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act
   // the normalised rows are packed [S][D] (what the route and the issues read)
   rc = rmsnorm_impl(c, *L, residual_dev, L->D, S, c->d_xn, L->D, act_dtype);
   // the shared expert rides in the routed group as one more row per token (weight 1, after the
-  // routed rows): one issue and one slot, the same sums as a separate shared issue taken after it
-  if (!rc)
-    rc = route_impl(c, layer, c->d_xn, act_dtype, S, K, topp, norm_topk, routed_scale, nullptr, L->shared_set);
+  // routed rows): one issue and one slot, the same sums as a separate shared issue taken after it,
+  // which is what runs when the rows do not fit one group
+  if (!rc) rc = route_impl(c, layer, c->d_xn, act_dtype, S, K, topp, norm_topk, routed_scale, nullptr, merge);
   if (!rc) {
     const int s = issue_impl(c, layer, c->d_xn, act_dtype, S, nullptr, false);
+    if (s < 0) rc = s;
+  }
+  if (!rc && L->shared_set && !merge) {
+    const int s = shared_issue_impl(c, layer, c->d_xn, act_dtype, S);
     if (s < 0) rc = s;
   }
   if (!rc) rc = take_impl(c, residual_dev, S);

@@ -1,7 +1,8 @@
 """The steps around the routed experts through the C ABI (MI355X only): rmsnorm against the
 oracle (bit for bit, away from rounding ties), the shared expert, and the whole MoE block in one
-call against the oracle's block, equal bit for bit to the same steps called one by one, and
-replayed from a captured graph."""
+call against the oracle's block, equal bit for bit to the same steps called one by one (the
+block's shared expert riding in the routed group, or in its own issue when the group is full),
+and replayed from a captured graph."""
 
 from __future__ import annotations
 
@@ -102,6 +103,9 @@ CASES = {
     # 16 tokens: the shared expert's entry (16 rows) and the routed entries of 8 rows or more run on
     # the matrix cores, the others on the vector kernels, in one block
     "prefill_like": ("small_batch", {"D": 2048, "I": 768, "E": 8, "K": 2, "S": 16}),
+    # S * K = 64 routed rows: no room for the shared rows in the routed group, so the shared
+    # expert takes its own issue and slot
+    "full_group": ("small_batch", {"D": 1024, "I": 512, "E": 16, "K": 8, "S": 8}),
 }
 
 
