@@ -17,33 +17,12 @@
 // counts below K are the selection positions.  No sequential rounds.
 #include <hip/hip_ext.h>
 
+#include "norm.h"
 #include "select.h"
 
 namespace i4moe {
 namespace {
 
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
-  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// Fixed-pattern wave sum of doubles; the total is returned wave-uniform.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v += dpp_f64<0xB1, 0xF>(v);
-  v += dpp_f64<0x4E, 0xF>(v);
-  v += dpp_f64<0x141, 0xF>(v);
-  v += dpp_f64<0x140, 0xF>(v);
-  v += dpp_f64<0x142, 0xA>(v);
-  v += dpp_f64<0x143, 0xC>(v);
-  const uint64_t u = __double_as_longlong(v);
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
-  return __longlong_as_double(((uint64_t)hi << 32) | lo);
-}
 
 __device__ __forceinline__ float x_at(const void *x, int bf16, size_t i) {
   if (bf16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(x)[i]) << 16);
