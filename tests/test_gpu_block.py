@@ -106,6 +106,9 @@ CASES = {
     # S * K = 64 routed rows: no room for the shared rows in the routed group, so the shared
     # expert takes its own issue and slot
     "full_group": ("small_batch", {"D": 1024, "I": 512, "E": 16, "K": 8, "S": 8}),
+    # one token over 128 experts: the select kernel (not the dual) builds the group with the
+    # shared row
+    "wide_router": ("small_batch", {"D": 1024, "I": 512, "E": 128, "K": 8, "S": 1}),
 }
 
 
