@@ -48,7 +48,7 @@ def check_group(ctx, layer, routes):
     return og
 
 
-def full_layer_check(cfg, layer=0):
+def full_layer_check(cfg, layer=0, mutate=None):
     """One layer against the oracle, element by element: the route (bit for bit away from
     near-ties), the group, every h row and every y row (the oracle's y from its own h, from x),
     and the layer delta.  A near-tie token's experts are checked on the GPU's own route, after the
@@ -56,10 +56,12 @@ def full_layer_check(cfg, layer=0):
     layer in the launch configuration the benchmark times (no host copy of the route, no taps:
     the selection deferred into the dual projection where it can be, the down projection fused
     into the take where it can be) must give the same delta bits, and the residual join must add
-    them exactly."""
+    them exactly.  mutate(L), if given, edits the generated layer first (e.g. its x)."""
     import torch
     from int4_grouped_expert_router_amd import binding as B
     L = make_layer(cfg, layer)
+    if mutate is not None:
+        mutate(L)
     ctx = new_ctx()
     upload_layer(ctx, L, layer)
     x = x_to_device(L.x, L.x_dtype)
@@ -142,6 +144,37 @@ def test_ragged_shapes(shape):
     cfg = get_config("tiny", D=D, I=I, E=E, K=K, S=S, formats=formats, gs=gs, x_dtype=xd, topp=0.9,
                      routed_scale=2.5, seed=100 + D + I)
     full_layer_check(cfg)
+
+
+DEGENERATE = {
+    # one expert, top-1, one token: the fused selection over a single score (with norm on, the
+    # layer is routed_scale * y, the oracle's closed-form pin)
+    "one_expert": dict(D=256, I=128, E=1, K=1, S=1, formats="row", gs=0, x_dtype="f32", topp=0.0),
+    # K = E: every expert for every token, entries of S rows
+    "k_equals_e": dict(D=512, I=256, E=8, K=8, S=2, formats="group", gs=64, x_dtype="bf16", topp=0.0),
+    # top-p near zero: one expert kept per token
+    "topp_keeps_one": dict(D=512, I=256, E=16, K=4, S=3, formats="mix_even_odd", gs=64, x_dtype="f32", topp=1e-6),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEGENERATE))
+def test_degenerate_layers(name):
+    print(f"[parity] degenerate {name}", flush=True)
+    cfg = get_config("tiny", routed_scale=2.5, seed=300, **DEGENERATE[name])
+    full_layer_check(cfg)
+
+
+def test_zero_activation_row():
+    """One token's activations all zero: its row exponent takes the zero-row value, its expert
+    rows are exactly zero (silu(0) * 0), and the router ranks it by the bias alone; the other
+    tokens as usual."""
+    print("[parity] zero activation row", flush=True)
+    cfg = get_config("tiny", D=1024, I=512, E=8, K=2, S=3, formats="mix_even_odd", gs=64, x_dtype="f32", seed=301)
+
+    def zero_row(L):
+        L.x[1, :] = 0.0
+
+    full_layer_check(cfg, mutate=zero_row)
 
 
 def test_determinism_medium():
