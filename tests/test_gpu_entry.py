@@ -5,7 +5,8 @@ exercised, and with repeated tokens inside an entry), checked row by row against
 (every h row and every y row, through the taps) and as a layer delta after the take, with pass
 sharing forced on and the matrix cores on and off; every run repeated for bitwise determinism.
 A device route at S = 64, K = 1 over 4 experts (about 16 rows each) is checked as a layer, and
-entries at the column cap (D = I = 8192) on the matrix cores and on the vector kernels."""
+entries at the column cap (D = I = 8192) and with all-zero activation rows, on the matrix cores
+and on the vector kernels."""
 
 from __future__ import annotations
 
@@ -142,19 +143,14 @@ def test_device_route_many_rows_per_expert():
         assert normwise_err(out[t], delta[t]) < TOL, t
 
 
-@pytest.mark.parametrize("mfma", ["8", "0"])
-def test_entries_at_column_cap(mfma, monkeypatch):
-    """D = I = 8192 (the column cap on both projections), group-wise g64 experts with f32 x: two
-    entries of 12 and 9 rows on the matrix cores (or on the vector kernels), every h and y row
-    and the layer delta against the oracle, run twice for bitwise determinism."""
+def check_entries_batched(cfg, L, S, sizes, mfma, monkeypatch, seed):
+    """Explicit entries of the given sizes, the matrix cores from `mfma` rows (0: off): every h
+    and y row and the layer delta against the oracle run one expert at a time (its rows as the
+    columns of one matrix), twice for bitwise determinism."""
     import torch
     from int4_grouped_expert_router_amd import Context
     from int4_grouped_expert_router_amd import binding as B
-    S, sizes = 16, [12, 9]
-    print(f"[entry] column cap D=I=8192 S={S} entries={sizes} mfma_min={mfma}", flush=True)
-    cfg = get_config("small_batch", D=8192, I=8192, E=4, S=S, layers=1, x_dtype="f32")
-    L = make_layer(cfg, 0)
-    rng = np.random.default_rng(8192)
+    rng = np.random.default_rng(seed)
     rows = make_rows(rng, S, sizes, cfg.E)
     monkeypatch.setenv("I4MOE_MFMA_MIN_ROWS", mfma)
     ctx = Context(0, torch.cuda.current_stream())
@@ -172,8 +168,6 @@ def test_entries_at_column_cap(mfma, monkeypatch):
         outs.append(out.cpu().numpy())
     ctx.close()
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(hs[0], hs[1]) and np.array_equal(ys[0], ys[1])
-
-    # the oracle one expert at a time, its rows as the columns of one matrix
     x64 = oracle.widen_activations(L.x, L.x_dtype)
     ordered = expert_major(rows)
     ref_h, ref_y = {}, {}
@@ -192,4 +186,35 @@ def test_entries_at_column_cap(mfma, monkeypatch):
     for t in range(S):
         if np.any(ref[t]):
             assert normwise_err(outs[0][t], ref[t]) < TOL, t
+        else:
+            assert not np.any(outs[0][t]), t
+    return rows, hs[0], ys[0], ordered
+
+
+@pytest.mark.parametrize("mfma", ["8", "0"])
+def test_entries_at_column_cap(mfma, monkeypatch):
+    """D = I = 8192 (the column cap on both projections), group-wise g64 experts with f32 x: two
+    entries of 12 and 9 rows on the matrix cores (or on the vector kernels), every h and y row
+    and the layer delta against the oracle, run twice for bitwise determinism."""
+    S, sizes = 16, [12, 9]
+    print(f"[entry] column cap D=I=8192 S={S} entries={sizes} mfma_min={mfma}", flush=True)
+    cfg = get_config("small_batch", D=8192, I=8192, E=4, S=S, layers=1, x_dtype="f32")
+    L = make_layer(cfg, 0)
+    rows, _, _, _ = check_entries_batched(cfg, L, S, sizes, mfma, monkeypatch, 8192)
     print(f"[entry] column cap: {len(rows)} rows ok", flush=True)
+
+
+@pytest.mark.parametrize("mfma", ["8", "0"])
+def test_entries_with_zero_activation_rows(mfma, monkeypatch):
+    """Two tokens' activations all zero inside matrix-core entries (bf16 x and f32 x): their
+    digit rows and exponents take the zero-row values and their h and y rows are exactly zero;
+    the other rows against the oracle."""
+    S, sizes = 16, [10, 14]
+    for xd in ("bf16", "f32"):
+        print(f"[entry] zero activation rows x={xd} mfma_min={mfma}", flush=True)
+        cfg = get_config("small_batch", D=2048, I=1024, E=6, S=S, layers=1, x_dtype=xd)
+        L = make_layer(cfg, 0)
+        L.x[[2, 9], :] = 0
+        rows, h, y, ordered = check_entries_batched(cfg, L, S, sizes, mfma, monkeypatch, 16)
+        zero = [i for i, r in enumerate(ordered) if r[1] in (2, 9)]
+        assert zero and not np.any(h[zero]) and not np.any(y[zero])
