@@ -409,13 +409,14 @@ def block(torch, B, name: str = "medium", layers: int = 8, steps: int = 400, war
 
 def tiered(torch, B, reps: int = 30):
     """The CPU tier's overlap: experts of the small-batch shape (D=6144, I=2048, g64, bf16; 64
-    experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1 and 4.
-    Per S: wall time of the device rows alone, the host rows alone, and both in one tiered issue
-    (route copy to the host excluded: the routes are computed once); prints one JSON line per S."""
+    experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1, 4 and 8.
+    Per S: wall time of the device rows alone, the host rows alone (with the host's integer dot
+    products when it has them, and with the float32 ones), and both in one tiered issue (route
+    copy to the host excluded: the routes are computed once); prints one JSON line per S."""
     from int4_grouped_expert_router_amd import Context
     from synth import gen_layer, get_config
     from synth.gen import gen_expert
-    for S in (1, 4):
+    for S in (1, 4, 8):
         cfg = get_config("small_batch", S=S, E=64)
         L = gen_layer(cfg, 0)
         ctx = Context(0, torch.cuda.current_stream())
@@ -440,12 +441,22 @@ def tiered(torch, B, reps: int = 30):
                     rs[t].idx[j], rs[t].w[j] = rec[t].idx[k], rec[t].w[k]
             return rs
 
-        arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": only(lambda e: e % 2 == 1), "tiered": rec}
-        res = {"S": S, "threads": None}
+        host = only(lambda e: e % 2 == 1)
+        # host_only_float: the same host rows with the float32 dot products (I4MOE_HOST_INT=0)
+        arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": host, "host_only_float": host,
+                "tiered": rec}
+        res = {"S": S, "threads": None, "host_int_path": int(B.i4moe_host_int_path())}
         walls = {k: [] for k in arms}
         cpus = []
+        prev = os.environ.get("I4MOE_HOST_INT")
         for rep in range(reps + 3):  # the arms interleaved, so they see the same machine state
             for name, routes in arms.items():
+                if name == "host_only_float":
+                    os.environ["I4MOE_HOST_INT"] = "0"
+                elif prev is None:
+                    os.environ.pop("I4MOE_HOST_INT", None)
+                else:
+                    os.environ["I4MOE_HOST_INT"] = prev
                 t0 = time.perf_counter()
                 _, tt = ctx.tiered_issue(0, x, routes)
                 ctx.take(out)
@@ -458,6 +469,14 @@ def tiered(torch, B, reps: int = 30):
         for name in arms:
             res[name + "_ms"] = round(float(np.median(walls[name])) * 1e3, 3)
         res["tiered_cpu_ms"] = round(float(np.median(cpus)), 3)
+        if prev is None:
+            os.environ.pop("I4MOE_HOST_INT", None)
+        else:
+            os.environ["I4MOE_HOST_INT"] = prev
+        # int4 weight bytes the host rows read (nibbles and scales of gate, up and down)
+        ex1 = gen_expert(cfg, 0, 1)
+        per_row = sum(t.packed.nbytes + t.scales.nbytes for t in (ex1.gate, ex1.up, ex1.down))
+        res["host_weight_gbps"] = round(res["host_rows"] * per_row / (res["host_only_ms"] * 1e-3) / 1e9, 1)
         res["serial_ms"] = round(res["device_only_ms"] + res["host_only_ms"], 3)
         res["hidden_ms"] = round(res["serial_ms"] - res["tiered_ms"], 3)
         hw = len(os.sched_getaffinity(0))

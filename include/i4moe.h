@@ -330,9 +330,13 @@ typedef struct {
 /* The experts of a host route (S records, e.g. from i4moe_route with host_out) split by tier
  * [PR342]: the rows (t, k < n_t) whose expert is bound on the device run as one explicit group on
  * the GPU (a slot, as i4moe_expert_group_issue); the rows whose expert is kept on the host are
- * computed on the CPU while that group runs, in float32 (each weight row summed over its columns
- * in order, group by group), and their weighted sum per token (rows in route order) goes to the
- * next slot as one row per token with weight 1.  i4moe_expert_group_take then joins both slots in
+ * computed on the CPU while that group runs, and their weighted sum per token (rows in route
+ * order, float32) goes to the next slot as one row per token with weight 1.  A weight row's dot
+ * product on the CPU: on a host with AVX-512 VNNI, when every host tensor is per-row or has a
+ * group size that is a multiple of 64 (see i4moe_host_int_path), the activation row (x, or a row
+ * of the gated product h) is taken in 24-bit fixed point with a power-of-two exponent of its own
+ * and each group's sum is an exact integer, scaled in double; otherwise each group's products
+ * are summed in float32, then scaled.  SiLU and the gated product are float32 either way.  i4moe_expert_group_take then joins both slots in
  * issue order (the device slot first), so the sum order is fixed and the result bitwise
  * reproducible [PR434].
  * x_dev ([S][D], F32 or BF16) is copied to the host on the stream before the device group's
@@ -351,12 +355,23 @@ int i4moe_tiered_issue(i4moe_ctx *ctx, int layer, const void *x_dev, int dtype, 
  * runs for its host rows) [PR342]: for r < n_rows, in order,
  *   P[token[r]][d] += weight[r] * (down[r] . (silu(gate[r] . x_t) * (up[r] . x_t)))[d]
  * with x: S x D float32 rows and P: S x D float32 (accumulated into), gate/up/down[r] host tensors
- * (I x D, I x D, D x I, layouts as i4moe_upload_expert_tensor), in float32 as described at
- * i4moe_tiered_issue.  threads >= 1 workers (the results do not depend on the count).
+ * (I x D, I x D, D x I, layouts as i4moe_upload_expert_tensor), with the arithmetic described at
+ * i4moe_tiered_issue.  threads >= 1 workers (the results do not depend on the count).  Rows
+ * whose three descriptors are equal (same pointers, format and shape) are one expert: its tensors
+ * are copied once and, on the integer path, each weight row is read once for all of them, as for
+ * an expert that several tokens of a tiered issue route to (the results are the same bits as
+ * row by row).
+ * Non-finite values in x give unspecified outputs.
  * Errors: EINVAL (bad shapes, tokens, NULL pointers, non-finite scales or weights), ENOMEM. */
 int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const float *weight,
                     const i4moe_host_tensor *gate, const i4moe_host_tensor *up, const i4moe_host_tensor *down,
                     const float *x, float *P, int threads);
+
+/* 1 when the CPU tier's dot products take the integer path on this host (AVX-512 F, BW, VL and
+ * VNNI present and I4MOE_HOST_INT is not "0" in the environment), else 0.  Tensors whose group
+ * size is not a multiple of 64 take the float32 path on any host.  The environment is read at
+ * every call, here and in the CPU tier. */
+int i4moe_host_int_path(void);
 
 /* ---- profiling ---------------------------------------------------------------------------- */
 

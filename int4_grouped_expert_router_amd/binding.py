@@ -78,6 +78,7 @@ SIGNATURES = {
     "i4moe_host_rows": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                                   C.POINTER(i4moe_host_tensor), C.POINTER(i4moe_host_tensor),
                                   C.POINTER(i4moe_host_tensor), C.c_void_p, C.c_void_p, C.c_int]),
+    "i4moe_host_int_path": (C.c_int, []),
     "i4moe_set_fail_after": (C.c_int, [_ctx_p, C.c_longlong]),
     "i4moe_debug_read": (C.c_int, [_ctx_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t]),
     "i4moe_debug_size": (C.c_size_t, [_ctx_p, C.c_int, C.c_int]),
@@ -138,6 +139,7 @@ i4moe_moe_block = _fn("i4moe_moe_block")
 i4moe_set_host_expert = _fn("i4moe_set_host_expert")
 i4moe_tiered_issue = _fn("i4moe_tiered_issue")
 i4moe_host_rows = _fn("i4moe_host_rows")
+i4moe_host_int_path = _fn("i4moe_host_int_path")
 i4moe_set_fail_after = _fn("i4moe_set_fail_after")
 i4moe_debug_read = _fn("i4moe_debug_read")
 i4moe_debug_size = _fn("i4moe_debug_size")

@@ -1621,13 +1621,21 @@ int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const
     }
     return I4MOE_OK;
   };
+  auto same = [](const i4moe_host_tensor &a, const i4moe_host_tensor &b) {
+    return a.fmt == b.fmt && a.gs == b.gs && a.O == b.O && a.C == b.C && a.packed == b.packed && a.scales == b.scales;
+  };
   for (int r = 0; r < n_rows; ++r) {
     if (token[r] < 0 || token[r] >= S || !std::isfinite(weight[r])) return I4MOE_EINVAL;
-    int rc;
-    if ((rc = copy(gate[r], I, D, ex[r].gate)) || (rc = copy(up[r], I, D, ex[r].up)) ||
-        (rc = copy(down[r], D, I, ex[r].down)))
-      return rc;
-    rows.push_back(HostRow{token[r], &ex[r], weight[r]});
+    // rows that name the same three tensors are one expert: one copy, computed together
+    int first = 0;
+    while (first < r && !(same(gate[first], gate[r]) && same(up[first], up[r]) && same(down[first], down[r]))) ++first;
+    if (first == r) {
+      int rc;
+      if ((rc = copy(gate[r], I, D, ex[r].gate)) || (rc = copy(up[r], I, D, ex[r].up)) ||
+          (rc = copy(down[r], D, I, ex[r].down)))
+        return rc;
+    }
+    rows.push_back(HostRow{token[r], &ex[first], weight[r]});
   }
   try {
     HostPool pool(threads);
@@ -1637,6 +1645,8 @@ int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const
   }
   return I4MOE_OK;
 }
+
+int i4moe_host_int_path(void) { return host_int_path_available() ? 1 : 0; }
 
 int i4moe_set_host_expert(i4moe_ctx *c, int layer, int expert, const i4moe_host_tensor *gate,
                           const i4moe_host_tensor *up, const i4moe_host_tensor *down) {

@@ -6,6 +6,7 @@
 // GPU works, then a take phase accumulates both.
 #pragma once
 
+#include <atomic>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -29,7 +30,9 @@ struct HostExpert {
 
 // Fixed worker threads.  run(n, fn) splits [0, n) into one contiguous range per thread (the same
 // split every time for the same n and thread count) and returns when all ranges are done; each
-// index is handled by exactly one thread, so per-index results never depend on timing.
+// index is handled by exactly one thread, so per-index results never depend on timing.  Between
+// runs a worker polls for the next one for about kSpinMicros before it sleeps, so the phases of
+// one computation follow each other without a wake-up through the kernel.
 class HostPool {
  public:
   explicit HostPool(int threads);
@@ -38,17 +41,18 @@ class HostPool {
   HostPool &operator=(const HostPool &) = delete;
   int threads() const { return (int)workers_.size() + 1; }
   void run(long n, const std::function<void(long begin, long end)> &fn);
+  static constexpr int kSpinMicros = 200;
 
  private:
   void work(int id);
   std::vector<std::thread> workers_;
   std::mutex m_;
-  std::condition_variable go_, done_;
+  std::condition_variable go_;
   const std::function<void(long, long)> *fn_ = nullptr;
   long n_ = 0;
-  unsigned gen_ = 0;
-  int pending_ = 0;
-  bool stop_ = false;
+  std::atomic<unsigned> gen_{0};
+  std::atomic<int> pending_{0}, sleepers_{0};
+  std::atomic<bool> stop_{false};
 };
 
 // One job at a time on a thread of its own: post(fn) hands fn over and returns at once, wait()
@@ -77,12 +81,22 @@ struct HostRow {
   float w;
 };
 
-// For the rows (in route order), in float32:
+// For the rows (in route order):
 //   P[t][d] += sum over the rows r of token t, in order, of w_r * y_r[d],
 //   y_r = down . (silu(gate . x_t) * (up . x_t))
-// x: S x D float32 rows, P: S x D float32 (accumulated into).  Each weight row's dot product is
-// summed group by group (a group's products summed, then scaled): in column order, or, on a host
-// with AVX2 and FMA, 32 columns at a time in four 8-wide partial sums added in a fixed order.
+// x: S x D float32 rows, P: S x D float32 (accumulated into).  Two ways to a weight row's dot
+// product, each deterministic:
+//  * integer (hosts with AVX-512 VNNI, when every tensor is per-row or its group size a multiple
+//    of 64): the activation row (x_t, or one row of h) in 24-bit fixed point with its own
+//    power-of-two exponent, as three int8 digits; each group's sum an exact integer, times its
+//    scale in double, rounded to float32 at the end;
+//  * float32 (otherwise, or with I4MOE_HOST_INT=0 in the environment): each group's products
+//    summed, then scaled: in column order, or, on a host with AVX2 and FMA, 32 columns at a time
+//    in four 8-wide partial sums added in a fixed order.
+// SiLU, the gated product and the weighted sum are float32 either way.
 void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const float *x, int D, int I, float *P);
+
+// Whether this host can take the integer path.
+bool host_int_path_available();
 
 }  // namespace i4moe

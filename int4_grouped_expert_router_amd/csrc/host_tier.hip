@@ -3,7 +3,10 @@
 
 #include <immintrin.h>
 
+#include <chrono>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 namespace i4moe {
 
@@ -14,7 +17,7 @@ HostPool::HostPool(int threads) {
 HostPool::~HostPool() {
   {
     std::lock_guard<std::mutex> lk(m_);
-    stop_ = true;
+    stop_.store(true);
   }
   go_.notify_all();
   for (auto &t : workers_) t.join();
@@ -23,22 +26,28 @@ HostPool::~HostPool() {
 void HostPool::work(int id) {
   unsigned seen = 0;
   for (;;) {
-    const std::function<void(long, long)> *fn;
-    long n;
-    {
-      std::unique_lock<std::mutex> lk(m_);
-      go_.wait(lk, [&] { return stop_ || gen_ != seen; });
-      if (stop_) return;
-      seen = gen_;
-      fn = fn_;
-      n = n_;
+    // poll for a new run, then sleep: a worker counts itself in sleepers_ before it looks at
+    // gen_ under the lock, and run() bumps gen_ before it looks at sleepers_, so either the
+    // worker sees the run or run() wakes it
+    const auto until = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinMicros);
+    unsigned g;
+    for (int i = 0;; ++i) {
+      g = gen_.load();
+      if (g != seen || stop_.load()) break;
+      _mm_pause();
+      if ((i & 255) == 255 && std::chrono::steady_clock::now() > until) {
+        std::unique_lock<std::mutex> lk(m_);
+        sleepers_.fetch_add(1);
+        go_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        sleepers_.fetch_sub(1);
+      }
     }
+    if (stop_.load()) return;
+    seen = g;
     const long T = threads();
-    (*fn)(n * id / T, n * (id + 1) / T);
-    {
-      std::lock_guard<std::mutex> lk(m_);
-      if (--pending_ == 0) done_.notify_one();
-    }
+    const long n = n_;
+    (*fn_)(n * id / T, n * (id + 1) / T);
+    pending_.fetch_sub(1);
   }
 }
 
@@ -48,17 +57,16 @@ void HostPool::run(long n, const std::function<void(long, long)> &fn) {
     fn(0, n);
     return;
   }
-  {
+  fn_ = &fn;
+  n_ = n;
+  pending_.store((int)workers_.size());
+  gen_.fetch_add(1);  // publishes fn_ and n_ (sequentially consistent)
+  if (sleepers_.load() > 0) {
     std::lock_guard<std::mutex> lk(m_);
-    fn_ = &fn;
-    n_ = n;
-    pending_ = (int)workers_.size();
-    ++gen_;
+    go_.notify_all();
   }
-  go_.notify_all();
   fn(0, n / threads());  // the calling thread takes range 0
-  std::unique_lock<std::mutex> lk(m_);
-  done_.wait(lk, [&] { return pending_ == 0; });
+  while (pending_.load() != 0) _mm_pause();
 }
 
 HostHelper::HostHelper() {
@@ -165,30 +173,364 @@ inline float row_dot(const HostTensor &T, int o, const float *x) {
   return acc;
 }
 
+// ---- Integer path: int8 dot products of fixed-point activations (AVX-512 VNNI) -------------
+//
+// An activation row v of C columns in fixed point: X[c] = rint(v[c] 2^E), E chosen from the
+// row's largest magnitude m (E = 148 - the biased exponent of m, so |X| <= 2^22), written as
+// three balanced base-256 digits X = d0 + 256 d1 + 65536 d2 (each in [-128, 127]).  A weight
+// nibble q stands for q - 8, so a row's group sum is
+//   sum_c (q_c - 8) X_c = sum_n 256^n (sum_c q_c d_n[c] - 8 sum_c d_n[c]),
+// every term an exact integer: vpdpbusd multiplies the unsigned nibbles by the signed digits,
+// four products per int32 lane, and the second sum is the lanes' start value.  A 64-column
+// block is 32 weight bytes: the low nibbles hold its even columns, the high nibbles its odd
+// ones, so each digit row is stored per block as the even columns' 32 digits, then the odd
+// columns' 32; int32 lane L of a block then takes the columns 8 L .. 8 L + 7.
+
+constexpr int kBlockCols = 64;
+constexpr int kPlanes = 3;
+constexpr int kBlockBytes = kPlanes * kBlockCols;  // digit bytes per block
+constexpr int kLanes = 8;                          // int32 lanes of a 256-bit register
+constexpr int kLaneInts = kPlanes * kLanes;        // start values per block
+
+struct DigitRow {
+  int E = 0, nb = 0;
+  std::vector<int8_t> dig;   // nb blocks x 3 digits x (32 even, 32 odd columns)
+  std::vector<int32_t> neg;  // nb x 3 x 8: -8 x (the sum of lane L's eight digits), per block and digit
+  std::vector<int32_t> pre;  // (nb + 1) x 3 x 8: the sums of neg over the blocks before
+};
+
+#define I4MOE_VNNI __attribute__((target("avx512f,avx512bw,avx512vl,avx512vnni,avx2,fma")))
+
+// The digit row of v (C columns), vectorised over a block at a time.
+I4MOE_VNNI void make_digit_row(const float *v, int C, DigitRow &r) {
+  r.nb = (C + kBlockCols - 1) / kBlockCols;
+  r.dig.resize((size_t)r.nb * kBlockBytes);
+  r.neg.resize((size_t)r.nb * kLaneInts);
+  r.pre.resize((size_t)(r.nb + 1) * kLaneInts);
+  __m512 mx = _mm512_setzero_ps();
+  for (int c = 0; c < C; c += 16) {
+    const __mmask16 k = C - c >= 16 ? (__mmask16)0xffff : (__mmask16)((1u << (C - c)) - 1u);
+    mx = _mm512_max_ps(mx, _mm512_abs_ps(_mm512_maskz_loadu_ps(k, v + c)));
+  }
+  const float m = _mm512_reduce_max_ps(mx);
+  uint32_t mb;
+  std::memcpy(&mb, &m, 4);
+  r.E = 148 - (int)(mb >> 23);
+  const __m512d scale = _mm512_set1_pd(std::ldexp(1.0, r.E));  // v 2^E is exact in double
+  // columns 0, 2, .., 14 then 1, 3, .., 15 of 16
+  const __m512i evens_odds = _mm512_setr_epi32(0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15);
+  const __m512i bias = _mm512_set1_epi32(0x808080);
+  const __m256i ones = _mm256_set1_epi8(1);
+  for (int b = 0; b < r.nb; ++b) {
+    int8_t *dst = r.dig.data() + (size_t)b * kBlockBytes;
+    for (int i = 0; i < 4; ++i) {  // 16 columns at a time
+      const int c = b * kBlockCols + 16 * i;
+      const __mmask16 k = c >= C ? (__mmask16)0 : C - c >= 16 ? (__mmask16)0xffff : (__mmask16)((1u << (C - c)) - 1u);
+      const __m512 f = _mm512_maskz_loadu_ps(k, v + (c < C ? c : 0));
+      const __m256i x0 = _mm512_cvtpd_epi32(_mm512_mul_pd(_mm512_cvtps_pd(_mm512_castps512_ps256(f)), scale));
+      const __m256i x1 = _mm512_cvtpd_epi32(
+          _mm512_mul_pd(_mm512_cvtps_pd(_mm256_castpd_ps(_mm512_extractf64x4_pd(_mm512_castps_pd(f), 1))), scale));
+      const __m512i X = _mm512_inserti64x4(_mm512_castsi256_si512(x0), x1, 1);  // round to nearest even
+      const __m512i u = _mm512_permutexvar_epi32(evens_odds, _mm512_xor_si512(_mm512_add_epi32(X, bias), bias));
+      for (int n = 0; n < kPlanes; ++n) {
+        const __m128i d = _mm512_cvtepi32_epi8(_mm512_srli_epi32(u, 8 * n));  // 8 even, then 8 odd digits
+        _mm_storel_epi64(reinterpret_cast<__m128i *>(dst + n * kBlockCols + 8 * i), d);
+        _mm_storel_epi64(reinterpret_cast<__m128i *>(dst + n * kBlockCols + 32 + 8 * i), _mm_srli_si128(d, 8));
+      }
+    }
+    for (int n = 0; n < kPlanes; ++n) {
+      const __m256i e = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + n * kBlockCols));
+      const __m256i o = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + n * kBlockCols + 32));
+      const __m256i sum = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(_mm256_setzero_si256(), ones, e), ones, o);
+      _mm256_storeu_si256(reinterpret_cast<__m256i *>(r.neg.data() + (size_t)b * kLaneInts + n * kLanes),
+                          _mm256_sub_epi32(_mm256_setzero_si256(), _mm256_slli_epi32(sum, 3)));
+    }
+  }
+  std::fill(r.pre.begin(), r.pre.begin() + kLaneInts, 0);
+  for (int b = 0; b < r.nb; ++b)
+    for (int i = 0; i < kLaneInts; ++i)
+      r.pre[(size_t)(b + 1) * kLaneInts + i] = r.pre[(size_t)b * kLaneInts + i] + r.neg[(size_t)b * kLaneInts + i];
+}
+
+// The integer path takes tensors whose groups are whole blocks (per-row, or gs a multiple of 64).
+inline bool vnni_fits(const HostTensor &T) { return T.ng == 1 || T.gs % kBlockCols == 0; }
+
+// The 32 weight bytes of block b of a row of rb bytes (zero past the row's end).
+I4MOE_VNNI inline __m256i weight_block(const uint8_t *row, int b, int rb) {
+  const int rest = rb - 32 * b;
+  return rest >= 32 ? _mm256_loadu_si256(reinterpret_cast<const __m256i *>(row + 32 * b))
+                    : _mm256_maskz_loadu_epi8((__mmask32)((1u << rest) - 1u), row + 32 * b);
+}
+
+// Lanes a0 + 256 a1 + 65536 a2 in int32 (exact when the group is at most 256 columns wide:
+// |lane| <= 32 x 8 x 2^22 = 2^30), times sc into the double lane sums.
+I4MOE_VNNI inline void join_narrow(__m256i a0, __m256i a1, __m256i a2, double sc, __m256d &s0, __m256d &s1) {
+  const __m256i j = _mm256_add_epi32(_mm256_add_epi32(a0, _mm256_slli_epi32(a1, 8)), _mm256_slli_epi32(a2, 16));
+  const __m256d k = _mm256_set1_pd(sc);
+  s0 = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(j)), k, s0);
+  s1 = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(j, 1)), k, s1);
+}
+
+// The same join in double (any width: each digit sum is exact in int32 up to the column cap).
+I4MOE_VNNI inline void join_wide(__m256i a0, __m256i a1, __m256i a2, double sc, __m256d &s0, __m256d &s1) {
+  const __m256d k1 = _mm256_set1_pd(256.0), k2 = _mm256_set1_pd(65536.0), k = _mm256_set1_pd(sc);
+  const __m256d lo = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(a2)), k2,
+                                     _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(a1)), k1,
+                                                     _mm256_cvtepi32_pd(_mm256_castsi256_si128(a0))));
+  const __m256d hi = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(a2, 1)), k2,
+                                     _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(a1, 1)), k1,
+                                                     _mm256_cvtepi32_pd(_mm256_extracti128_si256(a0, 1))));
+  s0 = _mm256_fmadd_pd(lo, k, s0);
+  s1 = _mm256_fmadd_pd(hi, k, s1);
+}
+
+// One output row of T against NR digit rows x[r] (each weight block loaded once for all of
+// them): per row, each group's exact integer lanes, times the group's scale, into double lane
+// sums; the eight lanes added in a fixed order, times 2^-E.  Row r's result takes the same steps
+// whatever NR is, so it does not depend on which rows share the call.
+template <int NR>
+I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow *const *x, double *res) {
+  const uint8_t *row = T.packed.data() + (size_t)o * (T.C / 2);
+  const float *s = T.scales.data() + (size_t)o * T.ng;
+  const int rb = T.C / 2, nb = x[0]->nb;
+  const __m256i low = _mm256_set1_epi8(0x0F);
+  const __m256i *dig[NR], *neg[NR], *pre[NR];
+  __m256d s0[NR], s1[NR];
+  for (int r = 0; r < NR; ++r) {
+    dig[r] = reinterpret_cast<const __m256i *>(x[r]->dig.data());
+    neg[r] = reinterpret_cast<const __m256i *>(x[r]->neg.data());
+    pre[r] = reinterpret_cast<const __m256i *>(x[r]->pre.data());
+    s0[r] = s1[r] = _mm256_setzero_pd();
+  }
+  if (T.ng == 1) {
+    // one group over the row: per row six accumulators (digit x even/odd) carried across blocks
+    __m256i a0[NR], a1[NR], a2[NR], b0[NR], b1[NR], b2[NR];
+    for (int r = 0; r < NR; ++r) a0[r] = a1[r] = a2[r] = b0[r] = b1[r] = b2[r] = _mm256_setzero_si256();
+    for (int b = 0; b < nb; ++b) {
+      const __m256i w = weight_block(row, b, rb);
+      const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
+      for (int r = 0; r < NR; ++r) {
+        const __m256i *d = dig[r] + 6 * b;
+        a0[r] = _mm256_dpbusd_epi32(a0[r], lo, _mm256_loadu_si256(d + 0));
+        b0[r] = _mm256_dpbusd_epi32(b0[r], hi, _mm256_loadu_si256(d + 1));
+        a1[r] = _mm256_dpbusd_epi32(a1[r], lo, _mm256_loadu_si256(d + 2));
+        b1[r] = _mm256_dpbusd_epi32(b1[r], hi, _mm256_loadu_si256(d + 3));
+        a2[r] = _mm256_dpbusd_epi32(a2[r], lo, _mm256_loadu_si256(d + 4));
+        b2[r] = _mm256_dpbusd_epi32(b2[r], hi, _mm256_loadu_si256(d + 5));
+      }
+    }
+    for (int r = 0; r < NR; ++r) {
+      const __m256i *p = pre[r] + kPlanes * nb;  // all blocks' start values
+      join_wide(_mm256_add_epi32(_mm256_add_epi32(a0[r], b0[r]), _mm256_loadu_si256(p + 0)),
+                _mm256_add_epi32(_mm256_add_epi32(a1[r], b1[r]), _mm256_loadu_si256(p + 1)),
+                _mm256_add_epi32(_mm256_add_epi32(a2[r], b2[r]), _mm256_loadu_si256(p + 2)), (double)s[0], s0[r],
+                s1[r]);
+    }
+  } else if (T.gs == kBlockCols) {
+    // one block per group
+    for (int b = 0; b < nb; ++b) {
+      const __m256i w = weight_block(row, b, rb);
+      const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
+      const double sc = (double)s[b];
+      for (int r = 0; r < NR; ++r) {
+        const __m256i *d = dig[r] + 6 * b;
+        const __m256i *z = neg[r] + kPlanes * b;
+        const __m256i a0 = _mm256_dpbusd_epi32(
+            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 0), lo, _mm256_loadu_si256(d + 0)), hi, _mm256_loadu_si256(d + 1));
+        const __m256i a1 = _mm256_dpbusd_epi32(
+            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 1), lo, _mm256_loadu_si256(d + 2)), hi, _mm256_loadu_si256(d + 3));
+        const __m256i a2 = _mm256_dpbusd_epi32(
+            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 2), lo, _mm256_loadu_si256(d + 4)), hi, _mm256_loadu_si256(d + 5));
+        join_narrow(a0, a1, a2, sc, s0[r], s1[r]);
+      }
+    }
+  } else {
+    // groups of several blocks (the last one may be narrower)
+    const int gb = T.gs / kBlockCols;
+    for (int g = 0, g0 = 0; g0 < nb; ++g, g0 += gb) {
+      const int g1 = g0 + gb < nb ? g0 + gb : nb;
+      __m256i a0[NR], a1[NR], a2[NR];
+      for (int r = 0; r < NR; ++r) {
+        a0[r] = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * g1 + 0), _mm256_loadu_si256(pre[r] + kPlanes * g0 + 0));
+        a1[r] = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * g1 + 1), _mm256_loadu_si256(pre[r] + kPlanes * g0 + 1));
+        a2[r] = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * g1 + 2), _mm256_loadu_si256(pre[r] + kPlanes * g0 + 2));
+      }
+      for (int b = g0; b < g1; ++b) {
+        const __m256i w = weight_block(row, b, rb);
+        const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
+        for (int r = 0; r < NR; ++r) {
+          const __m256i *d = dig[r] + 6 * b;
+          a0[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a0[r], lo, _mm256_loadu_si256(d + 0)), hi, _mm256_loadu_si256(d + 1));
+          a1[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a1[r], lo, _mm256_loadu_si256(d + 2)), hi, _mm256_loadu_si256(d + 3));
+          a2[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a2[r], lo, _mm256_loadu_si256(d + 4)), hi, _mm256_loadu_si256(d + 5));
+        }
+      }
+      for (int r = 0; r < NR; ++r) {
+        if (gb <= 4)
+          join_narrow(a0[r], a1[r], a2[r], (double)s[g], s0[r], s1[r]);
+        else
+          join_wide(a0[r], a1[r], a2[r], (double)s[g], s0[r], s1[r]);
+      }
+    }
+  }
+  for (int r = 0; r < NR; ++r) {
+    alignas(32) double t[8];
+    _mm256_store_pd(t, s0[r]);
+    _mm256_store_pd(t + 4, s1[r]);
+    const double total = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    res[r] = std::ldexp(total, -x[r]->E);
+  }
+}
+
+// The host rows of one expert, in route order.
+struct HostEntry {
+  const HostExpert *e;
+  std::vector<int> rows;
+};
+
+constexpr int kMaxShare = 4;  // activation rows that share one pass over a weight row
+
+// Gate, up and the SiLU-gated product of output o for the entry's rows rk[0 .. NR).
+template <int NR>
+I4MOE_VNNI void gate_up_rows(const HostEntry &en, const int *rk, int o, const std::vector<HostRow> &rows,
+                             const std::vector<DigitRow> &xd, int I, float *h) {
+  const DigitRow *xs[NR];
+  for (int r = 0; r < NR; ++r) xs[r] = &xd[rows[rk[r]].token];
+  double g[NR], u[NR];
+  row_dots_vnni<NR>(en.e->gate, o, xs, g);
+  row_dots_vnni<NR>(en.e->up, o, xs, u);
+  for (int r = 0; r < NR; ++r) {
+    const float gf = (float)g[r], uf = (float)u[r];
+    h[(size_t)rk[r] * I + o] = gf / (1.f + std::exp(-gf)) * uf;
+  }
+}
+
+// Output d of the down projection for the entry's rows rk[0 .. NR).
+template <int NR>
+I4MOE_VNNI void down_rows(const HostEntry &en, const int *rk, int d, const std::vector<DigitRow> &hd, int D, float *y) {
+  const DigitRow *hs[NR];
+  for (int r = 0; r < NR; ++r) hs[r] = &hd[rk[r]];
+  double v[NR];
+  row_dots_vnni<NR>(en.e->down, d, hs, v);
+  for (int r = 0; r < NR; ++r) y[(size_t)rk[r] * D + d] = (float)v[r];
+}
+
+// Calls f(rk, nr) for the entry's rows in chunks of at most kMaxShare, in order.
+template <class F>
+inline void for_chunks(const HostEntry &en, F &&f) {
+  const int n = (int)en.rows.size();
+  for (int i = 0; i < n; i += kMaxShare) f(en.rows.data() + i, n - i < kMaxShare ? n - i : kMaxShare);
+}
+
+I4MOE_VNNI void gate_up_entry(const HostEntry &en, int o, const std::vector<HostRow> &rows,
+                              const std::vector<DigitRow> &xd, int I, float *h) {
+  for_chunks(en, [&](const int *rk, int nr) {
+    switch (nr) {
+      case 1: gate_up_rows<1>(en, rk, o, rows, xd, I, h); break;
+      case 2: gate_up_rows<2>(en, rk, o, rows, xd, I, h); break;
+      case 3: gate_up_rows<3>(en, rk, o, rows, xd, I, h); break;
+      default: gate_up_rows<4>(en, rk, o, rows, xd, I, h); break;
+    }
+  });
+}
+
+I4MOE_VNNI void down_entry(const HostEntry &en, int d, const std::vector<DigitRow> &hd, int D, float *y) {
+  for_chunks(en, [&](const int *rk, int nr) {
+    switch (nr) {
+      case 1: down_rows<1>(en, rk, d, hd, D, y); break;
+      case 2: down_rows<2>(en, rk, d, hd, D, y); break;
+      case 3: down_rows<3>(en, rk, d, hd, D, y); break;
+      default: down_rows<4>(en, rk, d, hd, D, y); break;
+    }
+  });
+}
+
+// Work units: output o of entry i is rows(i) units, entries one after another (cum[i] units
+// before entry i).  A worker's range [b, e) takes the outputs whose first unit lies in it, so
+// the split follows the work and each output is computed by exactly one worker.
+template <class F>
+inline void for_outputs(const std::vector<HostEntry> &ent, const std::vector<long> &cum, int n_out, long b, long e,
+                        F &&f) {
+  size_t i = 0;
+  while (i + 1 < ent.size() && cum[i + 1] <= b) ++i;
+  for (; i < ent.size() && cum[i] < e; ++i) {
+    const long R = (long)ent[i].rows.size();
+    long o = b > cum[i] ? (b - cum[i] + R - 1) / R : 0;
+    for (; o < n_out && cum[i] + o * R < e; ++o) f(ent[i], (int)o);
+  }
+}
+
+const bool kVnni = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                   __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512vnni") && kAvx2;
+
 }  // namespace
+
+bool host_int_path_available() {
+  const char *env = std::getenv("I4MOE_HOST_INT");
+  return kVnni && !(env && env[0] == '0');
+}
 
 void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const float *x, int D, int I, float *P) {
   const long n = (long)rows.size();
   if (n == 0) return;
+  bool use_int = host_int_path_available();
+  for (const HostRow &r : rows) use_int = use_int && vnni_fits(r.e->gate) && vnni_fits(r.e->up) && vnni_fits(r.e->down);
   std::vector<float> h((size_t)n * I), y((size_t)n * D);
-  // gate and up, SiLU-gated product: one (row, output) pair per index
-  pool.run(n * I, [&](long b, long e) {
-    for (long k = b; k < e; ++k) {
-      const HostRow &r = rows[k / I];
-      const int o = (int)(k % I);
-      const float *xt = x + (size_t)r.token * D;
-      const float g = row_dot(r.e->gate, o, xt);
-      const float u = row_dot(r.e->up, o, xt);
-      h[k] = g / (1.f + std::exp(-g)) * u;
+  if (use_int) {
+    // the rows grouped by expert (first appearance order), so that a weight row is read once
+    // for all the rows of its expert
+    std::vector<HostEntry> ent;
+    for (long k = 0; k < n; ++k) {
+      size_t i = 0;
+      while (i < ent.size() && ent[i].e != rows[k].e) ++i;
+      if (i == ent.size()) ent.push_back(HostEntry{rows[k].e, {}});
+      ent[i].rows.push_back((int)k);
     }
-  });
-  // down
-  pool.run(n * D, [&](long b, long e) {
-    for (long k = b; k < e; ++k) {
-      const HostRow &r = rows[k / D];
-      y[k] = row_dot(r.e->down, (int)(k % D), h.data() + (size_t)(k / D) * I);
+    std::vector<long> cum_i(ent.size() + 1, 0), cum_d(ent.size() + 1, 0);
+    for (size_t i = 0; i < ent.size(); ++i) {
+      cum_i[i + 1] = cum_i[i] + (long)ent[i].rows.size() * I;
+      cum_d[i + 1] = cum_d[i] + (long)ent[i].rows.size() * D;
     }
-  });
+    // the digit rows of the tokens' x, then gate and up with the SiLU-gated product
+    int S = 0;
+    for (const HostRow &r : rows) S = r.token + 1 > S ? r.token + 1 : S;
+    std::vector<char> used(S, 0);
+    for (const HostRow &r : rows) used[r.token] = 1;
+    std::vector<DigitRow> xd(S), hd(n);
+    pool.run(S, [&](long b, long e) {
+      for (long t = b; t < e; ++t)
+        if (used[t]) make_digit_row(x + (size_t)t * D, D, xd[t]);
+    });
+    pool.run(cum_i.back(), [&](long b, long e) {
+      for_outputs(ent, cum_i, I, b, e, [&](const HostEntry &en, int o) { gate_up_entry(en, o, rows, xd, I, h.data()); });
+    });
+    // the digit rows of h, then down
+    pool.run(n, [&](long b, long e) {
+      for (long k = b; k < e; ++k) make_digit_row(h.data() + (size_t)k * I, I, hd[k]);
+    });
+    pool.run(cum_d.back(), [&](long b, long e) {
+      for_outputs(ent, cum_d, D, b, e, [&](const HostEntry &en, int d) { down_entry(en, d, hd, D, y.data()); });
+    });
+  } else {
+    // gate and up, SiLU-gated product: one (row, output) pair per index
+    pool.run(n * I, [&](long b, long e) {
+      for (long k = b; k < e; ++k) {
+        const HostRow &r = rows[k / I];
+        const int o = (int)(k % I);
+        const float *xt = x + (size_t)r.token * D;
+        const float g = row_dot(r.e->gate, o, xt);
+        const float u = row_dot(r.e->up, o, xt);
+        h[k] = g / (1.f + std::exp(-g)) * u;
+      }
+    });
+    // down
+    pool.run(n * D, [&](long b, long e) {
+      for (long k = b; k < e; ++k) {
+        const HostRow &r = rows[k / D];
+        y[k] = row_dot(r.e->down, (int)(k % D), h.data() + (size_t)(k / D) * I);
+      }
+    });
+  }
   // the weighted sum per token, rows in order: one column per index
   pool.run(D, [&](long b, long e) {
     for (long d = b; d < e; ++d)

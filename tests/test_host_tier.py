@@ -73,3 +73,75 @@ def test_host_rows_refuses_bad_arguments(lib):
         host_rows(3, cfg.D, cfg.I, [(0, 1.0, g, g, g)], x)
     assert e4.value.code == B.I4MOE_EINVAL
     assert B.i4moe_host_rows(0, 8, 8, 0, None, None, None, None, None, None, None, 1) == B.I4MOE_EINVAL
+
+
+# (D, I, formats, gs), each reaching one form of the integer path's dot product: one 64-column
+# block per group, groups of two blocks (digit sums joined in int32), of five blocks and whole
+# rows (joined in double); D = 1000 and I = 392 end in a partial block (40 and 8 columns).  g32
+# takes the float32 path on every host.
+SHAPES = [(1000, 392, "group", 64), (1000, 392, "group", 128), (1000, 392, "group", 320),
+          (1000, 392, "row", 0), (256, 200, "group", 32)]
+
+
+def shaped_case(D, I, formats, gs):
+    cfg = get_config("mix", D=D, I=I, E=3, formats=formats, gs=gs, layers=1)
+    ex = {e: gen_expert(cfg, 0, e) for e in range(cfg.E)}
+    rng = np.random.default_rng(D + I + gs)
+    x = rng.standard_normal((4, D)).astype(np.float32)
+    x[1] *= np.float32(1e-6)        # the fixed point follows each row's own magnitude
+    x[2, 17] = np.float32(3e4)      # one large column: the rest keep fewer bits
+    x[3] = 0.0                      # an all-zero row
+    plan = [(0, 0, 0.75), (1, 0, 1.5), (2, 1, 0.5), (0, 2, 0.25), (2, 3, 1.0), (1, 1, 2.0)]
+    rows = [(t, w, ex[e].gate, ex[e].up, ex[e].down) for e, t, w in plan]
+    ref = np.zeros((4, D))
+    for e, t, w in plan:
+        ref[t] += float(np.float32(w)) * oracle.expert_forward(ex[e].gate, ex[e].up, ex[e].down,
+                                                               x[t].astype(np.float64))[3]
+    return cfg, x, rows, ref
+
+
+@pytest.mark.parametrize("path", ["int", "float"])
+@pytest.mark.parametrize("D,I,formats,gs", SHAPES)
+def test_host_rows_paths_match_oracle(lib, monkeypatch, D, I, formats, gs, path):
+    from int4_grouped_expert_router_amd import binding as B
+    from int4_grouped_expert_router_amd import host_rows
+    monkeypatch.setenv("I4MOE_HOST_INT", "1" if path == "int" else "0")
+    if path == "int" and not B.i4moe_host_int_path():
+        pytest.skip("no AVX-512 VNNI on this host")
+    cfg, x, rows, ref = shaped_case(D, I, formats, gs)
+    P = host_rows(4, D, I, rows, x, threads=3)
+    for t in range(3):
+        # 24-bit activations and float32 SiLU: about 1e-7 of the output's norm
+        assert normwise_err(P[t], ref[t]) < 1e-5, (t, path)
+    assert not np.any(P[3])  # no row routes token 3
+    assert np.array_equal(host_rows(4, D, I, rows, x, threads=1), P)
+
+
+def test_host_int_path_query(lib, monkeypatch):
+    from int4_grouped_expert_router_amd import binding as B
+    with open("/proc/cpuinfo") as f:
+        flags = next((ln.split(":", 1)[1].split() for ln in f if ln.startswith("flags")), [])
+    has = all(fl in flags for fl in ("avx512f", "avx512bw", "avx512vl", "avx512_vnni"))
+    monkeypatch.setenv("I4MOE_HOST_INT", "1")
+    assert B.i4moe_host_int_path() == int(has)
+    monkeypatch.setenv("I4MOE_HOST_INT", "0")
+    assert B.i4moe_host_int_path() == 0
+
+
+@pytest.mark.parametrize("D,I,formats,gs", SHAPES[:4])
+def test_host_rows_shared_expert_same_bits_as_alone(lib, D, I, formats, gs):
+    """Rows naming the same tensors are one expert, computed together (on the integer path, four
+    activation rows per pass over a weight row): each row's result is the same bits as when it
+    is computed alone.  One row per token with weight 1, so P[t] is that row's output exactly."""
+    from int4_grouped_expert_router_amd import host_rows
+    cfg = get_config("mix", D=D, I=I, E=2, formats=formats, gs=gs, layers=1)
+    ex = [gen_expert(cfg, 0, e) for e in range(2)]
+    x = np.random.default_rng(5).standard_normal((7, D)).astype(np.float32)
+    plan = [0, 0, 0, 0, 0, 0, 1]  # token t -> expert: six rows of expert 0 (4 + 2), one of expert 1
+    rows = [(t, 1.0, ex[e].gate, ex[e].up, ex[e].down) for t, e in enumerate(plan)]
+    P = host_rows(7, D, I, rows, x, threads=4)
+    for t, e in enumerate(plan):
+        alone = host_rows(1, D, I, [(0, 1.0, ex[e].gate, ex[e].up, ex[e].down)], x[t:t + 1], threads=2)
+        assert np.array_equal(P[t], alone[0]), t
+        ref = oracle.expert_forward(ex[e].gate, ex[e].up, ex[e].down, x[t].astype(np.float64))[3]
+        assert normwise_err(P[t], ref) < 1e-5, t
