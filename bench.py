@@ -487,6 +487,53 @@ def tiered(torch, B, reps: int = 30):
         torch.cuda.empty_cache()
 
 
+def reread(torch, B, name: str = "medium", layers: int = 8, reps: int = 40):
+    """Whether weights read a moment ago read faster: the read probe over each layer's taken
+    experts, in bursts behind a GPU sleep, as down alone, gate + up then down, and gate + up,
+    down, down again (the second down read right after the first).  Median µs per launch from
+    HIP events on the library's stream; one JSON line."""
+    from int4_grouped_expert_router_amd import Context
+    from synth import get_config
+    cfg = get_config(name)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    ctx = Context(0, stream)
+    Ls = setup(cfg, layers, ctx, torch)
+    taken = []
+    for l, L in enumerate(Ls):
+        rec = ctx.route(l, L.x_dev, cfg.K, cfg.topp, cfg.norm_topk, cfg.routed_scale, host_out=True)
+        taken.append(sorted(set(int(rec[t].idx[k]) for t in range(cfg.S) for k in range(rec[t].n))))
+    sleep_cycles = calibrate_sleep(torch, stream, burst=reps)
+
+    def run(seq):
+        times = {}
+        for rep in range(3):  # the first burst warms up and is dropped
+            torch.cuda._sleep(sleep_cycles)
+            evs = []
+            for i in range(reps):
+                for label, mask in seq:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    ctx.read_probe(i % layers, mask, taken[i % layers])
+                    b.record()
+                    evs.append((label, a, b))
+            torch.cuda.synchronize()
+            if rep:
+                for label, a, b in evs:
+                    times.setdefault(label, []).append(a.elapsed_time(b) * 1e3)
+        return {k: round(float(np.median(v)), 2) for k, v in times.items()}
+
+    res = {"workload": workload_text(cfg, layers),
+           "gate_up_MB": round(sum(Ls[0].bytes_gate_up[e] for e in taken[0]) / 1e6, 2),
+           "down_MB": round(sum(Ls[0].bytes_down[e] for e in taken[0]) / 1e6, 2),
+           "down_alone_us": run([("down", 4)]),
+           "gate_up_then_down_us": run([("gate_up", 3), ("down", 4)]),
+           "down_read_twice_us": run([("gate_up", 3), ("down_first", 4), ("down_again", 4)])}
+    log(f"reread {name}: {res}")
+    print(json.dumps(res), flush=True)
+    ctx.close()
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -559,6 +606,8 @@ def main():
                     help="only time the MoE block (rmsnorm, route, routed and shared experts, join) on medium")
     ap.add_argument("--tiered", action="store_true",
                     help="only time the CPU tier: device rows, host rows, and both overlapped")
+    ap.add_argument("--reread", action="store_true",
+                    help="only time the read probe on medium weights read once and read again at once")
     ap.add_argument("--crossover-modes", default="", help="comma-separated launch modes (default: all)")
     ap.add_argument("--crossover-formats", default="group", choices=("group", "row"),
                     help="crossover experts: group-wise g64 (default) or per-row int4")
@@ -583,6 +632,9 @@ def main():
         return
     if args.block:
         block(torch, B)
+        return
+    if args.reread:
+        reread(torch, B)
         return
     if args.crossover:
         rows = tuple(int(v) for v in args.crossover_rows.split(",")) if args.crossover_rows else CROSS_ROWS
