@@ -411,7 +411,7 @@ def tiered(torch, B, reps: int = 30):
     """The CPU tier's overlap: experts of the small-batch shape (D=6144, I=2048, g64, bf16; 64
     experts, even ones on the device, odd ones kept on the host), top-8 routes at S = 1, 4 and 8.
     Per S: wall time of the device rows alone, the host rows alone (with the host's integer dot
-    products when it has them, and with the float32 ones), and both in one tiered issue (route
+    products when it has them, those at 256 bits, and the float32 ones), and both in one tiered issue (route
     copy to the host excluded: the routes are computed once); prints one JSON line per S."""
     from int4_grouped_expert_router_amd import Context
     from synth import gen_layer, get_config
@@ -442,17 +442,19 @@ def tiered(torch, B, reps: int = 30):
             return rs
 
         host = only(lambda e: e % 2 == 1)
-        # host_only_float: the same host rows with the float32 dot products (I4MOE_HOST_INT=0)
-        arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": host, "host_only_float": host,
-                "tiered": rec}
+        # the same host rows with the integer dot products kept at 256 bits (I4MOE_HOST_INT=256)
+        # and with the float32 ones (I4MOE_HOST_INT=0)
+        arms = {"device_only": only(lambda e: e % 2 == 0), "host_only": host, "host_only_256": host,
+                "host_only_float": host, "tiered": rec}
+        forced = {"host_only_256": "256", "host_only_float": "0"}
         res = {"S": S, "threads": None, "host_int_path": int(B.i4moe_host_int_path())}
         walls = {k: [] for k in arms}
         cpus = []
         prev = os.environ.get("I4MOE_HOST_INT")
         for rep in range(reps + 3):  # the arms interleaved, so they see the same machine state
             for name, routes in arms.items():
-                if name == "host_only_float":
-                    os.environ["I4MOE_HOST_INT"] = "0"
+                if name in forced:
+                    os.environ["I4MOE_HOST_INT"] = forced[name]
                 elif prev is None:
                     os.environ.pop("I4MOE_HOST_INT", None)
                 else:

@@ -368,9 +368,11 @@ int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const
                     const float *x, float *P, int threads);
 
 /* 1 when the CPU tier's dot products take the integer path on this host (AVX-512 F, BW, VL and
- * VNNI present and I4MOE_HOST_INT is not "0" in the environment), else 0.  Tensors whose group
- * size is not a multiple of 64 take the float32 path on any host.  The environment is read at
- * every call, here and in the CPU tier. */
+ * VNNI present and I4MOE_HOST_INT is not "0" in the environment), else 0.  The integer path
+ * handles two 64-column blocks per 512-bit instruction where the groups allow (per-row, gs 64,
+ * gs a multiple of 128; I4MOE_HOST_INT=256 keeps it at 256 bits); both widths give the same
+ * bits.  Tensors whose group size is not a multiple of 64 take the float32 path on any host.
+ * The environment is read at every call, here and in the CPU tier. */
 int i4moe_host_int_path(void);
 
 /* ---- profiling ---------------------------------------------------------------------------- */

@@ -183,29 +183,40 @@ inline float row_dot(const HostTensor &T, int o, const float *x) {
 // every term an exact integer: vpdpbusd multiplies the unsigned nibbles by the signed digits,
 // four products per int32 lane, and the second sum is the lanes' start value.  A 64-column
 // block is 32 weight bytes: the low nibbles hold its even columns, the high nibbles its odd
-// ones, so each digit row is stored per block as the even columns' 32 digits, then the odd
-// columns' 32; int32 lane L of a block then takes the columns 8 L .. 8 L + 7.
+// ones; int32 lane L of a block takes the columns 8 L .. 8 L + 7.  The digit rows are stored
+// in superblocks of two blocks (the 64 weight bytes of one 512-bit load): for each digit, the
+// even columns' digits of both blocks (2 x 32 bytes), then their odd columns' digits, so one
+// 512-bit operand covers two blocks and one 256-bit operand one block.  The start values are
+// laid out the same way: per superblock and digit, 8 lanes of each block.
 
 constexpr int kBlockCols = 64;
 constexpr int kPlanes = 3;
-constexpr int kBlockBytes = kPlanes * kBlockCols;  // digit bytes per block
-constexpr int kLanes = 8;                          // int32 lanes of a 256-bit register
-constexpr int kLaneInts = kPlanes * kLanes;        // start values per block
+constexpr int kSuperBytes = 2 * kPlanes * kBlockCols;  // digit bytes per superblock
+constexpr int kLanes = 8;                              // int32 lanes of a 256-bit register
+constexpr int kLaneInts = kPlanes * kLanes;            // start values per block
 
 struct DigitRow {
-  int E = 0, nb = 0;
-  std::vector<int8_t> dig;   // nb blocks x 3 digits x (32 even, 32 odd columns)
-  std::vector<int32_t> neg;  // nb x 3 x 8: -8 x (the sum of lane L's eight digits), per block and digit
-  std::vector<int32_t> pre;  // (nb + 1) x 3 x 8: the sums of neg over the blocks before
+  int E = 0, nb = 0;         // nb blocks, stored as (nb + 1) / 2 superblocks
+  std::vector<int8_t> dig;   // per superblock and digit: 64 even-column, then 64 odd-column digits
+  std::vector<int32_t> neg;  // per superblock and digit: 2 x 8 lanes of -8 x (the lane's eight digits)
+  std::vector<int32_t> pre;  // (nb + 1) x 3 x 8: the sums of each block's start values over the blocks before
 };
+
+// Offsets of block b's pieces: digit n's even (odd = 1: odd) columns, in bytes of dig, and its
+// start values, in ints of neg.
+inline size_t dig_at(int b, int n, int odd) {
+  return (size_t)(b >> 1) * kSuperBytes + n * 2 * kBlockCols + odd * kBlockCols + (b & 1) * 32;
+}
+inline size_t neg_at(int b, int n) { return ((size_t)(b >> 1) * kPlanes + n) * 2 * kLanes + (b & 1) * kLanes; }
 
 #define I4MOE_VNNI __attribute__((target("avx512f,avx512bw,avx512vl,avx512vnni,avx2,fma")))
 
 // The digit row of v (C columns), vectorised over a block at a time.
 I4MOE_VNNI void make_digit_row(const float *v, int C, DigitRow &r) {
   r.nb = (C + kBlockCols - 1) / kBlockCols;
-  r.dig.resize((size_t)r.nb * kBlockBytes);
-  r.neg.resize((size_t)r.nb * kLaneInts);
+  const int nsb = (r.nb + 1) / 2;
+  r.dig.assign((size_t)nsb * kSuperBytes, 0);  // a missing second block of the last superblock stays zero
+  r.neg.assign((size_t)nsb * 2 * kLaneInts, 0);
   r.pre.resize((size_t)(r.nb + 1) * kLaneInts);
   __m512 mx = _mm512_setzero_ps();
   for (int c = 0; c < C; c += 16) {
@@ -221,8 +232,8 @@ I4MOE_VNNI void make_digit_row(const float *v, int C, DigitRow &r) {
   const __m512i evens_odds = _mm512_setr_epi32(0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15);
   const __m512i bias = _mm512_set1_epi32(0x808080);
   const __m256i ones = _mm256_set1_epi8(1);
+  int8_t *dig = r.dig.data();
   for (int b = 0; b < r.nb; ++b) {
-    int8_t *dst = r.dig.data() + (size_t)b * kBlockBytes;
     for (int i = 0; i < 4; ++i) {  // 16 columns at a time
       const int c = b * kBlockCols + 16 * i;
       const __mmask16 k = c >= C ? (__mmask16)0 : C - c >= 16 ? (__mmask16)0xffff : (__mmask16)((1u << (C - c)) - 1u);
@@ -234,26 +245,30 @@ I4MOE_VNNI void make_digit_row(const float *v, int C, DigitRow &r) {
       const __m512i u = _mm512_permutexvar_epi32(evens_odds, _mm512_xor_si512(_mm512_add_epi32(X, bias), bias));
       for (int n = 0; n < kPlanes; ++n) {
         const __m128i d = _mm512_cvtepi32_epi8(_mm512_srli_epi32(u, 8 * n));  // 8 even, then 8 odd digits
-        _mm_storel_epi64(reinterpret_cast<__m128i *>(dst + n * kBlockCols + 8 * i), d);
-        _mm_storel_epi64(reinterpret_cast<__m128i *>(dst + n * kBlockCols + 32 + 8 * i), _mm_srli_si128(d, 8));
+        _mm_storel_epi64(reinterpret_cast<__m128i *>(dig + dig_at(b, n, 0) + 8 * i), d);
+        _mm_storel_epi64(reinterpret_cast<__m128i *>(dig + dig_at(b, n, 1) + 8 * i), _mm_srli_si128(d, 8));
       }
     }
     for (int n = 0; n < kPlanes; ++n) {
-      const __m256i e = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + n * kBlockCols));
-      const __m256i o = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dst + n * kBlockCols + 32));
+      const __m256i e = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dig + dig_at(b, n, 0)));
+      const __m256i o = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(dig + dig_at(b, n, 1)));
       const __m256i sum = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(_mm256_setzero_si256(), ones, e), ones, o);
-      _mm256_storeu_si256(reinterpret_cast<__m256i *>(r.neg.data() + (size_t)b * kLaneInts + n * kLanes),
+      _mm256_storeu_si256(reinterpret_cast<__m256i *>(r.neg.data() + neg_at(b, n)),
                           _mm256_sub_epi32(_mm256_setzero_si256(), _mm256_slli_epi32(sum, 3)));
     }
   }
   std::fill(r.pre.begin(), r.pre.begin() + kLaneInts, 0);
   for (int b = 0; b < r.nb; ++b)
-    for (int i = 0; i < kLaneInts; ++i)
-      r.pre[(size_t)(b + 1) * kLaneInts + i] = r.pre[(size_t)b * kLaneInts + i] + r.neg[(size_t)b * kLaneInts + i];
+    for (int n = 0; n < kPlanes; ++n)
+      for (int l = 0; l < kLanes; ++l)
+        r.pre[((size_t)(b + 1) * kPlanes + n) * kLanes + l] =
+            r.pre[((size_t)b * kPlanes + n) * kLanes + l] + r.neg[neg_at(b, n) + l];
 }
 
 // The integer path takes tensors whose groups are whole blocks (per-row, or gs a multiple of 64).
 inline bool vnni_fits(const HostTensor &T) { return T.ng == 1 || T.gs % kBlockCols == 0; }
+
+I4MOE_VNNI inline __m256i ld256(const void *p) { return _mm256_loadu_si256(reinterpret_cast<const __m256i *>(p)); }
 
 // The 32 weight bytes of block b of a row of rb bytes (zero past the row's end).
 I4MOE_VNNI inline __m256i weight_block(const uint8_t *row, int b, int rb) {
@@ -289,16 +304,18 @@ I4MOE_VNNI inline void join_wide(__m256i a0, __m256i a1, __m256i a2, double sc, 
 // sums; the eight lanes added in a fixed order, times 2^-E.  Row r's result takes the same steps
 // whatever NR is, so it does not depend on which rows share the call.
 template <int NR>
-I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow *const *x, double *res) {
+I4MOE_VNNI inline void row_dots_256(const HostTensor &T, int o, const DigitRow *const *x, double *res) {
   const uint8_t *row = T.packed.data() + (size_t)o * (T.C / 2);
   const float *s = T.scales.data() + (size_t)o * T.ng;
   const int rb = T.C / 2, nb = x[0]->nb;
   const __m256i low = _mm256_set1_epi8(0x0F);
-  const __m256i *dig[NR], *neg[NR], *pre[NR];
+  const int8_t *dig[NR];
+  const int32_t *neg[NR];
+  const __m256i *pre[NR];
   __m256d s0[NR], s1[NR];
   for (int r = 0; r < NR; ++r) {
-    dig[r] = reinterpret_cast<const __m256i *>(x[r]->dig.data());
-    neg[r] = reinterpret_cast<const __m256i *>(x[r]->neg.data());
+    dig[r] = x[r]->dig.data();
+    neg[r] = x[r]->neg.data();
     pre[r] = reinterpret_cast<const __m256i *>(x[r]->pre.data());
     s0[r] = s1[r] = _mm256_setzero_pd();
   }
@@ -310,13 +327,12 @@ I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow 
       const __m256i w = weight_block(row, b, rb);
       const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
       for (int r = 0; r < NR; ++r) {
-        const __m256i *d = dig[r] + 6 * b;
-        a0[r] = _mm256_dpbusd_epi32(a0[r], lo, _mm256_loadu_si256(d + 0));
-        b0[r] = _mm256_dpbusd_epi32(b0[r], hi, _mm256_loadu_si256(d + 1));
-        a1[r] = _mm256_dpbusd_epi32(a1[r], lo, _mm256_loadu_si256(d + 2));
-        b1[r] = _mm256_dpbusd_epi32(b1[r], hi, _mm256_loadu_si256(d + 3));
-        a2[r] = _mm256_dpbusd_epi32(a2[r], lo, _mm256_loadu_si256(d + 4));
-        b2[r] = _mm256_dpbusd_epi32(b2[r], hi, _mm256_loadu_si256(d + 5));
+        a0[r] = _mm256_dpbusd_epi32(a0[r], lo, ld256(dig[r] + dig_at(b, 0, 0)));
+        b0[r] = _mm256_dpbusd_epi32(b0[r], hi, ld256(dig[r] + dig_at(b, 0, 1)));
+        a1[r] = _mm256_dpbusd_epi32(a1[r], lo, ld256(dig[r] + dig_at(b, 1, 0)));
+        b1[r] = _mm256_dpbusd_epi32(b1[r], hi, ld256(dig[r] + dig_at(b, 1, 1)));
+        a2[r] = _mm256_dpbusd_epi32(a2[r], lo, ld256(dig[r] + dig_at(b, 2, 0)));
+        b2[r] = _mm256_dpbusd_epi32(b2[r], hi, ld256(dig[r] + dig_at(b, 2, 1)));
       }
     }
     for (int r = 0; r < NR; ++r) {
@@ -333,14 +349,15 @@ I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow 
       const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
       const double sc = (double)s[b];
       for (int r = 0; r < NR; ++r) {
-        const __m256i *d = dig[r] + 6 * b;
-        const __m256i *z = neg[r] + kPlanes * b;
         const __m256i a0 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 0), lo, _mm256_loadu_si256(d + 0)), hi, _mm256_loadu_si256(d + 1));
+            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 0)), lo, ld256(dig[r] + dig_at(b, 0, 0))), hi,
+            ld256(dig[r] + dig_at(b, 0, 1)));
         const __m256i a1 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 1), lo, _mm256_loadu_si256(d + 2)), hi, _mm256_loadu_si256(d + 3));
+            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 1)), lo, ld256(dig[r] + dig_at(b, 1, 0))), hi,
+            ld256(dig[r] + dig_at(b, 1, 1)));
         const __m256i a2 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(_mm256_loadu_si256(z + 2), lo, _mm256_loadu_si256(d + 4)), hi, _mm256_loadu_si256(d + 5));
+            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 2)), lo, ld256(dig[r] + dig_at(b, 2, 0))), hi,
+            ld256(dig[r] + dig_at(b, 2, 1)));
         join_narrow(a0, a1, a2, sc, s0[r], s1[r]);
       }
     }
@@ -359,10 +376,12 @@ I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow 
         const __m256i w = weight_block(row, b, rb);
         const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
         for (int r = 0; r < NR; ++r) {
-          const __m256i *d = dig[r] + 6 * b;
-          a0[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a0[r], lo, _mm256_loadu_si256(d + 0)), hi, _mm256_loadu_si256(d + 1));
-          a1[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a1[r], lo, _mm256_loadu_si256(d + 2)), hi, _mm256_loadu_si256(d + 3));
-          a2[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a2[r], lo, _mm256_loadu_si256(d + 4)), hi, _mm256_loadu_si256(d + 5));
+          a0[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a0[r], lo, ld256(dig[r] + dig_at(b, 0, 0))), hi,
+                                      ld256(dig[r] + dig_at(b, 0, 1)));
+          a1[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a1[r], lo, ld256(dig[r] + dig_at(b, 1, 0))), hi,
+                                      ld256(dig[r] + dig_at(b, 1, 1)));
+          a2[r] = _mm256_dpbusd_epi32(_mm256_dpbusd_epi32(a2[r], lo, ld256(dig[r] + dig_at(b, 2, 0))), hi,
+                                      ld256(dig[r] + dig_at(b, 2, 1)));
         }
       }
       for (int r = 0; r < NR; ++r) {
@@ -382,6 +401,148 @@ I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow 
   }
 }
 
+inline const __m512i *at512(const void *p) { return reinterpret_cast<const __m512i *>(p); }
+
+// The 64 weight bytes of superblock sb of a row of rb bytes (zero past the row's end).
+I4MOE_VNNI inline __m512i weight_super(const uint8_t *row, int sb, int rb) {
+  const int rest = rb - 64 * sb;
+  return rest >= 64 ? _mm512_loadu_si512(row + 64 * sb)
+                    : _mm512_maskz_loadu_epi8((__mmask64)((1ull << rest) - 1ull), row + 64 * sb);
+}
+
+// The two blocks' lanes of a 512-bit accumulator added lane by lane (exact in int32).
+I4MOE_VNNI inline __m256i fold(__m512i a) {
+  return _mm256_add_epi32(_mm512_castsi512_si256(a), _mm512_extracti64x4_epi64(a, 1));
+}
+
+// The same dot products as row_dots_256, two blocks per 512-bit instruction, for per-row tensors
+// and group sizes 64 and multiples of 128 (a group never splits a superblock).  Every integer
+// lane sum is exact and every double operation happens in the same order as in row_dots_256
+// (a 64-column group's two blocks join one after the other), so the results are the same bits.
+template <int NR>
+I4MOE_VNNI inline void row_dots_512(const HostTensor &T, int o, const DigitRow *const *x, double *res) {
+  const uint8_t *row = T.packed.data() + (size_t)o * (T.C / 2);
+  const float *s = T.scales.data() + (size_t)o * T.ng;
+  const int rb = T.C / 2, nb = x[0]->nb, nsb = (nb + 1) / 2;
+  const __m512i low = _mm512_set1_epi8(0x0F);
+  const int8_t *dig[NR];
+  const int32_t *neg[NR];
+  const __m256i *pre[NR];
+  __m256d s0[NR], s1[NR];
+  for (int r = 0; r < NR; ++r) {
+    dig[r] = x[r]->dig.data();
+    neg[r] = x[r]->neg.data();
+    pre[r] = reinterpret_cast<const __m256i *>(x[r]->pre.data());
+    s0[r] = s1[r] = _mm256_setzero_pd();
+  }
+  if (T.ng == 1) {
+    __m512i a0[NR], a1[NR], a2[NR], b0[NR], b1[NR], b2[NR];
+    for (int r = 0; r < NR; ++r) a0[r] = a1[r] = a2[r] = b0[r] = b1[r] = b2[r] = _mm512_setzero_si512();
+    for (int sb = 0; sb < nsb; ++sb) {
+      const __m512i w = weight_super(row, sb, rb);
+      const __m512i lo = _mm512_and_si512(w, low), hi = _mm512_and_si512(_mm512_srli_epi16(w, 4), low);
+      for (int r = 0; r < NR; ++r) {
+        const int8_t *d = dig[r] + (size_t)sb * kSuperBytes;
+        a0[r] = _mm512_dpbusd_epi32(a0[r], lo, _mm512_loadu_si512(d + 0));
+        b0[r] = _mm512_dpbusd_epi32(b0[r], hi, _mm512_loadu_si512(d + 64));
+        a1[r] = _mm512_dpbusd_epi32(a1[r], lo, _mm512_loadu_si512(d + 128));
+        b1[r] = _mm512_dpbusd_epi32(b1[r], hi, _mm512_loadu_si512(d + 192));
+        a2[r] = _mm512_dpbusd_epi32(a2[r], lo, _mm512_loadu_si512(d + 256));
+        b2[r] = _mm512_dpbusd_epi32(b2[r], hi, _mm512_loadu_si512(d + 320));
+      }
+    }
+    for (int r = 0; r < NR; ++r) {
+      const __m256i *p = pre[r] + kPlanes * nb;
+      join_wide(_mm256_add_epi32(_mm256_add_epi32(fold(a0[r]), fold(b0[r])), _mm256_loadu_si256(p + 0)),
+                _mm256_add_epi32(_mm256_add_epi32(fold(a1[r]), fold(b1[r])), _mm256_loadu_si256(p + 1)),
+                _mm256_add_epi32(_mm256_add_epi32(fold(a2[r]), fold(b2[r])), _mm256_loadu_si256(p + 2)), (double)s[0],
+                s0[r], s1[r]);
+    }
+  } else if (T.gs == kBlockCols) {
+    for (int sb = 0; sb < nsb; ++sb) {
+      const __m512i w = weight_super(row, sb, rb);
+      const __m512i lo = _mm512_and_si512(w, low), hi = _mm512_and_si512(_mm512_srli_epi16(w, 4), low);
+      const bool both = 2 * sb + 1 < nb;
+      const double sc0 = (double)s[2 * sb], sc1 = both ? (double)s[2 * sb + 1] : 0.0;
+      for (int r = 0; r < NR; ++r) {
+        const int8_t *d = dig[r] + (size_t)sb * kSuperBytes;
+        const int32_t *z = neg[r] + (size_t)sb * 2 * kLaneInts;
+        const __m512i a0 =
+            _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(_mm512_loadu_si512(z + 0), lo, _mm512_loadu_si512(d + 0)), hi,
+                                _mm512_loadu_si512(d + 64));
+        const __m512i a1 =
+            _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(_mm512_loadu_si512(z + 16), lo, _mm512_loadu_si512(d + 128)), hi,
+                                _mm512_loadu_si512(d + 192));
+        const __m512i a2 =
+            _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(_mm512_loadu_si512(z + 32), lo, _mm512_loadu_si512(d + 256)), hi,
+                                _mm512_loadu_si512(d + 320));
+        const __m512i j = _mm512_add_epi32(_mm512_add_epi32(a0, _mm512_slli_epi32(a1, 8)), _mm512_slli_epi32(a2, 16));
+        // block 2 sb, then block 2 sb + 1: the order of the 256-bit form
+        const __m256i jl = _mm512_castsi512_si256(j), jh = _mm512_extracti64x4_epi64(j, 1);
+        const __m256d k0 = _mm256_set1_pd(sc0);
+        s0[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(jl)), k0, s0[r]);
+        s1[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(jl, 1)), k0, s1[r]);
+        if (both) {
+          const __m256d k1 = _mm256_set1_pd(sc1);
+          s0[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(jh)), k1, s0[r]);
+          s1[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(jh, 1)), k1, s1[r]);
+        }
+      }
+    }
+  } else {
+    // groups of gs / 128 superblocks (the last one may be narrower)
+    const int gsb = T.gs / (2 * kBlockCols), gb = T.gs / kBlockCols;
+    for (int g = 0, g0 = 0; g0 < nsb; ++g, g0 += gsb) {
+      const int g1 = g0 + gsb < nsb ? g0 + gsb : nsb;
+      const int b0 = 2 * g0, b1 = 2 * g1 < nb ? 2 * g1 : nb;
+      __m512i a0[NR], a1[NR], a2[NR];
+      for (int r = 0; r < NR; ++r) a0[r] = a1[r] = a2[r] = _mm512_setzero_si512();
+      for (int sb = g0; sb < g1; ++sb) {
+        const __m512i w = weight_super(row, sb, rb);
+        const __m512i lo = _mm512_and_si512(w, low), hi = _mm512_and_si512(_mm512_srli_epi16(w, 4), low);
+        for (int r = 0; r < NR; ++r) {
+          const int8_t *d = dig[r] + (size_t)sb * kSuperBytes;
+          a0[r] = _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(a0[r], lo, _mm512_loadu_si512(d + 0)), hi,
+                                      _mm512_loadu_si512(d + 64));
+          a1[r] = _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(a1[r], lo, _mm512_loadu_si512(d + 128)), hi,
+                                      _mm512_loadu_si512(d + 192));
+          a2[r] = _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(a2[r], lo, _mm512_loadu_si512(d + 256)), hi,
+                                      _mm512_loadu_si512(d + 320));
+        }
+      }
+      for (int r = 0; r < NR; ++r) {
+        const __m256i c0 = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * b1 + 0), _mm256_loadu_si256(pre[r] + kPlanes * b0 + 0));
+        const __m256i c1 = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * b1 + 1), _mm256_loadu_si256(pre[r] + kPlanes * b0 + 1));
+        const __m256i c2 = _mm256_sub_epi32(_mm256_loadu_si256(pre[r] + kPlanes * b1 + 2), _mm256_loadu_si256(pre[r] + kPlanes * b0 + 2));
+        const __m256i A0 = _mm256_add_epi32(c0, fold(a0[r])), A1 = _mm256_add_epi32(c1, fold(a1[r])),
+                      A2 = _mm256_add_epi32(c2, fold(a2[r]));
+        if (gb <= 4)
+          join_narrow(A0, A1, A2, (double)s[g], s0[r], s1[r]);
+        else
+          join_wide(A0, A1, A2, (double)s[g], s0[r], s1[r]);
+      }
+    }
+  }
+  for (int r = 0; r < NR; ++r) {
+    alignas(32) double t[8];
+    _mm256_store_pd(t, s0[r]);
+    _mm256_store_pd(t + 4, s1[r]);
+    const double total = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    res[r] = std::ldexp(total, -x[r]->E);
+  }
+}
+
+// The tensors the 512-bit form takes: groups never split a superblock.
+inline bool fits_512(const HostTensor &T) { return T.ng == 1 || T.gs == kBlockCols || T.gs % (2 * kBlockCols) == 0; }
+
+template <int NR>
+I4MOE_VNNI inline void row_dots_vnni(const HostTensor &T, int o, const DigitRow *const *x, double *res, bool wide) {
+  if (wide && fits_512(T))
+    row_dots_512<NR>(T, o, x, res);
+  else
+    row_dots_256<NR>(T, o, x, res);
+}
+
 // The host rows of one expert, in route order.
 struct HostEntry {
   const HostExpert *e;
@@ -393,12 +554,12 @@ constexpr int kMaxShare = 4;  // activation rows that share one pass over a weig
 // Gate, up and the SiLU-gated product of output o for the entry's rows rk[0 .. NR).
 template <int NR>
 I4MOE_VNNI void gate_up_rows(const HostEntry &en, const int *rk, int o, const std::vector<HostRow> &rows,
-                             const std::vector<DigitRow> &xd, int I, float *h) {
+                             const std::vector<DigitRow> &xd, int I, float *h, bool wide) {
   const DigitRow *xs[NR];
   for (int r = 0; r < NR; ++r) xs[r] = &xd[rows[rk[r]].token];
   double g[NR], u[NR];
-  row_dots_vnni<NR>(en.e->gate, o, xs, g);
-  row_dots_vnni<NR>(en.e->up, o, xs, u);
+  row_dots_vnni<NR>(en.e->gate, o, xs, g, wide);
+  row_dots_vnni<NR>(en.e->up, o, xs, u, wide);
   for (int r = 0; r < NR; ++r) {
     const float gf = (float)g[r], uf = (float)u[r];
     h[(size_t)rk[r] * I + o] = gf / (1.f + std::exp(-gf)) * uf;
@@ -407,11 +568,12 @@ I4MOE_VNNI void gate_up_rows(const HostEntry &en, const int *rk, int o, const st
 
 // Output d of the down projection for the entry's rows rk[0 .. NR).
 template <int NR>
-I4MOE_VNNI void down_rows(const HostEntry &en, const int *rk, int d, const std::vector<DigitRow> &hd, int D, float *y) {
+I4MOE_VNNI void down_rows(const HostEntry &en, const int *rk, int d, const std::vector<DigitRow> &hd, int D, float *y,
+                          bool wide) {
   const DigitRow *hs[NR];
   for (int r = 0; r < NR; ++r) hs[r] = &hd[rk[r]];
   double v[NR];
-  row_dots_vnni<NR>(en.e->down, d, hs, v);
+  row_dots_vnni<NR>(en.e->down, d, hs, v, wide);
   for (int r = 0; r < NR; ++r) y[(size_t)rk[r] * D + d] = (float)v[r];
 }
 
@@ -423,24 +585,24 @@ inline void for_chunks(const HostEntry &en, F &&f) {
 }
 
 I4MOE_VNNI void gate_up_entry(const HostEntry &en, int o, const std::vector<HostRow> &rows,
-                              const std::vector<DigitRow> &xd, int I, float *h) {
+                              const std::vector<DigitRow> &xd, int I, float *h, bool wide) {
   for_chunks(en, [&](const int *rk, int nr) {
     switch (nr) {
-      case 1: gate_up_rows<1>(en, rk, o, rows, xd, I, h); break;
-      case 2: gate_up_rows<2>(en, rk, o, rows, xd, I, h); break;
-      case 3: gate_up_rows<3>(en, rk, o, rows, xd, I, h); break;
-      default: gate_up_rows<4>(en, rk, o, rows, xd, I, h); break;
+      case 1: gate_up_rows<1>(en, rk, o, rows, xd, I, h, wide); break;
+      case 2: gate_up_rows<2>(en, rk, o, rows, xd, I, h, wide); break;
+      case 3: gate_up_rows<3>(en, rk, o, rows, xd, I, h, wide); break;
+      default: gate_up_rows<4>(en, rk, o, rows, xd, I, h, wide); break;
     }
   });
 }
 
-I4MOE_VNNI void down_entry(const HostEntry &en, int d, const std::vector<DigitRow> &hd, int D, float *y) {
+I4MOE_VNNI void down_entry(const HostEntry &en, int d, const std::vector<DigitRow> &hd, int D, float *y, bool wide) {
   for_chunks(en, [&](const int *rk, int nr) {
     switch (nr) {
-      case 1: down_rows<1>(en, rk, d, hd, D, y); break;
-      case 2: down_rows<2>(en, rk, d, hd, D, y); break;
-      case 3: down_rows<3>(en, rk, d, hd, D, y); break;
-      default: down_rows<4>(en, rk, d, hd, D, y); break;
+      case 1: down_rows<1>(en, rk, d, hd, D, y, wide); break;
+      case 2: down_rows<2>(en, rk, d, hd, D, y, wide); break;
+      case 3: down_rows<3>(en, rk, d, hd, D, y, wide); break;
+      default: down_rows<4>(en, rk, d, hd, D, y, wide); break;
     }
   });
 }
@@ -467,7 +629,13 @@ const bool kVnni = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("
 
 bool host_int_path_available() {
   const char *env = std::getenv("I4MOE_HOST_INT");
-  return kVnni && !(env && env[0] == '0');
+  return kVnni && !(env && env[0] == '0' && env[1] == 0);
+}
+
+// I4MOE_HOST_INT=256 keeps the integer path at 256 bits.
+static bool host_int_512() {
+  const char *env = std::getenv("I4MOE_HOST_INT");
+  return !(env && std::strcmp(env, "256") == 0);
 }
 
 void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const float *x, int D, int I, float *P) {
@@ -477,6 +645,7 @@ void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const f
   for (const HostRow &r : rows) use_int = use_int && vnni_fits(r.e->gate) && vnni_fits(r.e->up) && vnni_fits(r.e->down);
   std::vector<float> h((size_t)n * I), y((size_t)n * D);
   if (use_int) {
+    const bool wide = host_int_512();
     // the rows grouped by expert (first appearance order), so that a weight row is read once
     // for all the rows of its expert
     std::vector<HostEntry> ent;
@@ -502,14 +671,15 @@ void host_rows_forward(HostPool &pool, const std::vector<HostRow> &rows, const f
         if (used[t]) make_digit_row(x + (size_t)t * D, D, xd[t]);
     });
     pool.run(cum_i.back(), [&](long b, long e) {
-      for_outputs(ent, cum_i, I, b, e, [&](const HostEntry &en, int o) { gate_up_entry(en, o, rows, xd, I, h.data()); });
+      for_outputs(ent, cum_i, I, b, e,
+                  [&](const HostEntry &en, int o) { gate_up_entry(en, o, rows, xd, I, h.data(), wide); });
     });
     // the digit rows of h, then down
     pool.run(n, [&](long b, long e) {
       for (long k = b; k < e; ++k) make_digit_row(h.data() + (size_t)k * I, I, hd[k]);
     });
     pool.run(cum_d.back(), [&](long b, long e) {
-      for_outputs(ent, cum_d, D, b, e, [&](const HostEntry &en, int d) { down_entry(en, d, hd, D, y.data()); });
+      for_outputs(ent, cum_d, D, b, e, [&](const HostEntry &en, int d) { down_entry(en, d, hd, D, y.data(), wide); });
     });
   } else {
     // gate and up, SiLU-gated product: one (row, output) pair per index

@@ -145,3 +145,19 @@ def test_host_rows_shared_expert_same_bits_as_alone(lib, D, I, formats, gs):
         assert np.array_equal(P[t], alone[0]), t
         ref = oracle.expert_forward(ex[e].gate, ex[e].up, ex[e].down, x[t].astype(np.float64))[3]
         assert normwise_err(P[t], ref) < 1e-5, t
+
+
+@pytest.mark.parametrize("D,I,formats,gs", SHAPES[:4])
+def test_host_int_widths_same_bits(lib, monkeypatch, D, I, formats, gs):
+    """The integer path's 512-bit form (per-row, g64 and multiples of 128) and its 256-bit form
+    (I4MOE_HOST_INT=256) do the same integer sums and the same double operations in the same
+    order: the same bits, shared experts included."""
+    from int4_grouped_expert_router_amd import binding as B
+    from int4_grouped_expert_router_amd import host_rows
+    monkeypatch.delenv("I4MOE_HOST_INT", raising=False)
+    if not B.i4moe_host_int_path():
+        pytest.skip("no AVX-512 VNNI on this host")
+    cfg, x, rows, ref = shaped_case(D, I, formats, gs)
+    wide = host_rows(4, D, I, rows, x, threads=3)
+    monkeypatch.setenv("I4MOE_HOST_INT", "256")
+    assert np.array_equal(host_rows(4, D, I, rows, x, threads=2), wide)
