@@ -161,3 +161,18 @@ def test_host_int_widths_same_bits(lib, monkeypatch, D, I, formats, gs):
     wide = host_rows(4, D, I, rows, x, threads=3)
     monkeypatch.setenv("I4MOE_HOST_INT", "256")
     assert np.array_equal(host_rows(4, D, I, rows, x, threads=2), wide)
+
+
+@pytest.mark.parametrize("path", ["int", "float"])
+def test_host_rows_nonfinite_x_is_not_an_error(lib, monkeypatch, path):
+    """Non-finite activations give unspecified values (the header says so), never an error or
+    a fault, on either path; the other tokens' rows are unaffected."""
+    from int4_grouped_expert_router_amd import host_rows
+    monkeypatch.setenv("I4MOE_HOST_INT", "1" if path == "int" else "0")
+    cfg, x, rows, ref = shaped_case(1000, 392, "group", 64)
+    clean = host_rows(4, 1000, 392, rows, x, threads=2)
+    xb = x.copy()
+    xb[1, 3], xb[1, 700] = np.nan, np.inf
+    P = host_rows(4, 1000, 392, rows, xb, threads=2)
+    for t in (0, 2, 3):  # token 1 alone has the bad values
+        assert np.array_equal(P[t], clean[t]), t
