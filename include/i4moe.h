@@ -335,10 +335,11 @@ typedef struct {
  * product on the CPU: on a host with AVX-512 VNNI, when every host tensor is per-row or has a
  * group size that is a multiple of 64 (see i4moe_host_int_path), the activation row (x, or a row
  * of the gated product h) is taken in 24-bit fixed point with a power-of-two exponent of its own
- * and each group's sum is an exact integer, scaled in double; otherwise each group's products
- * are summed in float32, then scaled.  SiLU and the gated product are float32 either way.  i4moe_expert_group_take then joins both slots in
- * issue order (the device slot first), so the sum order is fixed and the result bitwise
- * reproducible [PR434].
+ * and each group's sum is an exact integer, scaled in float32 lanes (gs 64) or in double
+ * (other group sizes, per-row); otherwise each group's products are summed in float32, then
+ * scaled.  SiLU and the gated product are float32 either way.  i4moe_expert_group_take then
+ * joins both slots in issue order (the device slot first), so the sum order is fixed and the
+ * result bitwise reproducible [PR434].
  * x_dev ([S][D], F32 or BF16) is copied to the host on the stream before the device group's
  * kernels are enqueued; the CPU rows start on a helper thread of the context when that copy has
  * landed, while the calling thread enqueues the device group, and the call returns when the CPU

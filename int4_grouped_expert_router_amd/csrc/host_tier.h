@@ -89,7 +89,8 @@ struct HostRow {
 //  * integer (hosts with AVX-512 VNNI, when every tensor is per-row or its group size a multiple
 //    of 64): the activation row (x_t, or one row of h) in 24-bit fixed point with its own
 //    power-of-two exponent, as three int8 digits; each group's sum an exact integer, times its
-//    scale in double, rounded to float32 at the end;
+//    scale (groups of 64 columns: in float32 lane sums, even and odd groups apart; otherwise in
+//    double), the lanes added in double, rounded to float32 at the end;
 //  * float32 (otherwise, or with I4MOE_HOST_INT=0 in the environment): each group's products
 //    summed, then scaled: in column order, or, on a host with AVX2 and FMA, 32 columns at a time
 //    in four 8-wide partial sums added in a fixed order.

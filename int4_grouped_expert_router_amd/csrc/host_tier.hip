@@ -299,9 +299,34 @@ I4MOE_VNNI inline void join_wide(__m256i a0, __m256i a1, __m256i a2, double sc, 
   s1 = _mm256_fmadd_pd(hi, k, s1);
 }
 
+// One 64-column block of a g64 row against NR digit rows: the exact lanes of its group,
+// rounded to float32, times the group's scale sc, into the float32 lane sums e.
+template <int NR>
+I4MOE_VNNI inline void g64_block(const uint8_t *row, int b, int rb, float sc, const int8_t *const (&dig)[NR],
+                                 const int32_t *const (&neg)[NR], __m256 (&e)[NR]) {
+  const __m256i low = _mm256_set1_epi8(0x0F);
+  const __m256i w = weight_block(row, b, rb);
+  const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
+  const __m256 k = _mm256_set1_ps(sc);
+  for (int r = 0; r < NR; ++r) {
+    const __m256i a0 = _mm256_dpbusd_epi32(
+        _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 0)), lo, ld256(dig[r] + dig_at(b, 0, 0))), hi,
+        ld256(dig[r] + dig_at(b, 0, 1)));
+    const __m256i a1 = _mm256_dpbusd_epi32(
+        _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 1)), lo, ld256(dig[r] + dig_at(b, 1, 0))), hi,
+        ld256(dig[r] + dig_at(b, 1, 1)));
+    const __m256i a2 = _mm256_dpbusd_epi32(
+        _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 2)), lo, ld256(dig[r] + dig_at(b, 2, 0))), hi,
+        ld256(dig[r] + dig_at(b, 2, 1)));
+    const __m256i j = _mm256_add_epi32(_mm256_add_epi32(a0, _mm256_slli_epi32(a1, 8)), _mm256_slli_epi32(a2, 16));
+    e[r] = _mm256_fmadd_ps(_mm256_cvtepi32_ps(j), k, e[r]);
+  }
+}
+
 // One output row of T against NR digit rows x[r] (each weight block loaded once for all of
-// them): per row, each group's exact integer lanes, times the group's scale, into double lane
-// sums; the eight lanes added in a fixed order, times 2^-E.  Row r's result takes the same steps
+// them), 256 bits at a time: per row, each group's exact integer lanes, times the group's scale,
+// into lane sums (double; float32 for groups of 64 columns, even and odd blocks apart); the
+// eight lanes added in a fixed order in double, times 2^-E.  Row r's result takes the same steps
 // whatever NR is, so it does not depend on which rows share the call.
 template <int NR>
 I4MOE_VNNI inline void row_dots_256(const HostTensor &T, int o, const DigitRow *const *x, double *res) {
@@ -343,23 +368,21 @@ I4MOE_VNNI inline void row_dots_256(const HostTensor &T, int o, const DigitRow *
                 s1[r]);
     }
   } else if (T.gs == kBlockCols) {
-    // one block per group
-    for (int b = 0; b < nb; ++b) {
-      const __m256i w = weight_block(row, b, rb);
-      const __m256i lo = _mm256_and_si256(w, low), hi = _mm256_and_si256(_mm256_srli_epi16(w, 4), low);
-      const double sc = (double)s[b];
-      for (int r = 0; r < NR; ++r) {
-        const __m256i a0 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 0)), lo, ld256(dig[r] + dig_at(b, 0, 0))), hi,
-            ld256(dig[r] + dig_at(b, 0, 1)));
-        const __m256i a1 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 1)), lo, ld256(dig[r] + dig_at(b, 1, 0))), hi,
-            ld256(dig[r] + dig_at(b, 1, 1)));
-        const __m256i a2 = _mm256_dpbusd_epi32(
-            _mm256_dpbusd_epi32(ld256(neg[r] + neg_at(b, 2)), lo, ld256(dig[r] + dig_at(b, 2, 0))), hi,
-            ld256(dig[r] + dig_at(b, 2, 1)));
-        join_narrow(a0, a1, a2, sc, s0[r], s1[r]);
-      }
+    // one block per group: each block's exact lanes rounded to float32, times its scale, into
+    // float32 lane sums kept apart for the even and the odd blocks (the two halves of the
+    // 512-bit form), joined lane by lane at the end
+    __m256 e0[NR], e1[NR];
+    for (int r = 0; r < NR; ++r) e0[r] = e1[r] = _mm256_setzero_ps();
+    int b = 0;
+    for (; b + 1 < nb; b += 2) {
+      g64_block<NR>(row, b, rb, s[b], dig, neg, e0);
+      g64_block<NR>(row, b + 1, rb, s[b + 1], dig, neg, e1);
+    }
+    if (b < nb) g64_block<NR>(row, b, rb, s[b], dig, neg, e0);
+    for (int r = 0; r < NR; ++r) {
+      const __m256 t = _mm256_add_ps(e0[r], e1[r]);
+      s0[r] = _mm256_cvtps_pd(_mm256_castps256_ps128(t));
+      s1[r] = _mm256_cvtps_pd(_mm256_extractf128_ps(t, 1));
     }
   } else {
     // groups of several blocks (the last one may be narrower)
@@ -459,11 +482,17 @@ I4MOE_VNNI inline void row_dots_512(const HostTensor &T, int o, const DigitRow *
                 s0[r], s1[r]);
     }
   } else if (T.gs == kBlockCols) {
+    // lanes 0-7: the even block's lanes, 8-15: the odd block's, each with its own scale (the
+    // 256-bit form's two float32 sums)
+    __m512 e[NR];
+    for (int r = 0; r < NR; ++r) e[r] = _mm512_setzero_ps();
+    const __m512i halves = _mm512_setr_epi32(0, 0, 0, 0, 0, 0, 0, 0, 1, 1, 1, 1, 1, 1, 1, 1);
     for (int sb = 0; sb < nsb; ++sb) {
       const __m512i w = weight_super(row, sb, rb);
       const __m512i lo = _mm512_and_si512(w, low), hi = _mm512_and_si512(_mm512_srli_epi16(w, 4), low);
       const bool both = 2 * sb + 1 < nb;
-      const double sc0 = (double)s[2 * sb], sc1 = both ? (double)s[2 * sb + 1] : 0.0;
+      const __m512 sc = _mm512_permutexvar_ps(
+          halves, _mm512_castps128_ps512(_mm_setr_ps(s[2 * sb], both ? s[2 * sb + 1] : 0.f, 0.f, 0.f)));
       for (int r = 0; r < NR; ++r) {
         const int8_t *d = dig[r] + (size_t)sb * kSuperBytes;
         const int32_t *z = neg[r] + (size_t)sb * 2 * kLaneInts;
@@ -477,17 +506,15 @@ I4MOE_VNNI inline void row_dots_512(const HostTensor &T, int o, const DigitRow *
             _mm512_dpbusd_epi32(_mm512_dpbusd_epi32(_mm512_loadu_si512(z + 32), lo, _mm512_loadu_si512(d + 256)), hi,
                                 _mm512_loadu_si512(d + 320));
         const __m512i j = _mm512_add_epi32(_mm512_add_epi32(a0, _mm512_slli_epi32(a1, 8)), _mm512_slli_epi32(a2, 16));
-        // block 2 sb, then block 2 sb + 1: the order of the 256-bit form
-        const __m256i jl = _mm512_castsi512_si256(j), jh = _mm512_extracti64x4_epi64(j, 1);
-        const __m256d k0 = _mm256_set1_pd(sc0);
-        s0[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(jl)), k0, s0[r]);
-        s1[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(jl, 1)), k0, s1[r]);
-        if (both) {
-          const __m256d k1 = _mm256_set1_pd(sc1);
-          s0[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_castsi256_si128(jh)), k1, s0[r]);
-          s1[r] = _mm256_fmadd_pd(_mm256_cvtepi32_pd(_mm256_extracti128_si256(jh, 1)), k1, s1[r]);
-        }
+        const __m512 jf = _mm512_cvtepi32_ps(j);
+        e[r] = both ? _mm512_fmadd_ps(jf, sc, e[r]) : _mm512_mask3_fmadd_ps(jf, sc, e[r], (__mmask16)0x00ff);
       }
+    }
+    for (int r = 0; r < NR; ++r) {
+      const __m256 t = _mm256_add_ps(_mm512_castps512_ps256(e[r]),
+                                     _mm256_castpd_ps(_mm512_extractf64x4_pd(_mm512_castps_pd(e[r]), 1)));
+      s0[r] = _mm256_cvtps_pd(_mm256_castps256_ps128(t));
+      s1[r] = _mm256_cvtps_pd(_mm256_extractf128_ps(t, 1));
     }
   } else {
     // groups of gs / 128 superblocks (the last one may be narrower)
