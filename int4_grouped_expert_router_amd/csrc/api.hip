@@ -1768,6 +1768,7 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
   if (host) {
     // the previous tiered issue's upload of the host sum must have read it
     if (c->ev_p_recorded && (e = hipEventSynchronize(c->ev_p)) != hipSuccess) return hip_fail(c, e, "wait for upload");
+    c->pool->warm();  // the workers poll while x is on its way
     c->helper->post([&, S, D, I] {
       host_err = hipEventSynchronize(c->ev_x);
       t_x = clk::now();

@@ -41,6 +41,9 @@ class HostPool {
   HostPool &operator=(const HostPool &) = delete;
   int threads() const { return (int)workers_.size() + 1; }
   void run(long n, const std::function<void(long begin, long end)> &fn);
+  // Sleeping workers start polling again (for kSpinMicros), so a run that follows within that
+  // time finds them awake: call it ahead of a run whose inputs are still on their way.
+  void warm();
   static constexpr int kSpinMicros = 200;
 
  private:
@@ -50,7 +53,7 @@ class HostPool {
   std::condition_variable go_;
   const std::function<void(long, long)> *fn_ = nullptr;
   long n_ = 0;
-  std::atomic<unsigned> gen_{0};
+  std::atomic<unsigned> gen_{0}, wake_{0};
   std::atomic<int> pending_{0}, sleepers_{0};
   std::atomic<bool> stop_{false};
 };

@@ -27,9 +27,10 @@ void HostPool::work(int id) {
   unsigned seen = 0;
   for (;;) {
     // poll for a new run, then sleep: a worker counts itself in sleepers_ before it looks at
-    // gen_ under the lock, and run() bumps gen_ before it looks at sleepers_, so either the
-    // worker sees the run or run() wakes it
-    const auto until = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinMicros);
+    // gen_ (and wake_) under the lock, and run() (warm()) bumps gen_ (wake_) before it looks at
+    // sleepers_, so either the worker sees the change or it is woken; a warm() wake-up polls
+    // for another kSpinMicros
+    auto until = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinMicros);
     unsigned g;
     for (int i = 0;; ++i) {
       g = gen_.load();
@@ -38,8 +39,10 @@ void HostPool::work(int id) {
       if ((i & 255) == 255 && std::chrono::steady_clock::now() > until) {
         std::unique_lock<std::mutex> lk(m_);
         sleepers_.fetch_add(1);
-        go_.wait(lk, [&] { return stop_.load() || gen_.load() != seen; });
+        const unsigned w = wake_.load();
+        go_.wait(lk, [&] { return stop_.load() || gen_.load() != seen || wake_.load() != w; });
         sleepers_.fetch_sub(1);
+        until = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinMicros);
       }
     }
     if (stop_.load()) return;
@@ -48,6 +51,14 @@ void HostPool::work(int id) {
     const long n = n_;
     (*fn_)(n * id / T, n * (id + 1) / T);
     pending_.fetch_sub(1);
+  }
+}
+
+void HostPool::warm() {
+  wake_.fetch_add(1);  // before sleepers_ is read, as in run()
+  if (sleepers_.load() > 0) {
+    std::lock_guard<std::mutex> lk(m_);
+    go_.notify_all();
   }
 }
 
