@@ -111,6 +111,30 @@ def copy_calibration(torch, nbytes: int = 256 << 20, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def torch_read(torch, gib: float = 1.5, reps: int = 10):
+    """Context for the plain-read figure: what PyTorch's own kernels reach on the same GPU, a
+    float32 sum (reads the tensor once) and a device copy (reads and writes it), on a resident
+    tensor of `gib` GiB; one JSON line of GB/s."""
+    torch.cuda.set_device(0)
+    n = int(gib * (1 << 30)) // 4
+    t = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    u = torch.empty_like(t)
+    res = {"tensor_bytes": 4 * n}
+    for name, fn, nbytes in (("sum_f32", lambda: t.sum(), 4 * n), ("copy", lambda: u.copy_(t), 8 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[name + "_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(res), flush=True)
+
+
 def workload_text(cfg, layers):
     extra = f", top-p {cfg.topp}" if cfg.topp else ""
     return (f"{cfg.name}: D={cfg.D} I={cfg.I} E={cfg.E} top-{cfg.K} S={cfg.S}, {cfg.formats} int4 (gs={cfg.gs}), "
@@ -601,6 +625,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="measure the headline workload only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device copies (scale for the HBM byte counters)")
+    ap.add_argument("--torch-read", action="store_true",
+                    help="only time PyTorch's own sum and copy of a resident 1.5 GiB tensor (read-rate context)")
     ap.add_argument("--crossover", action="store_true",
                     help="only time explicit groups of 1..64 rows per expert under each launch mode")
     ap.add_argument("--crossover-rows", default="", help="comma-separated rows per expert (default: all)")
@@ -624,6 +650,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.torch_read:
+        torch_read(torch)
         return
     from int4_grouped_expert_router_amd import binding as B
     from synth import get_config
