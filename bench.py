@@ -277,7 +277,7 @@ def measure(name, layers, steps, warmup, torch, B, eager=False):
     pr_gu = gu_bytes / (probe["gate_up"][0] * 1e-3) / 1e9
     pr_dn = dn_bytes / (probe["down"][0] * 1e-3) / 1e9
     res["plain_read"] = {
-        "kernel": "k_read_probe: the same experts' nibbles and scales as contiguous 16-row blocks, "
+        "kernel": "k_read_probe: the same experts' nibbles and scales as contiguous ~16 KB row blocks, "
                   "no arithmetic (HIP events, as the kernels above)",
         "gate_up_GBps": round(pr_gu, 1), "gate_up_pct_hbm_peak": round(100 * pr_gu / HBM_PEAK_GBPS, 2),
         "down_GBps": round(pr_dn, 1), "down_pct_hbm_peak": round(100 * pr_dn / HBM_PEAK_GBPS, 2),

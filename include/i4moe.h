@@ -400,10 +400,11 @@ int i4moe_profile_query(i4moe_ctx *ctx, int kernel, double *total_ms, long long 
  * are measured by [LOG-tc, PR651]).  One launch on the context's stream that reads every nibble
  * and scale byte of the listed experts' tensors of the layer (tensor_mask bit 0 gate, 1 up,
  * 2 down; n_experts 1..I4MOE_MAX_ROWS indices into the layer's table, each bound on the device)
- * and computes nothing: one wave per 16 rows of a tensor, read as one contiguous block of
- * nibbles and one of scales with eight 16-byte loads per lane in flight; it writes nothing the
- * caller reads.  Timed as I4MOE_K_PROBE when profiling is on.  Errors: EINVAL (bad layer, mask,
- * list or expert), ENOMEM (its 256-byte scratch, allocated on the first call). */
+ * and computes nothing: one wave per tile of a tensor's rows (about 16 KB of nibbles), read
+ * as one contiguous block of nibbles and one of scales with sixteen 16-byte loads per lane in
+ * flight; it writes nothing the caller reads.  Timed as I4MOE_K_PROBE when profiling is on.
+ * Errors: EINVAL (bad layer, mask, list or expert), ENOMEM (its 256-byte scratch, allocated on
+ * the first call). */
 int i4moe_read_probe(i4moe_ctx *ctx, int layer, int tensor_mask, int n_experts, const int32_t *experts);
 
 #ifdef __cplusplus

@@ -1877,17 +1877,20 @@ int i4moe_read_probe(i4moe_ctx *c, int layer, int tensor_mask, int n_experts, co
     const hipError_t e = dalloc(&c->d_sink, 64 * sizeof(uint32_t));
     if (e != hipSuccess) return hip_fail(c, e, "hipMalloc(read probe sink)");
   }
-  constexpr int kProbeTileRows = 16;
+  // tiles of about one wave pass of nibbles: 16 loads of 16 bytes per lane
+  constexpr int kProbePassBytes = 16 * 16 * kWave;
   a.tab = L->d_tab;
   a.sink = c->d_sink;
   a.n_experts = n_experts;
-  a.tile_rows = kProbeTileRows;
   int per_e = 0;
   for (int n = 0; n < 3; ++n)
     if (tensor_mask & (1 << n)) {
-      const int O = n < 2 ? L->I : L->D;
+      const int O = n < 2 ? L->I : L->D, C = n < 2 ? L->D : L->I;
+      const int row_bytes = (C / 2 + 15) / 16 * 16;
+      const int tr = std::max(1, std::min(64, kProbePassBytes / row_bytes));
       a.tensors[a.n_tensors] = n;
-      a.tiles[a.n_tensors] = (O + kProbeTileRows - 1) / kProbeTileRows;
+      a.tile_rows[a.n_tensors] = tr;
+      a.tiles[a.n_tensors] = (O + tr - 1) / tr;
       per_e += a.tiles[a.n_tensors++];
     }
   a.waves = n_experts * per_e;

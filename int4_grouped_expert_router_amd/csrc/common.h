@@ -212,8 +212,8 @@ struct ProbeArgs {
   uint32_t *sink;            // 64 dwords, written only when the folded loads equal a constant
   int16_t experts[kRows];    // expert indices into tab
   int n_experts;
-  int tensors[3], tiles[3];  // tensor indices (0 gate, 1 up, 2 down) and their row tiles
-  int n_tensors, tile_rows, waves;
+  int tensors[3], tiles[3], tile_rows[3];  // tensor indices (0 gate, 1 up, 2 down), their tiles, rows per tile
+  int n_tensors, waves;
 };
 hipError_t launch_read_probe(const ProbeArgs &a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Column slices of a matrix-core launch (about two workgroups per CU) and its partial-sum floats.

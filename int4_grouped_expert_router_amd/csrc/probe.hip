@@ -3,9 +3,10 @@
 // The bandwidth a projection reaches is reported against HBM peak and against a plain read of
 // the same bytes on the same GPU (the figure the pages' grouped kernels are measured by is
 // expert-weight bytes per second).  k_read_probe reads every nibble and scale byte of the listed
-// experts' tensors and computes nothing: one wave per tile of 16 rows of one tensor, whose rows
-// are one contiguous block of the nibble array (and one of the scale array), streamed with eight
-// 16-byte loads per lane in flight.  The loaded words are folded into one value that is stored
+// experts' tensors and computes nothing: one wave per tile of rows of one tensor (about 16 KB of
+// nibbles: 4 rows of 3.5 KB, 16 of 1 KB), whose rows are one contiguous block of the nibble array
+// (and one of the scale array), streamed with sixteen 16-byte loads per lane in flight (16 KB
+// per wave pass).  The loaded words are folded into one value that is stored
 // only if it equals a constant, so the loads stay live and every store stays in bounds whatever
 // the data.
 #include <hip/hip_ext.h>
@@ -15,7 +16,7 @@
 namespace i4moe {
 namespace {
 
-constexpr int kProbeLoads = 8;               // 16-byte loads per lane in flight
+constexpr int kProbeLoads = 16;              // 16-byte loads per lane in flight
 constexpr int kFarOffset = 0x7ffffff0;       // past every buffer range: reads zero, no access
 
 __global__ __launch_bounds__(kBlock) void k_read_probe(ProbeArgs a) {
@@ -32,7 +33,8 @@ __global__ __launch_bounds__(kBlock) void k_read_probe(ProbeArgs a) {
   const uint8_t *q = d.q;
   const float *sc = d.s;
   const int O = d.O, row_bytes = d.row_bytes, ng = d.ng;
-  const int r0 = rem * a.tile_rows, r1 = min(r0 + a.tile_rows, O);
+  const int tr = a.tile_rows[ni];
+  const int r0 = rem * tr, r1 = min(r0 + tr, O);
   // the tile's bytes: nibbles [r0, r1) x row_bytes, then scales [r0, r1) x ng x 4
   const int qb = r0 * row_bytes, qe = r1 * row_bytes;
   const int sb = r0 * ng * 4, se = r1 * ng * 4;
@@ -71,9 +73,10 @@ __global__ __launch_bounds__(kBlock) void k_read_probe(ProbeArgs a) {
 }  // namespace
 
 hipError_t launch_read_probe(const ProbeArgs &a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
-  if (a.n_experts < 1 || a.n_experts > kRows || a.n_tensors < 1 || a.n_tensors > 3 || a.tile_rows < 1 || a.waves < 1 ||
-      !a.tab || !a.sink)
+  if (a.n_experts < 1 || a.n_experts > kRows || a.n_tensors < 1 || a.n_tensors > 3 || a.waves < 1 || !a.tab || !a.sink)
     return hipErrorInvalidValue;
+  for (int n = 0; n < a.n_tensors; ++n)
+    if (a.tile_rows[n] < 1 || a.tiles[n] < 1) return hipErrorInvalidValue;
   const dim3 grid((a.waves + kBlock / kWave - 1) / (kBlock / kWave));
   if (t0 || t1)
     hipExtLaunchKernelGGL(k_read_probe, grid, dim3(kBlock), 0, st, t0, t1, 0, a);
