@@ -161,3 +161,35 @@ def test_tiered_errors_leave_nothing_pending():
     delta, _ = layer_delta_threads(rs, lambda e: gen_expert(cfg, 0, e), x64)
     for t in range(cfg.S):
         assert normwise_err(out.cpu().numpy()[t], delta[t]) < TOL
+
+
+def test_tiered_host_paths(monkeypatch):
+    """The CPU rows of a tiered issue on each host path: the integer path at 512 and at 256 bits
+    give the same bits, and the float32 path (I4MOE_HOST_INT=0) is within the bar of the oracle."""
+    from int4_grouped_expert_router_amd import binding as B
+    base, over = CASES["mix_f32"]
+    cfg = get_config(base, layers=1, **over)
+    L = make_layer(cfg, 0)
+    on_host = set(range(1, cfg.E, 2))
+    ctx = new_ctx()
+    bind(ctx, cfg, L, on_host)
+    x = x_to_device(L.x, L.x_dtype)
+    outs = {}
+    for path in ("default", "256", "0"):
+        print(f"[tier] host path {path}", flush=True)
+        if path == "default":
+            monkeypatch.delenv("I4MOE_HOST_INT", raising=False)
+        else:
+            monkeypatch.setenv("I4MOE_HOST_INT", path)
+        rec, n, times, outs[path] = run_tiered(ctx, cfg, L, x)
+        assert times.host_rows > 0
+    monkeypatch.delenv("I4MOE_HOST_INT", raising=False)
+    ctx.close()
+    if B.i4moe_host_int_path():
+        assert np.array_equal(outs["default"], outs["256"])
+    routes = gpu_routes(rec, cfg.S, cfg.K)
+    x64 = oracle.widen_activations(L.x, L.x_dtype)
+    delta, _ = layer_delta_threads(routes, lambda e: gen_expert(cfg, 0, e), x64)
+    for path, out in outs.items():
+        for t in range(cfg.S):
+            assert normwise_err(out[t], delta[t]) < TOL, (path, t)
