@@ -13,8 +13,9 @@
 // and scaled (a group-wise tensor's group scale, group sizes being multiples of 64; a per-row
 // tensor's row scale after the last step).  The result is (join) 2^-E / 16.
 //
-// Tiling: a workgroup of four waves owns 64 weight rows (one 16-row tile per wave) x every
-// 16-row token tile of one entry (an expert's group rows) x one slice of the columns; the slices
+// Tiling: a workgroup of eight waves owns 64 weight rows x every 16-row token tile of one entry
+// (an expert's group rows) x one slice of the columns; wave (w, h) takes weight tile w (16 rows)
+// against token tiles 2 h and 2 h + 1, so each SIMD holds two waves of the stage.  The slices
 // spread an entry over about two workgroups per CU.  Each stage (two steps of 64 columns: the
 // weight rows and the digit rows) is loaded by the whole workgroup with 16-byte loads into LDS
 // while the previous stage computes.  A slice's partial sums go to memory and a second launch
@@ -165,14 +166,16 @@ __device__ __forceinline__ void big_entry(const GroupBuf *grp, int mfma_min, int
 // LDS stage: kCh steps of 64 columns.  Weight rows of 32 bytes per step, digit rows of 64 bytes
 // per step and digit; rows padded so that the 16 rows one MFMA operand reads fall in distinct
 // banks.
-constexpr int kMW = 4;                       // waves per workgroup: one 16-row weight tile each
+constexpr int kMW = 4;                       // weight tiles per workgroup (16 rows each)
+constexpr int kMHalves = 2;                  // waves per weight tile: token tiles 0-1 and 2-3
+constexpr int kMThreads = kMW * kMHalves * kWave;
 constexpr int kMRows = 16 * kMW;             // weight rows per workgroup
 constexpr int kCh = 2;                       // steps per stage
 constexpr int kWRow = kCh * 32 + 8;          // LDS bytes per weight row
 constexpr int kXRow = kDigits * kCh * 64 + 16;  // LDS bytes per activation row (3 digits)
-constexpr int kXLoads = 64 * kDigits * kCh * 64 / 16 / (kMW * kWave);  // 16-byte loads per thread
-static_assert(kMRows * kCh * 32 / 16 == kMW * kWave, "one 16-byte weight load per thread and tensor");
-static_assert(kXLoads * kMW * kWave * 16 == 64 * kDigits * kCh * 64, "digit rows split evenly");
+constexpr int kXLoads = 64 * kDigits * kCh * 64 / 16 / kMThreads;  // 16-byte loads per thread
+static_assert(kMRows * kCh * 32 / 16 * 2 == kMThreads, "one 16-byte weight load per thread (two tensors)");
+static_assert(kXLoads * kMThreads * 16 == 64 * kDigits * kCh * 64, "digit rows split evenly");
 
 template <int NT>
 constexpr int stage_bytes() {
@@ -183,9 +186,8 @@ constexpr size_t mfma_lds_bytes() {
   return 2 * (size_t)stage_bytes<NT>();
 }
 
-template <int NT>
 struct MLoads {
-  u32x4 w[NT];
+  u32x4 w;  // tensor tid / 256 (when there is one)
   u32x4 x[kXLoads];
   float sc;
 };
@@ -198,11 +200,13 @@ struct MLoads {
 // ACC: every tensor of the launch is per-row, so each digit's sums accumulate in int32 over the
 // whole slice (at most 2^20 per step, 2^27 over kMaxCols columns) and are joined once at the end.
 template <int NT, bool ACC>
-__global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
+__global__ __launch_bounds__(kMThreads) void k_mfma(MfmaArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
   __shared__ int s_drow[64];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wave: weight tile w, token tiles 2 th and 2 th + 1
+  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & (kMW - 1));
+  const int th = __builtin_amdgcn_readfirstlane(tid >> 8);
   // blocks: (slot, weight block, column slice), slice fastest; one XCD takes a contiguous run,
   // so the slices of a weight block share an L2 for the digit rows
   const int L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
@@ -241,14 +245,15 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
     sr[n] = rsrc(T[n].s, O * T[n].ng * 4);
   }
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.dig, a.dig_rows * kDigits * a.C64);
-  // this thread's loads: weight row tid / 4, 16-byte chunk tid % 4 (every tensor); digit loads
-  // j: activation row m, digit d, chunk c of the stage's 128 bytes; one scale (thread < NT x 128)
-  const int wrow = tid >> 2, wch = tid & 3;
-  const bool w_ok = o0 + wrow < O;
+  // this thread's loads: tensor wn = tid / 256, weight row (tid % 256) / 4, 16-byte chunk tid % 4;
+  // digit loads j: activation row m, digit d, chunk c of the stage's 128 bytes; one scale
+  // (thread < NT x 128)
+  const int wn = tid >> 8, wrow = (tid & 255) >> 2, wch = tid & 3;
+  const bool w_ok = wn < NT && o0 + wrow < O;
   int xbase[kXLoads], xlds[kXLoads];
 #pragma unroll
   for (int j = 0; j < kXLoads; ++j) {
-    const int idx = tid + j * kMW * kWave;
+    const int idx = tid + j * kMThreads;
     const int m = idx / (kDigits * kCh * 4), rem = idx % (kDigits * kCh * 4);
     const int d = rem / (kCh * 4), c = rem % (kCh * 4);
     const int dr = s_drow[m];
@@ -260,13 +265,14 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   const int srow = (tid / kCh) % kMRows, sc_c = tid % kCh;
   const int sn_c = sn < NT ? sn : 0;
   const bool s_ok = sn < NT && o0 + srow < O;
-  auto load = [&](MLoads<NT> &r, int s0) {  // the stage starting at step s0
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
+  auto load = [&](MLoads &r, int s0) {  // the stage starting at step s0
+    {
       // a stage may reach up to 48 bytes past a row's padded end: the next row's first bytes (or
       // the tensor's 64-byte tail slack), multiplied by zero digits (columns C and up) or unused
-      const int off = w_ok ? (o0 + wrow) * T[n].row_bytes + 32 * s0 + 16 * wch : kFar;
-      r.w[n] = __builtin_amdgcn_raw_buffer_load_b128(wr[n], off, 0, kNontemporal);
+      const bool second = NT == 2 && (wn & 1);  // no indexing of T by a runtime value (keeps it in registers)
+      const int rb = second ? T[1 % NT].row_bytes : T[0].row_bytes;
+      const int off = w_ok ? (o0 + wrow) * rb + 32 * s0 + 16 * wch : kFar;
+      r.w = __builtin_amdgcn_raw_buffer_load_b128(second ? wr[1 % NT] : wr[0], off, 0, kNontemporal);
     }
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j)
@@ -281,11 +287,9 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
       r.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0));
     }
   };
-  auto store = [&](const MLoads<NT> &r, int stage) {
+  auto store = [&](const MLoads &r, int stage) {
     uint8_t *base = s_lds + stage * stage_bytes<NT>();
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<u32x4 *>(base + n * kMRows * kWRow + wrow * kWRow + 16 * wch) = r.w[n];
+    if (wn < NT) *reinterpret_cast<u32x4 *>(base + wn * kMRows * kWRow + wrow * kWRow + 16 * wch) = r.w;
     uint8_t *xb = base + NT * kMRows * kWRow;
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) *reinterpret_cast<u32x4 *>(xb + xlds[j]) = r.x[j];
@@ -296,17 +300,17 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   // Every step's three digit products start from zero and are joined into F at once: the
   // step's scale (group-wise) or 1 (per-row, its row scale applied after the last step).  Low
   // digits first in int32 (|r| <= 2^20 per step, so r1 * 256 + r0 is exact), then one float.
-  float F[4][NT][4];
+  float F[2][NT][4];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int v = 0; v < 4; ++v) F[tt][n][v] = 0.f;
   // ACC: the digit sums of the slice, digit d of tensor n and token tile tt
-  v4i I[ACC ? 4 : 1][NT][kDigits];
+  v4i I[ACC ? 2 : 1][NT][kDigits];
 #pragma unroll
-  for (int tt = 0; tt < (ACC ? 4 : 1); ++tt)
+  for (int tt = 0; tt < (ACC ? 2 : 1); ++tt)
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -337,12 +341,13 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) sc[n] = (!ACC && grp[n]) ? scb[(n * kMRows + 16 * w + li) * kCh + cs] : 1.f;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tt < TT) {
+      for (int tt = 0; tt < 2; ++tt) {
+        if (2 * th + tt < TT) {
           v4i A[kDigits];
 #pragma unroll
           for (int d = 0; d < kDigits; ++d)
-            A[d] = *reinterpret_cast<const v4i *>(xb + (16 * tt + li) * kXRow + d * (kCh * 64) + cs * 64 + 16 * q);
+            A[d] = *reinterpret_cast<const v4i *>(xb + (16 * (2 * th + tt) + li) * kXRow + d * (kCh * 64) + cs * 64 +
+                                                  16 * q);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             if constexpr (ACC) {
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   };
 
   // stages over this slice: load stage i + 1 while stage i computes
-  MLoads<NT> r;
+  MLoads r;
   if (k0 < k1) {
     load(r, k0);
     store(r, 0);
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   if constexpr (ACC) {
     // the slice's digit sums joined once (exactly, in double), one rounding to f32
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -397,20 +402,20 @@ __global__ __launch_bounds__(kMW * kWave) void k_mfma(MfmaArgs a) {
   for (int n = 0; n < NT; ++n)
     if (ACC || !grp[n])
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) F[tt][n][v] *= srow_s[n];
-  // partial sums of this slice: lane (li, q), element v = activation row 16 tt + 4 q + v,
+  // partial sums of this slice: lane (li, q), element v = activation row 16 (2 th + tt) + 4 q + v,
   // weight row o0 + 16 w + li
   const int o = o0 + 16 * w + li;
   if (o < O) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = 16 * tt + 4 * q + v;
+          const int m = 16 * (2 * th + tt) + 4 * q + v;
           if (m < size)
             a.part[((((size_t)ks * NT + n) * a.slots + slot) * 64 + m) * O + o] = F[tt][n][v];
         }
@@ -552,8 +557,8 @@ hipError_t launch_mfma(int NT, MfmaArgs a, hipStream_t st, hipEvent_t t0, hipEve
   hipError_t e = raise_lds_once(k, (int)lds, raised[NT - 1][acc]);
   if (e != hipSuccess) return e;
   void *params[] = {&a};
-  e = (t0) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st, t0, nullptr, 0)
-           : hipLaunchKernel(k, dim3(blocks), dim3(kMW * kWave), params, lds, st);
+  e = (t0) ? hipExtLaunchKernel(k, dim3(blocks), dim3(kMThreads), params, lds, st, t0, nullptr, 0)
+           : hipLaunchKernel(k, dim3(blocks), dim3(kMThreads), params, lds, st);
   if (e != hipSuccess) return e;
   // the reduction, with as many slice loads in flight as the smallest power of two >= ksplit
   const int kb = a.ksplit <= 4 ? 0 : a.ksplit <= 8 ? 1 : a.ksplit <= 16 ? 2 : 3;
