@@ -1690,13 +1690,11 @@ static int tier_buffers(i4moe_ctx *c) {
     c->ev_p = nullptr;
     return hip_fail(c, e, "hipEventCreate");
   }
-  if (!c->pool) {
-    c->pool.reset(new (std::nothrow) HostPool(c->host_threads));
-    if (!c->pool) return fail(c, I4MOE_ENOMEM, "host worker pool");
-  }
-  if (!c->helper) {
-    c->helper.reset(new (std::nothrow) HostHelper());
-    if (!c->helper) return fail(c, I4MOE_ENOMEM, "host helper thread");
+  try {  // thread creation can throw
+    if (!c->pool) c->pool.reset(new HostPool(c->host_threads));
+    if (!c->helper) c->helper.reset(new HostHelper());
+  } catch (const std::exception &) {
+    return fail(c, I4MOE_ENOMEM, "host worker threads");
   }
   return I4MOE_OK;
 }
@@ -1764,6 +1762,7 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
   // The host rows start on the helper thread as soon as x has landed, while this thread issues
   // the device group (its host-side work and launches overlap them too).
   hipError_t host_err = hipSuccess;
+  bool host_oom = false;
   auto t_x = clk::now(), t_cpu = t_x;
   if (host) {
     // the previous tiered issue's upload of the host sum must have read it
@@ -1773,18 +1772,22 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
       host_err = hipEventSynchronize(c->ev_x);
       t_x = clk::now();
       if (host_err != hipSuccess) return;
-      std::vector<float> xf((size_t)S * D);
-      if (dtype == I4MOE_DTYPE_F32) {
-        std::memcpy(xf.data(), c->h_x, sizeof(float) * xf.size());
-      } else {
-        const uint16_t *xb = static_cast<const uint16_t *>(c->h_x);
-        for (size_t i = 0; i < xf.size(); ++i) {
-          const uint32_t u = (uint32_t)xb[i] << 16;
-          std::memcpy(&xf[i], &u, 4);
+      try {  // host allocations can throw; nothing may escape the helper thread
+        std::vector<float> xf((size_t)S * D);
+        if (dtype == I4MOE_DTYPE_F32) {
+          std::memcpy(xf.data(), c->h_x, sizeof(float) * xf.size());
+        } else {
+          const uint16_t *xb = static_cast<const uint16_t *>(c->h_x);
+          for (size_t i = 0; i < xf.size(); ++i) {
+            const uint32_t u = (uint32_t)xb[i] << 16;
+            std::memcpy(&xf[i], &u, 4);
+          }
         }
+        std::memset(c->h_P, 0, sizeof(float) * (size_t)S * D);
+        host_rows_forward(*c->pool, hrows, xf.data(), D, I, c->h_P);
+      } catch (const std::exception &) {
+        host_oom = true;
       }
-      std::memset(c->h_P, 0, sizeof(float) * (size_t)S * D);
-      host_rows_forward(*c->pool, hrows, xf.data(), D, I, c->h_P);
       t_cpu = clk::now();
     });
   }
@@ -1804,6 +1807,10 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
     if (host_err != hipSuccess) {
       if (dev) c->poisoned = true;  // the device slot is issued but the host rows would be lost
       return hip_fail(c, host_err, "wait for x");
+    }
+    if (host_oom) {
+      if (dev) c->poisoned = true;
+      return fail(c, I4MOE_ENOMEM, "host rows: host memory");
     }
     // the host slot: one row per token, weight 1, holding the token's sum of host rows
     const int s = c->nslots;

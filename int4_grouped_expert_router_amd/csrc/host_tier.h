@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <condition_variable>
+#include <exception>
 #include <functional>
 #include <mutex>
 #include <stdint.h>
@@ -30,7 +31,8 @@ struct HostExpert {
 
 // Fixed worker threads.  run(n, fn) splits [0, n) into one contiguous range per thread (the same
 // split every time for the same n and thread count) and returns when all ranges are done; each
-// index is handled by exactly one thread, so per-index results never depend on timing.  Between
+// index is handled by exactly one thread, so per-index results never depend on timing.  An
+// exception thrown by a range is rethrown by run() on the calling thread once every range is done.  Between
 // runs a worker polls for the next one for about kSpinMicros before it sleeps, so the phases of
 // one computation follow each other without a wake-up through the kernel.
 class HostPool {
@@ -56,6 +58,7 @@ class HostPool {
   std::atomic<unsigned> gen_{0}, wake_{0};
   std::atomic<int> pending_{0}, sleepers_{0};
   std::atomic<bool> stop_{false};
+  std::exception_ptr error_;  // the first exception a worker's range threw in the current run
 };
 
 // One job at a time on a thread of its own: post(fn) hands fn over and returns at once, wait()

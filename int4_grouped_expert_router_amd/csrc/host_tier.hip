@@ -11,7 +11,17 @@
 namespace i4moe {
 
 HostPool::HostPool(int threads) {
-  for (int i = 1; i < threads; ++i) workers_.emplace_back([this, i] { work(i); });
+  try {
+    for (int i = 1; i < threads; ++i) workers_.emplace_back([this, i] { work(i); });
+  } catch (...) {  // a thread that could not start: stop and join the ones that did
+    {
+      std::lock_guard<std::mutex> lk(m_);
+      stop_.store(true);
+    }
+    go_.notify_all();
+    for (auto &t : workers_) t.join();
+    throw;
+  }
 }
 
 HostPool::~HostPool() {
@@ -49,7 +59,12 @@ void HostPool::work(int id) {
     seen = g;
     const long T = threads();
     const long n = n_;
-    (*fn_)(n * id / T, n * (id + 1) / T);
+    try {
+      (*fn_)(n * id / T, n * (id + 1) / T);
+    } catch (...) {  // handed to run(), which rethrows it on the calling thread
+      std::lock_guard<std::mutex> lk(m_);
+      if (!error_) error_ = std::current_exception();
+    }
     pending_.fetch_sub(1);
   }
 }
@@ -70,14 +85,22 @@ void HostPool::run(long n, const std::function<void(long, long)> &fn) {
   }
   fn_ = &fn;
   n_ = n;
+  error_ = nullptr;
   pending_.store((int)workers_.size());
   gen_.fetch_add(1);  // publishes fn_ and n_ (sequentially consistent)
   if (sleepers_.load() > 0) {
     std::lock_guard<std::mutex> lk(m_);
     go_.notify_all();
   }
-  fn(0, n / threads());  // the calling thread takes range 0
+  std::exception_ptr mine;
+  try {
+    fn(0, n / threads());  // the calling thread takes range 0
+  } catch (...) {
+    mine = std::current_exception();
+  }
   while (pending_.load() != 0) _mm_pause();
+  if (mine) std::rethrow_exception(mine);
+  if (error_) std::rethrow_exception(error_);
 }
 
 HostHelper::HostHelper() {
