@@ -513,7 +513,7 @@ void gemv_geometry(const Layer &L, RouteArgs &a) {
 
 extern "C" {
 
-int i4moe_ctx_create(int device, i4moe_ctx **out) {
+int i4moe_ctx_create(int device, i4moe_ctx **out) try {
   if (!out) return I4MOE_EINVAL;
   *out = nullptr;
   int n = 0;
@@ -586,9 +586,11 @@ int i4moe_ctx_create(int device, i4moe_ctx **out) {
   }
   *out = c;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_ctx_destroy(i4moe_ctx *c) {
+int i4moe_ctx_destroy(i4moe_ctx *c) try {
   if (!c) return I4MOE_OK;
   ensure_device(c);
   (void)hipStreamSynchronize(c->stream);
@@ -628,23 +630,29 @@ int i4moe_ctx_destroy(i4moe_ctx *c) {
   (void)hipGetLastError();
   delete c;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_set_stream(i4moe_ctx *c, void *stream) {
+int i4moe_set_stream(i4moe_ctx *c, void *stream) try {
   if (!c) return I4MOE_EINVAL;
   ensure_device(c);
   if (int rc = flush_all(c)) return rc;
   c->stream = reinterpret_cast<hipStream_t>(stream);
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-const char *i4moe_last_error(const i4moe_ctx *c) {
+const char *i4moe_last_error(const i4moe_ctx *c) try {
   if (!c) return "no context";
   return c->err.c_str();
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return "host memory exhausted";
 }
 
 i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, int C, const uint8_t *packed,
-                                        const float *scales) {
+                                        const float *scales) try {
   if (!c) return 0;
   if (fmt != I4MOE_FMT_ROW && fmt != I4MOE_FMT_GROUP) {
     fail(c, I4MOE_EUNSUPPORTED, "unsupported weight format %d (only 2 = per-row and 4 = group-wise int4)", fmt);
@@ -731,9 +739,11 @@ i4moe_tensor i4moe_upload_expert_tensor(i4moe_ctx *c, int fmt, int gs, int O, in
   const uint32_t h = c->next_handle++;
   c->tensors[h] = t;
   return h;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return 0;
 }
 
-int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
+int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) try {
   if (!c) return I4MOE_EINVAL;
   auto it = c->tensors.find(h);
   if (it == c->tensors.end()) return fail(c, I4MOE_EINVAL, "unknown tensor handle %u", h);
@@ -768,9 +778,11 @@ int i4moe_tensor_free(i4moe_ctx *c, i4moe_tensor h) {
   dfree(it->second.s);
   c->tensors.erase(it);
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
+int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) try {
   if (!c) return I4MOE_EINVAL;
   ensure_device(c);
   if (int rc = flush_all(c)) return rc;
@@ -809,9 +821,11 @@ int i4moe_set_expert(i4moe_ctx *c, int layer, int expert, i4moe_tensor gate, i4m
   // plan its launch from the new ones): the layer has to be routed again.
   L.routed = false;
   return write_table_entry(c, L, expert);
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, const float *bias) {
+int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, const float *bias) try {
   if (!c) return I4MOE_EINVAL;
   if (layer < 0 || E < 1 || E > kMaxE || D < 1 || !W) return fail(c, I4MOE_EINVAL, "bad router arguments");
   if ((size_t)E * D > ((size_t)1 << 28)) return fail(c, I4MOE_EUNSUPPORTED, "router too large");
@@ -857,6 +871,8 @@ int i4moe_upload_router(i4moe_ctx *c, int layer, int E, int D, const float *W, c
   L.D = D;
   L.routed = false;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // The compute entry points are the fault hook's gate and call count around these bodies; a
@@ -933,17 +949,19 @@ static int route_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
 }
 
 int i4moe_route(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
-                float routed_scale, i4moe_route_host *host_out) {
+                float routed_scale, i4moe_route_host *host_out) try {
   if (!c) return I4MOE_EINVAL;
   int rc = gate_compute(c);
   if (rc) return rc;
   rc = route_impl(c, layer, x_dev, dtype, S, K, topp, norm_topk, routed_scale, host_out);
   if (rc == I4MOE_OK) c->calls++;
   return rc;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 int i4moe_route_noalloc(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, int K, float topp, int norm_topk,
-                        float routed_scale, i4moe_route_host *route_dev) {
+                        float routed_scale, i4moe_route_host *route_dev) try {
   if (!c) return I4MOE_EINVAL;
   int rc = gate_compute(c);
   if (rc) return rc;
@@ -992,6 +1010,8 @@ int i4moe_route_noalloc(i4moe_ctx *c, int layer, const void *x_dev, int dtype, i
   if (e != hipSuccess) return hip_fail(c, e, "route launch");
   c->calls++;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // allow_shared: the group may name the layer's shared expert (kShared).
@@ -1249,13 +1269,15 @@ static int issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int
   return s;
 }
 
-int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group) {
+int i4moe_expert_group_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_group *group) try {
   if (!c) return I4MOE_EINVAL;
   int rc = gate_compute(c);
   if (rc) return rc;
   rc = issue_impl(c, layer, x_dev, dtype, S, group, false);
   if (rc >= 0) c->calls++;
   return rc;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // A failure here poisons the context (the routed experts would be dropped silently).
@@ -1311,7 +1333,7 @@ static int take_impl(i4moe_ctx *c, float *residual_dev, int S) {
   return I4MOE_OK;
 }
 
-int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
+int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) try {
   if (!c) return I4MOE_EINVAL;
   if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
   int rc = gate_compute(c);
@@ -1322,9 +1344,11 @@ int i4moe_expert_group_take(i4moe_ctx *c, float *residual_dev, int S) {
   rc = take_impl(c, residual_dev, S);
   if (rc == I4MOE_OK) c->calls++;
   return rc;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_set_shared_expert(i4moe_ctx *c, int layer, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) {
+int i4moe_set_shared_expert(i4moe_ctx *c, int layer, i4moe_tensor gate, i4moe_tensor up, i4moe_tensor down) try {
   if (!c) return I4MOE_EINVAL;
   ensure_device(c);
   if (int rc = flush_all(c)) return rc;
@@ -1353,9 +1377,11 @@ int i4moe_set_shared_expert(i4moe_ctx *c, int layer, i4moe_tensor gate, i4moe_te
   L.h_tab[kShared].t[1] = U;
   L.h_tab[kShared].t[2] = Dn;
   return write_table_entry(c, L, kShared);
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_upload_norm(i4moe_ctx *c, int layer, int D, const float *gamma, float eps) {
+int i4moe_upload_norm(i4moe_ctx *c, int layer, int D, const float *gamma, float eps) try {
   if (!c) return I4MOE_EINVAL;
   if (layer < 0 || D < 1 || !gamma) return fail(c, I4MOE_EINVAL, "bad norm arguments");
   if (!std::isfinite(eps) || eps < 0.f) return fail(c, I4MOE_EINVAL, "eps must be finite and >= 0");
@@ -1379,6 +1405,8 @@ int i4moe_upload_norm(i4moe_ctx *c, int layer, int D, const float *gamma, float 
   L.eps = eps;
   if (!L.D) L.D = D;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // The block's normalised rows, [kTokens][D] of float32 (bf16 uses half of it).  Grows only with
@@ -1415,7 +1443,7 @@ static int rmsnorm_impl(i4moe_ctx *c, const Layer &L, const float *x_dev, int ld
 }
 
 int i4moe_rmsnorm(i4moe_ctx *c, int layer, const float *x_dev, int ld_x, int S, void *out_dev, int ld_out,
-                  int out_dtype) {
+                  int out_dtype) try {
   if (!c) return I4MOE_EINVAL;
   int rc = gate_compute(c);
   if (rc) return rc;
@@ -1432,6 +1460,8 @@ int i4moe_rmsnorm(i4moe_ctx *c, int layer, const float *x_dev, int ld_x, int S, 
   rc = rmsnorm_impl(c, *L, x_dev, ld_x, S, out_dev, ld_out, out_dtype);
   if (rc == I4MOE_OK) c->calls++;
   return rc;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // The shared expert's group: one row per token, weight 1, listed in token order.
@@ -1450,17 +1480,19 @@ static int shared_issue_impl(i4moe_ctx *c, int layer, const void *x_dev, int dty
   return issue_impl(c, layer, x_dev, dtype, S, &g, true);
 }
 
-int i4moe_shared_expert_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S) {
+int i4moe_shared_expert_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S) try {
   if (!c) return I4MOE_EINVAL;
   int rc = gate_compute(c);
   if (rc) return rc;
   rc = shared_issue_impl(c, layer, x_dev, dtype, S);
   if (rc >= 0) c->calls++;
   return rc;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act_dtype, int K, float topp,
-                    int norm_topk, float routed_scale) {
+                    int norm_topk, float routed_scale) try {
   if (!c) return I4MOE_EINVAL;
   if (c->poisoned) return fail(c, I4MOE_EPOISONED, "context poisoned by a failed take");
   int rc = gate_compute(c);
@@ -1507,16 +1539,20 @@ int i4moe_moe_block(i4moe_ctx *c, int layer, float *residual_dev, int S, int act
   }
   c->calls++;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_set_fail_after(i4moe_ctx *c, long long n) {
+int i4moe_set_fail_after(i4moe_ctx *c, long long n) try {
   if (!c) return I4MOE_EINVAL;
   c->fail_after = n < 0 ? -1 : n;
   c->calls = 0;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-size_t i4moe_debug_size(i4moe_ctx *c, int what, int index) {
+size_t i4moe_debug_size(i4moe_ctx *c, int what, int index) try {
   if (!c) return 0;
   switch (what) {
     case I4MOE_TAP_LOGITS:
@@ -1536,9 +1572,11 @@ size_t i4moe_debug_size(i4moe_ctx *c, int what, int index) {
     default:
       return 0;
   }
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return 0;
 }
 
-int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t bytes) {
+int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t bytes) try {
   if (!c || !host_dst) return I4MOE_EINVAL;
   const size_t need = i4moe_debug_size(c, what, index);
   if (need == 0 || bytes != need) return fail(c, I4MOE_EINVAL, "tap %d/%d: need %zu bytes, got %zu", what, index, need, bytes);
@@ -1562,6 +1600,8 @@ int i4moe_debug_read(i4moe_ctx *c, int what, int index, void *host_dst, size_t b
   }
   if (e != hipSuccess) return hip_fail(c, e, "tap copy");
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 // ---- the CPU tier ----------------------------------------------------------------------------
@@ -1591,7 +1631,7 @@ static int host_tensor_copy(i4moe_ctx *c, const i4moe_host_tensor *h, const char
 
 int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const float *weight,
                     const i4moe_host_tensor *gate, const i4moe_host_tensor *up, const i4moe_host_tensor *down,
-                    const float *x, float *P, int threads) {
+                    const float *x, float *P, int threads) try {
   if (S < 1 || D < 2 || I < 2 || n_rows < 0 || threads < 1 || threads > 256 || !x || !P) return I4MOE_EINVAL;
   if (n_rows > 0 && (!token || !weight || !gate || !up || !down)) return I4MOE_EINVAL;
   std::vector<HostExpert> ex;
@@ -1644,12 +1684,14 @@ int i4moe_host_rows(int S, int D, int I, int n_rows, const int32_t *token, const
     return I4MOE_ENOMEM;
   }
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 int i4moe_host_int_path(void) { return host_int_path_available() ? 1 : 0; }
 
 int i4moe_set_host_expert(i4moe_ctx *c, int layer, int expert, const i4moe_host_tensor *gate,
-                          const i4moe_host_tensor *up, const i4moe_host_tensor *down) {
+                          const i4moe_host_tensor *up, const i4moe_host_tensor *down) try {
   if (!c) return I4MOE_EINVAL;
   if (layer < 0 || expert < 0 || expert >= kMaxE) return fail(c, I4MOE_EINVAL, "bad layer %d / expert %d", layer, expert);
   std::unique_ptr<HostExpert> he(new (std::nothrow) HostExpert());
@@ -1669,6 +1711,8 @@ int i4moe_set_host_expert(i4moe_ctx *c, int layer, int expert, const i4moe_host_
   L.host_I = I;
   L.host[expert] = std::move(he);
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 static int tier_buffers(i4moe_ctx *c) {
@@ -1700,7 +1744,7 @@ static int tier_buffers(i4moe_ctx *c) {
 }
 
 int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, int S, const i4moe_route_host *routes,
-                       i4moe_tier_times *times) {
+                       i4moe_tier_times *times) try {
   if (!c) return I4MOE_EINVAL;
   using clk = std::chrono::steady_clock;
   const auto t_start = clk::now();
@@ -1863,9 +1907,11 @@ int i4moe_tiered_issue(i4moe_ctx *c, int layer, const void *x_dev, int dtype, in
     times->host_rows = (int32_t)hrows.size();
   }
   return issued;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_read_probe(i4moe_ctx *c, int layer, int tensor_mask, int n_experts, const int32_t *experts) {
+int i4moe_read_probe(i4moe_ctx *c, int layer, int tensor_mask, int n_experts, const int32_t *experts) try {
   if (!c) return I4MOE_EINVAL;
   Layer *L = find_layer(c, layer);
   if (!L || !L->D || !L->I || !L->d_tab) return fail(c, I4MOE_EINVAL, "layer %d has no experts", layer);
@@ -1905,9 +1951,11 @@ int i4moe_read_probe(i4moe_ctx *c, int layer, int tensor_mask, int n_experts, co
     return launch_read_probe(a, c->stream, t0, t1);
   });
   return e != hipSuccess ? hip_fail(c, e, "read probe launch") : I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_set_profiling(i4moe_ctx *c, int on) {
+int i4moe_set_profiling(i4moe_ctx *c, int on) try {
   if (!c) return I4MOE_EINVAL;
   ensure_device(c);
   (void)hipStreamSynchronize(c->stream);
@@ -1918,15 +1966,19 @@ int i4moe_set_profiling(i4moe_ctx *c, int on) {
   }
   c->profiling = on != 0;
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
-int i4moe_profile_query(i4moe_ctx *c, int kernel, double *total_ms, long long *launches) {
+int i4moe_profile_query(i4moe_ctx *c, int kernel, double *total_ms, long long *launches) try {
   if (!c || kernel < 0 || kernel >= I4MOE_K_COUNT) return I4MOE_EINVAL;
   ensure_device(c);
   drain_profile(c);
   if (total_ms) *total_ms = c->prof_ms[kernel];
   if (launches) *launches = c->prof_n[kernel];
   return I4MOE_OK;
+} catch (...) {  // nothing thrown (host allocation, thread start) crosses the C ABI
+  return I4MOE_ENOMEM;
 }
 
 }  // extern "C"
