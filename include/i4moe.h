@@ -67,7 +67,9 @@ enum { I4MOE_FMT_ROW = 2, I4MOE_FMT_GROUP = 4 };
 /* Activation dtypes. */
 enum { I4MOE_DTYPE_F32 = 0, I4MOE_DTYPE_BF16 = 1 };
 
-/* Status codes. */
+/* Status codes.  No C++ exception leaves a function of this interface: a host allocation or a
+ * worker thread that cannot be had returns I4MOE_ENOMEM (0 from the functions that return a
+ * handle or a size). */
 enum {
   I4MOE_OK = 0,
   I4MOE_EINVAL = -1,       /* bad argument, shape, handle or state                      */
